@@ -1,0 +1,63 @@
+"""Plant plausible mistakes in a copy of the oracle and require the pins to catch each.
+
+Every mutant is built on the CPU from a patched copy of oracle.c in a
+temporary directory; the pin suite then runs against it in a subprocess and
+must fail.  Nothing here touches a GPU.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+# (name, text in oracle.c, replacement) -- the first occurrence is replaced
+MUTANTS = [
+    ("mean divides by block size", "o[c] = s / (double)(t1 - t0);", "o[c] = s / (double)bs;"),
+    ("score sign", "cand[j - c0].s = s;", "cand[j - c0].s = -s;"),
+    ("tie-break reversed", "return (x->j > y->j) - (x->j < y->j);",
+     "return (x->j < y->j) - (x->j > y->j);"),
+    ("group drops heads", "for (int32_t h = (int32_t)kvh * g; h < (int32_t)kvh * g + g; ++h)",
+     "for (int32_t h = (int32_t)kvh * g; h < (int32_t)kvh * g + 1; ++h)"),
+    ("no 1/sqrt(d) scale", "z[t] = s * scale;", "z[t] = s;"),
+    ("softmax exponent sign", "z[t] = exp(z[t] - zmax);", "z[t] = exp(zmax - z[t]);"),
+    ("K and V swapped", "rows, rows, k, v, NULL, NULL, scale, z,\n                      out",
+     "rows, rows, v, k, NULL, NULL, scale, z,\n                      out"),
+    ("wrong GQA head map", "int64_t b = bh / Hq, h = bh % Hq, kvh = h / g;",
+     "int64_t b = bh / Hq, h = bh % Hq, kvh = h % Hkv;"),
+    ("local range off by one", "int32_t l_beg = nb - n_local > 0 ? nb - n_local : 0;",
+     "int32_t l_beg = nb - n_local - 1 > 0 ? nb - n_local - 1 : 0;"),
+    ("keep ratio rounded up", "floor(keep_ratio * (double)nb + 0.5)", "ceil(keep_ratio * (double)nb)"),
+    ("window off by one", "int32_t t0 = p - window + 1 > 0 ? p - window + 1 : 0;",
+     "int32_t t0 = p - window > 0 ? p - window : 0;"),
+    ("tile pools one query", "int32_t i1 = i0 + q_tile < C ? i0 + q_tile : C;",
+     "int32_t i1 = i0 + 1;"),
+    ("branch average", "(o[0][c] + o[1][c] + o[2][c]) / 3.0", "(o[0][c] + o[1][c] + o[2][c]) / 2.0"),
+    ("bf16 ties away from zero", "double ri = rint(s);", "double ri = floor(s + 0.5);"),
+    ("dense branch reads K as V", "E128, rk, rk, NULL, NULL, k128, v128,",
+     "E128, rk, rk, NULL, NULL, k128, k128,"),
+    ("lse drops the max", "return zmax + log(l);", "return log(l);"),
+    ("weights not normalised", "double p = z[t] / l;", "double p = z[t];"),
+    ("pooled query skips a dimension", "for (int32_t c = 0; c < d; ++c) qbar[c] += bf(q[(b * Hq + h)",
+     "for (int32_t c = 1; c < d; ++c) qbar[c] += bf(q[(b * Hq + h)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor missing: {old!r}"
+    mutated = src.replace(old, new, 1)
+    cfile = tmp_path / "oracle.c"
+    cfile.write_text(mutated)
+    (tmp_path / "oracle.h").write_text(open(os.path.join(ROOT, "oracle", "oracle.h")).read())
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                    str(cfile), "-o", str(lib), "-lm"], check=True)
+    env = dict(os.environ, BSA_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutant '{name}'\n{r.stdout[-2000:]}"

@@ -1,0 +1,495 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: figures
+printed on the pages, closed forms, brute force on tiny inputs, or special
+cases that reduce to a library routine (numpy means, torch's
+scaled_dot_product_attention in float64).  Inputs on an integer grid are used
+where exact arithmetic makes the expected value unambiguous.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_block_summary_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_counts.txt")
+
+
+def golden():
+    vals = {}
+    for line in open(GOLDEN, encoding="utf-8"):
+        if line.startswith("#") or not line.strip():
+            continue
+        key, val, kind, _cite = line.rstrip("\n").split("\t")
+        vals[key] = (float(val), kind)
+    return vals
+
+
+def bf(x):
+    """float array -> bf16 bits (values must be bf16-representable or get rounded)."""
+    return synth.bf16_round(np.asarray(x, np.float32))
+
+
+def f(h):
+    return synth.bf16_to_f32(h).astype(np.float64)
+
+
+def grid(rng, shape, lo=-4, hi=4, den=8):
+    """bf16-exact values on a coarse grid (integers / den)."""
+    return rng.integers(lo * den, hi * den + 1, size=shape).astype(np.float32) / den
+
+
+def sdpa(q, k, v, mask=None, scale=None):
+    """torch float64 SDPA; q [..., Lq, d], k/v [..., Lk, d]."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float64))
+    return torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=None if mask is None else torch.from_numpy(mask),
+        scale=scale).numpy()
+
+
+# ---------------------------------------------------------------- page figures
+
+def test_entry_counts_match_pages(orc):
+    g = golden()
+    for key, (val, kind) in g.items():
+        if not key.startswith("entries_m"):
+            continue
+        m = int(key[len("entries_m"):])
+        n = orc.num_blocks(1_000_000, m)
+        if kind == "exact":
+            assert n == int(val), key
+        else:  # the page prints a rounded figure
+            assert abs(n - val) <= 1, key
+    # a partial block still forms an entry
+    assert orc.num_blocks(1_000_000, 128) == 7813
+    assert orc.num_blocks(0, 64) == 0
+    assert orc.num_blocks(1, 64) == 1
+
+
+def test_block_parameters_match_page_table(orc):
+    g = golden()
+    assert g["block_size"][0] == 64
+    assert g["local_tokens"][0] == g["local_blocks"][0] * g["block_size"][0]
+    # with the table's parameters the fixed part of the kept set is 3 blocks
+    assert orc.num_kept(100, 1, 2, 0) == 3
+
+
+def test_keep_ratio_reproduces_workload_top_k(orc):
+    # the decode workloads quote both a keep ratio and a top-k; the reading
+    # total = floor(r*nb + 0.5), k = total - sink - local reproduces all three
+    for nb, r, k in [(512, 0.15, 74), (2048, 0.10, 202), (16384, 0.10, 1635)]:
+        assert orc.num_kept(nb, 1, 2, -1, r) == k + 3
+        assert orc.num_kept(nb, 1, 2, k) == k + 3
+    # the 15 % variant of the 128K workload
+    assert orc.num_kept(2048, 1, 2, -1, 0.15) == 307
+
+
+def test_small_contexts_keep_everything(orc):
+    for nb in range(0, 4):
+        assert orc.num_kept(nb, 1, 2, 10) == nb
+    assert orc.num_kept(4, 1, 2, 10) == 4
+    assert orc.num_kept(4, 1, 2, 0) == 3
+
+
+# ---------------------------------------------------------------- bf16 rounding
+
+def test_round_bf16_matches_torch_on_fp32_values(orc):
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(2000).astype(np.float32) * 10,
+                        np.float32([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8),
+                                    1e-39, 3.0, 0.0])])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    got = np.array([orc.round_bf16(float(v)) for v in x], np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_round_bf16_ties_to_even(orc):
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties to the even mantissa (1)
+    assert orc.round_bf16(1.0 + 2 ** -8) == 0x3F80
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6: ties to 1 + 2^-6
+    assert orc.round_bf16(1.0 + 3 * 2 ** -8) == 0x3F82
+    # just above a tie rounds up (the fp64 value is not first rounded to fp32)
+    assert orc.round_bf16(1.0 + 2 ** -8 + 2 ** -40) == 0x3F81
+
+
+# ---------------------------------------------------------------- summaries
+
+def test_summaries_equal_numpy_mean(orc):
+    rng = np.random.default_rng(1)
+    B, H, N, d, bs = 2, 3, 64 * 5 + 17, 16, 64
+    x = bf(rng.standard_normal((B, H, N, d)) * 3)
+    s = orc.block_summaries(x, N, bs)
+    xf = f(x)
+    nb = -(-N // bs)
+    assert s.shape == (B, H, nb, d)
+    for j in range(nb):
+        ref = xf[:, :, j * bs:min((j + 1) * bs, N)].mean(axis=2)
+        np.testing.assert_allclose(s[:, :, j], ref, rtol=0, atol=1e-13)
+
+
+def test_summaries_closed_forms(orc):
+    rng = np.random.default_rng(2)
+    d = 8
+    row = grid(rng, (d,))
+    x = np.tile(row, (1, 1, 128, 1)).astype(np.float32)
+    x[0, 0, 64:] = -row
+    s = orc.block_summaries(bf(x), 128, 64)
+    assert np.array_equal(s[0, 0, 0], row.astype(np.float64))   # identical rows -> that row
+    assert np.array_equal(s[0, 0, 1], -row.astype(np.float64))
+    # block size 1 is the identity
+    y = bf(rng.standard_normal((1, 2, 50, d)))
+    assert np.array_equal(orc.block_summaries(y, 50, 1), f(y))
+    # linearity on exact data: mean(a + b) = mean(a) + mean(b)
+    a = grid(rng, (1, 1, 256, d), -2, 2)
+    b = grid(rng, (1, 1, 256, d), -2, 2)
+    sa, sb, sab = (orc.block_summaries(bf(z), 256, 4) for z in (a, b, a + b))
+    np.testing.assert_allclose(sab, sa + sb, atol=1e-15)
+
+
+def test_summaries_ignore_tokens_past_seq_len(orc):
+    rng = np.random.default_rng(3)
+    x = bf(rng.standard_normal((1, 1, 200, 4)))
+    x2 = x.copy()
+    x2[:, :, 130:] = bf(np.full((1, 1, 70, 4), 1000.0))
+    assert np.array_equal(orc.block_summaries(x, 130, 64), orc.block_summaries(x2, 130, 64))
+
+
+# ---------------------------------------------------------------- selection
+
+def tiny_inputs(seed=11):
+    cfg = synth.CONFIGS["tiny"]
+    return cfg, synth.gen_decode(cfg, seed)
+
+
+def test_selection_brute_force_tiny(orc):
+    cfg, t = tiny_inputs()
+    s = orc.block_summaries(t["k"], cfg.seq_len, 64)
+    idx, scores = orc.select_blocks(t["q"], s, cfg.n_kv_heads, 1, 2, cfg.top_k)
+    nb = 16
+    cand = list(range(1, nb - 2))
+    for kvh in range(cfg.n_kv_heads):
+        sc = scores[0, kvh]
+        best = max(itertools.combinations(cand, cfg.top_k), key=lambda c: sum(sc[j] for j in c))
+        assert len(list(itertools.combinations(cand, 4))) == 715
+        expect = sorted([0] + list(best) + [nb - 2, nb - 1])
+        assert idx[0, kvh].tolist() == expect
+
+
+def test_selection_scores_from_unit_rows(orc):
+    # block j's rows are all e_c, so its score is sum_h q[h][c] (a column sum of q)
+    d, nb, g = 8, 12, 3
+    rng = np.random.default_rng(4)
+    q = grid(rng, (1, g, d))
+    x = np.zeros((1, 1, nb * 64, d), np.float32)
+    cols = rng.integers(0, d, nb)
+    for j in range(nb):
+        x[0, 0, j * 64:(j + 1) * 64, cols[j]] = 1.0
+    s = orc.block_summaries(bf(x), nb * 64, 64)
+    _, scores = orc.select_blocks(bf(q), s, 1, 1, 2, 3)
+    for j in range(1, nb - 2):
+        assert scores[0, 0, j] == pytest.approx(q[0, :, cols[j]].sum(), abs=1e-12)
+    assert np.isnan(scores[0, 0, 0]) and np.isnan(scores[0, 0, nb - 1])
+
+
+def test_selection_group_is_sum_of_heads(orc):
+    cfg, t = tiny_inputs(12)
+    s = orc.block_summaries(t["k"][:, :1], cfg.seq_len, 64)
+    q = t["q"][:, :4]
+    _, sg = orc.select_blocks(q, s, 1, 1, 2, 4)       # 4 query heads share kv head 0
+    parts = [orc.select_blocks(q[:, h:h + 1], s, 1, 1, 2, 4)[1] for h in range(4)]
+    np.testing.assert_allclose(sg, sum(parts), rtol=1e-12, atol=1e-12)
+
+
+def test_selection_defining_property_and_invariants(orc):
+    cfg = synth.scaled(synth.CONFIGS["gqa32k"], batch=2, seq_len=64 * 300)
+    t = synth.gen_decode(cfg, 5)
+    s = orc.block_summaries(t["k"], cfg.seq_len, 64)
+    nb = 300
+    prev = None
+    for k in (0, 1, 10, 30, 31, 200, 297, 400):
+        idx, sc = orc.select_blocks(t["q"], s, cfg.n_kv_heads, 1, 2, k)
+        kk = min(k, nb - 3)
+        assert idx.shape[-1] == kk + 3
+        for b in range(2):
+            for h in range(cfg.n_kv_heads):
+                row = idx[b, h]
+                assert np.all(np.diff(row) > 0)
+                assert row[0] == 0 and row[-2] == nb - 2 and row[-1] == nb - 1
+                sel = set(row.tolist()) - {0, nb - 2, nb - 1}
+                uns = set(range(1, nb - 2)) - sel
+                if sel and uns:
+                    assert min(sc[b, h, list(sel)]) >= max(sc[b, h, list(uns)])
+                if prev is not None:
+                    assert set(prev[b, h].tolist()) <= set(row.tolist())  # nested in k
+        prev = idx
+    # scaling q by 2 (exact in bf16) keeps the selection
+    q2 = bf(f(t["q"]) * 2)
+    i1, s1 = orc.select_blocks(t["q"], s, cfg.n_kv_heads, 1, 2, 30)
+    i2, s2 = orc.select_blocks(q2, s, cfg.n_kv_heads, 1, 2, 30)
+    assert np.array_equal(i1, i2)
+    np.testing.assert_allclose(s2[~np.isnan(s2)], 2 * s1[~np.isnan(s1)], rtol=1e-14)
+
+
+def test_selection_sink_and_local_kept_when_lowest(orc):
+    d, nb = 8, 20
+    u = np.zeros(d, np.float32)
+    u[0] = 1
+    x = np.zeros((1, 1, nb * 64, d), np.float32)
+    for j in range(nb):
+        x[0, 0, j * 64:(j + 1) * 64, 0] = 1.0 + j % 5
+    x[0, 0, :64, 0] = -50          # sink block scores lowest
+    x[0, 0, -128:, 0] = -50        # local blocks score lowest
+    x[0, 0, 7 * 64:8 * 64, 0] = 40  # needle
+    q = np.tile(u, (1, 1, 1))
+    s = orc.block_summaries(bf(x), nb * 64, 64)
+    idx, _ = orc.select_blocks(bf(q), s, 1, 1, 2, 1)
+    assert idx[0, 0].tolist() == [0, 7, nb - 2, nb - 1]
+
+
+def test_selection_ties_prefer_lower_index(orc):
+    d, nb = 4, 12
+    x = np.zeros((1, 1, nb * 64, d), np.float32)
+    x[..., 0] = 1.0            # every block has the same summary
+    q = np.ones((1, 1, d), np.float32)
+    s = orc.block_summaries(bf(x), nb * 64, 64)
+    idx, _ = orc.select_blocks(bf(q), s, 1, 1, 2, 3)
+    assert idx[0, 0].tolist() == [0, 1, 2, 3, 10, 11]
+
+
+# ---------------------------------------------------------------- decode attention
+
+def gather_tokens(idx_row, bs, N):
+    return np.concatenate([np.arange(j * bs, min((j + 1) * bs, N)) for j in idx_row])
+
+
+def test_all_blocks_equal_dense_sdpa(orc):
+    cfg, t = tiny_inputs(13)
+    s = orc.block_summaries(t["k"], cfg.seq_len, 64)
+    idx, _ = orc.select_blocks(t["q"], s, cfg.n_kv_heads, 1, 2, 13)   # k covers every block
+    assert idx.shape[-1] == 16
+    out, lse, w = orc.sparse_decode_attn(t["q"], t["k"], t["v"], idx, cfg.seq_len,
+                                         want_weights=True)
+    q, k, v = f(t["q"]), f(t["k"]), f(t["v"])
+    ref = sdpa(q[0][:, None, :], k[0], v[0])[:, 0, :]
+    np.testing.assert_allclose(out[0], ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(w.sum(-1), 1.0, atol=1e-12)
+
+
+def test_gqa_partial_selection_equals_sdpa_over_gathered(orc):
+    cfg = synth.scaled(synth.CONFIGS["gqa32k"], batch=2, seq_len=64 * 40 + 23, head_dim=64)
+    t = synth.gen_decode(cfg, 6)
+    nb = 41
+    s = orc.block_summaries(t["k"], cfg.seq_len, 64)
+    idx, _ = orc.select_blocks(t["q"], s, cfg.n_kv_heads, 1, 2, 6)
+    out, lse, _ = orc.sparse_decode_attn(t["q"], t["k"], t["v"], idx, cfg.seq_len)
+    q, k, v = f(t["q"]), f(t["k"]), f(t["v"])
+    g = cfg.n_q_heads // cfg.n_kv_heads
+    assert idx[0, 0, -1] == nb - 1   # the partial last block is local
+    for b in range(2):
+        for h in range(cfg.n_q_heads):
+            toks = gather_tokens(idx[b, h // g], 64, cfg.seq_len)
+            ref = sdpa(q[b, h][None], k[b, h // g, toks], v[b, h // g, toks])[0]
+            np.testing.assert_allclose(out[b, h], ref, rtol=0, atol=1e-12)
+
+
+def test_weights_equal_sdpa_with_identity_values(orc):
+    # with V_t = e_t the attention output is the weight vector itself
+    rng = np.random.default_rng(7)
+    d, N = 64, 64
+    q = bf(rng.standard_normal((1, 1, d)))
+    k = bf(rng.standard_normal((1, 1, N, d)) * 2)
+    v = bf(np.eye(N, d, dtype=np.float32)[None, None])
+    idx = np.zeros((1, 1, 1), np.int32)
+    out, lse, w = orc.sparse_decode_attn(q, k, v, idx, N, want_weights=True)
+    ref = sdpa(f(q)[0], f(k)[0, 0], np.eye(N))[0]
+    np.testing.assert_allclose(w[0, 0], ref, atol=1e-14)
+    np.testing.assert_allclose(out[0, 0], ref, atol=1e-14)
+
+
+def test_decode_closed_forms(orc):
+    rng = np.random.default_rng(8)
+    d, N = 16, 256
+    v = bf(rng.standard_normal((1, 1, N, d)))
+    q = bf(rng.standard_normal((1, 2, d)))
+    idx = np.array([[[0, 2, 3]]], np.int32)
+    # zero keys: uniform weights -> mean of the kept values; lse = log(#tokens)
+    out, lse, _ = orc.sparse_decode_attn(q, bf(np.zeros((1, 1, N, d))), v, idx, N)
+    toks = gather_tokens(idx[0, 0], 64, N)
+    np.testing.assert_allclose(out[0, 0], f(v)[0, 0, toks].mean(0), atol=1e-14)
+    assert lse[0, 1] == pytest.approx(math.log(len(toks)), abs=1e-14)
+    # one dominant logit -> that token's value
+    k = np.zeros((1, 1, N, d), np.float32)
+    k[0, 0, 150] = 64 * f(q)[0, 0] / max(1e-3, np.abs(f(q)[0, 0]).max())
+    out, _, _ = orc.sparse_decode_attn(q[:, :1], bf(k), v, idx, N)
+    np.testing.assert_allclose(out[0, 0], f(v)[0, 0, 150], atol=1e-9)
+
+
+def test_decode_linear_in_v_and_scale_default(orc):
+    rng = np.random.default_rng(9)
+    d, N = 32, 192
+    q = bf(rng.standard_normal((1, 2, d)))
+    k = bf(rng.standard_normal((1, 1, N, d)))
+    v1, v2 = grid(rng, (1, 1, N, d), -2, 2), grid(rng, (1, 1, N, d), -2, 2)
+    idx = np.array([[[0, 2]]], np.int32)
+    o1, _, _ = orc.sparse_decode_attn(q, k, bf(v1), idx, N)
+    o2, _, _ = orc.sparse_decode_attn(q, k, bf(v2), idx, N)
+    o12, _, _ = orc.sparse_decode_attn(q, k, bf(v1 + v2), idx, N)
+    np.testing.assert_allclose(o12, o1 + o2, atol=1e-13)
+    oa, la, _ = orc.sparse_decode_attn(q, k, bf(v1), idx, N, scale=0.0)
+    ob, lb, _ = orc.sparse_decode_attn(q, k, bf(v1), idx, N, scale=1 / math.sqrt(d))
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+def test_lse_merges_disjoint_sets(orc):
+    # softmax over A u B from the parts: o = (e^lA oA + e^lB oB) / (e^lA + e^lB)
+    rng = np.random.default_rng(10)
+    d, N = 32, 64 * 6
+    q = bf(rng.standard_normal((1, 2, d)))
+    k = bf(rng.standard_normal((1, 1, N, d)) * 2)
+    v = bf(rng.standard_normal((1, 1, N, d)))
+    oa, la, _ = orc.sparse_decode_attn(q, k, v, np.array([[[0, 3]]], np.int32), N)
+    ob, lb, _ = orc.sparse_decode_attn(q, k, v, np.array([[[1, 5]]], np.int32), N)
+    oab, lab, _ = orc.sparse_decode_attn(q, k, v, np.array([[[0, 1, 3, 5]]], np.int32), N)
+    wa, wb = np.exp(la - lab)[..., None], np.exp(lb - lab)[..., None]
+    np.testing.assert_allclose(wa + wb, 1.0, atol=1e-12)
+    np.testing.assert_allclose(oab, wa * oa + wb * ob, atol=1e-12)
+
+
+def test_decode_rejects_bad_index_lists(orc):
+    q = np.zeros((1, 1, 8), np.uint16)
+    k = np.zeros((1, 1, 128, 8), np.uint16)
+    for bad in ([[[1, 1]]], [[[1, 0]]], [[[0, 2]]], [[[-1, 0]]]):
+        with pytest.raises(ValueError):
+            orc.sparse_decode_attn(q, k, k, np.array(bad, np.int32), 128)
+
+
+# ---------------------------------------------------------------- prefill
+
+def prefill_case(seed, P=256, C=40, Hq=4, Hkv=2, d=16, exact=True):
+    rng = np.random.default_rng(seed)
+    n = P + C
+    if exact:
+        k = grid(rng, (1, Hkv, n, d), -2, 2, 4)
+        v = grid(rng, (1, Hkv, n, d), -2, 2, 4)
+    else:
+        k = rng.standard_normal((1, Hkv, n, d)).astype(np.float32)
+        v = rng.standard_normal((1, Hkv, n, d)).astype(np.float32)
+    q = rng.standard_normal((1, C, Hq, d)).astype(np.float32)
+    return bf(q), bf(k), bf(v)
+
+
+def test_prefill_branch_b_m1_is_dense_attention(orc):
+    q, k, v = prefill_case(20)
+    P = 256
+    r = orc.sparse_prefill_attn(q, k, v, P, m_sparse=4, top_k=8, m_dense=1, window=4,
+                                q_tile=16, want_branches=True)
+    qf, kf, vf = f(q), f(k), f(v)
+    for h in range(4):
+        ref = sdpa(qf[0, :, h], kf[0, h // 2, :P], vf[0, h // 2, :P])
+        np.testing.assert_allclose(r["branches"][1, 0, :, h], ref, atol=1e-12)
+
+
+def test_prefill_branch_a_all_entries_is_dense_over_pooled(orc):
+    q, k, v = prefill_case(21)
+    P, m = 256, 2
+    r = orc.sparse_prefill_attn(q, k, v, P, m_sparse=m, top_k=10 ** 6, m_dense=64, window=4,
+                                q_tile=16, want_branches=True, want_sel=True)
+    assert r["sel"].shape[-1] == P // m
+    qf, kf, vf = f(q), f(k), f(v)
+    # grid data: the pooled means are exact in bf16, so numpy's mean is the operand
+    kp = kf[0, :, :P].reshape(2, P // m, m, -1).mean(2)
+    vp = vf[0, :, :P].reshape(2, P // m, m, -1).mean(2)
+    assert np.array_equal(f(bf(kp)), kp) and np.array_equal(f(bf(vp)), vp)
+    for h in range(4):
+        ref = sdpa(qf[0, :, h], kp[h // 2], vp[h // 2])
+        np.testing.assert_allclose(r["branches"][0, 0, :, h], ref, atol=1e-12)
+
+
+def test_prefill_branch_c_window(orc):
+    q, k, v = prefill_case(22, exact=False)
+    P, C = 256, 40
+    big = orc.sparse_prefill_attn(q, k, v, P, top_k=8, window=P + C, q_tile=16,
+                                  want_branches=True)
+    qf, kf, vf = f(q), f(k), f(v)
+    pos = P + np.arange(C)
+    mask = np.arange(P + C)[None, :] <= pos[:, None]          # causal
+    for h in range(4):
+        ref = sdpa(qf[0, :, h], kf[0, h // 2], vf[0, h // 2], mask=mask)
+        np.testing.assert_allclose(big["branches"][2, 0, :, h], ref, atol=1e-12)
+    one = orc.sparse_prefill_attn(q, k, v, P, top_k=8, window=1, q_tile=16, want_branches=True)
+    for h in range(4):
+        np.testing.assert_array_equal(one["branches"][2, 0, :, h], vf[0, h // 2, P:P + C])
+    # window 128 covers [p-127, p]
+    w = orc.sparse_prefill_attn(q, k, v, P, top_k=8, window=128, q_tile=16, want_branches=True)
+    mask = (np.arange(P + C)[None, :] <= pos[:, None]) & (np.arange(P + C)[None, :] > pos[:, None] - 128)
+    ref = sdpa(qf[0, :, 3], kf[0, 1], vf[0, 1], mask=mask)
+    np.testing.assert_allclose(w["branches"][2, 0, :, 3], ref, atol=1e-12)
+
+
+def test_prefill_average_and_rows(orc):
+    q, k, v = prefill_case(23, exact=False)
+    P = 256
+    full = orc.sparse_prefill_attn(q, k, v, P, top_k=8, m_dense=32, window=16, q_tile=16,
+                                   want_branches=True, want_sel=True)
+    br = full["branches"]
+    np.testing.assert_allclose(full["out"], (br[0] + br[1] + br[2]) / 3, atol=1e-15)
+    rows = np.array([39, 0, 17, 16])
+    part = orc.sparse_prefill_attn(q, k, v, P, top_k=8, m_dense=32, window=16, q_tile=16,
+                                   rows=rows)
+    np.testing.assert_array_equal(part["out"][0], full["out"][0, rows])
+    again = orc.sparse_prefill_attn(q, k, v, P, top_k=8, m_dense=32, window=16, q_tile=16,
+                                    sel_in=full["sel"])
+    np.testing.assert_array_equal(again["out"], full["out"])
+
+
+def test_prefill_tile_selection(orc):
+    P, C, d, m = 256, 48, 8, 4
+    E = P // m
+    k = np.zeros((1, 1, P + C, d), np.float32)
+    k[0, 0, :P, 1] = np.arange(P) % 7 * 0.25        # mild structure everywhere
+    k[0, 0, 20 * m:21 * m, 0] = 8.0                  # entry 20 points along +e0
+    k[0, 0, 33 * m:34 * m, 0] = -8.0                 # entry 33 points along -e0
+    q = np.zeros((1, C, 1, d), np.float32)
+    q[0, :16, 0, 0] = 1.0                            # tile 0 looks along +e0
+    q[0, 16:32, 0, 0] = -1.0                         # tile 1 looks along -e0
+    q[0, 32:, 0, 1] = 1.0                            # tile 2 looks along e1
+    r = orc.sparse_prefill_attn(bf(q), bf(k), bf(k), P, m_sparse=m, top_k=1, q_tile=16,
+                                want_sel=True, want_sel_scores=True)
+    assert r["sel"][0, :, 0, 0].tolist()[:2] == [20, 33]
+    ss = r["sel_scores"][0, 2, 0]
+    assert r["sel"][0, 2, 0, 0] == int(np.argmax(ss))            # first of the maxima
+    r8 = orc.sparse_prefill_attn(bf(q), bf(k), bf(k), P, m_sparse=m, top_k=8, q_tile=16,
+                                 want_sel=True, want_sel_scores=True)
+    for t in range(3):
+        sel = r8["sel"][0, t, 0]
+        sc = r8["sel_scores"][0, t, 0]
+        assert np.all(np.diff(sel) > 0)
+        uns = np.setdiff1d(np.arange(E), sel)
+        assert sc[sel].min() >= sc[uns].max()
+        # ties resolve to the lower index
+        tied = uns[sc[uns] == sc[sel].min()]
+        assert np.all(tied > sel[sc[sel] == sc[sel].min()].max())
+
+
+def test_prefill_tile_scores_from_unit_entries(orc):
+    # entry j's rows are all e_{c_j}: its score for a tile is the sum of q[., ., c_j]
+    # over the tile's queries and the kv head's query heads (ragged last tile too)
+    P, C, d, m, Hq, Hkv, qt = 128, 40, 8, 4, 4, 2, 16
+    E = P // m
+    rng = np.random.default_rng(24)
+    cols = rng.integers(0, d, E)
+    k = np.zeros((1, Hkv, P + C, d), np.float32)
+    for j in range(E):
+        k[0, :, j * m:(j + 1) * m, cols[j]] = 1.0
+    q = grid(rng, (1, C, Hq, d))
+    r = orc.sparse_prefill_attn(bf(q), bf(k), bf(k), P, m_sparse=m, top_k=3, q_tile=qt,
+                                want_sel_scores=True)
+    ss = r["sel_scores"][0]
+    for t in range(3):
+        for kvh in range(Hkv):
+            qs = q[0, t * qt:min((t + 1) * qt, C), kvh * 2:kvh * 2 + 2].sum(axis=(0, 1))
+            np.testing.assert_allclose(ss[t, kvh], qs[cols], atol=1e-12)
