@@ -1,0 +1,184 @@
+/* bsa.h -- block-summary sparse attention on MI355X (gfx950): the C ABI.
+ *
+ * The method (sources are web pages; sections as printed on them):
+ *  - Keys are grouped into fixed blocks of 64 consecutive tokens, the unit of
+ *    scoring and retention; the first block (attention sink) and the most
+ *    recent ~128 tokens (2 blocks) are always kept, and the middle blocks are
+ *    kept by importance, 10-20 % of the cache in total.  hotdry.top post
+ *    "claude-opus-long-context-kv-cache-sparse-attention", sections
+ *    "稀疏注意力与 KV Cache 压缩的工程实现" and the parameter table under
+ *    "可落地的配置参数与监控要点".
+ *  - Every block is scored, the top-k are kept, and exact scaled-dot-product
+ *    attention softmax(q K^T / sqrt(d)) V runs over the kept tokens only.
+ *    "CSA + HCA 混合注意力机制", §2.1 and §4.4 (块稀疏模式图解).
+ *  - Chunked-prefill variant: m consecutive tokens pooled into one compressed
+ *    entry with top-k selection (§4.1-4.2, m = 4), a heavily compressed
+ *    stream attended densely (§5.1-5.2, m' = 128), and a sliding window of
+ *    raw tokens (§4.3).  Mean pooling is the parameter-free pooling (§4.1).
+ *
+ * Conventions for every entry point
+ *  - Tensor pointers are DEVICE memory owned by the caller, row-major,
+ *    16-byte aligned.  bf16 tensors are passed as `const void*`.
+ *  - The library never allocates device memory and keeps no state between
+ *    calls except cached device properties; calls are thread-safe.
+ *  - Every call only enqueues work on `hip_stream` (a hipStream_t; NULL is
+ *    the default stream) and does not synchronise.  Outputs are valid once
+ *    the stream has completed the work.
+ *  - All argument checks run before any launch: a call that returns an
+ *    error has launched nothing and written nothing.
+ *  - Query head h reads kv head h / (n_q_heads / n_kv_heads).
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define BSA_OK 0
+#define BSA_INVALID_ARG (-1)       /* NULL pointer, bad shape, misalignment, n_keep mismatch */
+#define BSA_UNSUPPORTED (-2)       /* head_dim not in {64, 128}, unsupported block size or group */
+#define BSA_WORKSPACE_TOO_SMALL (-3)
+#define BSA_HIP_ERROR (-4)         /* a launch failed (hipGetLastError after launch) */
+
+typedef struct {
+  int32_t batch;       /* B */
+  int32_t n_q_heads;   /* Hq */
+  int32_t n_kv_heads;  /* Hkv; Hq % Hkv == 0 */
+  int32_t head_dim;    /* d: 64 or 128 */
+  int32_t seq_len;     /* N: valid tokens in the cache (prefill: prior tokens P) */
+  int32_t seq_stride;  /* cache capacity in tokens, >= seq_len (prefill: >= P + C) */
+} bsa_shape;
+
+typedef struct {
+  int32_t block_size;      /* tokens per block; the decode kernels support 64 */
+  int32_t n_sink_blocks;   /* always-kept leading blocks (1 on the page's table) */
+  int32_t n_local_blocks;  /* always-kept trailing blocks (2 on the page's table) */
+  int32_t top_k;           /* middle blocks kept by score; < 0: derive from keep_ratio */
+  float keep_ratio;        /* used when top_k < 0: total kept = floor(r * nb + 0.5) */
+} bsa_select_cfg;
+
+typedef struct {
+  int32_t m_sparse;      /* tokens per entry of the selected stream (4) */
+  int32_t top_k_sparse;  /* entries kept per (query tile, kv head) (2048) */
+  int32_t m_dense;       /* tokens per entry of the dense stream (128) */
+  int32_t window;        /* raw tokens attended up to and including the query (128) */
+  int32_t q_tile;        /* consecutive queries sharing one selection (64) */
+} bsa_prefill_cfg;
+
+/* ceil(n / m): blocks (or compressed entries) covering n tokens; -1 if m <= 0 or n < 0 */
+int32_t bsa_num_blocks(int32_t n, int32_t m);
+
+/* kept blocks per (batch, kv head) for nb blocks: |sink U local| + k, where
+ * the candidates are the blocks that are neither sink nor local and
+ * k = top_k (or floor(keep_ratio*nb + 0.5) - n_sink - n_local when top_k < 0),
+ * clamped to [0, #candidates].  With nb <= sink + local every block is kept.
+ * Returns -1 on an invalid cfg. */
+int32_t bsa_num_kept(int32_t nb, const bsa_select_cfg* cfg);
+
+/* workspace bytes needed by select_blocks / sparse_decode_attn /
+ * sparse_prefill_attn for these arguments (0 if none is needed; SIZE_MAX on
+ * invalid arguments).  n_splits = 0 selects the library's own split plan. */
+size_t bsa_select_workspace_size(const bsa_shape* shape, const bsa_select_cfg* cfg);
+size_t bsa_decode_workspace_size(const bsa_shape* shape, int32_t n_keep, int32_t block_size,
+                                 int32_t n_splits);
+size_t bsa_prefill_workspace_size(const bsa_shape* shape, int32_t chunk_len,
+                                  const bsa_prefill_cfg* cfg);
+
+/* human-readable text of a status code (static storage) */
+const char* bsa_status_string(int status);
+
+/* build_block_summaries -- mean of each block of `block_size` consecutive
+ * tokens (the block-level importance unit of the hotdry.top post, section
+ * 稀疏注意力与 KV Cache 压缩的工程实现; mean pooling per "CSA + HCA
+ * 混合注意力机制" §4.1; also the compressed streams of §4.1 and §5.1).
+ *   x         bf16 [B][n_kv_heads][seq_stride][d]
+ *   out_f32   fp32 [B][n_kv_heads][nb][d] or NULL    (nb = ceil(seq_len / block_size))
+ *   out_bf16  bf16 [B][n_kv_heads][nb][d] or NULL    (the fp32 mean rounded to nearest even)
+ * A partial last block is averaged over its valid tokens.  Tokens past
+ * seq_len are never read.  Sums are fp32.  At least one output is required.
+ * Any block_size >= 1 is supported. */
+int build_block_summaries(const void* x, const bsa_shape* shape, int32_t block_size,
+                          float* out_f32, void* out_bf16, void* hip_stream);
+
+/* select_blocks -- per (batch, kv head): pooled query qbar = sum of the
+ * group's query heads (fp32), block scores s_j = qbar . summary_j for the
+ * candidate blocks, and the kept list = sink blocks U top-k candidates (by
+ * descending score, lower index first on equal scores) U local blocks,
+ * ascending.  hotdry.top post, 稀疏注意力与 KV Cache 压缩的工程实现;
+ * "CSA + HCA 混合注意力机制" §4.4 steps 1-3.
+ *   q          bf16 [B][Hq][d]
+ *   summaries  fp32 [B][Hkv][nb][d] from build_block_summaries (nb = ceil(seq_len / block_size))
+ *   block_idx  int32 [B][Hkv][n_keep] output, n_keep = bsa_num_kept(nb, cfg)
+ *   scores_out fp32 [B][Hkv][nb] or NULL: candidate scores (other entries are not written)
+ *   workspace  bsa_select_workspace_size() bytes of device memory (may be NULL if 0)
+ * Requires seq_len >= 1. */
+int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
+                  const bsa_select_cfg* cfg, int32_t* block_idx, float* scores_out,
+                  void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* sparse_decode_attn -- exact softmax(q K^T * scale) V for every query head
+ * over the tokens of its kv head's kept blocks ("CSA + HCA 混合注意力机制"
+ * §2.1 and §4.4 step 4; the decode step of §2.3 reads the cache after the
+ * new token's K/V were appended, so no mask is applied).
+ *   q          bf16 [B][Hq][d]
+ *   k, v       bf16 [B][Hkv][seq_stride][d]
+ *   block_idx  int32 [B][Hkv][n_keep], strictly ascending block indices < nb
+ *              (not checked on the device: out-of-range entries are the caller's error)
+ *   scale      0 selects 1/sqrt(d)
+ *   out        fp32 [B][Hq][d]
+ *   lse        fp32 [B][Hq] natural-log log-sum-exp of the scaled logits, or NULL
+ *   workspace  bsa_decode_workspace_size(shape, n_keep, block_size, 0) bytes
+ * block_size must be 64; n_keep >= 1; Hq/Hkv in {1, 2, 4, 8, 16}.  A partial
+ * last block contributes only its tokens below seq_len. */
+int sparse_decode_attn(const void* q, const void* k, const void* v, const int32_t* block_idx,
+                       int32_t n_keep, const bsa_shape* shape, int32_t block_size, float scale,
+                       float* out, float* lse, void* workspace, size_t ws_bytes,
+                       void* hip_stream);
+
+/* sparse_decode_attn_split -- sparse_decode_attn with an explicit number of
+ * kept-block splits per (batch, kv head) (>= 1; 0 = the library's plan).
+ * The result equals sparse_decode_attn's up to fp32 rounding of the merge.
+ * Workspace: bsa_decode_workspace_size(shape, n_keep, block_size, n_splits). */
+int sparse_decode_attn_split(const void* q, const void* k, const void* v,
+                             const int32_t* block_idx, int32_t n_keep, const bsa_shape* shape,
+                             int32_t block_size, float scale, float* out, float* lse,
+                             void* workspace, size_t ws_bytes, int32_t n_splits,
+                             void* hip_stream);
+
+/* sparse_prefill_attn -- chunked prefill of C new queries at positions
+ * P + i (P = shape->seq_len prior tokens), three branches averaged:
+ *   A ("CSA + HCA 混合注意力机制" §4.1-4.2, §4.4): per (tile of q_tile
+ *     consecutive queries, kv head) the pooled query (sum over the tile's
+ *     queries and the group's heads) scores every m_sparse entry with the
+ *     fp32 stream; the top_k_sparse entries (descending, lower index first)
+ *     are attended with the bf16 streams;
+ *   B (§5.1-5.2): all m_dense entries, attended densely;
+ *   C (§4.3): raw tokens [P + i - window + 1, P + i] of k, v.
+ * The compressed streams cover the P prior tokens only; the chunk's own K/V
+ * are already appended at [P, P + C).
+ *   q                    bf16 [B][C][Hq][d]
+ *   k, v                 bf16 [B][Hkv][seq_stride][d], seq_stride >= P + C
+ *   k_cmp_sparse_f32     fp32 [B][Hkv][E_s][d]   (E_s = ceil(P / m_sparse); from build_block_summaries)
+ *   k/v_cmp_sparse_bf16  bf16 [B][Hkv][E_s][d]
+ *   k/v_cmp_dense_bf16   bf16 [B][Hkv][E_d][d]   (E_d = ceil(P / m_dense))
+ *   out                  fp32 [B][C][Hq][d] = (o_A + o_B + o_C) / 3
+ *   lse3                 fp32 [3][B][C][Hq] per-branch log-sum-exp, or NULL
+ *   sel_out              int32 [B][ceil(C / q_tile)][Hkv][min(top_k_sparse, E_s)] ascending, or NULL
+ *   workspace            bsa_prefill_workspace_size() bytes
+ * Requires P >= 1, head_dim 128, Hq/Hkv * q_tile <= 256 and a multiple of 16. */
+int sparse_prefill_attn(const void* q, int32_t chunk_len, const void* k, const void* v,
+                        const float* k_cmp_sparse_f32, const void* k_cmp_sparse_bf16,
+                        const void* v_cmp_sparse_bf16, const void* k_cmp_dense_bf16,
+                        const void* v_cmp_dense_bf16, const bsa_shape* shape,
+                        const bsa_prefill_cfg* cfg, float scale, float* out, float* lse3,
+                        int32_t* sel_out, void* workspace, size_t ws_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSA_H */

@@ -1,0 +1,261 @@
+"""Block-summary sparse attention for MI355X (gfx950).
+
+Thin ctypes binding of libbsa.so: argument marshalling only.  Every step of
+the path runs in the library's HIP kernels; torch provides device memory and
+the current stream.  The functions carry the names of the C entry points in
+include/bsa.h.  There is no CPU fallback: if libbsa.so is missing or a call
+fails, a BsaError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libbsa.so")
+
+BSA_OK, BSA_INVALID_ARG, BSA_UNSUPPORTED, BSA_WORKSPACE_TOO_SMALL, BSA_HIP_ERROR = 0, -1, -2, -3, -4
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+
+class BsaError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class bsa_shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("seq_len", ctypes.c_int32), ("seq_stride", ctypes.c_int32)]
+
+
+class bsa_select_cfg(ctypes.Structure):
+    _fields_ = [("block_size", ctypes.c_int32), ("n_sink_blocks", ctypes.c_int32),
+                ("n_local_blocks", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("keep_ratio", ctypes.c_float)]
+
+
+class bsa_prefill_cfg(ctypes.Structure):
+    _fields_ = [("m_sparse", ctypes.c_int32), ("top_k_sparse", ctypes.c_int32),
+                ("m_dense", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("q_tile", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libbsa.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, f32, vp, sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    P = ctypes.POINTER
+    L.bsa_num_blocks.argtypes, L.bsa_num_blocks.restype = [i32, i32], i32
+    L.bsa_num_kept.argtypes, L.bsa_num_kept.restype = [i32, P(bsa_select_cfg)], i32
+    L.bsa_select_workspace_size.argtypes = [P(bsa_shape), P(bsa_select_cfg)]
+    L.bsa_select_workspace_size.restype = sz
+    L.bsa_decode_workspace_size.argtypes = [P(bsa_shape), i32, i32, i32]
+    L.bsa_decode_workspace_size.restype = sz
+    L.bsa_prefill_workspace_size.argtypes = [P(bsa_shape), i32, P(bsa_prefill_cfg)]
+    L.bsa_prefill_workspace_size.restype = sz
+    L.bsa_status_string.argtypes, L.bsa_status_string.restype = [ctypes.c_int], ctypes.c_char_p
+    L.build_block_summaries.argtypes = [vp, P(bsa_shape), i32, vp, vp, vp]
+    L.select_blocks.argtypes = [vp, vp, P(bsa_shape), P(bsa_select_cfg), vp, vp, vp, sz, vp]
+    L.sparse_decode_attn.argtypes = [vp, vp, vp, vp, i32, P(bsa_shape), i32, f32, vp, vp, vp, sz,
+                                     vp]
+    L.sparse_decode_attn_split.argtypes = [vp, vp, vp, vp, i32, P(bsa_shape), i32, f32, vp, vp,
+                                           vp, sz, i32, vp]
+    L.sparse_prefill_attn.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, P(bsa_shape),
+                                      P(bsa_prefill_cfg), f32, vp, vp, vp, vp, sz, vp]
+    for fn in ("build_block_summaries", "select_blocks", "sparse_decode_attn",
+               "sparse_decode_attn_split", "sparse_prefill_attn"):
+        getattr(L, fn).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(fn, status):
+    if status != BSA_OK:
+        raise BsaError(fn, status, lib().bsa_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, name, dtype, ndim):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous {ndim}-d {dtype} tensor, got "
+                        f"{t.dtype} {tuple(t.shape)}")
+
+
+def make_shape(batch, n_q_heads, n_kv_heads, head_dim, seq_len, seq_stride):
+    return bsa_shape(batch, n_q_heads, n_kv_heads, head_dim, seq_len, seq_stride)
+
+
+def select_cfg(block_size=64, n_sink=1, n_local=2, top_k=-1, keep_ratio=0.0):
+    return bsa_select_cfg(block_size, n_sink, n_local, top_k, keep_ratio)
+
+
+def prefill_cfg(m_sparse=4, top_k_sparse=2048, m_dense=128, window=128, q_tile=64):
+    return bsa_prefill_cfg(m_sparse, top_k_sparse, m_dense, window, q_tile)
+
+
+def num_blocks(n, m):
+    return lib().bsa_num_blocks(n, m)
+
+
+def num_kept(nb, cfg):
+    return lib().bsa_num_kept(nb, ctypes.byref(cfg))
+
+
+# ------------------------------------------------------------------ entry points
+
+def build_block_summaries(x, seq_len, block_size, want_f32=True, want_bf16=False,
+                          out_f32=None, out_bf16=None):
+    """x bf16 [B][H][stride][d] -> (fp32 [B][H][nb][d] or None, bf16 [B][H][nb][d] or None)."""
+    import torch
+    _need(x, "x", torch.bfloat16, 4)
+    B, H, stride, d = x.shape
+    nb = num_blocks(seq_len, block_size)
+    if want_f32 and out_f32 is None:
+        out_f32 = torch.empty((B, H, nb, d), dtype=torch.float32, device=x.device)
+    if want_bf16 and out_bf16 is None:
+        out_bf16 = torch.empty((B, H, nb, d), dtype=torch.bfloat16, device=x.device)
+    shape = make_shape(B, H, H, d, seq_len, stride)
+    _check("build_block_summaries",
+           lib().build_block_summaries(_ptr(x), ctypes.byref(shape), block_size, _ptr(out_f32),
+                                       _ptr(out_bf16), _stream(x.device)))
+    return out_f32, out_bf16
+
+
+def select_blocks(q, summaries, seq_len, block_size=64, n_sink=1, n_local=2, top_k=-1,
+                  keep_ratio=0.0, want_scores=False, block_idx=None, workspace=None):
+    """q bf16 [B][Hq][d], summaries fp32 [B][Hkv][nb][d] -> (idx int32 [B][Hkv][n_keep], scores)."""
+    import torch
+    _need(q, "q", torch.bfloat16, 3)
+    _need(summaries, "summaries", torch.float32, 4)
+    B, Hq, d = q.shape
+    Hkv, nb = summaries.shape[1], summaries.shape[2]
+    cfg = select_cfg(block_size, n_sink, n_local, top_k, keep_ratio)
+    n_keep = num_kept(nb, cfg)
+    if n_keep < 0:
+        raise ValueError("invalid selection config")
+    shape = make_shape(B, Hq, Hkv, d, seq_len, seq_len)
+    if block_idx is None:
+        block_idx = torch.empty((B, Hkv, n_keep), dtype=torch.int32, device=q.device)
+    scores = None
+    if want_scores:
+        scores = torch.full((B, Hkv, nb), float("nan"), dtype=torch.float32, device=q.device)
+    ws_bytes = lib().bsa_select_workspace_size(ctypes.byref(shape), ctypes.byref(cfg))
+    if ws_bytes == SIZE_MAX:
+        raise ValueError("invalid select arguments")
+    if workspace is None and scores is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _check("select_blocks",
+           lib().select_blocks(_ptr(q), _ptr(summaries), ctypes.byref(shape), ctypes.byref(cfg),
+                               _ptr(block_idx), _ptr(scores), _ptr(workspace),
+                               workspace.numel() if workspace is not None else 0,
+                               _stream(q.device)))
+    return block_idx, scores
+
+
+def decode_workspace_size(B, Hq, Hkv, d, seq_len, n_keep, block_size=64, n_splits=0):
+    shape = make_shape(B, Hq, Hkv, d, seq_len, seq_len)
+    return lib().bsa_decode_workspace_size(ctypes.byref(shape), n_keep, block_size, n_splits)
+
+
+def sparse_decode_attn(q, k, v, block_idx, seq_len, block_size=64, scale=0.0, n_splits=0,
+                       out=None, lse=None, workspace=None, want_lse=True):
+    """q bf16 [B][Hq][d]; k, v bf16 [B][Hkv][stride][d]; block_idx int32 [B][Hkv][n_keep].
+
+    Returns (out fp32 [B][Hq][d], lse fp32 [B][Hq] or None)."""
+    import torch
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(block_idx, "block_idx", torch.int32, 3)
+    B, Hq, d = q.shape
+    Hkv, stride = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or block_idx.shape[:2] != (B, Hkv):
+        raise ValueError("k, v and block_idx shapes disagree")
+    n_keep = block_idx.shape[2]
+    shape = make_shape(B, Hq, Hkv, d, seq_len, stride)
+    ws_bytes = lib().bsa_decode_workspace_size(ctypes.byref(shape), n_keep, block_size, n_splits)
+    if ws_bytes == SIZE_MAX:
+        raise ValueError("invalid decode arguments")
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check("sparse_decode_attn",
+           lib().sparse_decode_attn_split(_ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), n_keep,
+                                          ctypes.byref(shape), block_size, scale, _ptr(out),
+                                          _ptr(lse), _ptr(workspace), workspace.numel(),
+                                          n_splits, _stream(q.device)))
+    return out, lse
+
+
+def sparse_prefill_attn(q, k, v, k_cmp_sparse_f32, k_cmp_sparse_bf16, v_cmp_sparse_bf16,
+                        k_cmp_dense_bf16, v_cmp_dense_bf16, prior_len, cfg=None, scale=0.0,
+                        want_lse3=False, want_sel=False, out=None, workspace=None):
+    """Chunked prefill: q bf16 [B][C][Hq][d]; k, v bf16 [B][Hkv][stride][d] with the chunk's
+    K/V at [prior_len, prior_len + C).  Returns (out fp32 [B][C][Hq][d], lse3, sel)."""
+    import torch
+    cfg = cfg or prefill_cfg()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(k_cmp_sparse_f32, "k_cmp_sparse_f32", torch.float32, 4)
+    for name, t in (("k_cmp_sparse_bf16", k_cmp_sparse_bf16),
+                    ("v_cmp_sparse_bf16", v_cmp_sparse_bf16),
+                    ("k_cmp_dense_bf16", k_cmp_dense_bf16), ("v_cmp_dense_bf16", v_cmp_dense_bf16)):
+        _need(t, name, torch.bfloat16, 4)
+    B, C, Hq, d = q.shape
+    Hkv, stride = k.shape[1], k.shape[2]
+    shape = make_shape(B, Hq, Hkv, d, prior_len, stride)
+    E_s = num_blocks(prior_len, cfg.m_sparse)
+    kk = min(cfg.top_k_sparse, E_s)
+    n_tiles = -(-C // cfg.q_tile)
+    ws_bytes = lib().bsa_prefill_workspace_size(ctypes.byref(shape), C, ctypes.byref(cfg))
+    if ws_bytes == SIZE_MAX:
+        raise ValueError("invalid prefill arguments")
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, C, Hq, d), dtype=torch.float32, device=q.device)
+    lse3 = torch.empty((3, B, C, Hq), dtype=torch.float32, device=q.device) if want_lse3 else None
+    sel = (torch.empty((B, n_tiles, Hkv, kk), dtype=torch.int32, device=q.device)
+           if want_sel else None)
+    _check("sparse_prefill_attn",
+           lib().sparse_prefill_attn(_ptr(q), C, _ptr(k), _ptr(v), _ptr(k_cmp_sparse_f32),
+                                     _ptr(k_cmp_sparse_bf16), _ptr(v_cmp_sparse_bf16),
+                                     _ptr(k_cmp_dense_bf16), _ptr(v_cmp_dense_bf16),
+                                     ctypes.byref(shape), ctypes.byref(cfg), scale, _ptr(out),
+                                     _ptr(lse3), _ptr(sel), _ptr(workspace), workspace.numel(),
+                                     _stream(q.device)))
+    return out, lse3, sel
+
+
+def decode_step(q, k, v, summaries, seq_len, block_size=64, n_sink=1, n_local=2, top_k=-1,
+                keep_ratio=0.0, scale=0.0):
+    """select_blocks then sparse_decode_attn (the per-token hot path)."""
+    idx, _ = select_blocks(q, summaries, seq_len, block_size, n_sink, n_local, top_k, keep_ratio)
+    out, lse = sparse_decode_attn(q, k, v, idx, seq_len, block_size, scale)
+    return out, lse, idx

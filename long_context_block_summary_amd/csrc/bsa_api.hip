@@ -1,0 +1,175 @@
+// bsa_api.hip -- the extern "C" entry points declared in include/bsa.h.
+// Every argument check runs before any launch; kernels are only enqueued on
+// the caller's stream.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/bsa.h"
+#include "bsa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool shape_ok(const bsa_shape* s) {
+  return s && s->batch >= 1 && s->n_q_heads >= 1 && s->n_kv_heads >= 1 &&
+         s->n_q_heads % s->n_kv_heads == 0 && s->head_dim >= 1 && s->seq_len >= 0 &&
+         s->seq_stride >= s->seq_len;
+}
+
+bool dim_supported(int d) { return d == 64 || d == 128; }
+
+bool group_supported(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+// candidate range [c0, c1) and |sink U local|
+void kept_ranges(int nb, int n_sink, int n_local, int* c0, int* c1, int* fixed) {
+  const int s_end = n_sink < nb ? n_sink : nb;
+  const int l_beg = nb - n_local > 0 ? nb - n_local : 0;
+  *c0 = s_end;
+  *c1 = l_beg > s_end ? l_beg : s_end;
+  *fixed = l_beg > s_end ? s_end + (nb - l_beg) : nb;
+}
+
+int middle_k(int nb, const bsa_select_cfg* cfg, int n_cand) {
+  int64_t k;
+  if (cfg->top_k >= 0)
+    k = cfg->top_k;
+  else
+    k = (int64_t)floor((double)cfg->keep_ratio * (double)nb + 0.5) - cfg->n_sink_blocks -
+        cfg->n_local_blocks;
+  if (k < 0) k = 0;
+  if (k > n_cand) k = n_cand;
+  return (int)k;
+}
+
+bool select_cfg_ok(const bsa_select_cfg* c) {
+  return c && c->block_size >= 1 && c->n_sink_blocks >= 0 && c->n_local_blocks >= 0 &&
+         (c->top_k >= 0 || (c->keep_ratio >= 0.f && c->keep_ratio <= 1.f));
+}
+
+int launch_status() {
+  return hipGetLastError() == hipSuccess ? BSA_OK : BSA_HIP_ERROR;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t bsa_num_blocks(int32_t n, int32_t m) {
+  if (n < 0 || m <= 0) return -1;
+  return (int32_t)(((int64_t)n + m - 1) / m);
+}
+
+int32_t bsa_num_kept(int32_t nb, const bsa_select_cfg* cfg) {
+  if (nb < 0 || !select_cfg_ok(cfg)) return -1;
+  int c0, c1, fixed;
+  kept_ranges(nb, cfg->n_sink_blocks, cfg->n_local_blocks, &c0, &c1, &fixed);
+  return fixed + middle_k(nb, cfg, c1 - c0);
+}
+
+size_t bsa_select_workspace_size(const bsa_shape* shape, const bsa_select_cfg* cfg) {
+  if (!shape_ok(shape) || !select_cfg_ok(cfg)) return SIZE_MAX;
+  const int nb = bsa_num_blocks(shape->seq_len, cfg->block_size);
+  return (size_t)shape->batch * shape->n_kv_heads * (size_t)nb * sizeof(float);
+}
+
+size_t bsa_decode_workspace_size(const bsa_shape* shape, int32_t n_keep, int32_t block_size,
+                                 int32_t n_splits) {
+  if (!shape_ok(shape) || n_keep < 1 || block_size < 1 || n_splits < 0) return SIZE_MAX;
+  const int g = shape->n_q_heads / shape->n_kv_heads;
+  const int64_t pairs = (int64_t)shape->batch * shape->n_kv_heads;
+  bsa::DecodePlan p = bsa::plan_decode(pairs, n_keep, g, n_splits);
+  return bsa::decode_workspace_bytes(pairs, shape->head_dim, p);
+}
+
+const char* bsa_status_string(int status) {
+  switch (status) {
+    case BSA_OK: return "ok";
+    case BSA_INVALID_ARG: return "invalid argument";
+    case BSA_UNSUPPORTED: return "unsupported configuration";
+    case BSA_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case BSA_HIP_ERROR: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int build_block_summaries(const void* x, const bsa_shape* shape, int32_t block_size,
+                          float* out_f32, void* out_bf16, void* hip_stream) {
+  if (!x || !shape_ok(shape) || block_size < 1 || (!out_f32 && !out_bf16)) return BSA_INVALID_ARG;
+  if (!aligned16(x) || (out_f32 && !aligned16(out_f32)) || (out_bf16 && !aligned16(out_bf16)))
+    return BSA_INVALID_ARG;
+  if (!dim_supported(shape->head_dim)) return BSA_UNSUPPORTED;
+  if (shape->seq_len == 0) return BSA_OK;
+  bsa::launch_summaries(static_cast<const uint16_t*>(x),
+                        (int64_t)shape->batch * shape->n_kv_heads, shape->seq_len,
+                        shape->seq_stride, shape->head_dim, block_size, out_f32,
+                        static_cast<uint16_t*>(out_bf16), static_cast<hipStream_t>(hip_stream));
+  return launch_status();
+}
+
+int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
+                  const bsa_select_cfg* cfg, int32_t* block_idx, float* scores_out,
+                  void* workspace, size_t ws_bytes, void* hip_stream) {
+  if (!q || !summaries || !block_idx || !shape_ok(shape) || !select_cfg_ok(cfg) ||
+      shape->seq_len < 1)
+    return BSA_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(summaries) || (scores_out && !aligned16(scores_out)))
+    return BSA_INVALID_ARG;
+  if (!dim_supported(shape->head_dim)) return BSA_UNSUPPORTED;
+  const int nb = bsa_num_blocks(shape->seq_len, cfg->block_size);
+  int c0, c1, fixed;
+  kept_ranges(nb, cfg->n_sink_blocks, cfg->n_local_blocks, &c0, &c1, &fixed);
+  const int k = middle_k(nb, cfg, c1 - c0);
+  const int n_keep = fixed + k;
+  float* scores = scores_out;
+  if (!scores) {
+    if (ws_bytes < bsa_select_workspace_size(shape, cfg)) return BSA_WORKSPACE_TOO_SMALL;
+    if (c1 > c0 && !workspace) return BSA_INVALID_ARG;
+    scores = static_cast<float*>(workspace);
+  }
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  bsa::launch_scores(static_cast<const uint16_t*>(q), summaries, shape->batch, shape->n_q_heads,
+                     shape->n_kv_heads, shape->head_dim, nb, c0, c1, scores, st);
+  bsa::launch_topk(scores, (int64_t)shape->batch * shape->n_kv_heads, nb, c0, c1, k, n_keep,
+                   block_idx, st);
+  return launch_status();
+}
+
+int sparse_decode_attn_split(const void* q, const void* k, const void* v,
+                             const int32_t* block_idx, int32_t n_keep, const bsa_shape* shape,
+                             int32_t block_size, float scale, float* out, float* lse,
+                             void* workspace, size_t ws_bytes, int32_t n_splits,
+                             void* hip_stream) {
+  if (!q || !k || !v || !block_idx || !out || !shape_ok(shape) || n_keep < 1 || n_splits < 0 ||
+      shape->seq_len < 1)
+    return BSA_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return BSA_INVALID_ARG;
+  if (block_size < 1) return BSA_INVALID_ARG;
+  if (n_keep > bsa_num_blocks(shape->seq_len, block_size)) return BSA_INVALID_ARG;
+  const int g = shape->n_q_heads / shape->n_kv_heads;
+  if (block_size != 64 || !dim_supported(shape->head_dim) || !group_supported(g))
+    return BSA_UNSUPPORTED;
+  const int64_t pairs = (int64_t)shape->batch * shape->n_kv_heads;
+  bsa::DecodePlan plan = bsa::plan_decode(pairs, n_keep, g, n_splits);
+  if (ws_bytes < bsa::decode_workspace_bytes(pairs, shape->head_dim, plan))
+    return BSA_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned16(workspace)) return BSA_INVALID_ARG;
+  if (scale == 0.f) scale = 1.f / sqrtf((float)shape->head_dim);
+  bsa::launch_decode(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), block_idx, n_keep, shape->batch,
+                     shape->n_q_heads, shape->n_kv_heads, shape->head_dim, shape->seq_len,
+                     shape->seq_stride, scale, plan, static_cast<float*>(workspace), out, lse,
+                     static_cast<hipStream_t>(hip_stream));
+  return launch_status();
+}
+
+int sparse_decode_attn(const void* q, const void* k, const void* v, const int32_t* block_idx,
+                       int32_t n_keep, const bsa_shape* shape, int32_t block_size, float scale,
+                       float* out, float* lse, void* workspace, size_t ws_bytes,
+                       void* hip_stream) {
+  return sparse_decode_attn_split(q, k, v, block_idx, n_keep, shape, block_size, scale, out, lse,
+                                  workspace, ws_bytes, 0, hip_stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// bsa_launch.h -- internal launch wrappers of libbsa (host side).
+// The C ABI in bsa_api.hip validates arguments and plans launches; these
+// functions only enqueue kernels on the given stream.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+// mean of every block of `bs` tokens: x [pairs][stride][d] -> [pairs][nb][d]
+void launch_summaries(const uint16_t* x, int64_t pairs, int N, int stride, int d, int bs,
+                      float* out_f32, uint16_t* out_bf16, hipStream_t st);
+
+// candidate scores s[pair][j] = qbar . summary_j for j in [c0, c1)
+void launch_scores(const uint16_t* q, const float* summ, int B, int Hq, int Hkv, int d, int nb,
+                   int c0, int c1, float* scores, hipStream_t st);
+
+// per pair: sink [0,c0) + top-k of scores[c0,c1) + local [c1,nb), ascending
+void launch_topk(const float* scores, int64_t pairs, int nb, int c0, int c1, int k, int n_keep,
+                 int32_t* idx_out, hipStream_t st);
+
+struct DecodePlan {
+  int g;           // query heads per kv head
+  int bps;         // kept blocks per split (one workgroup per split)
+  int n_splits;    // splits per (batch, kv head)
+};
+DecodePlan plan_decode(int64_t pairs, int n_keep, int g, int n_splits_req);
+size_t decode_workspace_bytes(int64_t pairs, int d, const DecodePlan& p);
+
+// split-K partials + merge.  ws holds [pairs][splits][g][d] o and [pairs][splits][g][2] (m, l)
+void launch_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
+                   int n_keep, int B, int Hq, int Hkv, int d, int N, int stride, float scale,
+                   const DecodePlan& plan, float* ws, float* out, float* lse, hipStream_t st);
+
+}  // namespace bsa

@@ -1,0 +1,266 @@
+// kernels_select.hip -- block summaries, block scoring and top-k selection.
+//
+// Block summaries are the per-block means of the key rows (blocks of 64
+// tokens as the unit of importance evaluation: hotdry.top post
+// "claude-opus-long-context-kv-cache-sparse-attention", section
+// 稀疏注意力与 KV Cache 压缩的工程实现; mean pooling per "CSA + HCA
+// 混合注意力机制" §4.1).  Scoring and top-k follow §4.4 steps 1-3 of that
+// page: every block gets a score, the highest-scoring ones are kept.
+#include "bsa_device.h"
+#include "bsa_launch.h"
+
+namespace bsa {
+
+// ---------------------------------------------------------------------------
+// Summaries.  One thread owns 8 consecutive columns of one block and walks
+// its rows in token order, so each 16-lane row group of a wave reads one
+// contiguous 256-byte key row per load.  HBM-bound: every key byte is read
+// once, the output is 2*(d*4)/(bs*d*2) of the input for bs=64.
+template <int D>
+__global__ __launch_bounds__(256) void summaries_kernel(const uint16_t* __restrict__ x,
+                                                        int64_t items, int N, int stride, int bs,
+                                                        int nb, float* __restrict__ out_f32,
+                                                        uint16_t* __restrict__ out_bf16) {
+  constexpr int TPR = D / 8;  // threads per row
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t item = gid / TPR;
+  const int part = (int)(gid % TPR);
+  if (item >= items) return;
+  const int64_t pair = item / nb;
+  const int j = (int)(item % nb);
+  const int t0 = j * bs;
+  const int n = min(bs, N - t0);
+  const uint4* src = reinterpret_cast<const uint4*>(x + ((int64_t)pair * stride + t0) * D) + part;
+  float acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+  int t = 0;
+  for (; t + 8 <= n; t += 8) {
+    uint4 w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w[u] = ld_stream(src + (int64_t)(t + u) * TPR);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float f[8];
+      unpack8(w[u], f);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] += f[c];
+    }
+  }
+  for (; t < n; ++t) {
+    float f[8];
+    unpack8(ld_stream(src + (int64_t)t * TPR), f);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] += f[c];
+  }
+  const float fn = (float)n;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = acc[c] / fn;
+  const int64_t o = item * D + part * 8;
+  if (out_f32) {
+    float4* dst = reinterpret_cast<float4*>(out_f32 + o);
+    dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+  if (out_bf16) {
+    uint4 w;
+    w.x = bf16_rne(acc[0]) | (bf16_rne(acc[1]) << 16);
+    w.y = bf16_rne(acc[2]) | (bf16_rne(acc[3]) << 16);
+    w.z = bf16_rne(acc[4]) | (bf16_rne(acc[5]) << 16);
+    w.w = bf16_rne(acc[6]) | (bf16_rne(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(out_bf16 + o) = w;
+  }
+}
+
+void launch_summaries(const uint16_t* x, int64_t pairs, int N, int stride, int d, int bs,
+                      float* out_f32, uint16_t* out_bf16, hipStream_t st) {
+  const int nb = (N + bs - 1) / bs;
+  const int64_t items = pairs * nb;
+  const int64_t threads = items * (d / 8);
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+  if (grid == 0) return;
+  if (d == 128)
+    summaries_kernel<128><<<grid, 256, 0, st>>>(x, items, N, stride, bs, nb, out_f32, out_bf16);
+  else
+    summaries_kernel<64><<<grid, 256, 0, st>>>(x, items, N, stride, bs, nb, out_f32, out_bf16);
+}
+
+// ---------------------------------------------------------------------------
+// Scores.  The pooled query qbar (fp32 sum over the group's query heads, in
+// head order) is built in LDS by each workgroup; 16 lanes share one summary
+// row (512 B for d=128) and reduce their partial dot products with DPP inside
+// the row.  Grid: (row chunks, pairs) so that even 8 pairs spread over the
+// whole chip.
+constexpr int SCORE_ROWS_PER_WG = 64;
+
+template <int D>
+__global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict__ q,
+                                                     const float* __restrict__ summ, int Hq,
+                                                     int Hkv, int nb, int c0, int c1,
+                                                     float* __restrict__ scores) {
+  constexpr int PER = D / 16;  // floats per lane
+  __shared__ float qbar[D];
+  const int pair = blockIdx.y;
+  const int b = pair / Hkv, kvh = pair % Hkv, g = Hq / Hkv;
+  const int tid = threadIdx.x;
+  if (tid < D) {
+    const uint16_t* qh = q + ((int64_t)b * Hq + (int64_t)kvh * g) * D + tid;
+    float s = 0.f;
+    for (int h = 0; h < g; ++h) s += __uint_as_float((uint32_t)qh[(int64_t)h * D] << 16);
+    qbar[tid] = s;
+  }
+  __syncthreads();
+  const int l16 = tid & 15;
+  float qv[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) qv[c] = qbar[l16 * PER + c];
+  const int r0 = c0 + blockIdx.x * SCORE_ROWS_PER_WG;
+  const int r1 = min(c1, r0 + SCORE_ROWS_PER_WG);
+  const float* base = summ + (int64_t)pair * nb * D;
+  for (int r = r0 + (tid >> 4); r < r1; r += 16) {
+    const float4* row = reinterpret_cast<const float4*>(base + (int64_t)r * D + l16 * PER);
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < PER / 4; ++c) {
+      float4 w = ld_stream(row + c);
+      s = fmaf(qv[4 * c + 0], w.x, s);
+      s = fmaf(qv[4 * c + 1], w.y, s);
+      s = fmaf(qv[4 * c + 2], w.z, s);
+      s = fmaf(qv[4 * c + 3], w.w, s);
+    }
+    s = row16_sum(s);
+    if (l16 == 0) scores[(int64_t)pair * nb + r] = s;
+  }
+}
+
+void launch_scores(const uint16_t* q, const float* summ, int B, int Hq, int Hkv, int d, int nb,
+                   int c0, int c1, float* scores, hipStream_t st) {
+  const int n = c1 - c0;
+  if (n <= 0) return;
+  dim3 grid((n + SCORE_ROWS_PER_WG - 1) / SCORE_ROWS_PER_WG, B * Hkv);
+  if (d == 128)
+    scores_kernel<128><<<grid, 256, 0, st>>>(q, summ, Hq, Hkv, nb, c0, c1, scores);
+  else
+    scores_kernel<64><<<grid, 256, 0, st>>>(q, summ, Hq, Hkv, nb, c0, c1, scores);
+}
+
+// ---------------------------------------------------------------------------
+// Top-k.  One workgroup of 1024 threads per (batch, kv head).
+// 1. Radix select over order-preserving uint32 keys, 8 bits per pass with a
+//    256-bin LDS histogram, finds T = the k-th largest key and how many keys
+//    equal to T must be taken (the ones with the lowest block index).
+// 2. An ordered compaction in index order (ballot + mbcnt inside a wave,
+//    wave offsets through LDS) writes the kept candidates ascending, so the
+//    output list (sink, selected, local) is sorted with no extra sort.
+constexpr int TOPK_THREADS = 1024;
+constexpr int TOPK_WAVES = TOPK_THREADS / 64;
+
+// block-wide exclusive prefix count of `flag` in thread order; returns the
+// thread's prefix and sets *total.  Uses wcnt[TOPK_WAVES] of LDS.
+__device__ __forceinline__ int block_prefix(bool flag, int* wcnt, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t m = __ballot(flag);
+  const int pre = (int)lane_prefix(m);
+  if (lane == 0) wcnt[wave] = __popcll(m);
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < TOPK_WAVES; ++w) {
+    const int c = wcnt[w];
+    off += (w < wave) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + pre;
+}
+
+__global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restrict__ scores,
+                                                            int nb, int c0, int c1, int k,
+                                                            int n_keep,
+                                                            int32_t* __restrict__ idx_out) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh_digit, sh_above;
+  __shared__ int wcnt[TOPK_WAVES];
+  const int pair = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* s = scores + (int64_t)pair * nb + c0;
+  int32_t* out = idx_out + (int64_t)pair * n_keep;
+  const int n = c1 - c0;
+  for (int i = tid; i < c0; i += TOPK_THREADS) out[i] = i;                 // sink
+  for (int i = tid; i < nb - c1; i += TOPK_THREADS) out[c0 + k + i] = c1 + i;  // local
+  if (k <= 0) return;
+  if (k >= n) {
+    for (int i = tid; i < n; i += TOPK_THREADS) out[c0 + i] = c0 + i;
+    return;
+  }
+  uint32_t prefix = 0;
+  uint32_t remaining = (uint32_t)k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += TOPK_THREADS) {
+      const uint32_t key = order_key(s[i]);
+      const bool match = (pass == 0) || ((key ^ prefix) >> (shift + 8)) == 0;
+      if (match) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns bins 255-4l .. 252-4l (descending order)
+      const int lane = tid;
+      uint32_t c[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = hist[255 - 4 * lane - e];
+      const uint32_t own = c[0] + c[1] + c[2] + c[3];
+      // inclusive scan over lanes (lane 0 = highest bins)
+      uint32_t inc = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t t = __shfl_up(inc, off);
+        if (lane >= off) inc += t;
+      }
+      const uint32_t exc = inc - own;
+      if (exc < remaining && remaining <= inc) {
+        uint32_t acc = exc;
+        for (int e = 0; e < 4; ++e) {
+          if (acc + c[e] >= remaining) {
+            sh_digit = (uint32_t)(255 - 4 * lane - e);
+            sh_above = acc;
+            break;
+          }
+          acc += c[e];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= sh_digit << shift;
+    remaining -= sh_above;
+    __syncthreads();
+  }
+  // T = prefix: keys above T are all taken, plus the first `remaining` keys equal to T
+  const uint32_t T = prefix;
+  const int need_eq = (int)remaining;
+  int carry_eq = 0, carry_sel = 0;
+  for (int base = 0; base < n; base += TOPK_THREADS) {
+    const int i = base + tid;
+    const bool valid = i < n;
+    const uint32_t key = valid ? order_key(s[i]) : 0u;
+    const bool eq = valid && key == T;
+    int tot_eq, tot_sel;
+    const int eq_rank = carry_eq + block_prefix(eq, wcnt, &tot_eq);
+    const bool sel = valid && (key > T || (eq && eq_rank < need_eq));
+    const int pos = carry_sel + block_prefix(sel, wcnt, &tot_sel);
+    if (sel) out[c0 + pos] = c0 + i;
+    carry_eq += tot_eq;
+    carry_sel += tot_sel;
+  }
+}
+
+void launch_topk(const float* scores, int64_t pairs, int nb, int c0, int c1, int k, int n_keep,
+                 int32_t* idx_out, hipStream_t st) {
+  if (pairs <= 0) return;
+  topk_kernel<<<(unsigned)pairs, TOPK_THREADS, 0, st>>>(scores, nb, c0, c1, k, n_keep, idx_out);
+}
+
+}  // namespace bsa

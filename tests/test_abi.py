@@ -1,0 +1,112 @@
+"""The C ABI library loads, exports every entry point of include/bsa.h, and its
+host-side logic (counts, workspace sizes, argument checks) behaves.  No GPU:
+every call here returns before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_block_summary_amd as bsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bsa.LIB_PATH):
+        pytest.fail("libbsa.so is not built")
+    return bsa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    for must in ("build_block_summaries", "select_blocks", "sparse_decode_attn",
+                 "sparse_prefill_attn"):
+        assert must in names
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_counts(L):
+    assert bsa.num_blocks(1_000_000, 4) == 250_000
+    assert bsa.num_blocks(1_000_000, 128) == 7813
+    assert bsa.num_blocks(-1, 4) == -1 and bsa.num_blocks(5, 0) == -1
+    for nb, r, k in [(512, 0.15, 74), (2048, 0.10, 202), (16384, 0.10, 1635)]:
+        assert bsa.num_kept(nb, bsa.select_cfg(keep_ratio=r)) == k + 3
+        assert bsa.num_kept(nb, bsa.select_cfg(top_k=k)) == k + 3
+    assert bsa.num_kept(3, bsa.select_cfg(top_k=5)) == 3
+    assert bsa.num_kept(16, bsa.select_cfg(top_k=100)) == 16
+    assert bsa.num_kept(16, bsa.select_cfg(n_sink=-1)) == -1
+
+
+def test_workspace_sizes(L):
+    sh = bsa.make_shape(4, 64, 8, 128, 131072, 131072)
+    cfg = bsa.select_cfg(top_k=202)
+    assert L.bsa_select_workspace_size(ctypes.byref(sh), ctypes.byref(cfg)) == 4 * 8 * 2048 * 4
+    ws1 = L.bsa_decode_workspace_size(ctypes.byref(sh), 205, 64, 1)
+    assert ws1 == 32 * 1 * 8 * 130 * 4
+    assert L.bsa_decode_workspace_size(ctypes.byref(sh), 205, 64, 0) >= ws1
+    bad = bsa.make_shape(4, 63, 8, 128, 10, 10)
+    assert L.bsa_decode_workspace_size(ctypes.byref(bad), 5, 64, 0) == bsa.SIZE_MAX
+
+
+def test_status_strings(L):
+    for s in (0, -1, -2, -3, -4, 7):
+        assert isinstance(L.bsa_status_string(s), bytes)
+
+
+def test_argument_checks_launch_nothing(L):
+    sh = bsa.make_shape(1, 4, 4, 128, 1024, 1024)
+    cfg = bsa.select_cfg(top_k=4)
+    fake = ctypes.c_void_p(0x1000)
+    # NULL input / outputs
+    assert L.build_block_summaries(None, ctypes.byref(sh), 64, fake, None, None) == -1
+    assert L.build_block_summaries(fake, ctypes.byref(sh), 64, None, None, None) == -1
+    # misaligned pointer
+    assert L.build_block_summaries(ctypes.c_void_p(0x1002), ctypes.byref(sh), 64, fake, None,
+                                   None) == -1
+    # unsupported head_dim
+    sh96 = bsa.make_shape(1, 4, 4, 96, 1024, 1024)
+    assert L.build_block_summaries(fake, ctypes.byref(sh96), 64, fake, None, None) == -2
+    # Hq % Hkv != 0
+    bad = bsa.make_shape(1, 6, 4, 128, 1024, 1024)
+    assert L.select_blocks(fake, fake, ctypes.byref(bad), ctypes.byref(cfg), fake, None, fake,
+                           1 << 20, None) == -1
+    # workspace too small
+    assert L.select_blocks(fake, fake, ctypes.byref(sh), ctypes.byref(cfg), fake, None, fake, 8,
+                           None) == -3
+    # decode: block size other than 64 is unsupported, n_keep beyond nb is invalid
+    assert L.sparse_decode_attn(fake, fake, fake, fake, 4, ctypes.byref(sh), 32, 0.0, fake, None,
+                                fake, 1 << 20, None) == -2
+    assert L.sparse_decode_attn(fake, fake, fake, fake, 17, ctypes.byref(sh), 64, 0.0, fake,
+                                None, fake, 1 << 20, None) == -1
+    assert L.sparse_decode_attn(fake, fake, fake, fake, 0, ctypes.byref(sh), 64, 0.0, fake, None,
+                                fake, 1 << 20, None) == -1
+    g32 = bsa.make_shape(1, 32, 1, 128, 1024, 1024)
+    assert L.sparse_decode_attn(fake, fake, fake, fake, 4, ctypes.byref(g32), 64, 0.0, fake,
+                                None, fake, 1 << 20, None) == -2
+    assert L.sparse_decode_attn(fake, fake, fake, fake, 4, ctypes.byref(sh), 64, 0.0, fake, None,
+                                fake, 16, None) == -3
+    # stride below seq_len
+    short = bsa.make_shape(1, 4, 4, 128, 1024, 1000)
+    assert L.sparse_decode_attn(fake, fake, fake, fake, 4, ctypes.byref(short), 64, 0.0, fake,
+                                None, fake, 1 << 20, None) == -1
+
+
+def test_product_path_has_no_oracle_import():
+    pkg = os.path.join(ROOT, "long_context_block_summary_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "liboracle" not in text and "oracle.h" not in text, f

@@ -1,0 +1,173 @@
+"""GPU parity of the decode path (summaries, selection, attention) against the oracle.
+
+Every case prints its name, seed and shapes before touching the GPU.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import long_context_block_summary_amd as bsa
+from long_context_block_summary_amd import synth
+from parity_rules import (OUT_ATOL, check_index_sets, from_dev_bf16, summary_tolerance, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    bsa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def announce(*a):
+    print("[case]", *a, flush=True)
+
+
+def score_bound(q_u16, o_summ, tol_summ, g):
+    """|fp32 score - exact| bound: summary error carried by |qbar| plus the fp32 dot."""
+    qf = synth.bf16_to_f32(q_u16).astype(np.float64)
+    B, Hq, d = qf.shape
+    qbar = np.abs(qf.reshape(B, Hq // g, g, d).sum(axis=2))          # [B][Hkv][d]
+    carried = np.einsum("bhc,bhjc->bhj", qbar, tol_summ)
+    dot = np.einsum("bhc,bhjc->bhj", qbar, np.abs(o_summ))
+    return carried + 40 * 2.0 ** -24 * dot + 1e-30
+
+
+def run_decode_case(cfg, seed, capacity=None, n_splits=0):
+    """Full path on the GPU vs the oracle; returns (exempted ties, max err)."""
+    import torch
+    announce(cfg.name, "seed", seed, "B", cfg.batch, "Hq", cfg.n_q_heads, "Hkv", cfg.n_kv_heads,
+             "d", cfg.head_dim, "N", cfg.seq_len, "top_k", cfg.top_k, "splits", n_splits)
+    t = synth.gen_decode(cfg, seed, capacity=capacity)
+    N, bs = cfg.seq_len, cfg.block_size
+    nb = -(-N // bs)
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    summ, _ = bsa.build_block_summaries(k, N, bs)
+    idx, scores = bsa.select_blocks(q, summ, N, bs, cfg.n_sink, cfg.n_local, cfg.top_k,
+                                    cfg.keep_ratio, want_scores=True)
+    out, lse = bsa.sparse_decode_attn(q, k, v, idx, N, bs, n_splits=n_splits)
+    torch.cuda.synchronize()
+    g_summ = summ.cpu().numpy()
+    g_idx = idx.cpu().numpy()
+    g_out, g_lse = out.cpu().numpy(), lse.cpu().numpy()
+    # summaries within the fp32 summation bound
+    o_summ = oracle.block_summaries(t["k"], N, bs)
+    tol = summary_tolerance(t["k"], N, bs)
+    assert np.all(np.abs(g_summ - o_summ) <= tol), "summaries out of bound"
+    # selection
+    o_idx, o_scores = oracle.select_blocks(t["q"], o_summ, cfg.n_kv_heads, cfg.n_sink,
+                                           cfg.n_local, cfg.top_k, cfg.keep_ratio)
+    exempt = check_index_sets(g_idx, o_idx, o_scores, nb, cfg.n_sink, cfg.n_local)
+    g_sc = scores.cpu().numpy()
+    cand = ~np.isnan(o_scores)
+    assert np.array_equal(np.isnan(g_sc), ~cand), "scores written outside the candidates"
+    bound = score_bound(t["q"], o_summ, tol, cfg.n_q_heads // cfg.n_kv_heads)
+    assert np.all(np.abs(g_sc[cand] - o_scores[cand]) <= bound[cand]), "score error"
+    # attention against the oracle on the GPU's own index set
+    o_out, o_lse, _ = oracle.sparse_decode_attn(t["q"], t["k"], t["v"], g_idx, N, bs)
+    err = np.abs(g_out - o_out).max()
+    lse_err = np.abs(g_lse - o_lse).max()
+    announce("  exempt ties", exempt, "max|out err|", err, "max|lse err|", lse_err)
+    assert err <= OUT_ATOL, err
+    assert lse_err <= 1e-3, lse_err
+    return exempt, err
+
+
+def test_tiny_all_heads():
+    cfg = synth.CONFIGS["tiny"]
+    for seed in (1, 101, 102):
+        run_decode_case(cfg, seed)
+
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_group_and_dim(g, d):
+    cfg = synth.scaled(synth.CONFIGS["gqa32k"], name=f"g{g}d{d}", batch=2, n_kv_heads=2,
+                       n_q_heads=2 * g, head_dim=d, seq_len=64 * 150 + 37, top_k=21)
+    run_decode_case(cfg, 7 + g + d)
+
+
+def test_edge_cases():
+    base = synth.CONFIGS["gqa32k"]
+    # k = 0: only sink + local; k beyond the candidates: every block
+    run_decode_case(synth.scaled(base, name="k0", batch=1, seq_len=64 * 40, top_k=0), 31)
+    run_decode_case(synth.scaled(base, name="kall", batch=1, seq_len=64 * 40, top_k=500), 32)
+    # fewer blocks than sink + local, one token, a partial block
+    run_decode_case(synth.scaled(base, name="nb2", batch=1, seq_len=100, top_k=5), 33)
+    run_decode_case(synth.scaled(base, name="n1", batch=1, seq_len=1, top_k=5), 34)
+    run_decode_case(synth.scaled(base, name="ragged", batch=3, seq_len=64 * 77 + 63, top_k=9), 35)
+    # cache capacity beyond seq_len, keep ratio instead of top-k
+    run_decode_case(synth.scaled(base, name="cap", batch=2, seq_len=64 * 90 + 1, top_k=-1,
+                                 keep_ratio=0.15), 36, capacity=64 * 100)
+
+
+def test_ties_prefer_lower_index():
+    import torch
+    announce("ties")
+    B, Hq, Hkv, d, N = 1, 8, 2, 128, 64 * 30
+    k = np.zeros((B, Hkv, N, d), np.float32)
+    k[..., 0] = 1.0
+    k[:, :, 64 * 10:64 * 11, 0] = 3.0     # one clear winner
+    v = np.random.default_rng(0).standard_normal((B, Hkv, N, d)).astype(np.float32)
+    q = np.ones((B, Hq, d), np.float32)
+    qd, kd, vd = (to_dev(synth.bf16_round(a)) for a in (q, k, v))
+    summ, _ = bsa.build_block_summaries(kd, N, 64)
+    idx, _ = bsa.select_blocks(qd, summ, N, top_k=4)
+    torch.cuda.synchronize()
+    expect = [0, 1, 2, 3, 10, 28, 29]
+    assert idx.cpu().numpy()[0, 0].tolist() == expect
+    assert idx.cpu().numpy()[0, 1].tolist() == expect
+
+
+def test_split_invariance_and_determinism():
+    import torch
+    cfg = synth.scaled(synth.CONFIGS["long128k"], name="splits", batch=1, seq_len=64 * 512,
+                       top_k=60)
+    announce("split invariance", cfg)
+    t = synth.gen_decode(cfg, 41)
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    summ, _ = bsa.build_block_summaries(k, cfg.seq_len, 64)
+    idx, _ = bsa.select_blocks(q, summ, cfg.seq_len, top_k=cfg.top_k)
+    ref, ref_lse = bsa.sparse_decode_attn(q, k, v, idx, cfg.seq_len)
+    again, _ = bsa.sparse_decode_attn(q, k, v, idx, cfg.seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, again), "same plan must be bitwise reproducible"
+    for s in (1, 2, 7, 16, 63):
+        o, l = bsa.sparse_decode_attn(q, k, v, idx, cfg.seq_len, n_splits=s)
+        torch.cuda.synchronize()
+        assert (o - ref).abs().max().item() <= 1e-5, s
+        assert (l - ref_lse).abs().max().item() <= 1e-5, s
+
+
+def test_summaries_bf16_and_compressed_block_sizes():
+    import torch
+    for m, N in ((4, 64 * 50 + 2), (128, 128 * 20 + 5), (64, 64 * 33)):
+        announce("summaries m", m, "N", N)
+        cfg = synth.scaled(synth.CONFIGS["gqa32k"], batch=1, seq_len=N)
+        t = synth.gen_decode(cfg, 50 + m, capacity=N + 70)
+        k = to_dev(t["k"])
+        f32, b16 = bsa.build_block_summaries(k, N, m, want_f32=True, want_bf16=True)
+        torch.cuda.synchronize()
+        g32 = f32.cpu().numpy()
+        gb = from_dev_bf16(b16)
+        ref = oracle.block_summaries(t["k"], N, m)
+        assert np.all(np.abs(g32 - ref) <= summary_tolerance(t["k"], N, m))
+        # bf16 copy = the fp32 mean rounded to nearest even
+        assert np.array_equal(gb, synth.bf16_round(g32))
+        # and within one bf16 step of the exact mean rounded directly
+        rb = synth.bf16_to_f32(gb).astype(np.float64)
+        assert np.all(np.abs(rb - ref) <= np.abs(ref) * 2.0 ** -7 + summary_tolerance(t["k"], N, m))
+
+
+@pytest.mark.parametrize("name", ["gqa32k", "long128k", "long128k_15"])
+def test_full_size_workloads(name):
+    cfg = synth.CONFIGS[name]
+    run_decode_case(cfg, synth.DEFAULT_SEED[name])
+
+
+def test_full_size_1m():
+    run_decode_case(synth.CONFIGS["ctx1m"], synth.DEFAULT_SEED["ctx1m"])
