@@ -1,0 +1,245 @@
+"""Benchmark of the block-summary sparse decode step on one MI355X.
+
+A step is one pass of the per-token hot path over the workload's batch:
+select_blocks (block scores + top-k) then sparse_decode_attn (split-K
+attention over the kept blocks + exact merge).  Block summaries are built once
+when the cache is ingested and timed separately.
+
+Timing: W untimed warmup steps, then exactly K timed steps between a
+synchronize on both sides.  Before every step an untimed flush reads and
+writes 1 GiB so that neither L2 nor the 256 MB Infinity Cache still holds the
+previous step's KV: each step streams its kept KV from HBM.  Every call is
+bracketed by HIP events recorded on the stream the kernels are launched on.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-decode attn queries·heads/s + achieved HBM GB/s at 128K ctx, 15% keep"
+HBM_PEAK_GBS = 8000.0
+
+
+def decode_bytes(cfg, n_keep):
+    """Algorithmic bytes of one decode step (select + attend), split by call.
+
+    select: summaries (fp32) of every block + q; attend: kept K and V (bf16),
+    q, fp32 output and the index list.  Unselected KV and implementation
+    scratch (scores, split partials) are not counted."""
+    B, Hq, Hkv, d = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    nb = -(-cfg.seq_len // cfg.block_size)
+    kept_tokens = min(n_keep * cfg.block_size, cfg.seq_len)
+    sel = B * Hkv * nb * d * 4 + B * Hq * d * 2
+    att = B * Hkv * kept_tokens * d * 2 * 2 + B * Hq * d * 2 + B * Hq * d * 4 + B * Hkv * n_keep * 4
+    return sel, att
+
+
+def kv_bytes_per_token(n_layers, width, elem_bytes):
+    """K and V bytes of one token: layers x (heads*head_dim) x bytes x 2."""
+    return n_layers * width * elem_bytes * 2
+
+
+def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30):
+    import numpy as np
+    import torch
+
+    import long_context_block_summary_amd as bsa
+    from long_context_block_summary_amd import synth
+
+    dev = torch.device("cuda:0")
+    t = synth.gen_decode(cfg)
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to(t["q"]), to(t["k"]), to(t["v"])
+    N, bs = cfg.seq_len, cfg.block_size
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev)
+    flush.zero_()
+
+    # ingest: summaries (S1), cold
+    summ = torch.empty((cfg.batch, cfg.n_kv_heads, -(-N // bs), cfg.head_dim),
+                       dtype=torch.float32, device=dev)
+    sum_ms = []
+    for _ in range(3):
+        flush.add_(1.0)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        bsa.build_block_summaries(k, N, bs, out_f32=summ)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sum_ms.append(e0.elapsed_time(e1))
+
+    cfgc = bsa.select_cfg(bs, cfg.n_sink, cfg.n_local, cfg.top_k, cfg.keep_ratio)
+    n_keep = bsa.num_kept(-(-N // bs), cfgc)
+    idx = torch.empty((cfg.batch, cfg.n_kv_heads, n_keep), dtype=torch.int32, device=dev)
+    out = torch.empty((cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.batch, cfg.n_q_heads), dtype=torch.float32, device=dev)
+    ws_sel = torch.empty(cfg.batch * cfg.n_kv_heads * (-(-N // bs)) * 4, dtype=torch.uint8,
+                         device=dev)
+    ws_dec = torch.zeros(max(16, bsa.decode_workspace_size(cfg.batch, cfg.n_q_heads,
+                                                           cfg.n_kv_heads, cfg.head_dim, N,
+                                                           n_keep)),
+                         dtype=torch.uint8, device=dev)
+
+    def step(e0=None, e1=None, e2=None):
+        if e0 is not None:
+            e0.record(stream)
+        bsa.select_blocks(q, summ, N, bs, cfg.n_sink, cfg.n_local, cfg.top_k, cfg.keep_ratio,
+                          block_idx=idx, workspace=ws_sel)
+        if e1 is not None:
+            e1.record(stream)
+        bsa.sparse_decode_attn(q, k, v, idx, N, bs, out=out, lse=lse, workspace=ws_dec)
+        if e2 is not None:
+            e2.record(stream)
+
+    for _ in range(warmup):
+        flush.add_(1.0)
+        step()
+    events = [(ev(), ev(), ev()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for e in events:
+        flush.add_(1.0)
+        step(*e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    sel_ms = [a.elapsed_time(b) for a, b, _ in events]
+    att_ms = [b.elapsed_time(c) for _, b, c in events]
+    step_ms = [a.elapsed_time(c) for a, _, c in events]
+
+    # warm-cache (no flush) for reference only
+    torch.cuda.synchronize()
+    we = [(ev(), ev(), ev()) for _ in range(steps)]
+    for e in we:
+        step(*e)
+    torch.cuda.synchronize()
+    warm_ms = [a.elapsed_time(c) for a, _, c in we]
+    return {
+        "n_keep": n_keep,
+        "sum_ms": sorted(sum_ms)[len(sum_ms) // 2],
+        "sel_ms": sum(sel_ms) / len(sel_ms),
+        "att_ms": sum(att_ms) / len(att_ms),
+        "step_ms": sum(step_ms) / len(step_ms),
+        "step_ms_median": sorted(step_ms)[len(step_ms) // 2],
+        "warm_step_ms": sum(warm_ms) / len(warm_ms),
+        "wall_s": wall,
+        "inputs": t,
+    }
+
+
+def run_cpu_baseline(cfg, t, budget_s=20.0):
+    """Oracle select + attend (given its fp64 summaries) on a bounded sample."""
+    import numpy as np
+
+    import oracle
+    B = cfg.batch
+    summ = oracle.block_summaries(t["k"], cfg.seq_len, cfg.block_size)
+
+    def one(bsl):
+        t0 = time.perf_counter()
+        idx, _ = oracle.select_blocks(t["q"][bsl], summ[bsl], cfg.n_kv_heads, cfg.n_sink,
+                                      cfg.n_local, cfg.top_k, cfg.keep_ratio)
+        oracle.sparse_decode_attn(t["q"][bsl], t["k"][bsl], t["v"][bsl], idx, cfg.seq_len,
+                                  cfg.block_size)
+        return time.perf_counter() - t0
+
+    first = one(slice(0, 1))
+    nb_used = 1
+    if first * B <= budget_s and B > 1:
+        elapsed = one(slice(0, B))
+        nb_used = B
+    else:
+        elapsed = first
+    qh = nb_used * cfg.n_q_heads
+    return {"value": qh / elapsed, "unit": "queries*heads/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{cfg.name}: select + attend (fp64 oracle, summaries precomputed) for "
+                      f"{nb_used} of {B} batch entries ({qh} query heads), one pass, "
+                      f"{elapsed:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long128k_15")
+    ap.add_argument("--also", default="long128k",
+                    help="comma list of extra decode workloads reported alongside ('none' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path shards by (batch, kv head) with no exchange; see the design "
+              "notes)", file=sys.stderr)
+        sys.exit(2)
+
+    from long_context_block_summary_amd import synth
+    cfg = synth.CONFIGS[args.workload]
+    r = run_gpu(cfg, args.steps, args.warmup)
+    sel_b, att_b = decode_bytes(cfg, r["n_keep"])
+    qh = cfg.batch * cfg.n_q_heads
+    step_s = r["step_ms"] / 1e3
+    att_gbs = att_b / (r["att_ms"] / 1e3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": qh / step_s,
+        "unit": "queries*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "n_q_heads": cfg.n_q_heads,
+                   "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
+                   "seq_len": cfg.seq_len, "block_size": cfg.block_size,
+                   "n_sink_blocks": cfg.n_sink, "n_local_blocks": cfg.n_local,
+                   "top_k": cfg.top_k, "n_keep": r["n_keep"],
+                   "keep_pct": round(100.0 * r["n_keep"] / -(-cfg.seq_len // cfg.block_size), 2)},
+        "step_GBps": (sel_b + att_b) / step_s / 1e9,
+        "roofline": {"bound": "hbm", "kernel": "sparse_decode_attn",
+                     "achieved": att_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": att_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": att_b, "avg_us": r["att_ms"] * 1e3},
+        "breakdown_us": {"select_blocks": r["sel_ms"] * 1e3,
+                         "sparse_decode_attn": r["att_ms"] * 1e3,
+                         "build_block_summaries_ingest": r["sum_ms"] * 1e3},
+        "select_GBps": sel_b / (r["sel_ms"] / 1e3) / 1e9,
+        "warm_cache_ms_per_step": r["warm_step_ms"],
+        "step_ms_median": r["step_ms_median"],
+        "timed_wall_s": r["wall_s"],
+        "cache_flush": "1 GiB read+write before every step (untimed)",
+    }
+    extra = {}
+    for name in [s for s in args.also.split(",") if s and s != "none"]:
+        c2 = synth.CONFIGS[name]
+        r2 = run_gpu(c2, max(10, args.steps // 2), 3)
+        s2, a2 = decode_bytes(c2, r2["n_keep"])
+        extra[name] = {"queries_heads_per_s": c2.batch * c2.n_q_heads / (r2["step_ms"] / 1e3),
+                       "ms_per_step": r2["step_ms"], "n_keep": r2["n_keep"],
+                       "attn_GBps": a2 / (r2["att_ms"] / 1e3) / 1e9,
+                       "attn_frac": a2 / (r2["att_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                       "step_GBps": (s2 + a2) / (r2["step_ms"] / 1e3) / 1e9,
+                       "select_us": r2["sel_ms"] * 1e3, "attn_us": r2["att_ms"] * 1e3}
+        del r2
+    if extra:
+        line["also"] = extra
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = run_cpu_baseline(cfg, r["inputs"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -132,7 +132,9 @@ int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
  *   scale      0 selects 1/sqrt(d)
  *   out        fp32 [B][Hq][d]
  *   lse        fp32 [B][Hq] natural-log log-sum-exp of the scaled logits, or NULL
- *   workspace  bsa_decode_workspace_size(shape, n_keep, block_size, 0) bytes
+ *   workspace  bsa_decode_workspace_size(shape, n_keep, block_size, 0) bytes, 16-byte
+ *              aligned: split partials (o, m, l); contents on entry are irrelevant.
+ *              Calls that overlap in time must not share a workspace.
  * block_size must be 64; n_keep >= 1; Hq/Hkv in {1, 2, 4, 8, 16}.  A partial
  * last block contributes only its tokens below seq_len. */
 int sparse_decode_attn(const void* q, const void* k, const void* v, const int32_t* block_idx,

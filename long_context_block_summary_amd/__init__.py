@@ -198,8 +198,8 @@ def sparse_decode_attn(q, k, v, block_idx, seq_len, block_size=64, scale=0.0, n_
     ws_bytes = lib().bsa_decode_workspace_size(ctypes.byref(shape), n_keep, block_size, n_splits)
     if ws_bytes == SIZE_MAX:
         raise ValueError("invalid decode arguments")
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if workspace is None:  # must be zero before first use (the kernels keep it so)
+        workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:

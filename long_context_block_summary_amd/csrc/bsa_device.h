@@ -15,6 +15,11 @@ __device__ __forceinline__ uint4 ld_stream(const uint4* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ uint2 ld_stream(const uint2* p) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ float4 ld_stream(const float4* p) {
   const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
   return make_float4(v.x, v.y, v.z, v.w);

@@ -1,23 +1,30 @@
 // kernels_decode.hip -- split-K sparse decode attention over kept 64-token blocks.
 //
 // Exact softmax(q K^T * scale) V over the tokens of the kept blocks only
-// ("CSA + HCA 混合注意力机制" §2.1 and §4.4 step 4).  Decode reads the whole
-// kept KV once per step and does g flop per KV byte (g = query heads per kv
-// head), so the kernel is built to stream bf16 K/V at HBM rate on the VALU:
+// ("CSA + HCA 混合注意力机制" §2.1 and §4.4 step 4).  Decode streams the kept
+// KV once per step; its rate is set by how many bytes each CU keeps in
+// flight, so the kernel is built around a deep per-wave load pipeline:
 //
-//  * a workgroup = 4 waves owns one split (a contiguous run of the pair's
-//    kept-block list); wave w takes every 4th block of the run;
-//  * QK: lane t owns token t of the block and holds its whole key row
-//    (d/8 16-byte loads, one contiguous row per lane), the group's queries
-//    sit in LDS and are read as broadcasts; v_dot2_f32_bf16 does 2 MACs per
-//    lane per instruction with exact bf16 products and fp32 sums;
-//  * online softmax in base 2 with a wave-uniform running max per head;
-//  * PV: lane (tg, dc) owns 8 value columns (dc) of every TG-th token (tg),
-//    so each load instruction reads TG consecutive value rows (1 KiB
-//    contiguous for d=128); the weights go through LDS (written by token
-//    lanes, read as 16-byte broadcasts), fp32 FMA accumulation;
-//  * the 4 waves merge in LDS and write one (o, m, l) partial per head;
-//  * a second kernel merges the splits exactly with log-sum-exp weights.
+//  * a workgroup of 4 waves owns one split (a contiguous run of one
+//    (batch, kv head) pair's kept-block list); wave w owns tokens
+//    [16w, 16w+16) of every block of the run, i.e. one 16-token tile per
+//    block, and keeps its own online-softmax state;
+//  * per tile a wave needs only 4 KiB of K and 4 KiB of V, so P tiles
+//    (P = 4, or 2 for 16 query heads per kv head) are requested ahead into
+//    registers: the loop always issues the tile P-1 steps ahead (a dummy
+//    broadcast load past the end) and never branches around its loads;
+//  * QK on the matrix cores: the g query heads of the kv group share each
+//    key tile, S^T[16 x 16] = K_tile[16 x d] q^T[d x 16] is d/32
+//    v_mfma_f32_16x16x32_bf16 (heads past g are zero); q stays in
+//    registers as the B operand; K fragments come straight from HBM in the
+//    A-operand layout (lane l: token l%16, 16 bytes at 32*kstep + 8*(l/16));
+//  * online softmax in base 2 per head in the MFMA accumulator layout, the
+//    tile max across the 4 lanes of a head by two cross-lane exchanges;
+//  * PV on the VALU: lane (ts, dq) owns 4 value columns (dq) of every
+//    (64/(d/4))-th token of the tile, so each 8-byte load instruction reads
+//    whole value rows; the weights reach those lanes through LDS;
+//  * the 4 waves merge in LDS into one (o, m, l) partial per head, and a
+//    second small kernel merges the splits exactly with log-sum-exp weights.
 #include <math.h>
 
 #include "bsa_device.h"
@@ -25,218 +32,266 @@
 
 namespace bsa {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
 constexpr int DEC_WAVES = 4;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-template <int D, int G>
-__global__ __launch_bounds__(256) void decode_partial_kernel(
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// blocks in flight per wave (register budget: two waves per SIMD)
+template <int G> struct DecStages { static constexpr int value = G >= 16 ? 2 : 4; };
+
+template <int D, int G, int P>
+__global__ __launch_bounds__(256, 2) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, int n_keep, int Hq, int Hkv,
     int N, int stride, float scale_log2, int bps, int n_splits, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
-  constexpr int DC = D / 8;        // 16-byte column chunks per row
-  constexpr int TG = 64 / DC;      // token groups in the PV layout
-  constexpr int TPL = 64 / TG;     // tokens per lane in the PV layout
-  constexpr int PROW = TPL + 4;    // padded LDS row of weights (bank spread)
-  __shared__ __align__(16) uint4 q_lds[G * DC];
-  __shared__ __align__(16) float p_lds[DEC_WAVES][G][TG * PROW];
+  constexpr int KS = D / 32;        // MFMA k-steps over the head dim
+  constexpr int DQ = D / 4;         // 4-column groups per row: lane owns one group
+  constexpr int VT = 64 / DQ;       // token subgroups in the PV layout (2 for d=128)
+  constexpr int TPL = 16 / VT;      // tokens of the tile per lane (PV layout)
+  constexpr int GP = G < 4 ? 4 : G;  // padded weights row
+  __shared__ __align__(16) float p_lds[DEC_WAVES][16 * GP];
+  __shared__ __align__(16) float a_lds[DEC_WAVES][GP];
   __shared__ __align__(16) float m_lds[DEC_WAVES][G][2];
   __shared__ __align__(16) float o_lds[DEC_WAVES][G][D];
 
   const int split = blockIdx.x;
   const int pair = blockIdx.y;
   const int b = pair / Hkv, kvh = pair % Hkv;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int l16 = lane & 15, j4 = lane >> 4;
+  const int dq = lane % DQ, ts = lane / DQ;
 
-  {  // the group's queries -> LDS
+  // q^T as the MFMA B operand: lane l holds head l%16, dims 32*ks + 8*(l/16) .. +8
+  uint4 qf[KS];
+  {
     const uint4* qs = reinterpret_cast<const uint4*>(q + ((int64_t)b * Hq + (int64_t)kvh * G) * D);
-    for (int i = tid; i < G * DC; i += 256) q_lds[i] = qs[i];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = (l16 < G) ? qs[l16 * (D / 8) + ks * 4 + j4] : make_uint4(0, 0, 0, 0);
   }
-  __syncthreads();
 
   const int blk0 = split * bps;
-  const int blk1 = min(n_keep, blk0 + bps);
-  const int32_t* list = idx + (int64_t)pair * n_keep;
-  const uint16_t* kbase = k + (int64_t)pair * stride * D;
-  const uint16_t* vbase = v + (int64_t)pair * stride * D;
-  const int tg = lane / DC, dc = lane % DC;
+  const int nblk = min(n_keep, blk0 + bps) - blk0;
+  const int32_t* list = idx + (int64_t)pair * n_keep + blk0;
+  const char* kb = reinterpret_cast<const char*>(k + (int64_t)pair * stride * D);
+  const char* vb = reinterpret_cast<const char*>(v + (int64_t)pair * stride * D);
+  const int tile0 = 16 * wave;  // this wave's 16 tokens of every block
 
-  float m_run[G], l_lane[G], acc[G][8];
+  float m_run = -INFINITY, l_run = 0.f;  // head l16 over this lane's tokens
+  float acc[G][4];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m_run[h] = -INFINITY;
-    l_lane[h] = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
-  }
+  for (int h = 0; h < G; ++h) acc[h][0] = acc[h][1] = acc[h][2] = acc[h][3] = 0.f;
 
-  for (int blk = blk0 + wave; blk < blk1; blk += DEC_WAVES) {
-    const int t0 = list[blk] * 64;
-    // key row of token t0 + lane; values: TPL rows per lane
-    uint4 kr[DC];
-    uint4 vr[TPL];
-    const bool kvalid = t0 + lane < N;
-    {
-      const uint4* kp = reinterpret_cast<const uint4*>(kbase + (int64_t)(t0 + lane) * D);
+  // register pipeline: P blocks in flight per wave (K tile + V tile)
+  uint4 kbuf[P][KS];
+  uint2 vbuf[P][TPL];
+  // j >= nblk issues a dummy load (every lane reads the pair's first row) so
+  // the pipeline never branches around its loads
+  auto issue = [&](int slot, int j) {
+    const bool real = j < nblk;
+    const int t0 = list[real ? j : 0] * 64 + tile0;
+    const uint32_t koff =
+        real ? (uint32_t)min(t0 + l16, N - 1) * (D * 2) + j4 * 16 : 0u;
 #pragma unroll
-      for (int c = 0; c < DC; ++c) kr[c] = kvalid ? ld_stream(kp + c) : make_uint4(0, 0, 0, 0);
-      const uint4* vp = reinterpret_cast<const uint4*>(vbase + (int64_t)(t0 + tg) * D) + dc;
+    for (int ks = 0; ks < KS; ++ks)
+      kbuf[slot][ks] = ld_stream(reinterpret_cast<const uint4*>(kb + koff + (real ? ks * 64 : 0)));
 #pragma unroll
-      for (int i = 0; i < TPL; ++i) {
-        const bool ok = t0 + i * TG + tg < N;
-        vr[i] = ok ? ld_stream(vp + (int64_t)i * TG * DC) : make_uint4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < TPL; ++i) {
+      const uint32_t voff =
+          real ? (uint32_t)min(t0 + ts + VT * i, N - 1) * (D * 2) + dq * 8 : 0u;
+      vbuf[slot][i] = ld_stream(reinterpret_cast<const uint2*>(vb + voff));
     }
-    // logits (base 2) of this lane's token for every head
-    float z[G];
+  };
+  float* pl = p_lds[wave];
+  auto compute = [&](int slot, int j) {
+    const int t0 = list[j] * 64 + tile0;
+    // S^T tile: lane l gets tokens 4*(l/16) + i of the tile, head l%16
+    f32x4v sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kbuf[slot][ks]), as_bf16x8(qf[ks]),
+                                                   sc, 0, 0, 0);
+    float z[4];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = (t0 + 4 * j4 + i < N) ? sc[i] * scale_log2 : -INFINITY;
+      bm = fmaxf(bm, z[i]);
+    }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float m_new = fmaxf(m_run, bm);
+    // a tile past seq_len has no valid token: keep everything at zero
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = __builtin_amdgcn_exp2f(z[i] - m_use);
+      ps += p;
+      if (l16 < G) pl[(4 * j4 + i) * GP + l16] = p;
+    }
+    l_run = l_run * alpha + ps;
+    if (j4 == 0 && l16 < G) a_lds[wave][l16] = alpha;
+    wave_lds_sync();
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float s0 = 0.f, s1 = 0.f;
+      const float al = a_lds[wave][h];
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        const uint4 qq = q_lds[h * DC + c];
-        s0 = dot2(qq.x, kr[c].x, s0);
-        s1 = dot2(qq.y, kr[c].y, s1);
-        s0 = dot2(qq.z, kr[c].z, s0);
-        s1 = dot2(qq.w, kr[c].w, s1);
-      }
-      z[h] = kvalid ? (s0 + s1) * scale_log2 : -INFINITY;
+      for (int c = 0; c < 4; ++c) acc[h][c] *= al;
     }
-    // online softmax; weights of token `lane` go to LDS in the PV layout
-    const int pw = (lane % TG) * PROW + lane / TG;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float m_new = fmaxf(m_run[h], wave_max(z[h]));
-      const float alpha = exp2f(m_run[h] - m_new);
-      const float p = exp2f(z[h] - m_new);
-      l_lane[h] = l_lane[h] * alpha + p;
-      m_run[h] = m_new;
+    for (int i = 0; i < TPL; ++i) {
+      const float vv[4] = {bf_lo(vbuf[slot][i].x), bf_hi(vbuf[slot][i].x),
+                           bf_lo(vbuf[slot][i].y), bf_hi(vbuf[slot][i].y)};
+      const float* prow = pl + (ts + VT * i) * GP;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[h][c] *= alpha;
-      p_lds[wave][h][pw] = p;
-    }
-    wave_lds_sync();
-    // PV
+      for (int h4 = 0; h4 < G; h4 += 4) {
+        const float4 pp = *reinterpret_cast<const float4*>(prow + h4);
+        const float pv[4] = {pp.x, pp.y, pp.z, pp.w};
 #pragma unroll
-    for (int i4 = 0; i4 < TPL; i4 += 4) {
-      float vf[4][8];
+        for (int u = 0; u < 4; ++u)
+          if (h4 + u < G) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) unpack8(vr[i4 + u], vf[u]);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float4 pp = *reinterpret_cast<const float4*>(&p_lds[wave][h][tg * PROW + i4]);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          float a = acc[h][c];
-          a = fmaf(pp.x, vf[0][c], a);
-          a = fmaf(pp.y, vf[1][c], a);
-          a = fmaf(pp.z, vf[2][c], a);
-          a = fmaf(pp.w, vf[3][c], a);
-          acc[h][c] = a;
-        }
+            for (int c = 0; c < 4; ++c) acc[h4 + u][c] = fmaf(pv[u], vv[c], acc[h4 + u][c]);
+          }
       }
     }
     wave_lds_sync();
+  };
+
+#pragma unroll
+  for (int s = 0; s < P - 1; ++s) issue(s, s);
+  for (int it = 0; it < nblk; it += P) {
+#pragma unroll
+    for (int s = 0; s < P; ++s) {
+      issue((s + P - 1) % P, it + s + P - 1);
+      if (it + s < nblk) compute(s, it + s);
+    }
   }
 
-  // per wave: combine token groups (lanes dc + DC*tg) and the per-lane l
+  // per wave: l over the 4 lanes of a head; acc over the token subgroups
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float lt = wave_sum(l_lane[h]);
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float a = acc[h][c];
+    for (int off = DQ; off < 64; off <<= 1)
 #pragma unroll
-      for (int off = DC; off < 64; off <<= 1) a += __shfl_xor(a, off);
-      acc[h][c] = a;
-    }
-    if (lane < DC) {
-      float4* dst = reinterpret_cast<float4*>(&o_lds[wave][h][lane * 8]);
-      dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-      dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-    }
-    if (lane == 0) {
-      m_lds[wave][h][0] = m_run[h];
-      m_lds[wave][h][1] = lt;
-    }
+      for (int c = 0; c < 4; ++c) acc[h][c] += __shfl_xor(acc[h][c], off);
+  if (ts == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      *reinterpret_cast<float4*>(&o_lds[wave][h][4 * dq]) =
+          make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+  }
+  if (j4 == 0 && l16 < G) {
+    m_lds[wave][l16][0] = m_run;
+    m_lds[wave][l16][1] = l_run;
   }
   __syncthreads();
-  // merge the 4 waves (a wave with no block has m = -inf, l = 0, o = 0)
+  // merge the 4 waves: each holds a softmax partial over its quarter of every block
   const int64_t pbase = ((int64_t)pair * n_splits + split) * G;
   for (int e = tid; e < G * D; e += 256) {
     const int h = e / D, c = e % D;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < DEC_WAVES; ++w) M = fmaxf(M, m_lds[w][h][0]);
-    float o = 0.f;
+    float o = 0.f, L = 0.f;
 #pragma unroll
     for (int w = 0; w < DEC_WAVES; ++w) {
       const float mw = m_lds[w][h][0];
       const float sc = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
       o = fmaf(sc, o_lds[w][h][c], o);
+      L = fmaf(sc, m_lds[w][h][1], L);
     }
     part_o[(pbase + h) * D + c] = o;
     if (c == 0) {
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < DEC_WAVES; ++w) {
-        const float mw = m_lds[w][h][0];
-        const float sc = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-        L = fmaf(sc, m_lds[w][h][1], L);
-      }
       part_ml[(pbase + h) * 2 + 0] = M;
       part_ml[(pbase + h) * 2 + 1] = L;
     }
   }
 }
 
-// exact merge of the splits of one (batch, query head): one wave, d/64 columns per lane
+// Exact merge of the splits of one (batch, query head): M = max m_s,
+// L = sum 2^(m_s - M) l_s, o = sum 2^(m_s - M) o_s / L, lse = (M + log2 L) ln 2.
+// One workgroup of D threads per (batch, query head); the split weights are
+// computed once into LDS, then every column sums its splits with independent
+// loads.  A separate launch: the kernel boundary makes the partials of all
+// workgroups visible (an agent-scope fence per workgroup is far more costly
+// on a multi-XCD part).
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part_o,
-                                                          const float* __restrict__ part_ml,
-                                                          int G, int Hq, int Hkv, int S,
-                                                          float* __restrict__ out,
-                                                          float* __restrict__ lse) {
-  constexpr int PER = D / 64;
+__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ part_o,
+                                                         const float* __restrict__ part_ml,
+                                                         int G, int Hq, int Hkv, int S,
+                                                         float* __restrict__ out,
+                                                         float* __restrict__ lse) {
+  constexpr int SMAX = 1024;
+  __shared__ float w_lds[SMAX];
+  __shared__ float red[D / 64][2];
   const int bh = blockIdx.x;
   const int b = bh / Hq, h = bh % Hq;
   const int pair = b * Hkv + h / G, hh = h % G;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r0 = (int64_t)pair * S * G + hh;  // row of split s: r0 + s * G
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, part_ml[(((int64_t)pair * S + s) * G + hh) * 2]);
-  float L = 0.f, o[PER];
+  for (int s2 = tid; s2 < S; s2 += D) M = fmaxf(M, part_ml[(r0 + (int64_t)s2 * G) * 2]);
+  M = wave_max(M);
+  if (lane == 0) red[wave][0] = M;
+  __syncthreads();
 #pragma unroll
-  for (int c = 0; c < PER; ++c) o[c] = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const int64_t r = ((int64_t)pair * S + s) * G + hh;
-    const float ms = part_ml[r * 2];
-    const float sc = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-    L = fmaf(sc, part_ml[r * 2 + 1], L);
-#pragma unroll
-    for (int c = 0; c < PER; ++c) o[c] = fmaf(sc, part_o[r * D + lane + 64 * c], o[c]);
+  for (int w = 0; w < D / 64; ++w) M = fmaxf(M, red[w][0]);
+  float L = 0.f, o = 0.f;
+  for (int sb = 0; sb < S; sb += SMAX) {
+    const int se = min(S, sb + SMAX);
+    __syncthreads();
+    for (int s2 = sb + tid; s2 < se; s2 += D) {
+      const int64_t r = r0 + (int64_t)s2 * G;
+      const float ms = part_ml[r * 2];
+      const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      w_lds[s2 - sb] = w;
+      L = fmaf(w, part_ml[r * 2 + 1], L);
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int s2 = sb; s2 < se; ++s2) o = fmaf(w_lds[s2 - sb], part_o[(r0 + (int64_t)s2 * G) * D + tid], o);
   }
-  const float inv = 1.f / L;
+  L = wave_sum(L);
+  if (lane == 0) red[wave][1] = L;
+  __syncthreads();
+  L = 0.f;
 #pragma unroll
-  for (int c = 0; c < PER; ++c) out[(int64_t)bh * D + lane + 64 * c] = o[c] * inv;
-  if (lse && lane == 0) lse[bh] = (M + log2f(L)) * LN2;
+  for (int w = 0; w < D / 64; ++w) L += red[w][1];
+  out[(int64_t)bh * D + tid] = o / L;
+  if (lse && tid == 0) lse[bh] = (M + log2f(L)) * LN2;
 }
+
+// Two workgroups of 4 waves fit per CU (two waves per SIMD), so the plan aims
+// at one full round of 512 workgroups over the MI355X's 256 CUs: splits per
+// pair = round(512 / pairs), each split a contiguous run of the kept-block
+// list.  More pairs than that: one split per pair.
+constexpr int DEC_TARGET_WGS = 512;
 
 DecodePlan plan_decode(int64_t pairs, int n_keep, int g, int n_splits_req) {
   DecodePlan p;
   p.g = g;
-  if (n_splits_req > 0) {
-    const int s = n_splits_req < n_keep ? n_splits_req : n_keep;
-    p.bps = (n_keep + s - 1) / s;
-  } else {
-    // about 1024 workgroups (4 per CU), at least one block per wave
-    const int64_t total = pairs * (int64_t)n_keep;
-    int64_t bps = (total + 1023) / 1024;
-    if (bps < DEC_WAVES) bps = DEC_WAVES;
-    bps = (bps + DEC_WAVES - 1) / DEC_WAVES * DEC_WAVES;
-    if (bps > n_keep) bps = n_keep;
-    p.bps = (int)bps;
+  int64_t s = n_splits_req;
+  if (s <= 0) {
+    s = (DEC_TARGET_WGS + pairs / 2) / pairs;
+    if (s < 1) s = 1;
   }
+  if (s > n_keep) s = n_keep;
+  p.bps = (int)((n_keep + s - 1) / s);
   p.n_splits = (n_keep + p.bps - 1) / p.bps;
   return p;
 }
@@ -251,14 +306,14 @@ static void launch_decode_t(const uint16_t* q, const uint16_t* k, const uint16_t
                             int stride, float scale, const DecodePlan& plan, float* ws,
                             float* out, float* lse, hipStream_t st) {
   const int64_t pairs = (int64_t)B * Hkv;
-  float* part_o = ws;
-  float* part_ml = ws + (size_t)pairs * plan.n_splits * G * D;
+  float* part_ml = ws;
+  float* part_o = part_ml + (size_t)pairs * plan.n_splits * G * 2;
   dim3 grid(plan.n_splits, (unsigned)pairs);
-  decode_partial_kernel<D, G><<<grid, 256, 0, st>>>(q, k, v, idx, n_keep, Hq, Hkv, N, stride,
-                                                    scale * LOG2E, plan.bps, plan.n_splits,
-                                                    part_o, part_ml);
-  decode_merge_kernel<D><<<(unsigned)(B * Hq), 64, 0, st>>>(part_o, part_ml, G, Hq, Hkv,
-                                                            plan.n_splits, out, lse);
+  decode_kernel<D, G, DecStages<G>::value><<<grid, 256, 0, st>>>(
+      q, k, v, idx, n_keep, Hq, Hkv, N, stride, scale * LOG2E, plan.bps, plan.n_splits, part_o,
+      part_ml);
+  decode_merge_kernel<D><<<(unsigned)(B * Hq), D, 0, st>>>(part_o, part_ml, G, Hq, Hkv,
+                                                           plan.n_splits, out, lse);
 }
 
 void launch_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,

@@ -53,7 +53,7 @@ def test_workspace_sizes(L):
     cfg = bsa.select_cfg(top_k=202)
     assert L.bsa_select_workspace_size(ctypes.byref(sh), ctypes.byref(cfg)) == 4 * 8 * 2048 * 4
     ws1 = L.bsa_decode_workspace_size(ctypes.byref(sh), 205, 64, 1)
-    assert ws1 == 32 * 1 * 8 * 130 * 4
+    assert ws1 == 32 * 1 * 8 * 130 * 4   # (o, m, l) split partials
     assert L.bsa_decode_workspace_size(ctypes.byref(sh), 205, 64, 0) >= ws1
     bad = bsa.make_shape(4, 63, 8, 128, 10, 10)
     assert L.bsa_decode_workspace_size(ctypes.byref(bad), 5, 64, 0) == bsa.SIZE_MAX
