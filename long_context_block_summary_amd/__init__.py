@@ -259,3 +259,24 @@ def decode_step(q, k, v, summaries, seq_len, block_size=64, n_sink=1, n_local=2,
     idx, _ = select_blocks(q, summaries, seq_len, block_size, n_sink, n_local, top_k, keep_ratio)
     out, lse = sparse_decode_attn(q, k, v, idx, seq_len, block_size, scale)
     return out, lse, idx
+
+
+def build_compressed_streams(k, v, prior_len, cfg=None):
+    """The prefill's pooled streams over the prior tokens: fp32 + bf16 keys and bf16 values at
+    m_sparse, bf16 keys and values at m_dense (all via build_block_summaries)."""
+    cfg = cfg or prefill_cfg()
+    k4f, k4b = build_block_summaries(k, prior_len, cfg.m_sparse, want_f32=True, want_bf16=True)
+    _, v4b = build_block_summaries(v, prior_len, cfg.m_sparse, want_f32=False, want_bf16=True)
+    _, k128b = build_block_summaries(k, prior_len, cfg.m_dense, want_f32=False, want_bf16=True)
+    _, v128b = build_block_summaries(v, prior_len, cfg.m_dense, want_f32=False, want_bf16=True)
+    return k4f, k4b, v4b, k128b, v128b
+
+
+def prefill_step(q, k, v, prior_len, cfg=None, scale=0.0, want_lse3=False, want_sel=False,
+                 streams=None):
+    """Chunked prefill: pooled streams (unless given), then sparse_prefill_attn."""
+    cfg = cfg or prefill_cfg()
+    if streams is None:
+        streams = build_compressed_streams(k, v, prior_len, cfg)
+    return sparse_prefill_attn(q, k, v, *streams, prior_len, cfg=cfg, scale=scale,
+                               want_lse3=want_lse3, want_sel=want_sel)

@@ -32,4 +32,25 @@ void launch_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, cons
                    int n_keep, int B, int Hq, int Hkv, int d, int N, int stride, float scale,
                    const DecodePlan& plan, float* ws, float* out, float* lse, hipStream_t st);
 
+// chunked prefill: pooled queries, scores, top-k, three-branch attention
+struct PrefillLaunch {
+  const uint16_t* q;      // [B][C][Hq][128]
+  const uint16_t* k;      // [B][Hkv][stride][128]
+  const uint16_t* v;
+  const float* k4f;       // [B][Hkv][E4][128] fp32 (scoring copy)
+  const uint16_t* k4b;    // [B][Hkv][E4][128] bf16
+  const uint16_t* v4b;
+  const uint16_t* k128b;  // [B][Hkv][E128][128] bf16
+  const uint16_t* v128b;
+  float* out;             // [B][C][Hq][128]
+  float* lse3;            // [3][B][C][Hq] or null
+  int32_t* sel_out;       // [B][n_tiles][Hkv][ksel] or null (then kept in the workspace)
+  void* workspace;
+  int B, C, Hq, Hkv, P, stride, E4, E128, ksel, window, q_tile, n_tiles;
+  float scale;
+};
+constexpr int PREFILL_MAX_E4 = 131072;  // entries of the selected stream per (b, kv head)
+size_t prefill_workspace_bytes(int B, int Hkv, int D, int n_tiles, int E4, int ksel, bool need_sel);
+bool launch_prefill(const PrefillLaunch& L, hipStream_t st);
+
 }  // namespace bsa

@@ -10,7 +10,7 @@
 //    [16w, 16w+16) of every block of the run, i.e. one 16-token tile per
 //    block, and keeps its own online-softmax state;
 //  * per tile a wave needs only 4 KiB of K and 4 KiB of V, so P tiles
-//    (P = 4, or 2 for 16 query heads per kv head) are requested ahead into
+//    (P = 3, or 2 for 16 query heads per kv head) are requested ahead into
 //    registers: the loop always issues the tile P-1 steps ahead (a dummy
 //    broadcast load past the end) and never branches around its loads;
 //  * QK on the matrix cores: the g query heads of the kv group share each
@@ -44,7 +44,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
 }
 
 // blocks in flight per wave (register budget: two waves per SIMD)
-template <int G> struct DecStages { static constexpr int value = G >= 16 ? 2 : 4; };
+template <int G> struct DecStages { static constexpr int value = G >= 16 ? 2 : 3; };
 
 template <int D, int G, int P>
 __global__ __launch_bounds__(256, 2) void decode_kernel(

@@ -1,0 +1,106 @@
+"""GPU parity of the chunked-prefill path (streams, tile selection, three branches) vs the oracle.
+
+Every case prints its name, seed and shapes before touching the GPU.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import long_context_block_summary_amd as bsa
+from long_context_block_summary_amd import synth
+from parity_rules import OUT_ATOL, TIE_REL, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    bsa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def announce(*a):
+    print("[case]", *a, flush=True)
+
+
+def check_tile_selection(g_sel, o_sel, o_scores, rel=TIE_REL):
+    """Per (b, tile, kvh): equal sets, or differences only at near-ties of the k-th score."""
+    exempt = 0
+    B, T, H, k = g_sel.shape
+    for b in range(B):
+        for t in range(T):
+            for h in range(H):
+                g, o = g_sel[b, t, h], o_sel[b, t, h]
+                assert np.all(np.diff(g) > 0), (b, t, h)
+                if np.array_equal(g, o):
+                    continue
+                sc = o_scores[b, t, h]
+                tau = sc[o].min()
+                for j in set(g.tolist()) ^ set(o.tolist()):
+                    assert abs(sc[j] - tau) <= rel * max(abs(sc[j]), abs(tau)), (b, t, h, j)
+                    exempt += 1
+    return exempt
+
+
+def run_prefill_case(cfg, seed, rows=None):
+    import torch
+    announce(cfg.name, "seed", seed, "B", cfg.batch, "Hq", cfg.n_q_heads, "Hkv", cfg.n_kv_heads,
+             "P", cfg.prior_len, "C", cfg.chunk_len, "m", cfg.m_sparse, cfg.m_dense, "top_k",
+             cfg.top_k_sparse, "window", cfg.window, "q_tile", cfg.q_tile)
+    t = synth.gen_prefill(cfg, seed)
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    pc = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile)
+    out, lse3, sel = bsa.prefill_step(q, k, v, cfg.prior_len, pc, want_lse3=True, want_sel=True)
+    torch.cuda.synchronize()
+    g_out, g_lse3, g_sel = out.cpu().numpy(), lse3.cpu().numpy(), sel.cpu().numpy()
+    common = dict(m_sparse=cfg.m_sparse, top_k=cfg.top_k_sparse, m_dense=cfg.m_dense,
+                  window=cfg.window, q_tile=cfg.q_tile)
+    ref_sel = oracle.sparse_prefill_attn(t["q"], t["k"], t["v"], cfg.prior_len, rows=[0],
+                                         want_sel=True, want_sel_scores=True, **common)
+    exempt = check_tile_selection(g_sel, ref_sel["sel"], ref_sel["sel_scores"])
+    ref = oracle.sparse_prefill_attn(t["q"], t["k"], t["v"], cfg.prior_len, sel_in=g_sel,
+                                     rows=rows, **common)
+    gsub = g_out if rows is None else g_out[:, rows]
+    lsub = g_lse3 if rows is None else g_lse3[:, :, rows]
+    err = np.abs(gsub - ref["out"]).max()
+    lerr = np.abs(lsub - ref["lse3"]).max()
+    announce("  exempt ties", exempt, "max|out err|", err, "max|lse err|", lerr)
+    assert np.isfinite(gsub).all()
+    assert err <= OUT_ATOL, err
+    assert lerr <= 1e-3, lerr
+    return err
+
+
+def small(**kw):
+    base = dict(name="pf_small", batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                prior_len=64 * 40 + 16, chunk_len=100, top_k_sparse=96, window=128)
+    base.update(kw)
+    return synth.PrefillConfig(**base)
+
+
+def test_prefill_small_ragged_g4():
+    run_prefill_case(small(), 61)
+
+
+@pytest.mark.parametrize("g", [1, 2])
+def test_prefill_small_groups(g):
+    run_prefill_case(small(name=f"pf_g{g}", n_q_heads=2 * g, batch=2), 62 + g)
+
+
+def test_prefill_window_and_topk_edges():
+    # window longer than the whole context; top-k covering every entry
+    run_prefill_case(small(name="pf_bigwin", window=10_000, top_k_sparse=10_000), 71)
+    # window of one token (the query itself); top-1
+    run_prefill_case(small(name="pf_win1", window=1, top_k_sparse=1, chunk_len=70), 72)
+    # small prior context (fewer entries than top-k), partial dense entry
+    run_prefill_case(small(name="pf_tiny_prior", prior_len=300, chunk_len=64), 73)
+
+
+def test_prefill_full_size_sampled_rows():
+    cfg = synth.CONFIGS["prefill256k"]
+    rows = np.array([0, 1, 63, 64, 500, 1023, 1024, 1500, 2046, 2047])
+    run_prefill_case(cfg, synth.DEFAULT_SEED["prefill256k"], rows=rows)
