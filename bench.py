@@ -42,12 +42,34 @@ def decode_bytes(cfg, n_keep):
     return sel, att
 
 
+def measured_traffic(workload):
+    """HBM bytes per sparse_decode_attn call from the committed counter summary, or None when
+    the summary is for another workload or the decode kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_traffic.md")
+    src = os.path.join(ROOT, "long_context_block_summary_amd", "csrc", "kernels_decode.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path, encoding="utf-8"):
+        if ":" in line and not line.startswith(("|", "#", "`")):
+            key, _, val = line.partition(":")
+            fields[key.strip()] = val.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if fields.get("kernel_source_sha256_prefix") != sha:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def kv_bytes_per_token(n_layers, width, elem_bytes):
     """K and V bytes of one token: layers x (heads*head_dim) x bytes x 2."""
     return n_layers * width * elem_bytes * 2
 
 
-def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30):
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30, inputs=None):
     import numpy as np
     import torch
 
@@ -55,7 +77,7 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30):
     from long_context_block_summary_amd import synth
 
     dev = torch.device("cuda:0")
-    t = synth.gen_decode(cfg)
+    t = inputs if inputs is not None else synth.gen_decode(cfg)
     to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
     q, k, v = to(t["q"]), to(t["k"]), to(t["v"])
     N, bs = cfg.seq_len, cfg.block_size
@@ -135,6 +157,67 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30):
     }
 
 
+def prefill_flops(cfg, ksel, n_dense):
+    """Algorithmic flops of the three attention branches (QK^T and PV, 2 flops per MAC)."""
+    return 4 * cfg.head_dim * cfg.chunk_len * cfg.batch * cfg.n_q_heads * (ksel + n_dense + cfg.window)
+
+
+def run_prefill(cfg, steps, warmup, flush_bytes=1 << 30):
+    import numpy as np
+    import torch
+
+    import long_context_block_summary_amd as bsa
+    from long_context_block_summary_amd import synth
+
+    dev = torch.device("cuda:0")
+    t = synth.gen_prefill(cfg)
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to(t["q"]), to(t["k"]), to(t["v"])
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev)
+    pc = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile)
+    r1 = []
+    for _ in range(3):
+        flush.add_(1.0)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        streams = bsa.build_compressed_streams(k, v, cfg.prior_len, pc)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        r1.append(e0.elapsed_time(e1))
+    out = torch.empty((cfg.batch, cfg.chunk_len, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32,
+                      device=dev)
+    import ctypes
+    shape = bsa.make_shape(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.prior_len,
+                           k.shape[2])
+    ws = torch.empty(bsa.lib().bsa_prefill_workspace_size(ctypes.byref(shape), cfg.chunk_len,
+                                                          ctypes.byref(pc)),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        flush.add_(1.0)
+        bsa.sparse_prefill_attn(q, k, v, *streams, cfg.prior_len, cfg=pc, out=out, workspace=ws)
+    ts = []
+    for _ in range(steps):
+        flush.add_(1.0)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        bsa.sparse_prefill_attn(q, k, v, *streams, cfg.prior_len, cfg=pc, out=out, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    e4 = -(-cfg.prior_len // cfg.m_sparse)
+    e128 = -(-cfg.prior_len // cfg.m_dense)
+    ksel = min(cfg.top_k_sparse, e4)
+    fl = prefill_flops(cfg, ksel, e128)
+    ms = sum(ts) / len(ts)
+    return {"workload": cfg.name, "ms_per_call": ms, "algorithmic_gflop": fl / 1e9,
+            "achieved_tflops": fl / (ms / 1e3) / 1e12,
+            "frac_of_bf16_mfma_peak": fl / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "timed": "sparse_prefill_attn call: pooled queries + scores + top-k + 3-branch attention",
+            "streams_ingest_ms": sorted(r1)[1]}
+
+
 def run_cpu_baseline(cfg, t, budget_s=20.0):
     """Oracle select + attend (given its fp64 summaries) on a bounded sample."""
     import numpy as np
@@ -175,6 +258,8 @@ def main():
     ap.add_argument("--also", default="long128k",
                     help="comma list of extra decode workloads reported alongside ('none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", default="prefill256k",
+                    help="prefill workload reported alongside ('none' to skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -211,7 +296,7 @@ def main():
         "step_GBps": (sel_b + att_b) / step_s / 1e9,
         "roofline": {"bound": "hbm", "kernel": "sparse_decode_attn",
                      "achieved": att_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": att_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": att_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(cfg.name),
                      "algorithmic_bytes": att_b, "avg_us": r["att_ms"] * 1e3},
         "breakdown_us": {"select_blocks": r["sel_ms"] * 1e3,
                          "sparse_decode_attn": r["att_ms"] * 1e3,
@@ -225,7 +310,10 @@ def main():
     extra = {}
     for name in [s for s in args.also.split(",") if s and s != "none"]:
         c2 = synth.CONFIGS[name]
-        r2 = run_gpu(c2, max(10, args.steps // 2), 3)
+        same = (c2.batch, c2.n_q_heads, c2.n_kv_heads, c2.head_dim, c2.seq_len) == \
+            (cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len) and \
+            synth.DEFAULT_SEED.get(name) == synth.DEFAULT_SEED.get(cfg.name)
+        r2 = run_gpu(c2, max(10, args.steps // 2), 3, inputs=r["inputs"] if same else None)
         s2, a2 = decode_bytes(c2, r2["n_keep"])
         extra[name] = {"queries_heads_per_s": c2.batch * c2.n_q_heads / (r2["step_ms"] / 1e3),
                        "ms_per_step": r2["step_ms"], "n_keep": r2["n_keep"],
@@ -234,6 +322,8 @@ def main():
                        "step_GBps": (s2 + a2) / (r2["step_ms"] / 1e3) / 1e9,
                        "select_us": r2["sel_ms"] * 1e3, "attn_us": r2["att_ms"] * 1e3}
         del r2
+    if args.prefill and args.prefill != "none":
+        line["prefill"] = run_prefill(synth.CONFIGS[args.prefill], max(5, args.steps // 5), 2)
     if extra:
         line["also"] = extra
     if not args.no_cpu_baseline:
