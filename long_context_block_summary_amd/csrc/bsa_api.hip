@@ -205,7 +205,8 @@ int sparse_prefill_attn(const void* q, int32_t chunk_len, const void* k, const v
   const int g = shape->n_q_heads / shape->n_kv_heads;
   const int rows = cfg->q_tile * g;
   const int E4 = bsa_num_blocks(shape->seq_len, cfg->m_sparse);
-  if (shape->head_dim != 128 || (rows != 64 && rows != 128 && rows != 256) || E4 > bsa::PREFILL_MAX_E4)
+  if (shape->head_dim != 128 || (rows != 64 && rows != 128 && rows != 256) || E4 > bsa::PREFILL_MAX_E4 ||
+      (cfg->top_k_sparse < E4 ? cfg->top_k_sparse : E4) > bsa::PREFILL_MAX_SEL)
     return BSA_UNSUPPORTED;
   const int n_tiles = bsa_num_blocks(chunk_len, cfg->q_tile);
   const int ksel = cfg->top_k_sparse < E4 ? cfg->top_k_sparse : E4;

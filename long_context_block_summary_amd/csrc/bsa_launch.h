@@ -50,6 +50,7 @@ struct PrefillLaunch {
   float scale;
 };
 constexpr int PREFILL_MAX_E4 = 131072;  // entries of the selected stream per (b, kv head)
+constexpr int PREFILL_MAX_SEL = 4096;   // selected entries per (tile, kv head)
 size_t prefill_workspace_bytes(int B, int Hkv, int D, int n_tiles, int E4, int ksel, bool need_sel);
 bool launch_prefill(const PrefillLaunch& L, hipStream_t st);
 

@@ -30,6 +30,7 @@ namespace bsa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float PF_LOG2E = 1.4426950408889634f;
@@ -37,67 +38,102 @@ constexpr float PF_LN2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------
 // pooled tile queries: qbar[b][tile][kvh][c] = sum over the tile's queries and
-// the kv head's query heads of q[b][i][h][c]
-__global__ void prefill_qbar_kernel(const uint16_t* __restrict__ q, int C, int Hq, int Hkv, int D,
-                                    int q_tile, int n_tiles, float* __restrict__ qbar) {
+// the kv head's query heads of q[b][i][h][c].  One workgroup per (b, tile,
+// kv head): thread t sums the 16-byte piece t%16 of every 16th (query, head)
+// row, then the 16 row groups are added through LDS.
+__global__ __launch_bounds__(256) void prefill_qbar_kernel(const uint16_t* __restrict__ q, int C,
+                                                           int Hq, int Hkv, int q_tile, int n_tiles,
+                                                           float* __restrict__ qbar) {
+  constexpr int D = 128;
+  __shared__ float part[16][D];
   const int prob = blockIdx.x;
   const int b = prob / (n_tiles * Hkv), tile = (prob / Hkv) % n_tiles, kvh = prob % Hkv;
   const int g = Hq / Hkv;
-  const int c = threadIdx.x;
-  if (c >= D) return;
-  const int i0 = tile * q_tile, i1 = min(C, i0 + q_tile);
-  float s = 0.f;
-  for (int i = i0; i < i1; ++i) {
-    const uint16_t* qi = q + (((int64_t)b * C + i) * Hq + (int64_t)kvh * g) * D + c;
-    for (int h = 0; h < g; ++h) s += __uint_as_float((uint32_t)qi[(int64_t)h * D] << 16);
+  const int t = threadIdx.x, col = t % 16, rg = t / 16;
+  const int i0 = tile * q_tile;
+  const int rows = min(q_tile, C - i0) * g;  // valid (query, head) rows of the tile
+  float acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+#pragma unroll 4
+  for (int r = rg; r < rows; r += 16) {
+    const int i = i0 + r / g, h = kvh * g + r % g;
+    float f[8];
+    unpack8(reinterpret_cast<const uint4*>(q + (((int64_t)b * C + i) * Hq + h) * D)[col], f);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] += f[c];
   }
-  qbar[(((int64_t)b * n_tiles + tile) * Hkv + kvh) * D + c] = s;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) part[rg][8 * col + c] = acc[c];
+  __syncthreads();
+  if (t < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += part[r][t];
+    qbar[(((int64_t)b * n_tiles + tile) * Hkv + kvh) * D + t] = s;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // scores[b][kvh][tile][j] = qbar[b][tile][kvh] . ks[b][kvh][j] (fp32).
-// A wave computes S^T[16 entries x 16 tiles] with v_mfma_f32_16x16x4_f32:
+// A wave computes S^T[16 entries x 16 tiles] tiles with v_mfma_f32_16x16x4_f32:
 // A = pooled-key rows (lane l: entry l%16), B = qbar^T (lane l: tile l%16);
 // the k index l/16 of every step maps to dim 16m + 4(l/16) + e on both sides.
+// A workgroup covers 256 entries (64 per wave, all loads issued up front); the
+// pooled queries of 16 tiles at a time are staged in LDS.
+constexpr int PSC_GROUPS = 4;  // 16-entry groups per wave
+
 template <int D>
 __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __restrict__ ks,
                                                              const float* __restrict__ qbar,
                                                              int n_tiles, int Hkv, int E,
                                                              float* __restrict__ scores) {
   constexpr int M = D / 16;
+  __shared__ __align__(16) float qs[16][D];
   const int kvh = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, j4 = lane >> 4;
-  const int e0 = blockIdx.x * 64 + 16 * wave;
-  if (e0 >= E) return;
-  const float* krow = ks + (((int64_t)b * Hkv + kvh) * E + min(e0 + l16, E - 1)) * D;
-  float4 ka[M];
+  const int e0 = blockIdx.x * (64 * PSC_GROUPS) + wave * (16 * PSC_GROUPS);
+  float4 ka[PSC_GROUPS][M];
 #pragma unroll
-  for (int m = 0; m < M; ++m) ka[m] = ld_stream(reinterpret_cast<const float4*>(krow + 16 * m + 4 * j4));
+  for (int gi = 0; gi < PSC_GROUPS; ++gi) {
+    const float* krow = ks + (((int64_t)b * Hkv + kvh) * E + min(e0 + 16 * gi + l16, E - 1)) * D;
+#pragma unroll
+    for (int m = 0; m < M; ++m) ka[gi][m] = ld_stream(reinterpret_cast<const float4*>(krow + 16 * m + 4 * j4));
+  }
   for (int ng = 0; ng * 16 < n_tiles; ++ng) {
-    const int tile = 16 * ng + l16;
+    __syncthreads();
+    for (int c = tid; c < 16 * D; c += 256) {
+      const int tl = c / D, dd = c % D, tile = 16 * ng + tl;
+      qs[tl][dd] = tile < n_tiles ? qbar[(((int64_t)b * n_tiles + tile) * Hkv + kvh) * D + dd] : 0.f;
+    }
+    __syncthreads();
     float4 qb[M];
-    const float* qrow = qbar + (((int64_t)b * n_tiles + min(tile, n_tiles - 1)) * Hkv + kvh) * D;
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      qb[m] = *reinterpret_cast<const float4*>(qrow + 16 * m + 4 * j4);
-      if (tile >= n_tiles) qb[m] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < M; ++m) qb[m] = *reinterpret_cast<const float4*>(&qs[l16][16 * m + 4 * j4]);
+    const int tile = 16 * ng + l16;
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[m].x, qb[m].x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[m].y, qb[m].y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[m].z, qb[m].z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[m].w, qb[m].w, acc, 0, 0, 0);
-    }
-    // lane l holds entries e0 + 4(l/16) + i of tile 16ng + l%16
-    if (tile < n_tiles) {
-      float* dst = scores + (((int64_t)b * Hkv + kvh) * n_tiles + tile) * E;
-      const int e = e0 + 4 * j4;
+    for (int gi = 0; gi < PSC_GROUPS; ++gi) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (e + i < E) dst[e + i] = acc[i];
+      for (int m = 0; m < M; ++m) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[gi][m].x, qb[m].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[gi][m].y, qb[m].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[gi][m].z, qb[m].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[gi][m].w, qb[m].w, acc, 0, 0, 0);
+      }
+      // lane l holds entries e0 + 16gi + 4(l/16) + i of tile 16ng + l%16
+      if (tile < n_tiles) {
+        float* dst = scores + (((int64_t)b * Hkv + kvh) * n_tiles + tile) * E;
+        const int e = e0 + 16 * gi + 4 * j4;
+        if (e + 3 < E) {
+          *reinterpret_cast<float4*>(dst + e) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (e + i < E) dst[e + i] = acc[i];
+        }
+      }
     }
   }
 }
@@ -109,6 +145,7 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __rest
 // taken and the first k - #(> T) keys equal to T in index order.
 constexpr int PTK_THREADS = 1024;
 constexpr int PTK_WAVES = PTK_THREADS / 64;
+static_assert(PTK_THREADS * 128 >= PREFILL_MAX_E4, "largest key count per thread is 128");
 
 __device__ __forceinline__ int ptk_block_sum(int v, int* red, int parity) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -167,38 +204,65 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
     const uint32_t cand = T | (1u << bit);
     int cnt = 0;
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) cnt += __popcll(__ballot(key[u] >= cand));
+    for (int u = 0; u < KPT; ++u) cnt += key[u] >= cand ? 1 : 0;
+    cnt = (int)wave_sum((float)cnt);  // exact: at most 64 * KPT
     const int total = ptk_block_sum((threadIdx.x & 63) == 0 ? cnt : 0, red, parity);
     parity ^= 1;
     if (total >= k) T = cand;
   }
-  int n_gt = 0, n_eq = 0;
+  // masks of this thread's keys (<= 64 per mask word) above and equal to T
+  constexpr int NW64 = (KPT + 63) / 64;
+  uint64_t gt[NW64], eq[NW64];
+#pragma unroll
+  for (int w = 0; w < NW64; ++w) gt[w] = eq[w] = 0;
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
-    n_gt += key[u] > T;
-    n_eq += key[u] == T;
+    gt[u / 64] |= (uint64_t)(key[u] > T) << (u % 64);
+    eq[u / 64] |= (uint64_t)(key[u] == T) << (u % 64);
+  }
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int w = 0; w < NW64; ++w) {
+    n_gt += __popcll(gt[w]);
+    n_eq += __popcll(eq[w]);
   }
   __syncthreads();
   int tot_gt, tot_eq, tot_sel;
   (void)ptk_block_exscan(n_gt, red, &tot_gt);
   const int need_eq = k - tot_gt;                 // >= 1 by the choice of T
   const int eq_first = ptk_block_exscan(n_eq, red, &tot_eq);
-  // selected keys of this thread: all > T, and the keys == T whose rank in
-  // index order is below need_eq
-  int n_sel = n_gt + max(0, min(n_eq, need_eq - eq_first));
-  int pos = ptk_block_exscan(n_sel, red, &tot_sel);
-  int rank = eq_first;
+  // keys equal to T are taken in index order while their rank is below need_eq
+  int take_eq = max(0, min(n_eq, need_eq - eq_first));
 #pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    bool take = key[u] > T;
-    if (key[u] == T) take = rank++ < need_eq;
-    if (take) out[pos++] = j0 + u;
+  for (int w = 0; w < NW64; ++w) {
+    uint64_t m = eq[w], keep = 0;
+    while (m && take_eq > 0) {
+      const uint64_t low = m & (~m + 1);
+      keep |= low;
+      m ^= low;
+      --take_eq;
+    }
+    gt[w] |= keep;
+  }
+  int n_sel = 0;
+#pragma unroll
+  for (int w = 0; w < NW64; ++w) n_sel += __popcll(gt[w]);
+  int pos = ptk_block_exscan(n_sel, red, &tot_sel);
+#pragma unroll
+  for (int w = 0; w < NW64; ++w) {
+    uint64_t m = gt[w];
+    while (m) {
+      const int bit = __builtin_ctzll(m);
+      out[pos++] = j0 + 64 * w + bit;
+      m &= m - 1;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // attention over the three branches.
-constexpr int PF_CH = 64;  // entries per chunk
+constexpr int PF_CH = 64;         // entries per chunk
+constexpr int PF_MAX_SEL = PREFILL_MAX_SEL;  // branch-A entries per (tile, kv head) kept in LDS
 
 struct PrefillAttnArgs {
   const uint16_t* q;     // [B][C][Hq][D]
@@ -221,9 +285,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillAttnArgs a
   constexpr int RW = 16 * NT;  // (query, head) rows per wave
   constexpr int U = (PF_CH * (D / 8)) / NTH;  // 16-byte K (and V) pieces per thread per chunk
   __shared__ __align__(16) uint4 k_lds[2][PF_CH * (D / 8)];      // entry rows, 16 B pieces, xor-swizzled
-  __shared__ __align__(16) uint16_t vt_lds[2][D * PF_CH];        // V^T fp16 [dim][entry], 8 B pieces swizzled
+  __shared__ __align__(16) uint16_t vt_lds[2][D * PF_CH];        // V^T fp16 [dim][entry], 8 B groups swizzled
   __shared__ __align__(16) float xch[NW][2][RW];
   __shared__ __align__(16) uint4 q_lds[NW * RW * (D / 8)];      // the tile's rows, xor-swizzled
+  __shared__ int32_t sel_lds[PF_MAX_SEL];                        // the tile's branch-A entries
 
   constexpr int RWG = NW * RW;  // rows per workgroup
   const int g = a.Hq / a.Hkv;
@@ -255,19 +320,27 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillAttnArgs a
   const int T1 = min(a.P + a.C, a.P + tile * a.q_tile + a.q_tile);
   const int nC = (T1 - T0 + PF_CH - 1) / PF_CH;
   const int total = nA + nB + nC;
-  const int32_t* sel = a.sel + ((int64_t)(b * a.n_tiles + tile) * a.Hkv + kvh) * a.ksel;
+  {
+    const int32_t* sel = a.sel + ((int64_t)(b * a.n_tiles + tile) * a.Hkv + kvh) * a.ksel;
+    for (int j = tid; j < a.ksel; j += NTH) sel_lds[j] = sel[j];
+  }
+  __syncthreads();
 
-  // global -> registers for one chunk
-  uint4 kreg[U], vreg[U];
-  auto load_chunk = [&](int gc) {
+  // global -> registers for one chunk; two register sets keep two chunks in flight.
+  // Lane l of wave w handles the 16-byte piece l%16 of the four consecutive
+  // entries 16w + 4(l/16) + u, u < 4: a load instruction reads four whole
+  // 256-byte rows, and the lane holds the four entries of a V^T group.
+  static_assert(NW == 4 && U == 4 && PF_CH == 64, "four waves of 16 entries, four entries per lane");
+  const int e_lane = 16 * wave + 4 * j4;  // first entry of this lane's group
+  uint4 kreg[2][U], vreg[2][U];
+  auto load_chunk = [&](int set, int gc) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = tid + NTH * u;
-      const int e = c / (D / 8), col = c % (D / 8);
+      const int e = e_lane + u;
       const uint16_t *kr, *vr;
       if (gc < nA) {
         const int j = min(gc * PF_CH + e, a.ksel - 1);
-        const int64_t row = pair * a.E4 + sel[j];
+        const int64_t row = pair * a.E4 + sel_lds[j];
         kr = a.k4 + row * D;
         vr = a.v4 + row * D;
       } else if (gc < nA + nB) {
@@ -281,28 +354,37 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillAttnArgs a
         kr = a.k + row * D;
         vr = a.v + row * D;
       }
-      kreg[u] = ld_stream(reinterpret_cast<const uint4*>(kr) + col);
-      vreg[u] = ld_stream(reinterpret_cast<const uint4*>(vr) + col);
+      kreg[set][u] = ld_stream(reinterpret_cast<const uint4*>(kr) + l16);
+      vreg[set][u] = ld_stream(reinterpret_cast<const uint4*>(vr) + l16);
     }
   };
-  auto store_chunk = [&](int buf) {
+  // V^T rows hold 64 fp16 entries as 16 groups of 4 (8 bytes); group G of dim
+  // row d sits at slot G ^ vt_swz(d).  vt_swz is a bijection both on 16
+  // consecutive dims (the PV operand reads) and on dims 8c + x, c < 16 (the
+  // stores below), so neither access pattern repeats a slot within 16 lanes.
+  auto vt_swz = [](int dim) { return (dim & 15) ^ ((dim >> 4) & 7); };
+  auto store_chunk = [&](int set, int buf) {
+    const int grp = e_lane >> 2;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = tid + NTH * u;
-      const int e = c / (D / 8), col = c % (D / 8);
-      k_lds[buf][e * (D / 8) + (col ^ (e & 15))] = kreg[u];
-      const uint32_t w[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
+      const int e = e_lane + u;
+      k_lds[buf][e * (D / 8) + (l16 ^ (e & 15))] = kreg[set][u];
+    }
+    uint2* vt = reinterpret_cast<uint2*>(vt_lds[buf]);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < 8; ++x) {
+      _Float16 h[4];
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          const int dim = 8 * col + 2 * x + y;
-          const float f = y ? bf_hi(w[x]) : bf_lo(w[x]);
-          const _Float16 hv = (_Float16)f;
-          vt_lds[buf][dim * PF_CH + ((((e >> 2) ^ (dim & 15)) << 2) | (e & 3))] =
-              __builtin_bit_cast(uint16_t, hv);
-        }
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t w = (x >> 1) == 0 ? vreg[set][u].x
+                         : (x >> 1) == 1 ? vreg[set][u].y
+                         : (x >> 1) == 2 ? vreg[set][u].z : vreg[set][u].w;
+        h[u] = (_Float16)((x & 1) ? bf_hi(w) : bf_lo(w));
       }
+      const int dim = 8 * l16 + x;
+      vt[dim * (PF_CH / 4) + (grp ^ vt_swz(dim))] =
+          make_uint2(__builtin_bit_cast(uint32_t, (f16x2_t){h[0], h[1]}),
+                     __builtin_bit_cast(uint32_t, (f16x2_t){h[2], h[3]}));
     }
   };
 
@@ -321,12 +403,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillAttnArgs a
     l_run[nt] = 0.f;
   }
 
-  load_chunk(0);
-  for (int gc = 0; gc < total; ++gc) {
+  auto chunk = [&](int gc, int set) {
     const int buf = gc & 1;
-    store_chunk(buf);
+    store_chunk(set, buf);
     __syncthreads();
-    if (gc + 1 < total) load_chunk(gc + 1);
+    if (gc + 2 < total) load_chunk(set, gc + 2);
     // what this chunk holds
     const int br = gc < nA ? 0 : (gc < nA + nB ? 1 : 2);
     const int nvalid = br == 0 ? min(PF_CH, a.ksel - gc * PF_CH)
@@ -418,10 +499,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillAttnArgs a
     for (int nd = 0; nd < D / 16; ++nd) {
       const int dim = 16 * nd + l16;
       const uint2* vrow = reinterpret_cast<const uint2*>(&vt_lds[buf][dim * PF_CH]);
+      const int sw = vt_swz(dim);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const uint2 lo = vrow[(8 * kk + j4) ^ (dim & 15)];
-        const uint2 hi = vrow[(8 * kk + 4 + j4) ^ (dim & 15)];
+        const uint2 lo = vrow[(8 * kk + j4) ^ sw];
+        const uint2 hi = vrow[(8 * kk + 4 + j4) ^ sw];
         const uint4 vb4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
         const f16x8_t vb = __builtin_bit_cast(f16x8_t, vb4);
 #pragma unroll
@@ -463,6 +545,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillAttnArgs a
       }
     }
     wave_lds_sync();
+  };
+  load_chunk(0, 0);
+  if (total > 1) load_chunk(1, 1);
+  for (int gc = 0; gc < total; gc += 2) {
+    chunk(gc, 0);
+    if (gc + 1 < total) chunk(gc + 1, 1);
   }
   // out = (o_A + o_B + o_C) / 3; lane holds rows 16nt + 4(l/16) + i, dim 16nd + l%16
 #pragma unroll
@@ -505,8 +593,8 @@ bool launch_prefill(const PrefillLaunch& L, hipStream_t st) {
   ws += al((size_t)L.B * L.Hkv * L.n_tiles * (size_t)L.E4 * 4);
   int32_t* sel = L.sel_out ? L.sel_out : reinterpret_cast<int32_t*>(ws);
   const unsigned probs = (unsigned)(L.B * L.n_tiles * L.Hkv);
-  prefill_qbar_kernel<<<probs, D, 0, st>>>(L.q, L.C, L.Hq, L.Hkv, D, L.q_tile, L.n_tiles, qbar);
-  dim3 sg((L.E4 + 63) / 64, L.Hkv, L.B);
+  prefill_qbar_kernel<<<probs, 256, 0, st>>>(L.q, L.C, L.Hq, L.Hkv, L.q_tile, L.n_tiles, qbar);
+  dim3 sg((L.E4 + 64 * PSC_GROUPS - 1) / (64 * PSC_GROUPS), L.Hkv, L.B);
   prefill_scores_kernel<128><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, scores);
   const int kpt = prefill_topk_kpt(L.E4);
 #define BSA_PTK(KK)                                                                              \
