@@ -279,41 +279,66 @@ struct PrefillAttnArgs {
   float scale_log2;
 };
 
+// Piece of an entry row handled by one thread: 8 bytes (512 threads) or 16.
+template <int PB> struct PieceT;
+template <> struct PieceT<8> { using type = uint2; };
+template <> struct PieceT<16> { using type = uint4; };
+__device__ __forceinline__ uint32_t piece_word(const uint2& p, int i) { return i == 0 ? p.x : p.y; }
+__device__ __forceinline__ uint32_t piece_word(const uint4& p, int i) {
+  return i == 0 ? p.x : (i == 1 ? p.y : (i == 2 ? p.z : p.w));
+}
+
+// V^T rows hold 64 fp16 entries as 16 groups of 4 (8 bytes); group G of dim
+// row d sits at slot G ^ vt_swz(d).  vt_swz is a bijection on any 16
+// consecutive dims (the PV operand reads) and on the dims x + 4m and x + 8m,
+// m < 16 (the stores of one instruction), so neither pattern repeats a slot
+// within 16 lanes.
+__device__ __forceinline__ int vt_swz(int dim) { return (dim & 15) ^ ((dim >> 4) & 7); }
+
+// One workgroup per (b, tile, kv head): NW waves of 16*NT (query, head) rows.
+// Per chunk of 64 entries: S^T = K Q^T (bf16 MFMA, Q fragments in registers),
+// online softmax in base 2 with the row maximum raised only when it grows by
+// more than 2^8 (exact: the weights and their sum share the stale maximum),
+// P in fp16, O += P V (fp16 MFMA, V^T staged in LDS).  At the end of a branch
+// the normalised rows are added into `out` by the lanes that own them.
 template <int NW, int NT>
-__global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillAttnArgs a) {
+__global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArgs a) {
   constexpr int D = 128, KS = D / 32, NTH = NW * 64;
-  constexpr int RW = 16 * NT;  // (query, head) rows per wave
-  constexpr int U = (PF_CH * (D / 8)) / NTH;  // 16-byte K (and V) pieces per thread per chunk
+  constexpr int RW = 16 * NT;          // (query, head) rows per wave
+  constexpr int PB = 4096 / NTH;       // bytes of each of its 4 entry rows a thread moves per chunk
+  constexpr int LPR = 256 / PB;        // threads per entry row
+  constexpr int NDT = PB / 2;          // dims per thread per entry
+  using Piece = typename PieceT<PB>::type;
+  static_assert(PF_CH == 64 && NTH / LPR == 16, "16 groups of 4 entries per chunk");
   __shared__ __align__(16) uint4 k_lds[2][PF_CH * (D / 8)];      // entry rows, 16 B pieces, xor-swizzled
   __shared__ __align__(16) uint16_t vt_lds[2][D * PF_CH];        // V^T fp16 [dim][entry], 8 B groups swizzled
   __shared__ __align__(16) float xch[NW][2][RW];
-  __shared__ __align__(16) uint4 q_lds[NW * RW * (D / 8)];      // the tile's rows, xor-swizzled
   __shared__ int32_t sel_lds[PF_MAX_SEL];                        // the tile's branch-A entries
 
-  constexpr int RWG = NW * RW;  // rows per workgroup
   const int g = a.Hq / a.Hkv;
-  const int nrb = (a.q_tile * g) / RWG;  // workgroups per (tile, kv head)
-  const int prob = blockIdx.x / nrb;
-  const int row0 = (blockIdx.x % nrb) * RWG;  // this workgroup's first row of the tile
+  const int prob = blockIdx.x;
   const int b = prob / (a.n_tiles * a.Hkv), tile = (prob / a.Hkv) % a.n_tiles, kvh = prob % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, j4 = lane >> 4;
   const int64_t pair = (int64_t)b * a.Hkv + kvh;
 
-  // the tile's (query, head) rows -> LDS; row r = query r / g of the tile, head r % g
-  for (int c = tid; c < NW * RW * (D / 8); c += NTH) {
-    const int r = c / (D / 8), col = c % (D / 8);
-    const int i = min(tile * a.q_tile + (row0 + r) / g, a.C - 1);
-    const int h = kvh * g + (row0 + r) % g;
-    q_lds[r * (D / 8) + (col ^ (r & 15))] =
-        reinterpret_cast<const uint4*>(a.q + (((int64_t)b * a.C + i) * a.Hq + h) * D)[col];
-  }
+  // Q^T fragments (B operand of S^T): lane l holds row RW*wave + 16nt + l%16,
+  // dims 32ks + 8(l/16) .. +8.  Row r = query r / g of the tile, head r % g.
+  uint4 qf[NT][KS];
   int qpos[NT];  // absolute position of the row's query (for the window mask)
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) qpos[nt] = a.P + tile * a.q_tile + (row0 + RW * wave + 16 * nt + l16) / g;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = RW * wave + 16 * nt + l16;
+    const int i = min(tile * a.q_tile + r / g, a.C - 1);
+    const uint4* qp =
+        reinterpret_cast<const uint4*>(a.q + (((int64_t)b * a.C + i) * a.Hq + kvh * g + r % g) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[nt][ks] = qp[4 * ks + j4];
+    qpos[nt] = a.P + tile * a.q_tile + r / g;
+  }
 
-  // chunk schedule
+  // chunk schedule: branch A (selected entries), B (all dense entries), C (window)
   const int nA = (a.ksel + PF_CH - 1) / PF_CH;
   const int nB = (a.E128 + PF_CH - 1) / PF_CH;
   const int T0 = max(0, a.P + tile * a.q_tile - a.window + 1);
@@ -326,82 +351,72 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillAttnArgs a
   }
   __syncthreads();
 
-  // global -> registers for one chunk; two register sets keep two chunks in flight.
-  // Lane l of wave w handles the 16-byte piece l%16 of the four consecutive
-  // entries 16w + 4(l/16) + u, u < 4: a load instruction reads four whole
-  // 256-byte rows, and the lane holds the four entries of a V^T group.
-  static_assert(NW == 4 && U == 4 && PF_CH == 64, "four waves of 16 entries, four entries per lane");
-  const int e_lane = 16 * wave + 4 * j4;  // first entry of this lane's group
-  uint4 kreg[2][U], vreg[2][U];
+  // global -> registers for one chunk; two register sets keep two chunks in
+  // flight.  Thread t moves bytes [PB*(t % LPR), +PB) of the four consecutive
+  // entries 4*(t / LPR) + u: one load instruction reads whole rows.
+  const int eg = tid / LPR, pc = tid % LPR;
+  Piece kreg[2][4], vreg[2][4];
   auto load_chunk = [&](int set, int gc) {
+    const uint16_t *kb, *vb;
+    int64_t row[4];
+    if (gc < nA) {  // uniform
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = e_lane + u;
-      const uint16_t *kr, *vr;
-      if (gc < nA) {
-        const int j = min(gc * PF_CH + e, a.ksel - 1);
-        const int64_t row = pair * a.E4 + sel_lds[j];
-        kr = a.k4 + row * D;
-        vr = a.v4 + row * D;
-      } else if (gc < nA + nB) {
-        const int j = min((gc - nA) * PF_CH + e, a.E128 - 1);
-        const int64_t row = pair * a.E128 + j;
-        kr = a.k128 + row * D;
-        vr = a.v128 + row * D;
-      } else {
-        const int t = min(T0 + (gc - nA - nB) * PF_CH + e, T1 - 1);
-        const int64_t row = pair * a.stride + t;
-        kr = a.k + row * D;
-        vr = a.v + row * D;
-      }
-      kreg[set][u] = ld_stream(reinterpret_cast<const uint4*>(kr) + l16);
-      vreg[set][u] = ld_stream(reinterpret_cast<const uint4*>(vr) + l16);
+      for (int u = 0; u < 4; ++u) row[u] = pair * a.E4 + sel_lds[min(gc * PF_CH + 4 * eg + u, a.ksel - 1)];
+      kb = a.k4;
+      vb = a.v4;
+    } else if (gc < nA + nB) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) row[u] = pair * a.E128 + min((gc - nA) * PF_CH + 4 * eg + u, a.E128 - 1);
+      kb = a.k128;
+      vb = a.v128;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        row[u] = pair * a.stride + min(T0 + (gc - nA - nB) * PF_CH + 4 * eg + u, T1 - 1);
+      kb = a.k;
+      vb = a.v;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      kreg[set][u] = ld_stream(reinterpret_cast<const Piece*>(kb + row[u] * D) + pc);
+      vreg[set][u] = ld_stream(reinterpret_cast<const Piece*>(vb + row[u] * D) + pc);
     }
   };
-  // V^T rows hold 64 fp16 entries as 16 groups of 4 (8 bytes); group G of dim
-  // row d sits at slot G ^ vt_swz(d).  vt_swz is a bijection both on 16
-  // consecutive dims (the PV operand reads) and on dims 8c + x, c < 16 (the
-  // stores below), so neither access pattern repeats a slot within 16 lanes.
-  auto vt_swz = [](int dim) { return (dim & 15) ^ ((dim >> 4) & 7); };
   auto store_chunk = [&](int set, int buf) {
-    const int grp = e_lane >> 2;
+    const int p16 = (pc * PB) / 16, sub = ((pc * PB) % 16) / PB;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = e_lane + u;
-      k_lds[buf][e * (D / 8) + (l16 ^ (e & 15))] = kreg[set][u];
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * eg + u;
+      reinterpret_cast<Piece*>(&k_lds[buf][e * (D / 8) + (p16 ^ (e & 15))])[sub] = kreg[set][u];
     }
     uint2* vt = reinterpret_cast<uint2*>(vt_lds[buf]);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
+    for (int x = 0; x < NDT; ++x) {
       _Float16 h[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t w = (x >> 1) == 0 ? vreg[set][u].x
-                         : (x >> 1) == 1 ? vreg[set][u].y
-                         : (x >> 1) == 2 ? vreg[set][u].z : vreg[set][u].w;
+        const uint32_t w = piece_word(vreg[set][u], x >> 1);
         h[u] = (_Float16)((x & 1) ? bf_hi(w) : bf_lo(w));
       }
-      const int dim = 8 * l16 + x;
-      vt[dim * (PF_CH / 4) + (grp ^ vt_swz(dim))] =
+      const int dim = NDT * pc + x;
+      vt[dim * (PF_CH / 4) + (eg ^ vt_swz(dim))] =
           make_uint2(__builtin_bit_cast(uint32_t, (f16x2_t){h[0], h[1]}),
                      __builtin_bit_cast(uint32_t, (f16x2_t){h[2], h[3]}));
     }
   };
 
-  f32x4_t O[NT][D / 16], osum[NT][D / 16];
+  f32x4_t O[NT][D / 16];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int nd = 0; nd < D / 16; ++nd) {
-      O[nt][nd] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-      osum[nt][nd] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    }
+    for (int nd = 0; nd < D / 16; ++nd) O[nt][nd] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   float m_run[NT], l_run[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m_run[nt] = -INFINITY;
     l_run[nt] = 0.f;
   }
+  const float c = a.scale_log2;
 
   auto chunk = [&](int gc, int set) {
     const int buf = gc & 1;
@@ -414,6 +429,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillAttnArgs a
                                : (br == 1 ? min(PF_CH, a.E128 - (gc - nA) * PF_CH)
                                           : min(PF_CH, T1 - T0 - (gc - nA - nB) * PF_CH));
     const int tbase = T0 + (gc - nA - nB) * PF_CH;  // branch C: token of entry 0
+    const bool masked = br == 2 || nvalid < PF_CH;   // uniform
     // S^T = K Q^T : lane gets entries 16mt + 4(l/16) + i of row 16nt + l%16
     f32x4_t s[NT][4];
 #pragma unroll
@@ -424,75 +440,89 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillAttnArgs a
         ka[ks] = k_lds[buf][(16 * mt + l16) * (D / 8) + ((4 * ks + j4) ^ l16)];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        // Q^T fragment: lane l holds row RW*wave + 16nt + l%16, dims 32ks + 8(l/16) .. +8
-        const int r = RW * wave + 16 * nt + l16;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const uint4 qv = q_lds[r * (D / 8) + ((4 * ks + j4) ^ l16)];
+        for (int ks = 0; ks < KS; ++ks)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
-                                                        __builtin_bit_cast(bf16x8_t, qv),
+                                                        __builtin_bit_cast(bf16x8_t, qf[nt][ks]),
                                                         acc, 0, 0, 0);
-        }
         s[nt][mt] = acc;
       }
+      if (mt & 1) __builtin_amdgcn_sched_barrier(0);  // bound the hoisted fragment reads
     }
-    // online softmax per row; P packed to fp16 as the A operand of P V
-    f16x8_t pa[NT][2];
+    if (masked) {
+      // valid entries of row 16nt + l%16 are e in [lo, hi]
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        int lo = 0, hi = nvalid - 1;
+        if (br == 2) {
+          lo = max(lo, qpos[nt] - a.window + 1 - tbase);
+          hi = min(hi, qpos[nt] - tbase);
+        }
+        const uint32_t span = (uint32_t)(hi - lo);  // huge when hi < lo: nothing valid
+        const int d0 = 4 * j4 - lo;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = hi >= lo && (uint32_t)(d0 + 16 * mt + i) <= span;
+            s[nt][mt][i] = ok ? s[nt][mt][i] : -INFINITY;
+          }
+      }
+    }
+    // row maxima of the chunk (scaled to base 2); raise the running maximum
+    // only where it grows by more than 8
+    float mc[NT];
+    bool grow = false;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      float z[4][4];
       float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 16 * mt + 4 * j4 + i;
-          bool ok = e < nvalid;
-          if (br == 2) {
-            const int t = tbase + e;
-            ok = ok && t <= qpos[nt] && t > qpos[nt] - a.window;
-          }
-          z[mt][i] = ok ? s[nt][mt][i] * a.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, z[mt][i]);
-        }
+        mx = fmaxf(mx, fmaxf(fmaxf(s[nt][mt][0], s[nt][mt][1]), fmaxf(s[nt][mt][2], s[nt][mt][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[nt], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
-      m_run[nt] = m_new;
+      mc[nt] = mx * c;
+      grow = grow || (mc[nt] > m_run[nt] + 8.f);
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // uniform
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float m_new = fmaxf(m_run[nt], mc[nt]);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+        m_run[nt] = m_new;
+        l_run[nt] *= alpha;
+        if (j4 == 0) xch[wave][0][16 * nt + l16] = alpha;
+      }
+      wave_lds_sync();
+      // rescale O rows (lane holds rows 16nt + 4(l/16) + i) by their alpha
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float4 al = *reinterpret_cast<const float4*>(&xch[wave][0][16 * nt + 4 * j4]);
+#pragma unroll
+        for (int nd = 0; nd < D / 16; ++nd) {
+          O[nt][nd][0] *= al.x;
+          O[nt][nd][1] *= al.y;
+          O[nt][nd][2] *= al.z;
+          O[nt][nd][3] *= al.w;
+        }
+      }
+    }
+    // P = 2^(s c - m) in fp16 as the A operand of P V
+    f16x8_t pa[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float neg_m = m_run[nt] == -INFINITY ? 0.f : -m_run[nt];
       float ps = 0.f;
-      float p[4][4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[mt][i] = __builtin_amdgcn_exp2f(z[mt][i] - m_use);
-          ps += p[mt][i];
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[nt][mt][i], c, neg_m));
+          ps += p;
+          pa[nt][mt >> 1][4 * (mt & 1) + i] = (_Float16)p;
         }
-      l_run[nt] = l_run[nt] * alpha + ps;
-      if (j4 == 0) xch[wave][0][16 * nt + l16] = alpha;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pa[nt][kk][i] = (_Float16)p[2 * kk][i];
-          pa[nt][kk][4 + i] = (_Float16)p[2 * kk + 1][i];
-        }
-    }
-    wave_lds_sync();
-    // rescale O rows (lane holds rows 16nt + 4(l/16) + i) by their alpha
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float4 al = *reinterpret_cast<const float4*>(&xch[wave][0][16 * nt + 4 * j4]);
-#pragma unroll
-      for (int nd = 0; nd < D / 16; ++nd) {
-        O[nt][nd][0] *= al.x;
-        O[nt][nd][1] *= al.y;
-        O[nt][nd][2] *= al.z;
-        O[nt][nd][3] *= al.w;
-      }
+      l_run[nt] += ps;
     }
     // O += P V: B operand lane l = dim 16nd + l%16, entries of the P k-slots
 #pragma unroll
@@ -504,14 +534,15 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillAttnArgs a
       for (int kk = 0; kk < 2; ++kk) {
         const uint2 lo = vrow[(8 * kk + j4) ^ sw];
         const uint2 hi = vrow[(8 * kk + 4 + j4) ^ sw];
-        const uint4 vb4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        const f16x8_t vb = __builtin_bit_cast(f16x8_t, vb4);
+        const f16x8_t vb = __builtin_bit_cast(f16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           O[nt][nd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[nt][kk], vb, O[nt][nd], 0, 0, 0);
       }
+      if (nd & 1) __builtin_amdgcn_sched_barrier(0);
     }
-    // end of a branch: normalise, add into the running sum, reset
+    // end of a branch: normalise, add into out (A writes, B adds, C adds and
+    // divides by 3), reset
     const bool last = (gc == nA - 1) || (gc == nA + nB - 1) || (gc == total - 1);
     if (last) {
 #pragma unroll
@@ -521,7 +552,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillAttnArgs a
         lt += __shfl_xor(lt, 32);
         if (j4 == 0) {
           xch[wave][1][16 * nt + l16] = lt;
-          const int r = row0 + RW * wave + 16 * nt + l16;
+          const int r = RW * wave + 16 * nt + l16;
           const int i = tile * a.q_tile + r / g;
           if (a.lse3 && i < a.C) {
             const int h = kvh * g + r % g;
@@ -533,13 +564,41 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillAttnArgs a
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const float4 l4 = *reinterpret_cast<const float4*>(&xch[wave][1][16 * nt + 4 * j4]);
-        const float inv[4] = {1.f / l4.x, 1.f / l4.y, 1.f / l4.z, 1.f / l4.w};
+        const float inv[4] = {__builtin_amdgcn_rcpf(l4.x), __builtin_amdgcn_rcpf(l4.y),
+                              __builtin_amdgcn_rcpf(l4.z), __builtin_amdgcn_rcpf(l4.w)};
+        float* dst[4];
 #pragma unroll
-        for (int nd = 0; nd < D / 16; ++nd) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) osum[nt][nd][i] = fmaf(O[nt][nd][i], inv[i], osum[nt][nd][i]);
-          O[nt][nd] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i) {
+          const int r = RW * wave + 16 * nt + 4 * j4 + i;
+          const int qi = min(tile * a.q_tile + r / g, a.C - 1);
+          dst[i] = a.out + (((int64_t)b * a.C + qi) * a.Hq + kvh * g + r % g) * D + l16;
         }
+        // rows past the chunk's end (qi clamped) belong to no query: skip them
+        bool live[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) live[i] = tile * a.q_tile + (RW * wave + 16 * nt + 4 * j4 + i) / g < a.C;
+        if (br == 0) {  // uniform
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (live[i])
+#pragma unroll
+              for (int nd = 0; nd < D / 16; ++nd) dst[i][16 * nd] = O[nt][nd][i] * inv[i];
+        } else if (br == 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (live[i])
+#pragma unroll
+              for (int nd = 0; nd < D / 16; ++nd) dst[i][16 * nd] += O[nt][nd][i] * inv[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (live[i])
+#pragma unroll
+              for (int nd = 0; nd < D / 16; ++nd)
+                dst[i][16 * nd] = (dst[i][16 * nd] + O[nt][nd][i] * inv[i]) * (1.f / 3.f);
+        }
+#pragma unroll
+        for (int nd = 0; nd < D / 16; ++nd) O[nt][nd] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
         m_run[nt] = -INFINITY;
         l_run[nt] = 0.f;
       }
@@ -552,19 +611,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillAttnArgs a
     chunk(gc, 0);
     if (gc + 1 < total) chunk(gc + 1, 1);
   }
-  // out = (o_A + o_B + o_C) / 3; lane holds rows 16nt + 4(l/16) + i, dim 16nd + l%16
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = row0 + RW * wave + 16 * nt + 4 * j4 + i;
-      const int qi = tile * a.q_tile + r / g;
-      if (qi >= a.C) continue;
-      const int h = kvh * g + r % g;
-      float* dst = a.out + (((int64_t)b * a.C + qi) * a.Hq + h) * D + l16;
-#pragma unroll
-      for (int nd = 0; nd < D / 16; ++nd) dst[16 * nd] = osum[nt][nd][i] * (1.f / 3.f);
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -614,11 +660,11 @@ bool launch_prefill(const PrefillLaunch& L, hipStream_t st) {
   a.E4 = L.E4; a.E128 = L.E128; a.ksel = L.ksel; a.window = L.window; a.q_tile = L.q_tile;
   a.n_tiles = L.n_tiles; a.scale_log2 = L.scale * PF_LOG2E;
   const int rows = L.q_tile * g;
-  // 4 waves of 32 (query, head) rows per workgroup; 64-row tiles use 16 rows per wave
+  // one workgroup per (b, tile, kv head); 16 rows per MFMA tile, NT tiles per wave
   switch (rows) {
     case 64: prefill_attn_kernel<4, 1><<<probs, 256, 0, st>>>(a); break;
     case 128: prefill_attn_kernel<4, 2><<<probs, 256, 0, st>>>(a); break;
-    case 256: prefill_attn_kernel<4, 2><<<probs * 2, 256, 0, st>>>(a); break;
+    case 256: prefill_attn_kernel<8, 2><<<probs, 512, 0, st>>>(a); break;
     default: return false;
   }
   return true;
