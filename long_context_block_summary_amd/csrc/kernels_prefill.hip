@@ -351,12 +351,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
   }
   __syncthreads();
 
-  // global -> registers for one chunk; two register sets keep two chunks in
-  // flight.  Thread t moves bytes [PB*(t % LPR), +PB) of the four consecutive
-  // entries 4*(t / LPR) + u: one load instruction reads whole rows.
+  // global -> registers for the next chunk, issued before this chunk's
+  // compute and stored to the other LDS buffer after it.  Thread t moves bytes
+  // [PB*(t % LPR), +PB) of the four consecutive entries 4*(t / LPR) + u: one
+  // load instruction reads whole rows.
   const int eg = tid / LPR, pc = tid % LPR;
-  Piece kreg[2][4], vreg[2][4];
-  auto load_chunk = [&](int set, int gc) {
+  Piece kreg[4], vreg[4];
+  auto load_chunk = [&](int gc) {
     const uint16_t *kb, *vb;
     int64_t row[4];
     if (gc < nA) {  // uniform
@@ -378,16 +379,16 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      kreg[set][u] = ld_stream(reinterpret_cast<const Piece*>(kb + row[u] * D) + pc);
-      vreg[set][u] = ld_stream(reinterpret_cast<const Piece*>(vb + row[u] * D) + pc);
+      kreg[u] = ld_stream(reinterpret_cast<const Piece*>(kb + row[u] * D) + pc);
+      vreg[u] = ld_stream(reinterpret_cast<const Piece*>(vb + row[u] * D) + pc);
     }
   };
-  auto store_chunk = [&](int set, int buf) {
+  auto store_chunk = [&](int buf) {
     const int p16 = (pc * PB) / 16, sub = ((pc * PB) % 16) / PB;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = 4 * eg + u;
-      reinterpret_cast<Piece*>(&k_lds[buf][e * (D / 8) + (p16 ^ (e & 15))])[sub] = kreg[set][u];
+      reinterpret_cast<Piece*>(&k_lds[buf][e * (D / 8) + (p16 ^ (e & 15))])[sub] = kreg[u];
     }
     uint2* vt = reinterpret_cast<uint2*>(vt_lds[buf]);
 #pragma unroll
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
       _Float16 h[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t w = piece_word(vreg[set][u], x >> 1);
+        const uint32_t w = piece_word(vreg[u], x >> 1);
         h[u] = (_Float16)((x & 1) ? bf_hi(w) : bf_lo(w));
       }
       const int dim = NDT * pc + x;
@@ -418,11 +419,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
   }
   const float c = a.scale_log2;
 
-  auto chunk = [&](int gc, int set) {
+  auto chunk = [&](int gc) {
     const int buf = gc & 1;
-    store_chunk(set, buf);
-    __syncthreads();
-    if (gc + 2 < total) load_chunk(set, gc + 2);
+    if (gc + 1 < total) load_chunk(gc + 1);
     // what this chunk holds
     const int br = gc < nA ? 0 : (gc < nA + nB ? 1 : 2);
     const int nvalid = br == 0 ? min(PF_CH, a.ksel - gc * PF_CH)
@@ -566,17 +565,22 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
         const float4 l4 = *reinterpret_cast<const float4*>(&xch[wave][1][16 * nt + 4 * j4]);
         const float inv[4] = {__builtin_amdgcn_rcpf(l4.x), __builtin_amdgcn_rcpf(l4.y),
                               __builtin_amdgcn_rcpf(l4.z), __builtin_amdgcn_rcpf(l4.w)};
+        // row addresses from an opaque copy of the lane id: computed here
+        // rather than kept live across the chunk loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int jo = ln >> 4;
         float* dst[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = RW * wave + 16 * nt + 4 * j4 + i;
+          const int r = RW * wave + 16 * nt + 4 * jo + i;
           const int qi = min(tile * a.q_tile + r / g, a.C - 1);
-          dst[i] = a.out + (((int64_t)b * a.C + qi) * a.Hq + kvh * g + r % g) * D + l16;
+          dst[i] = a.out + (((int64_t)b * a.C + qi) * a.Hq + kvh * g + r % g) * D + (ln & 15);
         }
         // rows past the chunk's end (qi clamped) belong to no query: skip them
         bool live[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) live[i] = tile * a.q_tile + (RW * wave + 16 * nt + 4 * j4 + i) / g < a.C;
+        for (int i = 0; i < 4; ++i) live[i] = tile * a.q_tile + (RW * wave + 16 * nt + 4 * jo + i) / g < a.C;
         if (br == 0) {  // uniform
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -603,14 +607,15 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
         l_run[nt] = 0.f;
       }
     }
-    wave_lds_sync();
+    // the other buffer was last read in chunk gc - 1, which every wave
+    // finished before the barrier that ended it
+    if (gc + 1 < total) store_chunk(buf ^ 1);
+    __syncthreads();
   };
-  load_chunk(0, 0);
-  if (total > 1) load_chunk(1, 1);
-  for (int gc = 0; gc < total; gc += 2) {
-    chunk(gc, 0);
-    if (gc + 1 < total) chunk(gc + 1, 1);
-  }
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  for (int gc = 0; gc < total; ++gc) chunk(gc);
 }
 
 // ---------------------------------------------------------------------------
