@@ -351,13 +351,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
   }
   __syncthreads();
 
-  // global -> registers for the next chunk, issued before this chunk's
-  // compute and stored to the other LDS buffer after it.  Thread t moves bytes
+  // global -> registers two chunks ahead (two register sets), stored to LDS
+  // after the compute of the chunk before it.  Thread t moves bytes
   // [PB*(t % LPR), +PB) of the four consecutive entries 4*(t / LPR) + u: one
   // load instruction reads whole rows.
   const int eg = tid / LPR, pc = tid % LPR;
-  Piece kreg[4], vreg[4];
-  auto load_chunk = [&](int gc) {
+  Piece kreg[2][4], vreg[2][4];
+  auto load_chunk = [&](int set, int gc) {
     const uint16_t *kb, *vb;
     int64_t row[4];
     if (gc < nA) {  // uniform
@@ -379,16 +379,16 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      kreg[u] = ld_stream(reinterpret_cast<const Piece*>(kb + row[u] * D) + pc);
-      vreg[u] = ld_stream(reinterpret_cast<const Piece*>(vb + row[u] * D) + pc);
+      kreg[set][u] = ld_stream(reinterpret_cast<const Piece*>(kb + row[u] * D) + pc);
+      vreg[set][u] = ld_stream(reinterpret_cast<const Piece*>(vb + row[u] * D) + pc);
     }
   };
-  auto store_chunk = [&](int buf) {
+  auto store_chunk = [&](int set, int buf) {
     const int p16 = (pc * PB) / 16, sub = ((pc * PB) % 16) / PB;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = 4 * eg + u;
-      reinterpret_cast<Piece*>(&k_lds[buf][e * (D / 8) + (p16 ^ (e & 15))])[sub] = kreg[u];
+      reinterpret_cast<Piece*>(&k_lds[buf][e * (D / 8) + (p16 ^ (e & 15))])[sub] = kreg[set][u];
     }
     uint2* vt = reinterpret_cast<uint2*>(vt_lds[buf]);
 #pragma unroll
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
       _Float16 h[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t w = piece_word(vreg[u], x >> 1);
+        const uint32_t w = piece_word(vreg[set][u], x >> 1);
         h[u] = (_Float16)((x & 1) ? bf_hi(w) : bf_lo(w));
       }
       const int dim = NDT * pc + x;
@@ -419,9 +419,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
   }
   const float c = a.scale_log2;
 
-  auto chunk = [&](int gc) {
-    const int buf = gc & 1;
-    if (gc + 1 < total) load_chunk(gc + 1);
+  auto chunk = [&](int gc, int set) {  // set == gc & 1
+    const int buf = set;
+    // unconditional (the last chunk again past the end) so that the wait
+    // before each store counts exactly the newer set's loads
+    load_chunk(set, min(gc + 2, total - 1));
     // what this chunk holds
     const int br = gc < nA ? 0 : (gc < nA + nB ? 1 : 2);
     const int nvalid = br == 0 ? min(PF_CH, a.ksel - gc * PF_CH)
@@ -447,7 +449,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
                                                         acc, 0, 0, 0);
         s[nt][mt] = acc;
       }
-      if (mt & 1) __builtin_amdgcn_sched_barrier(0);  // bound the hoisted fragment reads
+      __builtin_amdgcn_sched_barrier(0);  // bound the hoisted fragment reads
     }
     if (masked) {
       // valid entries of row 16nt + l%16 are e in [lo, hi]
@@ -538,7 +540,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
         for (int nt = 0; nt < NT; ++nt)
           O[nt][nd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[nt][kk], vb, O[nt][nd], 0, 0, 0);
       }
-      if (nd & 1) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // end of a branch: normalise, add into out (A writes, B adds, C adds and
     // divides by 3), reset
@@ -609,13 +611,17 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
     }
     // the other buffer was last read in chunk gc - 1, which every wave
     // finished before the barrier that ended it
-    if (gc + 1 < total) store_chunk(buf ^ 1);
+    if (gc + 1 < total) store_chunk(set ^ 1, buf ^ 1);
     __syncthreads();
   };
-  load_chunk(0);
-  store_chunk(0);
+  load_chunk(0, 0);
+  if (total > 1) load_chunk(1, 1);
+  store_chunk(0, 0);
   __syncthreads();
-  for (int gc = 0; gc < total; ++gc) chunk(gc);
+  for (int gc = 0; gc < total; gc += 2) {
+    chunk(gc, 0);
+    if (gc + 1 < total) chunk(gc + 1, 1);
+  }
 }
 
 // ---------------------------------------------------------------------------
