@@ -86,7 +86,7 @@ constexpr int PSC_GROUPS = 4;  // 16-entry groups per wave
 template <int D>
 __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __restrict__ ks,
                                                              const float* __restrict__ qbar,
-                                                             int n_tiles, int Hkv, int E,
+                                                             int n_tiles, int Hkv, int E, int Es,
                                                              float* __restrict__ scores) {
   constexpr int M = D / 16;
   __shared__ __align__(16) float qs[16][D];
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __rest
       }
       // lane l holds entries e0 + 16gi + 4(l/16) + i of tile 16ng + l%16
       if (tile < n_tiles) {
-        float* dst = scores + (((int64_t)b * Hkv + kvh) * n_tiles + tile) * E;
+        float* dst = scores + (((int64_t)b * Hkv + kvh) * n_tiles + tile) * Es;
         const int e = e0 + 16 * gi + 4 * j4;
         if (e + 3 < E) {
           *reinterpret_cast<float4*>(dst + e) = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -139,123 +139,131 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------------------
-// top-k per (b, tile, kvh).  Thread t owns the keys [KPT*t, KPT*t + KPT) in
-// registers.  T = the k-th largest key is built bit by bit from the MSB:
-// keep bit b set if at least k keys are >= (T | bit).  Then every key > T is
-// taken and the first k - #(> T) keys equal to T in index order.
+// top-k per (b, tile, kvh) over the E scores of a row (row stride Es, a
+// multiple of 4).  Wave w owns the keys [64*KPT*w, 64*KPT*(w+1)); lane l holds
+// keys 256v + 4l + c (v < KPT/4, c < 4) of that range, so each float4 load of
+// a wave reads 1 KB of consecutive scores.  T = the k-th largest key is built
+// bit by bit from the MSB: keep bit b set if at least k keys are >= (T | bit),
+// counted with wave ballots.  Then every key > T is taken, and the first
+// k - #(> T) keys equal to T in index order; the output is written in index
+// order (wave prefix over waves, ballot/mbcnt prefix inside a wave).
 constexpr int PTK_THREADS = 1024;
 constexpr int PTK_WAVES = PTK_THREADS / 64;
 static_assert(PTK_THREADS * 128 >= PREFILL_MAX_E4, "largest key count per thread is 128");
 
-__device__ __forceinline__ int ptk_block_sum(int v, int* red, int parity) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) red[parity * PTK_WAVES + wave] = v;
-  __syncthreads();
-  int t = 0;
-#pragma unroll
-  for (int w = 0; w < PTK_WAVES; ++w) t += red[parity * PTK_WAVES + w];
-  return t;
+__device__ __forceinline__ int ballot_count(bool p) {
+  return __builtin_popcountll(__builtin_amdgcn_ballot_w64(p));
 }
-
-// exclusive prefix over threads in thread order; *total gets the sum
-__device__ __forceinline__ int ptk_block_exscan(int v, int* red, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(inc, off);
-    if (lane >= off) inc += t;
-  }
-  if (lane == 63) red[wave] = inc;
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < PTK_WAVES; ++w) {
-    const int c = red[w];
-    before += (w < wave) ? c : 0;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + inc - v;
+__device__ __forceinline__ int ballot_below(bool p) {  // lanes below this one with p set
+  const uint64_t m = __builtin_amdgcn_ballot_w64(p);
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
 template <int KPT>
 __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* __restrict__ scores,
                                                                    int n_tiles, int Hkv, int E,
-                                                                   int k, int32_t* __restrict__ sel) {
-  __shared__ int red[2 * PTK_WAVES];
+                                                                   int Es, int k,
+                                                                   int32_t* __restrict__ sel) {
+  constexpr int NV = KPT / 4;
+  __shared__ int red[2][PTK_WAVES];
+  __shared__ int wcnt[2][PTK_WAVES];
   const int prob = blockIdx.x;  // sel order: [b][tile][kvh]
   const int b = prob / (n_tiles * Hkv), tile = (prob / Hkv) % n_tiles, kvh = prob % Hkv;
-  const float* s = scores + (((int64_t)b * Hkv + kvh) * n_tiles + tile) * E;
+  const float* s = scores + (((int64_t)b * Hkv + kvh) * n_tiles + tile) * Es;
   int32_t* out = sel + (int64_t)prob * k;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (k >= E) {
     for (int j = tid; j < E; j += PTK_THREADS) out[j] = j;
     return;
   }
-  uint32_t key[KPT];
-  const int j0 = KPT * tid;
+  const int wbase = wave * 64 * KPT;
+  uint32_t key[NV][4];
 #pragma unroll
-  for (int u = 0; u < KPT; ++u) key[u] = (j0 + u < E) ? order_key(s[j0 + u]) : 0u;  // 0: below any real key
+  for (int v = 0; v < NV; ++v) {
+    const int j = wbase + 256 * v + 4 * lane;
+    if (j + 3 < E) {
+      const float4 f = *reinterpret_cast<const float4*>(s + j);
+      key[v][0] = order_key(f.x);
+      key[v][1] = order_key(f.y);
+      key[v][2] = order_key(f.z);
+      key[v][3] = order_key(f.w);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) key[v][c] = (j + c < E) ? order_key(s[j + c]) : 0u;  // 0: below any real key
+    }
+  }
   uint32_t T = 0;
   int parity = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
     int cnt = 0;
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) cnt += key[u] >= cand ? 1 : 0;
-    cnt = (int)wave_sum((float)cnt);  // exact: at most 64 * KPT
-    const int total = ptk_block_sum((threadIdx.x & 63) == 0 ? cnt : 0, red, parity);
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) cnt += ballot_count(key[v][c] >= cand);
+    if (lane == 0) red[parity][wave] = cnt;
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < PTK_WAVES; ++w) total += red[parity][w];
     parity ^= 1;
     if (total >= k) T = cand;
   }
-  // masks of this thread's keys (<= 64 per mask word) above and equal to T
-  constexpr int NW64 = (KPT + 63) / 64;
-  uint64_t gt[NW64], eq[NW64];
-#pragma unroll
-  for (int w = 0; w < NW64; ++w) gt[w] = eq[w] = 0;
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    gt[u / 64] |= (uint64_t)(key[u] > T) << (u % 64);
-    eq[u / 64] |= (uint64_t)(key[u] == T) << (u % 64);
-  }
+  // per-wave counts above and equal to T, prefixes over the waves
   int n_gt = 0, n_eq = 0;
 #pragma unroll
-  for (int w = 0; w < NW64; ++w) {
-    n_gt += __popcll(gt[w]);
-    n_eq += __popcll(eq[w]);
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      n_gt += ballot_count(key[v][c] > T);
+      n_eq += ballot_count(key[v][c] == T);
+    }
+  if (lane == 0) {
+    wcnt[0][wave] = n_gt;
+    wcnt[1][wave] = n_eq;
   }
   __syncthreads();
-  int tot_gt, tot_eq, tot_sel;
-  (void)ptk_block_exscan(n_gt, red, &tot_gt);
-  const int need_eq = k - tot_gt;                 // >= 1 by the choice of T
-  const int eq_first = ptk_block_exscan(n_eq, red, &tot_eq);
-  // keys equal to T are taken in index order while their rank is below need_eq
-  int take_eq = max(0, min(n_eq, need_eq - eq_first));
+  int gt_before = 0, eq_before = 0, tot_gt = 0;
 #pragma unroll
-  for (int w = 0; w < NW64; ++w) {
-    uint64_t m = eq[w], keep = 0;
-    while (m && take_eq > 0) {
-      const uint64_t low = m & (~m + 1);
-      keep |= low;
-      m ^= low;
-      --take_eq;
-    }
-    gt[w] |= keep;
+  for (int w = 0; w < PTK_WAVES; ++w) {
+    const int cg = wcnt[0][w], ce = wcnt[1][w];
+    tot_gt += cg;
+    gt_before += w < wave ? cg : 0;
+    eq_before += w < wave ? ce : 0;
   }
-  int n_sel = 0;
+  const int need_eq = k - tot_gt;  // >= 1 by the choice of T
+  int pos = gt_before + min(eq_before, need_eq);  // selected keys of the earlier waves
+  int eq_rank = eq_before;                        // equal keys before this group
 #pragma unroll
-  for (int w = 0; w < NW64; ++w) n_sel += __popcll(gt[w]);
-  int pos = ptk_block_exscan(n_sel, red, &tot_sel);
+  for (int v = 0; v < NV; ++v) {
+    bool e[4], t[4];
+    int eq_pre = 0, eq_cnt = 0;
 #pragma unroll
-  for (int w = 0; w < NW64; ++w) {
-    uint64_t m = gt[w];
-    while (m) {
-      const int bit = __builtin_ctzll(m);
-      out[pos++] = j0 + 64 * w + bit;
-      m &= m - 1;
+    for (int c = 0; c < 4; ++c) {
+      e[c] = key[v][c] == T;
+      eq_pre += ballot_below(e[c]);
+      eq_cnt += ballot_count(e[c]);
     }
+    int own = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      t[c] = key[v][c] > T || (e[c] && eq_rank + eq_pre + own < need_eq);
+      own += e[c] ? 1 : 0;
+    }
+    int sel_pre = 0, sel_cnt = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      sel_pre += ballot_below(t[c]);
+      sel_cnt += ballot_count(t[c]);
+    }
+    int p = pos + sel_pre;
+    const int j = wbase + 256 * v + 4 * lane;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (t[c]) out[p++] = j + c;
+    pos += sel_cnt;
+    eq_rank += eq_cnt;
   }
 }
 
@@ -628,13 +636,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
 size_t prefill_workspace_bytes(int B, int Hkv, int D, int n_tiles, int E4, int ksel, bool need_sel) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t s = al((size_t)B * n_tiles * Hkv * D * 4);           // qbar
-  s += al((size_t)B * Hkv * n_tiles * (size_t)E4 * 4);        // scores
+  s += al((size_t)B * Hkv * n_tiles * (size_t)((E4 + 3) & ~3) * 4);  // scores, rows padded to 4
   if (need_sel) s += al((size_t)B * n_tiles * Hkv * (size_t)ksel * 4);
   return s;
 }
 
 int prefill_topk_kpt(int E4) {
-  int kpt = 1;
+  int kpt = 4;  // multiple of 4: one float4 per lane per group
   while (kpt * PTK_THREADS < E4) kpt *= 2;
   return kpt;
 }
@@ -647,20 +655,21 @@ bool launch_prefill(const PrefillLaunch& L, hipStream_t st) {
   float* qbar = reinterpret_cast<float*>(ws);
   ws += al((size_t)L.B * L.n_tiles * L.Hkv * D * 4);
   float* scores = reinterpret_cast<float*>(ws);
-  ws += al((size_t)L.B * L.Hkv * L.n_tiles * (size_t)L.E4 * 4);
+  const int Es = (L.E4 + 3) & ~3;
+  ws += al((size_t)L.B * L.Hkv * L.n_tiles * (size_t)Es * 4);
   int32_t* sel = L.sel_out ? L.sel_out : reinterpret_cast<int32_t*>(ws);
   const unsigned probs = (unsigned)(L.B * L.n_tiles * L.Hkv);
   prefill_qbar_kernel<<<probs, 256, 0, st>>>(L.q, L.C, L.Hq, L.Hkv, L.q_tile, L.n_tiles, qbar);
   dim3 sg((L.E4 + 64 * PSC_GROUPS - 1) / (64 * PSC_GROUPS), L.Hkv, L.B);
-  prefill_scores_kernel<128><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, scores);
+  prefill_scores_kernel<128><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores);
   const int kpt = prefill_topk_kpt(L.E4);
 #define BSA_PTK(KK)                                                                              \
   case KK:                                                                                       \
-    prefill_topk_kernel<KK><<<probs, PTK_THREADS, 0, st>>>(scores, L.n_tiles, L.Hkv, L.E4,      \
+    prefill_topk_kernel<KK><<<probs, PTK_THREADS, 0, st>>>(scores, L.n_tiles, L.Hkv, L.E4, Es, \
                                                            L.ksel, sel);                         \
     break;
   switch (kpt) {
-    BSA_PTK(1) BSA_PTK(2) BSA_PTK(4) BSA_PTK(8) BSA_PTK(16) BSA_PTK(32) BSA_PTK(64) BSA_PTK(128)
+    BSA_PTK(4) BSA_PTK(8) BSA_PTK(16) BSA_PTK(32) BSA_PTK(64) BSA_PTK(128)
     default: return false;
   }
 #undef BSA_PTK
