@@ -112,49 +112,112 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30, inputs=None):
                          dtype=torch.uint8, device=dev)
 
     def step(e0=None, e1=None, e2=None):
+        st = torch.cuda.current_stream(dev)
         if e0 is not None:
-            e0.record(stream)
+            e0.record(st)
         bsa.select_blocks(q, summ, N, bs, cfg.n_sink, cfg.n_local, cfg.top_k, cfg.keep_ratio,
                           block_idx=idx, workspace=ws_sel)
         if e1 is not None:
-            e1.record(stream)
+            e1.record(st)
         bsa.sparse_decode_attn(q, k, v, idx, N, bs, out=out, lse=lse, workspace=ws_dec)
         if e2 is not None:
-            e2.record(stream)
+            e2.record(st)
 
     for _ in range(warmup):
         flush.add_(1.0)
         step()
-    events = [(ev(), ev(), ev()) for _ in range(steps)]
+    # headline: events at the step boundaries only (a timing event between the two calls
+    # costs the GPU a few microseconds of idle time)
+    events = [(ev(), ev()) for _ in range(steps)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    for e in events:
+    for e0, e2 in events:
+        flush.add_(1.0)
+        step(e0=e0, e2=e2)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    step_ms = [a.elapsed_time(b) for a, b in events]
+
+    # per-call breakdown (separate pass with an event between the calls)
+    bevents = [(ev(), ev(), ev()) for _ in range(steps)]
+    for e in bevents:
         flush.add_(1.0)
         step(*e)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    sel_ms = [a.elapsed_time(b) for a, b, _ in events]
-    att_ms = [b.elapsed_time(c) for _, b, c in events]
-    step_ms = [a.elapsed_time(c) for a, _, c in events]
+    sel_ms = [a.elapsed_time(b) for a, b, _ in bevents]
+    att_ms = [b.elapsed_time(c) for _, b, c in bevents]
+
+    # the same step captured once in a HIP graph and replayed (flush outside the graph)
+    graph_ms = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()  # warm the side stream once outside capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            step()
+        torch.cuda.synchronize()
+        gevents = [(ev(), ev()) for _ in range(steps)]
+        for e0, e1 in gevents:
+            flush.add_(1.0)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = [a.elapsed_time(b) for a, b in gevents]
+        del g
+    except Exception as exc:  # report, never fall back silently
+        graph_ms = f"capture failed: {exc!r}"
 
     # warm-cache (no flush) for reference only
     torch.cuda.synchronize()
-    we = [(ev(), ev(), ev()) for _ in range(steps)]
-    for e in we:
-        step(*e)
+    we = [(ev(), ev()) for _ in range(steps)]
+    for e0, e2 in we:
+        step(e0=e0, e2=e2)
     torch.cuda.synchronize()
-    warm_ms = [a.elapsed_time(c) for a, _, c in we]
+    warm_ms = [a.elapsed_time(b) for a, b in we]
     return {
         "n_keep": n_keep,
         "sum_ms": sorted(sum_ms)[len(sum_ms) // 2],
         "sel_ms": sum(sel_ms) / len(sel_ms),
         "att_ms": sum(att_ms) / len(att_ms),
         "step_ms": sum(step_ms) / len(step_ms),
-        "step_ms_median": sorted(step_ms)[len(step_ms) // 2],
+        "step_pct": pct(step_ms),
+        "graph_ms": graph_ms,
         "warm_step_ms": sum(warm_ms) / len(warm_ms),
         "wall_s": wall,
         "inputs": t,
     }
+
+
+def pct(xs):
+    """p10 / median / p90 of a list of times."""
+    s = sorted(xs)
+    at = lambda f: s[min(len(s) - 1, int(round(f * (len(s) - 1))))]
+    return {"p10": at(0.1), "median": at(0.5), "p90": at(0.9)}
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=10):
+    """Plain device-to-device copy of nbytes (read + write) as a measured ceiling, GB/s."""
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = sorted(ts)[len(ts) // 2]
+    del a, b
+    return {"bytes_moved": 2 * nbytes, "median_ms": ms, "GBps": 2 * nbytes / (ms / 1e3) / 1e9,
+            "what": "torch copy_ of 1 GiB fp32 (read + write), median of 10"}
 
 
 def prefill_flops(cfg, ksel, n_dense):
@@ -194,31 +257,61 @@ def run_prefill(cfg, steps, warmup, flush_bytes=1 << 30):
     ws = torch.empty(bsa.lib().bsa_prefill_workspace_size(ctypes.byref(shape), cfg.chunk_len,
                                                           ctypes.byref(pc)),
                      dtype=torch.uint8, device=dev)
-    for _ in range(warmup):
-        flush.add_(1.0)
-        bsa.sparse_prefill_attn(q, k, v, *streams, cfg.prior_len, cfg=pc, out=out, workspace=ws)
-    ts = []
-    for _ in range(steps):
-        flush.add_(1.0)
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        bsa.sparse_prefill_attn(q, k, v, *streams, cfg.prior_len, cfg=pc, out=out, workspace=ws)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
+    sel = torch.empty((cfg.batch, -(-cfg.chunk_len // cfg.q_tile), cfg.n_kv_heads,
+                       min(cfg.top_k_sparse, -(-cfg.prior_len // cfg.m_sparse))),
+                      dtype=torch.int32, device=dev)
+    calls = {
+        "sparse_prefill_attn": lambda: bsa.sparse_prefill_attn(
+            q, k, v, *streams, cfg.prior_len, cfg=pc, out=out, workspace=ws),
+        "select_prefill_entries": lambda: bsa.select_prefill_entries(
+            q, k, streams[0], cfg.prior_len, cfg=pc, sel=sel, workspace=ws),
+        "sparse_prefill_attn_selected": lambda: bsa.sparse_prefill_attn_selected(
+            q, k, v, *streams[1:], sel, cfg.prior_len, cfg=pc, out=out),
+    }
+    times = {}
+    for name, fn in calls.items():
+        for _ in range(warmup):
+            flush.add_(1.0)
+            fn()
+        ts = []
+        for _ in range(steps):
+            flush.add_(1.0)
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        times[name] = ts
     e4 = -(-cfg.prior_len // cfg.m_sparse)
     e128 = -(-cfg.prior_len // cfg.m_dense)
     ksel = min(cfg.top_k_sparse, e4)
     fl = prefill_flops(cfg, ksel, e128)
-    ms = sum(ts) / len(ts)
-    return {"workload": cfg.name, "ms_per_call": ms, "algorithmic_gflop": fl / 1e9,
+    mean = lambda xs: sum(xs) / len(xs)
+    ms = mean(times["sparse_prefill_attn"])
+    att = mean(times["sparse_prefill_attn_selected"])
+    r2 = mean(times["select_prefill_entries"])
+    n_tiles = -(-cfg.chunk_len // cfg.q_tile)
+    r2_bytes = cfg.batch * cfg.n_kv_heads * e4 * cfg.head_dim * 4  # fp32 scoring stream, read once
+    r2_flops = 2 * cfg.batch * cfg.n_kv_heads * n_tiles * e4 * cfg.head_dim
+    gather_a = cfg.batch * cfg.n_kv_heads * n_tiles * ksel * cfg.head_dim * 2 * 2
+    return {"workload": cfg.name, "ms_per_call": ms, "call_pct": pct(times["sparse_prefill_attn"]),
+            "algorithmic_gflop": fl / 1e9,
             "achieved_tflops": fl / (ms / 1e3) / 1e12,
             "frac_of_bf16_mfma_peak": fl / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "timed": "sparse_prefill_attn call: pooled queries + scores + top-k + 3-branch attention",
+            "attention_R3_R6": {"call": "sparse_prefill_attn_selected", "ms": att,
+                                "achieved_tflops": fl / (att / 1e3) / 1e12,
+                                "frac_of_bf16_mfma_peak": fl / (att / 1e3) / 1e12
+                                / MFMA_BF16_PEAK_TFLOPS,
+                                "branch_A_gather_GBps_over_call": gather_a / (att / 1e3) / 1e9},
+            "selection_R2": {"call": "select_prefill_entries", "ms": r2,
+                             "stream_GBps": r2_bytes / (r2 / 1e3) / 1e9,
+                             "fp32_gflop": r2_flops / 1e9},
             "streams_ingest_ms": sorted(r1)[1]}
 
 
-def run_cpu_baseline(cfg, t, budget_s=20.0):
+def run_cpu_baseline(cfg, t, budget_s=20.0, min_s=10.0):
     """Oracle select + attend (given its fp64 summaries) on a bounded sample."""
     import numpy as np
 
@@ -237,16 +330,18 @@ def run_cpu_baseline(cfg, t, budget_s=20.0):
     first = one(slice(0, 1))
     nb_used = 1
     if first * B <= budget_s and B > 1:
-        elapsed = one(slice(0, B))
         nb_used = B
-    else:
-        elapsed = first
-    qh = nb_used * cfg.n_q_heads
+    # repeat the pass until about min_s of CPU time has been spent (bounded by budget_s)
+    reps, elapsed = 0, 0.0
+    while reps == 0 or (elapsed < min_s and elapsed + elapsed / reps <= budget_s):
+        elapsed += one(slice(0, nb_used))
+        reps += 1
+    qh = reps * nb_used * cfg.n_q_heads
     return {"value": qh / elapsed, "unit": "queries*heads/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"{cfg.name}: select + attend (fp64 oracle, summaries precomputed) for "
-                      f"{nb_used} of {B} batch entries ({qh} query heads), one pass, "
-                      f"{elapsed:.2f} s"}
+                      f"{nb_used} of {B} batch entries ({nb_used * cfg.n_q_heads} query heads), "
+                      f"{reps} passes, {elapsed:.2f} s"}
 
 
 def main():
@@ -303,7 +398,12 @@ def main():
                          "build_block_summaries_ingest": r["sum_ms"] * 1e3},
         "select_GBps": sel_b / (r["sel_ms"] / 1e3) / 1e9,
         "warm_cache_ms_per_step": r["warm_step_ms"],
-        "step_ms_median": r["step_ms_median"],
+        "step_ms_pct": r["step_pct"],
+        "graph_step": (r["graph_ms"] if isinstance(r["graph_ms"], str) else
+                       {"ms_per_step": sum(r["graph_ms"]) / len(r["graph_ms"]),
+                        "queries_heads_per_s": qh / (sum(r["graph_ms"]) / len(r["graph_ms"]) / 1e3),
+                        **pct(r["graph_ms"])}),
+        "copy_ceiling": copy_bandwidth(),
         "timed_wall_s": r["wall_s"],
         "cache_flush": "1 GiB read+write before every step (untimed)",
     }

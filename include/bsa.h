@@ -171,14 +171,42 @@ int sparse_decode_attn_split(const void* q, const void* k, const void* v,
  *   out                  fp32 [B][C][Hq][d] = (o_A + o_B + o_C) / 3
  *   lse3                 fp32 [3][B][C][Hq] per-branch log-sum-exp, or NULL
  *   sel_out              int32 [B][ceil(C / q_tile)][Hkv][min(top_k_sparse, E_s)] ascending, or NULL
- *   workspace            bsa_prefill_workspace_size() bytes
- * Requires P >= 1, head_dim 128, Hq/Hkv * q_tile <= 256 and a multiple of 16. */
+ *   workspace            bsa_prefill_workspace_size() bytes, 16-byte aligned
+ * Requires P >= 1, head_dim 128, q_tile * Hq/Hkv in {64, 128, 256},
+ * E_s <= 131072 and min(top_k_sparse, E_s) <= 4096 (else BSA_UNSUPPORTED).
+ * Equals select_prefill_entries followed by sparse_prefill_attn_selected. */
 int sparse_prefill_attn(const void* q, int32_t chunk_len, const void* k, const void* v,
                         const float* k_cmp_sparse_f32, const void* k_cmp_sparse_bf16,
                         const void* v_cmp_sparse_bf16, const void* k_cmp_dense_bf16,
                         const void* v_cmp_dense_bf16, const bsa_shape* shape,
                         const bsa_prefill_cfg* cfg, float scale, float* out, float* lse3,
                         int32_t* sel_out, void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* select_prefill_entries -- the selection step of sparse_prefill_attn alone
+ * (the indexer role of "CSA + HCA 混合注意力机制" §4.2 with the pooled tile
+ * query of §4.4): per (tile, kv head) the pooled query scores every m_sparse
+ * entry with the fp32 stream and the top_k_sparse entries are written,
+ * ascending (descending score, lower index first on equal scores).
+ *   q                 bf16 [B][C][Hq][d]
+ *   k_cmp_sparse_f32  fp32 [B][Hkv][E_s][d]
+ *   sel_out           int32 [B][ceil(C / q_tile)][Hkv][min(top_k_sparse, E_s)]
+ *   workspace         bsa_prefill_workspace_size() bytes, 16-byte aligned
+ * Same requirements as sparse_prefill_attn. */
+int select_prefill_entries(const void* q, int32_t chunk_len, const float* k_cmp_sparse_f32,
+                           const bsa_shape* shape, const bsa_prefill_cfg* cfg, int32_t* sel_out,
+                           void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* sparse_prefill_attn_selected -- the three attention branches and their
+ * average (§4.3, §5.2 and the average of sparse_prefill_attn) over a given
+ * branch-A selection `sel` (layout of select_prefill_entries' sel_out; each
+ * list ascending).  Entry indices outside [0, E_s) are clamped into it.
+ * Needs no workspace.  Same requirements as sparse_prefill_attn. */
+int sparse_prefill_attn_selected(const void* q, int32_t chunk_len, const void* k, const void* v,
+                                 const void* k_cmp_sparse_bf16, const void* v_cmp_sparse_bf16,
+                                 const void* k_cmp_dense_bf16, const void* v_cmp_dense_bf16,
+                                 const int32_t* sel, const bsa_shape* shape,
+                                 const bsa_prefill_cfg* cfg, float scale, float* out, float* lse3,
+                                 void* hip_stream);
 
 #ifdef __cplusplus
 }

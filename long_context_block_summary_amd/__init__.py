@@ -73,8 +73,13 @@ def lib():
                                            vp, sz, i32, vp]
     L.sparse_prefill_attn.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, P(bsa_shape),
                                       P(bsa_prefill_cfg), f32, vp, vp, vp, vp, sz, vp]
+    L.select_prefill_entries.argtypes = [vp, i32, vp, P(bsa_shape), P(bsa_prefill_cfg), vp, vp,
+                                         sz, vp]
+    L.sparse_prefill_attn_selected.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp,
+                                               P(bsa_shape), P(bsa_prefill_cfg), f32, vp, vp, vp]
     for fn in ("build_block_summaries", "select_blocks", "sparse_decode_attn",
-               "sparse_decode_attn_split", "sparse_prefill_attn"):
+               "sparse_decode_attn_split", "sparse_prefill_attn", "select_prefill_entries",
+               "sparse_prefill_attn_selected"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -198,8 +203,8 @@ def sparse_decode_attn(q, k, v, block_idx, seq_len, block_size=64, scale=0.0, n_
     ws_bytes = lib().bsa_decode_workspace_size(ctypes.byref(shape), n_keep, block_size, n_splits)
     if ws_bytes == SIZE_MAX:
         raise ValueError("invalid decode arguments")
-    if workspace is None:  # must be zero before first use (the kernels keep it so)
-        workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
@@ -251,6 +256,68 @@ def sparse_prefill_attn(q, k, v, k_cmp_sparse_f32, k_cmp_sparse_bf16, v_cmp_spar
                                      _ptr(lse3), _ptr(sel), _ptr(workspace), workspace.numel(),
                                      _stream(q.device)))
     return out, lse3, sel
+
+
+def _prefill_shape(q, k, prior_len, cfg):
+    import torch
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    B, C, Hq, d = q.shape
+    shape = make_shape(B, Hq, k.shape[1], d, prior_len, k.shape[2])
+    n_tiles = -(-C // cfg.q_tile)
+    kk = min(cfg.top_k_sparse, num_blocks(prior_len, cfg.m_sparse))
+    return shape, n_tiles, kk
+
+
+def select_prefill_entries(q, k, k_cmp_sparse_f32, prior_len, cfg=None, sel=None, workspace=None):
+    """The prefill's entry selection alone: sel int32 [B][n_tiles][Hkv][min(top_k, E_s)].
+    k (bf16 [B][Hkv][stride][d]) only supplies the cache shape."""
+    import torch
+    cfg = cfg or prefill_cfg()
+    _need(k_cmp_sparse_f32, "k_cmp_sparse_f32", torch.float32, 4)
+    shape, n_tiles, kk = _prefill_shape(q, k, prior_len, cfg)
+    C = q.shape[1]
+    ws_bytes = lib().bsa_prefill_workspace_size(ctypes.byref(shape), C, ctypes.byref(cfg))
+    if ws_bytes == SIZE_MAX:
+        raise ValueError("invalid prefill arguments")
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if sel is None:
+        sel = torch.empty((q.shape[0], n_tiles, k.shape[1], kk), dtype=torch.int32,
+                          device=q.device)
+    _check("select_prefill_entries",
+           lib().select_prefill_entries(_ptr(q), C, _ptr(k_cmp_sparse_f32), ctypes.byref(shape),
+                                        ctypes.byref(cfg), _ptr(sel), _ptr(workspace),
+                                        workspace.numel(), _stream(q.device)))
+    return sel
+
+
+def sparse_prefill_attn_selected(q, k, v, k_cmp_sparse_bf16, v_cmp_sparse_bf16, k_cmp_dense_bf16,
+                                 v_cmp_dense_bf16, sel, prior_len, cfg=None, scale=0.0,
+                                 want_lse3=False, out=None):
+    """The prefill's three branches and their average over a given selection `sel`."""
+    import torch
+    cfg = cfg or prefill_cfg()
+    _need(v, "v", torch.bfloat16, 4)
+    for name, t in (("k_cmp_sparse_bf16", k_cmp_sparse_bf16),
+                    ("v_cmp_sparse_bf16", v_cmp_sparse_bf16),
+                    ("k_cmp_dense_bf16", k_cmp_dense_bf16), ("v_cmp_dense_bf16", v_cmp_dense_bf16)):
+        _need(t, name, torch.bfloat16, 4)
+    _need(sel, "sel", torch.int32, 4)
+    shape, n_tiles, kk = _prefill_shape(q, k, prior_len, cfg)
+    B, C, Hq, d = q.shape
+    if tuple(sel.shape) != (B, n_tiles, k.shape[1], kk):
+        raise ValueError(f"sel must be [{B}, {n_tiles}, {k.shape[1]}, {kk}]")
+    if out is None:
+        out = torch.empty((B, C, Hq, d), dtype=torch.float32, device=q.device)
+    lse3 = torch.empty((3, B, C, Hq), dtype=torch.float32, device=q.device) if want_lse3 else None
+    _check("sparse_prefill_attn_selected",
+           lib().sparse_prefill_attn_selected(_ptr(q), C, _ptr(k), _ptr(v),
+                                              _ptr(k_cmp_sparse_bf16), _ptr(v_cmp_sparse_bf16),
+                                              _ptr(k_cmp_dense_bf16), _ptr(v_cmp_dense_bf16),
+                                              _ptr(sel), ctypes.byref(shape), ctypes.byref(cfg),
+                                              scale, _ptr(out), _ptr(lse3), _stream(q.device)))
+    return out, lse3
 
 
 def decode_step(q, k, v, summaries, seq_len, block_size=64, n_sink=1, n_local=2, top_k=-1,

@@ -184,63 +184,131 @@ size_t bsa_prefill_workspace_size(const bsa_shape* shape, int32_t chunk_len,
                                       E4, ksel, true);
 }
 
+}  // extern "C"
+
+namespace {
+// Shared checks of the prefill entry points; fills the launch description
+// (pointers the caller does not pass stay null).
+int prefill_setup(const void* q, int32_t chunk_len, const bsa_shape* shape,
+                  const bsa_prefill_cfg* cfg, float scale, bsa::PrefillLaunch* L) {
+  if (!q || !shape_ok(shape) || !cfg || chunk_len < 1 || shape->seq_len < 1) return BSA_INVALID_ARG;
+  if (cfg->m_sparse < 1 || cfg->m_dense < 1 || cfg->top_k_sparse < 1 || cfg->window < 1 ||
+      cfg->q_tile < 1)
+    return BSA_INVALID_ARG;
+  if ((int64_t)shape->seq_len + chunk_len > shape->seq_stride) return BSA_INVALID_ARG;
+  if (!aligned16(q)) return BSA_INVALID_ARG;
+  const int g = shape->n_q_heads / shape->n_kv_heads;
+  const int rows = cfg->q_tile * g;
+  const int E4 = bsa_num_blocks(shape->seq_len, cfg->m_sparse);
+  const int ksel = cfg->top_k_sparse < E4 ? cfg->top_k_sparse : E4;
+  if (shape->head_dim != 128 || (rows != 64 && rows != 128 && rows != 256) ||
+      E4 > bsa::PREFILL_MAX_E4 || ksel > bsa::PREFILL_MAX_SEL)
+    return BSA_UNSUPPORTED;
+  *L = bsa::PrefillLaunch{};
+  L->q = static_cast<const uint16_t*>(q);
+  L->B = shape->batch;
+  L->C = chunk_len;
+  L->Hq = shape->n_q_heads;
+  L->Hkv = shape->n_kv_heads;
+  L->P = shape->seq_len;
+  L->stride = shape->seq_stride;
+  L->E4 = E4;
+  L->E128 = bsa_num_blocks(shape->seq_len, cfg->m_dense);
+  L->ksel = ksel;
+  L->window = cfg->window;
+  L->q_tile = cfg->q_tile;
+  L->n_tiles = bsa_num_blocks(chunk_len, cfg->q_tile);
+  L->scale = scale == 0.f ? 1.f / sqrtf(128.f) : scale;
+  return BSA_OK;
+}
+
+int prefill_set_streams(const void* k, const void* v, const void* k_cmp_sparse_bf16,
+                        const void* v_cmp_sparse_bf16, const void* k_cmp_dense_bf16,
+                        const void* v_cmp_dense_bf16, float* out, bsa::PrefillLaunch* L) {
+  const void* ptrs[] = {k, v, k_cmp_sparse_bf16, v_cmp_sparse_bf16, k_cmp_dense_bf16,
+                        v_cmp_dense_bf16, out};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return BSA_INVALID_ARG;
+  L->k = static_cast<const uint16_t*>(k);
+  L->v = static_cast<const uint16_t*>(v);
+  L->k4b = static_cast<const uint16_t*>(k_cmp_sparse_bf16);
+  L->v4b = static_cast<const uint16_t*>(v_cmp_sparse_bf16);
+  L->k128b = static_cast<const uint16_t*>(k_cmp_dense_bf16);
+  L->v128b = static_cast<const uint16_t*>(v_cmp_dense_bf16);
+  L->out = out;
+  return BSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int select_prefill_entries(const void* q, int32_t chunk_len, const float* k_cmp_sparse_f32,
+                           const bsa_shape* shape, const bsa_prefill_cfg* cfg, int32_t* sel_out,
+                           void* workspace, size_t ws_bytes, void* hip_stream) {
+  bsa::PrefillLaunch L;
+  int st = prefill_setup(q, chunk_len, shape, cfg, 0.f, &L);
+  if (st != BSA_OK) return st;
+  if (!k_cmp_sparse_f32 || !aligned16(k_cmp_sparse_f32) || !sel_out || !workspace ||
+      !aligned16(workspace))
+    return BSA_INVALID_ARG;
+  if (ws_bytes < bsa::prefill_workspace_bytes(L.B, L.Hkv, 128, L.n_tiles, L.E4, L.ksel, false))
+    return BSA_WORKSPACE_TOO_SMALL;
+  L.k4f = k_cmp_sparse_f32;
+  L.workspace = workspace;
+  if (!bsa::launch_prefill_select(L, sel_out, static_cast<hipStream_t>(hip_stream)))
+    return BSA_UNSUPPORTED;
+  return launch_status();
+}
+
+int sparse_prefill_attn_selected(const void* q, int32_t chunk_len, const void* k, const void* v,
+                                 const void* k_cmp_sparse_bf16, const void* v_cmp_sparse_bf16,
+                                 const void* k_cmp_dense_bf16, const void* v_cmp_dense_bf16,
+                                 const int32_t* sel, const bsa_shape* shape,
+                                 const bsa_prefill_cfg* cfg, float scale, float* out, float* lse3,
+                                 void* hip_stream) {
+  bsa::PrefillLaunch L;
+  int st = prefill_setup(q, chunk_len, shape, cfg, scale, &L);
+  if (st != BSA_OK) return st;
+  st = prefill_set_streams(k, v, k_cmp_sparse_bf16, v_cmp_sparse_bf16, k_cmp_dense_bf16,
+                           v_cmp_dense_bf16, out, &L);
+  if (st != BSA_OK) return st;
+  if (!sel) return BSA_INVALID_ARG;
+  L.lse3 = lse3;
+  if (!bsa::launch_prefill_attend(L, sel, static_cast<hipStream_t>(hip_stream)))
+    return BSA_UNSUPPORTED;
+  return launch_status();
+}
+
 int sparse_prefill_attn(const void* q, int32_t chunk_len, const void* k, const void* v,
                         const float* k_cmp_sparse_f32, const void* k_cmp_sparse_bf16,
                         const void* v_cmp_sparse_bf16, const void* k_cmp_dense_bf16,
                         const void* v_cmp_dense_bf16, const bsa_shape* shape,
                         const bsa_prefill_cfg* cfg, float scale, float* out, float* lse3,
                         int32_t* sel_out, void* workspace, size_t ws_bytes, void* hip_stream) {
-  if (!q || !k || !v || !k_cmp_sparse_f32 || !k_cmp_sparse_bf16 || !v_cmp_sparse_bf16 ||
-      !k_cmp_dense_bf16 || !v_cmp_dense_bf16 || !out || !shape_ok(shape) || !cfg || chunk_len < 1 ||
-      shape->seq_len < 1)
-    return BSA_INVALID_ARG;
-  if (cfg->m_sparse < 1 || cfg->m_dense < 1 || cfg->top_k_sparse < 1 || cfg->window < 1 ||
-      cfg->q_tile < 1)
-    return BSA_INVALID_ARG;
-  if ((int64_t)shape->seq_len + chunk_len > shape->seq_stride) return BSA_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, k_cmp_sparse_f32, k_cmp_sparse_bf16, v_cmp_sparse_bf16,
-                        k_cmp_dense_bf16, v_cmp_dense_bf16, out, workspace};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return BSA_INVALID_ARG;
-  const int g = shape->n_q_heads / shape->n_kv_heads;
-  const int rows = cfg->q_tile * g;
-  const int E4 = bsa_num_blocks(shape->seq_len, cfg->m_sparse);
-  if (shape->head_dim != 128 || (rows != 64 && rows != 128 && rows != 256) || E4 > bsa::PREFILL_MAX_E4 ||
-      (cfg->top_k_sparse < E4 ? cfg->top_k_sparse : E4) > bsa::PREFILL_MAX_SEL)
-    return BSA_UNSUPPORTED;
-  const int n_tiles = bsa_num_blocks(chunk_len, cfg->q_tile);
-  const int ksel = cfg->top_k_sparse < E4 ? cfg->top_k_sparse : E4;
-  if (ws_bytes < bsa::prefill_workspace_bytes(shape->batch, shape->n_kv_heads, 128, n_tiles, E4,
-                                              ksel, sel_out == nullptr))
-    return BSA_WORKSPACE_TOO_SMALL;
-  if (!workspace) return BSA_INVALID_ARG;
   bsa::PrefillLaunch L;
-  L.q = static_cast<const uint16_t*>(q);
-  L.k = static_cast<const uint16_t*>(k);
-  L.v = static_cast<const uint16_t*>(v);
+  int st = prefill_setup(q, chunk_len, shape, cfg, scale, &L);
+  if (st != BSA_OK) return st;
+  st = prefill_set_streams(k, v, k_cmp_sparse_bf16, v_cmp_sparse_bf16, k_cmp_dense_bf16,
+                           v_cmp_dense_bf16, out, &L);
+  if (st != BSA_OK) return st;
+  if (!k_cmp_sparse_f32 || !aligned16(k_cmp_sparse_f32) || !workspace || !aligned16(workspace))
+    return BSA_INVALID_ARG;
+  if (ws_bytes < bsa::prefill_workspace_bytes(L.B, L.Hkv, 128, L.n_tiles, L.E4, L.ksel,
+                                              sel_out == nullptr))
+    return BSA_WORKSPACE_TOO_SMALL;
   L.k4f = k_cmp_sparse_f32;
-  L.k4b = static_cast<const uint16_t*>(k_cmp_sparse_bf16);
-  L.v4b = static_cast<const uint16_t*>(v_cmp_sparse_bf16);
-  L.k128b = static_cast<const uint16_t*>(k_cmp_dense_bf16);
-  L.v128b = static_cast<const uint16_t*>(v_cmp_dense_bf16);
-  L.out = out;
   L.lse3 = lse3;
-  L.sel_out = sel_out;
   L.workspace = workspace;
-  L.B = shape->batch;
-  L.C = chunk_len;
-  L.Hq = shape->n_q_heads;
-  L.Hkv = shape->n_kv_heads;
-  L.P = shape->seq_len;
-  L.stride = shape->seq_stride;
-  L.E4 = E4;
-  L.E128 = bsa_num_blocks(shape->seq_len, cfg->m_dense);
-  L.ksel = ksel;
-  L.window = cfg->window;
-  L.q_tile = cfg->q_tile;
-  L.n_tiles = n_tiles;
-  L.scale = scale == 0.f ? 1.f / sqrtf(128.f) : scale;
-  if (!bsa::launch_prefill(L, static_cast<hipStream_t>(hip_stream))) return BSA_UNSUPPORTED;
+  int32_t* sel = sel_out;
+  if (!sel) {  // after the pooled queries and the scores
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    sel = reinterpret_cast<int32_t*>(
+        static_cast<char*>(workspace) + al((size_t)L.B * L.n_tiles * L.Hkv * 128 * 4) +
+        al((size_t)L.B * L.Hkv * L.n_tiles * (size_t)((L.E4 + 3) & ~3) * 4));
+  }
+  hipStream_t hs = static_cast<hipStream_t>(hip_stream);
+  if (!bsa::launch_prefill_select(L, sel, hs) || !bsa::launch_prefill_attend(L, sel, hs))
+    return BSA_UNSUPPORTED;
   return launch_status();
 }
 

@@ -44,14 +44,16 @@ struct PrefillLaunch {
   const uint16_t* v128b;
   float* out;             // [B][C][Hq][128]
   float* lse3;            // [3][B][C][Hq] or null
-  int32_t* sel_out;       // [B][n_tiles][Hkv][ksel] or null (then kept in the workspace)
-  void* workspace;
+  void* workspace;        // pooled queries + scores (R2 only)
   int B, C, Hq, Hkv, P, stride, E4, E128, ksel, window, q_tile, n_tiles;
   float scale;
 };
 constexpr int PREFILL_MAX_E4 = 131072;  // entries of the selected stream per (b, kv head)
 constexpr int PREFILL_MAX_SEL = 4096;   // selected entries per (tile, kv head)
 size_t prefill_workspace_bytes(int B, int Hkv, int D, int n_tiles, int E4, int ksel, bool need_sel);
-bool launch_prefill(const PrefillLaunch& L, hipStream_t st);
+// R2 (pooled queries, scores, top-k) -> sel [B][n_tiles][Hkv][ksel]
+bool launch_prefill_select(const PrefillLaunch& L, int32_t* sel, hipStream_t st);
+// R3-R6 over sel
+bool launch_prefill_attend(const PrefillLaunch& L, const int32_t* sel, hipStream_t st);
 
 }  // namespace bsa

@@ -355,7 +355,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
   const int total = nA + nB + nC;
   {
     const int32_t* sel = a.sel + ((int64_t)(b * a.n_tiles + tile) * a.Hkv + kvh) * a.ksel;
-    for (int j = tid; j < a.ksel; j += NTH) sel_lds[j] = sel[j];
+    // clamped: a caller's out-of-range entry index never leaves the stream
+    for (int j = tid; j < a.ksel; j += NTH) sel_lds[j] = min(max(sel[j], 0), a.E4 - 1);
   }
   __syncthreads();
 
@@ -633,7 +634,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
 }
 
 // ---------------------------------------------------------------------------
-size_t prefill_workspace_bytes(int B, int Hkv, int D, int n_tiles, int E4, int ksel, bool need_sel) {
+size_t prefill_workspace_bytes(int B, int Hkv, int D, int n_tiles, int E4, int ksel, bool need_sel) {  // R2 scratch (+ sel)
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t s = al((size_t)B * n_tiles * Hkv * D * 4);           // qbar
   s += al((size_t)B * Hkv * n_tiles * (size_t)((E4 + 3) & ~3) * 4);  // scores, rows padded to 4
@@ -647,17 +648,15 @@ int prefill_topk_kpt(int E4) {
   return kpt;
 }
 
-bool launch_prefill(const PrefillLaunch& L, hipStream_t st) {
+// R2: pooled tile queries, scores against the fp32 stream, top-k -> sel
+bool launch_prefill_select(const PrefillLaunch& L, int32_t* sel, hipStream_t st) {
   const int D = 128;
-  const int g = L.Hq / L.Hkv;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   char* ws = static_cast<char*>(L.workspace);
   float* qbar = reinterpret_cast<float*>(ws);
   ws += al((size_t)L.B * L.n_tiles * L.Hkv * D * 4);
   float* scores = reinterpret_cast<float*>(ws);
   const int Es = (L.E4 + 3) & ~3;
-  ws += al((size_t)L.B * L.Hkv * L.n_tiles * (size_t)Es * 4);
-  int32_t* sel = L.sel_out ? L.sel_out : reinterpret_cast<int32_t*>(ws);
   const unsigned probs = (unsigned)(L.B * L.n_tiles * L.Hkv);
   prefill_qbar_kernel<<<probs, 256, 0, st>>>(L.q, L.C, L.Hq, L.Hkv, L.q_tile, L.n_tiles, qbar);
   dim3 sg((L.E4 + 64 * PSC_GROUPS - 1) / (64 * PSC_GROUPS), L.Hkv, L.B);
@@ -673,15 +672,21 @@ bool launch_prefill(const PrefillLaunch& L, hipStream_t st) {
     default: return false;
   }
 #undef BSA_PTK
+  return true;
+}
+
+// R3-R6: the three branches over a given selection, averaged into out
+bool launch_prefill_attend(const PrefillLaunch& L, const int32_t* sel, hipStream_t st) {
+  const int g = L.Hq / L.Hkv;
+  const unsigned probs = (unsigned)(L.B * L.n_tiles * L.Hkv);
   PrefillAttnArgs a;
   a.q = L.q; a.k = L.k; a.v = L.v; a.k4 = L.k4b; a.v4 = L.v4b; a.k128 = L.k128b; a.v128 = L.v128b;
   a.sel = sel; a.out = L.out; a.lse3 = L.lse3;
   a.B = L.B; a.C = L.C; a.Hq = L.Hq; a.Hkv = L.Hkv; a.P = L.P; a.stride = L.stride;
   a.E4 = L.E4; a.E128 = L.E128; a.ksel = L.ksel; a.window = L.window; a.q_tile = L.q_tile;
   a.n_tiles = L.n_tiles; a.scale_log2 = L.scale * PF_LOG2E;
-  const int rows = L.q_tile * g;
   // one workgroup per (b, tile, kv head); 16 rows per MFMA tile, NT tiles per wave
-  switch (rows) {
+  switch (L.q_tile * g) {
     case 64: prefill_attn_kernel<4, 1><<<probs, 256, 0, st>>>(a); break;
     case 128: prefill_attn_kernel<4, 2><<<probs, 256, 0, st>>>(a); break;
     case 256: prefill_attn_kernel<8, 2><<<probs, 512, 0, st>>>(a); break;

@@ -102,6 +102,39 @@ def test_argument_checks_launch_nothing(L):
                                 None, fake, 1 << 20, None) == -1
 
 
+def test_prefill_argument_checks_launch_nothing(L):
+    fake = ctypes.c_void_p(0x1000)
+    pc = bsa.prefill_cfg()
+    sh = bsa.make_shape(1, 32, 8, 128, 4096, 4096 + 128)
+    # NULL q; chunk overruns the cache capacity; bad tile shape; workspace too small
+    assert L.select_prefill_entries(None, 128, fake, ctypes.byref(sh), ctypes.byref(pc), fake,
+                                    fake, 1 << 30, None) == -1
+    assert L.select_prefill_entries(fake, 256, fake, ctypes.byref(sh), ctypes.byref(pc), fake,
+                                    fake, 1 << 30, None) == -1
+    odd = bsa.prefill_cfg(q_tile=48)
+    assert L.select_prefill_entries(fake, 128, fake, ctypes.byref(sh), ctypes.byref(odd), fake,
+                                    fake, 1 << 30, None) == -2
+    assert L.select_prefill_entries(fake, 128, fake, ctypes.byref(sh), ctypes.byref(pc), fake,
+                                    fake, 64, None) == -3
+    # attention over a given selection: NULL selection, misaligned stream
+    args = [fake, 128, fake, fake, fake, fake, fake, fake]
+    assert L.sparse_prefill_attn_selected(*args, None, ctypes.byref(sh), ctypes.byref(pc), 0.0,
+                                          fake, None, None) == -1
+    args[4] = ctypes.c_void_p(0x1004)
+    assert L.sparse_prefill_attn_selected(*args, fake, ctypes.byref(sh), ctypes.byref(pc), 0.0,
+                                          fake, None, None) == -1
+    # more selected entries than the kernel keeps in LDS; compressed stream too long
+    big_k = bsa.prefill_cfg(top_k_sparse=8192)
+    sh_long = bsa.make_shape(1, 32, 8, 128, 1 << 16, (1 << 16) + 128)
+    assert L.sparse_prefill_attn(fake, 128, fake, fake, fake, fake, fake, fake, fake,
+                                 ctypes.byref(sh_long), ctypes.byref(big_k), 0.0, fake, None,
+                                 None, fake, 1 << 40, None) == -2
+    sh_huge = bsa.make_shape(1, 32, 8, 128, 1 << 20, (1 << 20) + 128)
+    assert L.sparse_prefill_attn(fake, 128, fake, fake, fake, fake, fake, fake, fake,
+                                 ctypes.byref(sh_huge), ctypes.byref(pc), 0.0, fake, None,
+                                 None, fake, 1 << 40, None) == -2
+
+
 def test_product_path_has_no_oracle_import():
     pkg = os.path.join(ROOT, "long_context_block_summary_amd")
     for dirpath, _, files in os.walk(pkg):

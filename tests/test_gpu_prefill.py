@@ -104,3 +104,46 @@ def test_prefill_full_size_sampled_rows():
     cfg = synth.CONFIGS["prefill256k"]
     rows = np.array([0, 1, 63, 64, 500, 1023, 1024, 1500, 2046, 2047])
     run_prefill_case(cfg, synth.DEFAULT_SEED["prefill256k"], rows=rows)
+
+
+def test_prefill_split_entry_points_compose():
+    """select_prefill_entries + sparse_prefill_attn_selected equal sparse_prefill_attn bit for
+    bit; the attention step alone matches the oracle on the oracle's own selection; selection
+    indices out of range are clamped (memory-safe) like an explicitly clamped list."""
+    import torch
+    cfg = small(name="pf_split", batch=2, chunk_len=130)
+    seed = 81
+    announce(cfg.name, "seed", seed, "split entry points")
+    t = synth.gen_prefill(cfg, seed)
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    pc = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile)
+    st = bsa.build_compressed_streams(k, v, cfg.prior_len, pc)
+    out, _, sel = bsa.sparse_prefill_attn(q, k, v, *st, cfg.prior_len, cfg=pc, want_sel=True)
+    sel2 = bsa.select_prefill_entries(q, k, st[0], cfg.prior_len, cfg=pc)
+    out2, _ = bsa.sparse_prefill_attn_selected(q, k, v, *st[1:], sel2, cfg.prior_len, cfg=pc)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel2)
+    assert torch.equal(out, out2)
+    common = dict(m_sparse=cfg.m_sparse, top_k=cfg.top_k_sparse, m_dense=cfg.m_dense,
+                  window=cfg.window, q_tile=cfg.q_tile)
+    o_sel = oracle.sparse_prefill_attn(t["q"], t["k"], t["v"], cfg.prior_len, rows=[0],
+                                       want_sel=True, **common)["sel"]
+    ref = oracle.sparse_prefill_attn(t["q"], t["k"], t["v"], cfg.prior_len, sel_in=o_sel,
+                                     **common)
+    out3, lse3 = bsa.sparse_prefill_attn_selected(q, k, v, *st[1:],
+                                                  torch.from_numpy(o_sel).to(q.device),
+                                                  cfg.prior_len, cfg=pc, want_lse3=True)
+    torch.cuda.synchronize()
+    err = np.abs(out3.cpu().numpy() - ref["out"]).max()
+    lerr = np.abs(lse3.cpu().numpy() - ref["lse3"]).max()
+    announce("  oracle selection: max|out err|", err, "max|lse err|", lerr)
+    assert err <= OUT_ATOL and lerr <= 1e-3
+    e_s = bsa.num_blocks(cfg.prior_len, cfg.m_sparse)
+    wild = sel2.clone()
+    wild[..., -1] = e_s + 1000
+    wild[..., 0] = -7
+    tame = wild.clamp(0, e_s - 1)
+    o_w, _ = bsa.sparse_prefill_attn_selected(q, k, v, *st[1:], wild, cfg.prior_len, cfg=pc)
+    o_t, _ = bsa.sparse_prefill_attn_selected(q, k, v, *st[1:], tame, cfg.prior_len, cfg=pc)
+    torch.cuda.synchronize()
+    assert torch.equal(o_w, o_t)
