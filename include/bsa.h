@@ -173,7 +173,8 @@ int sparse_decode_attn_split(const void* q, const void* k, const void* v,
  *   sel_out              int32 [B][ceil(C / q_tile)][Hkv][min(top_k_sparse, E_s)] ascending, or NULL
  *   workspace            bsa_prefill_workspace_size() bytes, 16-byte aligned
  * Requires P >= 1, head_dim 128, q_tile * Hq/Hkv in {64, 128, 256},
- * E_s <= 131072 and min(top_k_sparse, E_s) <= 4096 (else BSA_UNSUPPORTED).
+ * E_s <= 131072, min(top_k_sparse, E_s) <= 4096 and, for the selection,
+ * ceil(C / q_tile) <= 64 (else BSA_UNSUPPORTED).
  * Equals select_prefill_entries followed by sparse_prefill_attn_selected. */
 int sparse_prefill_attn(const void* q, int32_t chunk_len, const void* k, const void* v,
                         const float* k_cmp_sparse_f32, const void* k_cmp_sparse_bf16,

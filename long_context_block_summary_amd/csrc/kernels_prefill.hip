@@ -75,13 +75,15 @@ __global__ __launch_bounds__(256) void prefill_qbar_kernel(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// scores[b][kvh][tile][j] = qbar[b][tile][kvh] . ks[b][kvh][j] (fp32).
-// A wave computes S^T[16 entries x 16 tiles] tiles with v_mfma_f32_16x16x4_f32:
-// A = pooled-key rows (lane l: entry l%16), B = qbar^T (lane l: tile l%16);
-// the k index l/16 of every step maps to dim 16m + 4(l/16) + e on both sides.
-// A workgroup covers 256 entries (64 per wave, all loads issued up front); the
-// pooled queries of 16 tiles at a time are staged in LDS.
-constexpr int PSC_GROUPS = 4;  // 16-entry groups per wave
+// scores[b][kvh][tile][j] = qbar[b][tile][kvh] . ks[b][kvh][j] (fp32), row
+// stride Es.  A wave computes S^T[16 entries x 16 tiles] tiles with
+// v_mfma_f32_16x16x4_f32: A = pooled-key rows (lane l: entry l%16), B = qbar^T
+// (lane l: tile l%16); the k index l/16 of every step maps to dim
+// 16m + 4(l/16) + e on both sides.  Each wave walks PSC_GROUPS groups of 16
+// consecutive entries, loading group i+1 into a second register set while the
+// MFMAs of group i run; the pooled queries of all tiles sit in LDS.
+constexpr int PSC_GROUPS = 8;     // 16-entry groups per wave
+constexpr int PSC_MAX_TILES = 64; // pooled queries held in LDS per workgroup
 
 template <int D>
 __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __restrict__ ks,
@@ -89,43 +91,43 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __rest
                                                              int n_tiles, int Hkv, int E, int Es,
                                                              float* __restrict__ scores) {
   constexpr int M = D / 16;
-  __shared__ __align__(16) float qs[16][D];
+  __shared__ __align__(16) float qs[PSC_MAX_TILES][D];
   const int kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, j4 = lane >> 4;
-  const int e0 = blockIdx.x * (64 * PSC_GROUPS) + wave * (16 * PSC_GROUPS);
-  float4 ka[PSC_GROUPS][M];
-#pragma unroll
-  for (int gi = 0; gi < PSC_GROUPS; ++gi) {
-    const float* krow = ks + (((int64_t)b * Hkv + kvh) * E + min(e0 + 16 * gi + l16, E - 1)) * D;
-#pragma unroll
-    for (int m = 0; m < M; ++m) ka[gi][m] = ld_stream(reinterpret_cast<const float4*>(krow + 16 * m + 4 * j4));
+  const int ntb = (n_tiles + 15) / 16;  // tile blocks of 16
+  for (int c = tid; c < ntb * 16 * D; c += 256) {
+    const int tl = c / D, dd = c % D;
+    qs[tl][dd] = tl < n_tiles ? qbar[(((int64_t)b * n_tiles + tl) * Hkv + kvh) * D + dd] : 0.f;
   }
-  for (int ng = 0; ng * 16 < n_tiles; ++ng) {
-    __syncthreads();
-    for (int c = tid; c < 16 * D; c += 256) {
-      const int tl = c / D, dd = c % D, tile = 16 * ng + tl;
-      qs[tl][dd] = tile < n_tiles ? qbar[(((int64_t)b * n_tiles + tile) * Hkv + kvh) * D + dd] : 0.f;
-    }
-    __syncthreads();
-    float4 qb[M];
+  __syncthreads();
+  const float* kbase = ks + ((int64_t)b * Hkv + kvh) * E * D;
+  float* sbase = scores + ((int64_t)b * Hkv + kvh) * n_tiles * Es;
+  const int e_first = (blockIdx.x * 4 + wave) * (16 * PSC_GROUPS);
+  float4 ka[2][M];
+  auto load = [&](int set, int gi) {
+    const float* krow = kbase + (int64_t)min(e_first + 16 * gi + l16, E - 1) * D;
 #pragma unroll
-    for (int m = 0; m < M; ++m) qb[m] = *reinterpret_cast<const float4*>(&qs[l16][16 * m + 4 * j4]);
-    const int tile = 16 * ng + l16;
-#pragma unroll
-    for (int gi = 0; gi < PSC_GROUPS; ++gi) {
+    for (int m = 0; m < M; ++m)
+      ka[set][m] = ld_stream(reinterpret_cast<const float4*>(krow + 16 * m + 4 * j4));
+  };
+  auto group = [&](int set, int gi) {
+    const int e = e_first + 16 * gi + 4 * j4;  // lane's first entry of the output tile
+    for (int tb = 0; tb < ntb; ++tb) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[gi][m].x, qb[m].x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[gi][m].y, qb[m].y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[gi][m].z, qb[m].z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[gi][m].w, qb[m].w, acc, 0, 0, 0);
+        const float4 qb = *reinterpret_cast<const float4*>(&qs[16 * tb + l16][16 * m + 4 * j4]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[set][m].x, qb.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[set][m].y, qb.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[set][m].z, qb.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[set][m].w, qb.w, acc, 0, 0, 0);
       }
-      // lane l holds entries e0 + 16gi + 4(l/16) + i of tile 16ng + l%16
+      // lane l holds entries e + i of tile 16tb + l%16
+      const int tile = 16 * tb + l16;
       if (tile < n_tiles) {
-        float* dst = scores + (((int64_t)b * Hkv + kvh) * n_tiles + tile) * Es;
-        const int e = e0 + 16 * gi + 4 * j4;
+        float* dst = sbase + (int64_t)tile * Es;
         if (e + 3 < E) {
           *reinterpret_cast<float4*>(dst + e) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         } else {
@@ -135,6 +137,16 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __rest
         }
       }
     }
+  };
+  // groups past E are loaded clamped (and their stores skipped), so the
+  // loads stay unconditional
+  load(0, 0);
+#pragma unroll
+  for (int gi = 0; gi < PSC_GROUPS; gi += 2) {
+    load(1, gi + 1);
+    group(0, gi);
+    if (gi + 2 < PSC_GROUPS) load(0, gi + 2);
+    group(1, gi + 1);
   }
 }
 
@@ -660,6 +672,7 @@ bool launch_prefill_select(const PrefillLaunch& L, int32_t* sel, hipStream_t st)
   const unsigned probs = (unsigned)(L.B * L.n_tiles * L.Hkv);
   prefill_qbar_kernel<<<probs, 256, 0, st>>>(L.q, L.C, L.Hq, L.Hkv, L.q_tile, L.n_tiles, qbar);
   dim3 sg((L.E4 + 64 * PSC_GROUPS - 1) / (64 * PSC_GROUPS), L.Hkv, L.B);
+  if (L.n_tiles > PSC_MAX_TILES) return false;
   prefill_scores_kernel<128><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores);
   const int kpt = prefill_topk_kpt(L.E4);
 #define BSA_PTK(KK)                                                                              \
