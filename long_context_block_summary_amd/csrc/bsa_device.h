@@ -99,8 +99,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // fp32 -> uint32 key with the same order (-0 folded onto +0)
 __device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  // negative: all bits flipped; otherwise the sign bit set (no compare mask)
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {

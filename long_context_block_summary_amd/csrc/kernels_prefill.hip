@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __rest
                                                              int n_tiles, int Hkv, int E, int Es,
                                                              float* __restrict__ scores) {
   constexpr int M = D / 16;
-  __shared__ __align__(16) float qs[PSC_MAX_TILES][D];
+  __shared__ __align__(16) float qs[PSC_MAX_TILES][D + 4];  // +16 B per row: rows spread over the banks
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -155,30 +155,84 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __rest
 // multiple of 4).  Wave w owns the keys [64*KPT*w, 64*KPT*(w+1)); lane l holds
 // keys 256v + 4l + c (v < KPT/4, c < 4) of that range, so each float4 load of
 // a wave reads 1 KB of consecutive scores.  T = the k-th largest key is built
-// bit by bit from the MSB: keep bit b set if at least k keys are >= (T | bit),
-// counted with wave ballots.  Then every key > T is taken, and the first
-// k - #(> T) keys equal to T in index order; the output is written in index
-// order (wave prefix over waves, ballot/mbcnt prefix inside a wave).
-constexpr int PTK_THREADS = 1024;
-constexpr int PTK_WAVES = PTK_THREADS / 64;
-static_assert(PTK_THREADS * 128 >= PREFILL_MAX_E4, "largest key count per thread is 128");
+// bit by bit from the MSB: keep bit b set if at least k keys are >= (T | bit).
+// Then every key > T is taken, and the first k - #(> T) keys equal to T in
+// index order; the output is written in index order (prefix over the waves,
+// then a lane scan inside the wave).
+constexpr int PTK_MAX_WAVES = 16;  // 1024 threads
+static_assert(PTK_MAX_WAVES * 64 * 128 >= PREFILL_MAX_E4, "largest key count per thread is 128");
 
-__device__ __forceinline__ int ballot_count(bool p) {
-  return __builtin_popcountll(__builtin_amdgcn_ballot_w64(p));
-}
-__device__ __forceinline__ int ballot_below(bool p) {  // lanes below this one with p set
-  const uint64_t m = __builtin_amdgcn_ballot_w64(p);
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+constexpr int PTK_CAP = 4096;  // undecided keys moved to LDS for the last bits
+
+// block sum of one value per wave (lane 0's), through LDS slot set `parity`
+template <int NWV>
+__device__ __forceinline__ int ptk_block_sum(int v, int (*red)[PTK_MAX_WAVES], int parity) {
+  if ((threadIdx.x & 63) == 0) red[parity][threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) t += red[parity][w];
+  return t;
 }
 
-template <int KPT>
+// exclusive prefix over threads in thread order; *total gets the sum
+template <int NWV>
+__device__ __forceinline__ int ptk_block_exscan(int v, int* red, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
+  }
+  __syncthreads();
+  if (lane == 63) red[wave] = inc;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    const int c = red[w];
+    before += (w < wave) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + inc - v;
+}
+
+// cnt + (key >= cand), through VCC: one compare mask live at a time (the
+// compiler otherwise keeps every compare of an unrolled pass in SGPR pairs)
+__device__ __forceinline__ int add_ge(int cnt, uint32_t key, uint32_t cand) {
+  asm("v_cmp_ge_u32_e32 vcc, %1, %2\n\tv_addc_co_u32_e32 %0, vcc, 0, %0, vcc"
+      : "+v"(cnt)
+      : "v"(key), "v"(cand)
+      : "vcc");
+  return cnt;
+}
+
+// exclusive prefix of x over the lanes of the wave; *total gets the wave sum
+__device__ __forceinline__ int wave_exscan(int x, int* total) {
+  const int lane = threadIdx.x & 63;
+  int inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
+  }
+  *total = __shfl(inc, 63);
+  return inc - x;
+}
+
+template <int KPT, int PTK_THREADS>
 __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* __restrict__ scores,
                                                                    int n_tiles, int Hkv, int E,
                                                                    int Es, int k,
                                                                    int32_t* __restrict__ sel) {
   constexpr int NV = KPT / 4;
-  __shared__ int red[2][PTK_WAVES];
+  constexpr int PTK_WAVES = PTK_THREADS / 64;
+  __shared__ int red[2][PTK_MAX_WAVES];
   __shared__ int wcnt[2][PTK_WAVES];
+  __shared__ uint32_t und[PTK_CAP + 64];  // undecided keys (+ a dummy slot per lane)
   const int prob = blockIdx.x;  // sel order: [b][tile][kvh]
   const int b = prob / (n_tiles * Hkv), tile = (prob / Hkv) % n_tiles, kvh = prob % Hkv;
   const float* s = scores + (((int64_t)b * Hkv + kvh) * n_tiles + tile) * Es;
@@ -193,34 +247,89 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
   uint32_t key[NV][4];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
+    // branch-free: the load is clamped into the (padded) row, keys past E are 0
     const int j = wbase + 256 * v + 4 * lane;
-    if (j + 3 < E) {
-      const float4 f = *reinterpret_cast<const float4*>(s + j);
-      key[v][0] = order_key(f.x);
-      key[v][1] = order_key(f.y);
-      key[v][2] = order_key(f.z);
-      key[v][3] = order_key(f.w);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) key[v][c] = (j + c < E) ? order_key(s[j + c]) : 0u;  // 0: below any real key
-    }
+    const float4 f = *reinterpret_cast<const float4*>(s + min(j, Es - 4));
+    // all-ones where j + c < E (sign of j + c - E), else 0: no compare masks
+    // held across the load
+    auto keep = [&](int c) { return (uint32_t)((j + c - E) >> 31); };
+    key[v][0] = order_key(f.x) & keep(0);  // 0: below any real key
+    key[v][1] = order_key(f.y) & keep(1);
+    key[v][2] = order_key(f.z) & keep(2);
+    key[v][3] = order_key(f.w) & keep(3);
   }
+  // Threshold search.  Before each bit the undecided keys are those in
+  // [T, T + 2^(bit+1)); n_ge counts keys >= T and n_top keys above the range.
+  // Full passes over the registers run until at most PTK_CAP keys are
+  // undecided; those are then copied to LDS and the remaining bits count only
+  // them (plus the n_top keys above them).
   uint32_t T = 0;
   int parity = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  int bit = 31;
+  int n_ge = PTK_THREADS * KPT, n_top = 0;
+  for (; bit >= 0 && n_ge - n_top > PTK_CAP; --bit) {  // uniform
     const uint32_t cand = T | (1u << bit);
     int cnt = 0;
 #pragma unroll
     for (int v = 0; v < NV; ++v)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) cnt += ballot_count(key[v][c] >= cand);
-    if (lane == 0) red[parity][wave] = cnt;
-    __syncthreads();
-    int total = 0;
-#pragma unroll
-    for (int w = 0; w < PTK_WAVES; ++w) total += red[parity][w];
+      for (int c = 0; c < 4; ++c) cnt = add_ge(cnt, key[v][c], cand);
+    cnt = ptk_block_sum<PTK_WAVES>((int)wave_sum((float)cnt), red, parity);  // exact: < 2^24
     parity ^= 1;
-    if (total >= k) T = cand;
+    if (cnt >= k) {
+      T = cand;
+      n_ge = cnt;
+    } else {
+      n_top = cnt;
+    }
+  }
+  if (bit >= 0) {
+    // undecided: key in [T, T + 2^sh), T a multiple of 2^sh.  Branch-free:
+    // out-of-range keys go to a per-lane dummy slot past PTK_CAP.
+    const int sh = bit + 1;  // uniform, 1..32
+    const uint32_t pre = sh == 32 ? 0u : (T >> sh);
+    auto outside_p = [&](uint32_t kv, uint32_t p) -> uint32_t {  // 1 when kv is decided
+      const uint32_t x = sh == 32 ? 0u : ((kv >> sh) ^ p);
+      return (x | (0u - x)) >> 31;
+    };
+    auto outside = [&](uint32_t kv) { return outside_p(kv, pre); };
+    int mine = 0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mine += 1 - (int)outside(key[v][c]);
+    int n_und;
+    int at = ptk_block_exscan<PTK_WAVES>(mine, red[0], &n_und);
+    const int dummy = PTK_CAP + lane;
+    // recomputed from an opaque copy of the prefix: not kept live across the scan
+    uint32_t pre2 = pre;
+    asm volatile("" : "+v"(pre2));
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t o = outside_p(key[v][c], pre2);
+        const uint32_t m = 0u - o;  // all ones when decided
+        und[((uint32_t)at & ~m) | ((uint32_t)dummy & m)] = key[v][c];
+        at += 1 - (int)o;
+      }
+    __syncthreads();
+    uint32_t lk[PTK_CAP / PTK_THREADS];
+#pragma unroll
+    for (int r = 0; r < PTK_CAP / PTK_THREADS; ++r) {
+      const int j = tid + PTK_THREADS * r;
+      lk[r] = j < n_und ? und[j] : 0u;  // 0 never reaches a candidate (>= 1)
+    }
+    const int n_above = n_top;
+    for (; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int r = 0; r < PTK_CAP / PTK_THREADS; ++r) cnt += lk[r] >= cand ? 1 : 0;
+      cnt = n_above + ptk_block_sum<PTK_WAVES>((int)wave_sum((float)cnt), red, parity);
+      parity ^= 1;
+      if (cnt >= k) T = cand;
+    }
   }
   // per-wave counts above and equal to T, prefixes over the waves
   int n_gt = 0, n_eq = 0;
@@ -228,9 +337,12 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
   for (int v = 0; v < NV; ++v)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      n_gt += ballot_count(key[v][c] > T);
-      n_eq += ballot_count(key[v][c] == T);
+      n_gt = add_ge(n_gt, key[v][c], T + 1);  // T < 2^32 - 1: keys are finite floats
+      n_eq = add_ge(n_eq, key[v][c], T);
     }
+  n_eq -= n_gt;  // counted >= T above
+  n_gt = (int)wave_sum((float)n_gt);
+  n_eq = (int)wave_sum((float)n_eq);
   if (lane == 0) {
     wcnt[0][wave] = n_gt;
     wcnt[1][wave] = n_eq;
@@ -247,30 +359,30 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
   const int need_eq = k - tot_gt;  // >= 1 by the choice of T
   int pos = gt_before + min(eq_before, need_eq);  // selected keys of the earlier waves
   int eq_rank = eq_before;                        // equal keys before this group
+  // entry indices from an opaque copy of the lane id: computed here instead of
+  // being kept live from the loads on
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    bool e[4], t[4];
-    int eq_pre = 0, eq_cnt = 0;
+    // keys of group v in index order: lane-major, then c
+    int ne = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ne += key[v][c] == T ? 1 : 0;
+    int eq_cnt;
+    const int eq_pre = wave_exscan(ne, &eq_cnt);
+    bool t[4];
+    int own = 0, ns = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      e[c] = key[v][c] == T;
-      eq_pre += ballot_below(e[c]);
-      eq_cnt += ballot_count(e[c]);
+      const bool e = key[v][c] == T;
+      t[c] = key[v][c] > T || (e && eq_rank + eq_pre + own < need_eq);
+      own += e ? 1 : 0;
+      ns += t[c] ? 1 : 0;
     }
-    int own = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      t[c] = key[v][c] > T || (e[c] && eq_rank + eq_pre + own < need_eq);
-      own += e[c] ? 1 : 0;
-    }
-    int sel_pre = 0, sel_cnt = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      sel_pre += ballot_below(t[c]);
-      sel_cnt += ballot_count(t[c]);
-    }
-    int p = pos + sel_pre;
-    const int j = wbase + 256 * v + 4 * lane;
+    int sel_cnt;
+    int p = pos + wave_exscan(ns, &sel_cnt);
+    const int j = wbase + 256 * v + 4 * ln;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       if (t[c]) out[p++] = j + c;
@@ -654,9 +766,11 @@ size_t prefill_workspace_bytes(int B, int Hkv, int D, int n_tiles, int E4, int k
   return s;
 }
 
-int prefill_topk_kpt(int E4) {
+// keys per thread for 512 threads (up to 128 keys: 65536 entries), else 1024
+int prefill_topk_kpt(int E4, int* threads) {
+  *threads = E4 > 512 * 128 ? 1024 : 512;
   int kpt = 4;  // multiple of 4: one float4 per lane per group
-  while (kpt * PTK_THREADS < E4) kpt *= 2;
+  while (kpt * *threads < E4) kpt *= 2;
   return kpt;
 }
 
@@ -674,18 +788,18 @@ bool launch_prefill_select(const PrefillLaunch& L, int32_t* sel, hipStream_t st)
   dim3 sg((L.E4 + 64 * PSC_GROUPS - 1) / (64 * PSC_GROUPS), L.Hkv, L.B);
   if (L.n_tiles > PSC_MAX_TILES) return false;
   prefill_scores_kernel<128><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores);
-  const int kpt = prefill_topk_kpt(L.E4);
-#define BSA_PTK(KK)                                                                              \
-  case KK:                                                                                       \
-    prefill_topk_kernel<KK><<<probs, PTK_THREADS, 0, st>>>(scores, L.n_tiles, L.Hkv, L.E4, Es, \
-                                                           L.ksel, sel);                         \
-    break;
-  switch (kpt) {
-    BSA_PTK(4) BSA_PTK(8) BSA_PTK(16) BSA_PTK(32) BSA_PTK(64) BSA_PTK(128)
-    default: return false;
+  int nthr;
+  const int kpt = prefill_topk_kpt(L.E4, &nthr);
+#define BSA_PTK(KK, NT)                                                                         \
+  if (kpt == KK && nthr == NT) {                                                                \
+    prefill_topk_kernel<KK, NT><<<probs, NT, 0, st>>>(scores, L.n_tiles, L.Hkv, L.E4, Es, L.ksel, \
+                                                      sel);                                     \
+    return true;                                                                                \
   }
+  BSA_PTK(4, 512) BSA_PTK(8, 512) BSA_PTK(16, 512) BSA_PTK(32, 512) BSA_PTK(64, 512)
+  BSA_PTK(128, 512) BSA_PTK(128, 1024)
 #undef BSA_PTK
-  return true;
+  return false;
 }
 
 // R3-R6: the three branches over a given selection, averaged into out
