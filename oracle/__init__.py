@@ -55,8 +55,8 @@ def load(path=LIB_PATH):
                                               i32, f64, vp, vp, vp]
     lib.oracle_sparse_decode_attn.restype = ctypes.c_int
     lib.oracle_sparse_prefill_attn.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
-                                               i32, i32, i32, i32, i32, f64, vp, vp, i32, vp, vp,
-                                               vp, vp, vp]
+                                               i32, i32, i32, i32, i32, f64, vp, vp, i32, i32, vp,
+                                               vp, vp, vp, vp, vp]
     lib.oracle_sparse_prefill_attn.restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
@@ -145,8 +145,11 @@ def sparse_decode_attn(q, k, v, idx, seq_len, block_size=64, scale=0.0, want_wei
 
 def sparse_prefill_attn(q, k, v, prior_len, m_sparse=4, top_k=2048, m_dense=128, window=128,
                         q_tile=64, scale=0.0, sel_in=None, rows=None, want_branches=False,
-                        want_sel=False, want_sel_scores=False, lib=None):
+                        want_sel=False, want_sel_scores=False, combine=0, sink_logits=None,
+                        lib=None):
     """q uint16 [B][C][Hq][d]; k, v uint16 [B][Hkv][stride][d] (prior + chunk tokens).
+    combine 0 averages the three branches, 1 takes one softmax over their
+    concatenated logits; sink_logits [Hq] (natural log) or None.
 
     Returns dict: out [B][R][Hq][d], lse3 [3][B][R][Hq], and optionally
     branches [3][B][R][Hq][d], sel [B][tiles][Hkv][k'], sel_scores."""
@@ -168,10 +171,14 @@ def sparse_prefill_attn(q, k, v, prior_len, m_sparse=4, top_k=2048, m_dense=128,
     if sel_in is not None:
         sel_in = np.ascontiguousarray(sel_in, dtype=np.int32)
         assert sel_in.shape == (B, n_tiles, Hkv, kk)
+    if sink_logits is not None:
+        sink_logits = np.ascontiguousarray(sink_logits, dtype=np.float64)
+        assert sink_logits.shape == (Hq,)
     rc = lib.oracle_sparse_prefill_attn(_p(q), C, _p(k), _p(v), B, prior_len, Hq, Hkv, d,
                                         stride, m_sparse, top_k, m_dense, window, q_tile,
-                                        float(scale), _p(sel_in), _p(rows),
-                                        R, _p(out), _p(br), _p(lse3), _p(sel), _p(ss))
+                                        float(scale), _p(sel_in), _p(rows), R, int(combine),
+                                        _p(sink_logits), _p(out), _p(br), _p(lse3), _p(sel),
+                                        _p(ss))
     if rc:
         raise ValueError(f"oracle_sparse_prefill_attn rc={rc}")
     return {"out": out, "lse3": lse3, "branches": br, "sel": sel, "sel_scores": ss}

@@ -310,12 +310,12 @@ int oracle_sparse_prefill_attn(const uint16_t* q, int32_t C, const uint16_t* k,
                                int32_t Hkv, int32_t d, int32_t stride, int32_t m_sparse,
                                int32_t top_k, int32_t m_dense, int32_t window,
                                int32_t q_tile, double scale, const int32_t* sel_in,
-                               const int32_t* rows, int32_t n_rows, double* out,
-                               double* branch_out, double* lse3, int32_t* sel_out,
-                               double* sel_scores) {
+                               const int32_t* rows, int32_t n_rows, int32_t combine,
+                               const double* sink_logits, double* out, double* branch_out,
+                               double* lse3, int32_t* sel_out, double* sel_scores) {
   if (!q || !k || !v || !out || C <= 0 || B <= 0 || P < 0 || Hq <= 0 || Hkv <= 0 ||
       Hq % Hkv || d <= 0 || stride < P + C || m_sparse <= 0 || top_k < 0 || m_dense <= 0 ||
-      window <= 0 || q_tile <= 0 || d > 512)
+      window <= 0 || q_tile <= 0 || d > 512 || (combine != 0 && combine != 1))
     return -1;
   if (!rows) n_rows = C;
   if (n_rows < 0) return -1;
@@ -400,6 +400,7 @@ int oracle_sparse_prefill_attn(const uint16_t* q, int32_t C, const uint16_t* k,
   int32_t maxn = kk;
   if (E128 > maxn) maxn = E128;
   if (window > maxn) maxn = window;
+  int32_t max_all = kk + E128 + window + 1; /* concatenated logits (+ the sink) */
 #pragma omp parallel for schedule(dynamic)
   for (int64_t wi = 0; wi < nwork; ++wi) {
     int64_t b = wi / ((int64_t)n_rows * Hq);
@@ -427,7 +428,62 @@ int oracle_sparse_prefill_attn(const uint16_t* q, int32_t C, const uint16_t* k,
     for (int32_t t = t0; t <= p; ++t) rk[n++] = (pair * stride + t) * (int64_t)d;
     l[2] = attend(qh, NULL, d, n, rk, rk, k, v, NULL, NULL, scale, z, o[2], NULL);
     double* dst = out + wi * d;
-    for (int32_t c = 0; c < d; ++c) dst[c] = (o[0][c] + o[1][c] + o[2][c]) / 3.0;
+    int has_sink = sink_logits != NULL;
+    double zs = has_sink ? sink_logits[h] : 0.0;
+    if (combine == 0) {
+      /* average of the three branch outputs; with a sink logit each branch's
+       * softmax also holds one extra logit zs whose value vector is zero
+       * ("CSA + HCA 混合注意力机制" §5.4) */
+      for (int32_t c = 0; c < d; ++c) dst[c] = 0.0;
+      for (int32_t br = 0; br < 3; ++br) {
+        double keep = has_sink ? 1.0 / (1.0 + exp(zs - l[br])) : 1.0;
+        for (int32_t c = 0; c < d; ++c) dst[c] += o[br][c] * keep;
+      }
+      for (int32_t c = 0; c < d; ++c) dst[c] /= 3.0;
+    } else {
+      /* one softmax over the concatenated logits of A, B and C (and the sink
+       * logit, value zero): §4.3 attends the compressed entries, the window
+       * and the tail together */
+      int64_t* rka = (int64_t*)malloc(sizeof(int64_t) * ((size_t)max_all + 1));
+      double* za = (double*)malloc(sizeof(double) * ((size_t)max_all + 1));
+      int32_t src[3] = {0, 0, 0}, na = 0;
+      /* logits of each branch in order */
+      for (int32_t t = 0; t < kk; ++t) rka[na++] = (pair * E4 + list[t]) * (int64_t)d;
+      src[0] = na;
+      for (int32_t t = 0; t < E128; ++t) rka[na++] = (pair * E128 + t) * (int64_t)d;
+      src[1] = na;
+      for (int32_t t = t0; t <= p; ++t) rka[na++] = (pair * stride + t) * (int64_t)d;
+      src[2] = na;
+      double zmax = has_sink ? zs : -INFINITY;
+      for (int32_t t = 0; t < na; ++t) {
+        double sdot = 0.0;
+        for (int32_t c = 0; c < d; ++c) {
+          double kc = t < src[0]   ? (double)k4[rka[t] + c]
+                      : t < src[1] ? (double)k128[rka[t] + c]
+                                   : bf(k[rka[t] + c]);
+          sdot += bf(qh[c]) * kc;
+        }
+        za[t] = sdot * scale;
+        if (za[t] > zmax) zmax = za[t];
+      }
+      double den = has_sink ? exp(zs - zmax) : 0.0;
+      for (int32_t t = 0; t < na; ++t) {
+        za[t] = exp(za[t] - zmax);
+        den += za[t];
+      }
+      for (int32_t c = 0; c < d; ++c) dst[c] = 0.0;
+      for (int32_t t = 0; t < na; ++t) {
+        double pw = za[t] / den;
+        for (int32_t c = 0; c < d; ++c) {
+          double vc = t < src[0]   ? (double)v4[rka[t] + c]
+                      : t < src[1] ? (double)v128[rka[t] + c]
+                                   : bf(v[rka[t] + c]);
+          dst[c] += pw * vc;
+        }
+      }
+      free(rka);
+      free(za);
+    }
     int64_t nb3 = (int64_t)B * n_rows * Hq;
     for (int32_t br = 0; br < 3; ++br) {
       if (branch_out)

@@ -55,7 +55,7 @@ int oracle_sparse_decode_attn(const uint16_t* q, const uint16_t* k, const uint16
                               int32_t bs, double scale, double* out, double* lse,
                               double* weights);
 
-/* chunked prefill with three branches averaged:
+/* chunked prefill with three branches, combined by `combine`:
  *   A: top_k entries of the m_sparse mean-pooled stream, chosen per
  *      (query tile of q_tile queries, kv head);
  *   B: all entries of the m_dense mean-pooled stream;
@@ -67,15 +67,20 @@ int oracle_sparse_decode_attn(const uint16_t* q, const uint16_t* k, const uint16
  * (use this selection for branch A instead of the oracle's own);
  * sel_out [B][n_tiles][Hkv][top_k'] or NULL (every tile);
  * sel_scores [B][n_tiles][Hkv][E_sparse] or NULL (every tile).
- * top_k' = min(top_k, E_sparse). */
+ * top_k' = min(top_k, E_sparse).
+ * combine 0: out = mean of the three branch softmax outputs; 1: one softmax
+ * over the concatenated logits of all three branches.  sink_logits [Hq] or
+ * NULL: one extra logit per head (natural-log units) with a zero value vector,
+ * in each branch's softmax (combine 0) or in the concatenated one (combine 1).
+ * branch_out and lse3 always describe the branches without the sink. */
 int oracle_sparse_prefill_attn(const uint16_t* q, int32_t C, const uint16_t* k,
                                const uint16_t* v, int32_t B, int32_t P, int32_t Hq,
                                int32_t Hkv, int32_t d, int32_t stride, int32_t m_sparse,
                                int32_t top_k, int32_t m_dense, int32_t window,
                                int32_t q_tile, double scale, const int32_t* sel_in,
-                               const int32_t* rows, int32_t n_rows, double* out,
-                               double* branch_out, double* lse3, int32_t* sel_out,
-                               double* sel_scores);
+                               const int32_t* rows, int32_t n_rows, int32_t combine,
+                               const double* sink_logits, double* out, double* branch_out,
+                               double* lse3, int32_t* sel_out, double* sel_scores);
 
 /* round an fp64 value to the nearest bf16 (ties to even); returns bits */
 uint16_t oracle_round_bf16(double x);

@@ -34,7 +34,16 @@ MUTANTS = [
      "int32_t t0 = p - window > 0 ? p - window : 0;"),
     ("tile pools one query", "int32_t i1 = i0 + q_tile < C ? i0 + q_tile : C;",
      "int32_t i1 = i0 + 1;"),
-    ("branch average", "(o[0][c] + o[1][c] + o[2][c]) / 3.0", "(o[0][c] + o[1][c] + o[2][c]) / 2.0"),
+    ("branch average", "for (int32_t c = 0; c < d; ++c) dst[c] /= 3.0;",
+     "for (int32_t c = 0; c < d; ++c) dst[c] /= 2.0;"),
+    ("concat drops the query's own token", "for (int32_t t = t0; t <= p; ++t) rka[na++]",
+     "for (int32_t t = t0; t < p; ++t) rka[na++]"),
+    ("concat reads K as V for the dense entries", ": t < src[1] ? (double)v128[rka[t] + c]",
+     ": t < src[1] ? (double)k128[rka[t] + c]"),
+    ("sink logit sign", "double den = has_sink ? exp(zs - zmax) : 0.0;",
+     "double den = has_sink ? exp(zmax - zs) : 0.0;"),
+    ("branch sink uses the wrong lse", "double keep = has_sink ? 1.0 / (1.0 + exp(zs - l[br])) : 1.0;",
+     "double keep = has_sink ? 1.0 / (1.0 + exp(zs - l[0])) : 1.0;"),
     ("bf16 ties away from zero", "double ri = rint(s);", "double ri = floor(s + 0.5);"),
     ("dense branch reads K as V", "E128, rk, rk, NULL, NULL, k128, v128,",
      "E128, rk, rk, NULL, NULL, k128, k128,"),

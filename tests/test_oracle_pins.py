@@ -493,3 +493,71 @@ def test_prefill_tile_scores_from_unit_entries(orc):
         for kvh in range(Hkv):
             qs = q[0, t * qt:min((t + 1) * qt, C), kvh * 2:kvh * 2 + 2].sum(axis=(0, 1))
             np.testing.assert_allclose(ss[t, kvh], qs[cols], atol=1e-12)
+
+
+# ------------------------------------------- branch combination and sink logits
+# "CSA + HCA 混合注意力机制" §4.3 attends the compressed entries, the window and the
+# tail in one softmax; §5.4 adds a learnable sink logit (no value) to the softmax.
+
+def _lse(x, axis=0):
+    m = np.max(x, axis=axis, keepdims=True)
+    return (m + np.log(np.exp(x - m).sum(axis=axis, keepdims=True))).squeeze(axis)
+
+
+def test_prefill_concat_is_lse_weighted_branches(orc):
+    # one softmax over the concatenated logits = sum_X e^(lse_X - L) o_X,
+    # L = log sum_X e^(lse_X); the concat path computes its logits itself
+    q, k, v = prefill_case(25, exact=False)
+    P = 256
+    kw = dict(top_k=8, m_dense=32, window=20, q_tile=16, want_branches=True)
+    r = orc.sparse_prefill_attn(q, k, v, P, combine=1, **kw)
+    lse3, br = r["lse3"], r["branches"]
+    L = _lse(lse3, axis=0)
+    ref = (np.exp(lse3 - L)[..., None] * br).sum(axis=0)
+    np.testing.assert_allclose(r["out"], ref, atol=1e-12)
+    # the branches themselves do not depend on the combination
+    r0 = orc.sparse_prefill_attn(q, k, v, P, combine=0, **kw)
+    np.testing.assert_array_equal(r0["branches"], br)
+    np.testing.assert_array_equal(r0["lse3"], lse3)
+
+
+def test_prefill_sink_closed_forms(orc):
+    q, k, v = prefill_case(26, exact=False)
+    P, Hq = 256, 4
+    kw = dict(top_k=8, m_dense=32, window=20, q_tile=16, want_branches=True)
+    z = np.array([-1.5, 0.0, 2.0, 7.0])
+    for combine in (0, 1):
+        base = orc.sparse_prefill_attn(q, k, v, P, combine=combine, **kw)
+        # a sink logit far below every logit changes nothing
+        far = orc.sparse_prefill_attn(q, k, v, P, combine=combine,
+                                      sink_logits=np.full(Hq, -1e300), **kw)
+        np.testing.assert_array_equal(far["out"], base["out"])
+        # a sink logit far above every logit takes all the mass
+        big = orc.sparse_prefill_attn(q, k, v, P, combine=combine,
+                                      sink_logits=np.full(Hq, 1e3), **kw)
+        assert np.abs(big["out"]).max() < 1e-300
+        r = orc.sparse_prefill_attn(q, k, v, P, combine=combine, sink_logits=z, **kw)
+        lse3, br = base["lse3"], base["branches"]
+        if combine == 0:
+            # each branch keeps e^lse / (e^lse + e^z) of its mass
+            keep = 1.0 / (1.0 + np.exp(z[None, None, None, :] - lse3))
+            ref = (keep[..., None] * br).sum(axis=0) / 3.0
+        else:
+            L = _lse(lse3, axis=0)
+            ref = base["out"] / (1.0 + np.exp(z[None, None, :] - L))[..., None]
+        np.testing.assert_allclose(r["out"], ref, atol=1e-12)
+    # a sink logit equal to a branch's lse halves that branch (single branch view)
+    one = orc.sparse_prefill_attn(q, k, v, P, combine=0, **kw)
+    h_lse = one["lse3"][0, 0, 5, :]  # branch A, query 5, every head
+    rows = np.array([5], np.int32)
+    rr = orc.sparse_prefill_attn(q, k, v, P, combine=0, rows=rows, sink_logits=h_lse, **kw)
+    keep = 1.0 / (1.0 + np.exp(h_lse[None, :] - one["lse3"][:, 0, 5, :]))
+    assert np.allclose(keep[0], 0.5, atol=1e-15)
+    ref = (keep[..., None] * one["branches"][:, 0, 5]).sum(axis=0) / 3.0
+    np.testing.assert_allclose(rr["out"][0, 0], ref, atol=1e-12)
+
+
+def test_prefill_combine_rejects_unknown_mode(orc):
+    q, k, v = prefill_case(27)
+    with pytest.raises(ValueError):
+        orc.sparse_prefill_attn(q, k, v, 256, top_k=8, combine=2)
