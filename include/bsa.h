@@ -68,7 +68,13 @@ typedef struct {
   int32_t m_dense;       /* tokens per entry of the dense stream (128) */
   int32_t window;        /* raw tokens attended up to and including the query (128) */
   int32_t q_tile;        /* consecutive queries sharing one selection (64) */
+  int32_t combine;       /* BSA_COMBINE_AVERAGE or BSA_COMBINE_CONCAT */
 } bsa_prefill_cfg;
+
+/* how sparse_prefill_attn joins its three branches */
+#define BSA_COMBINE_AVERAGE 0 /* (o_A + o_B + o_C) / 3, each branch its own softmax */
+#define BSA_COMBINE_CONCAT 1  /* one softmax over the concatenated logits of all three
+                                 ("CSA + HCA 混合注意力机制" §4.3) */
 
 /* ceil(n / m): blocks (or compressed entries) covering n tokens; -1 if m <= 0 or n < 0 */
 int32_t bsa_num_blocks(int32_t n, int32_t m);
@@ -168,7 +174,11 @@ int sparse_decode_attn_split(const void* q, const void* k, const void* v,
  *   k_cmp_sparse_f32     fp32 [B][Hkv][E_s][d]   (E_s = ceil(P / m_sparse); from build_block_summaries)
  *   k/v_cmp_sparse_bf16  bf16 [B][Hkv][E_s][d]
  *   k/v_cmp_dense_bf16   bf16 [B][Hkv][E_d][d]   (E_d = ceil(P / m_dense))
- *   out                  fp32 [B][C][Hq][d] = (o_A + o_B + o_C) / 3
+ *   sink_logits          fp32 [Hq] or NULL: one learnable sink logit per query head
+ *                        (natural-log units, "CSA + HCA 混合注意力机制" §5.4): an extra
+ *                        logit with a zero value vector in each branch's softmax
+ *                        (average) or in the single concatenated softmax (concat)
+ *   out                  fp32 [B][C][Hq][d]: the branches joined per cfg->combine
  *   lse3                 fp32 [3][B][C][Hq] per-branch log-sum-exp, or NULL
  *   sel_out              int32 [B][ceil(C / q_tile)][Hkv][min(top_k_sparse, E_s)] ascending, or NULL
  *   workspace            bsa_prefill_workspace_size() bytes, 16-byte aligned
@@ -180,8 +190,9 @@ int sparse_prefill_attn(const void* q, int32_t chunk_len, const void* k, const v
                         const float* k_cmp_sparse_f32, const void* k_cmp_sparse_bf16,
                         const void* v_cmp_sparse_bf16, const void* k_cmp_dense_bf16,
                         const void* v_cmp_dense_bf16, const bsa_shape* shape,
-                        const bsa_prefill_cfg* cfg, float scale, float* out, float* lse3,
-                        int32_t* sel_out, void* workspace, size_t ws_bytes, void* hip_stream);
+                        const bsa_prefill_cfg* cfg, float scale, const float* sink_logits,
+                        float* out, float* lse3, int32_t* sel_out, void* workspace,
+                        size_t ws_bytes, void* hip_stream);
 
 /* select_prefill_entries -- the selection step of sparse_prefill_attn alone
  * (the indexer role of "CSA + HCA 混合注意力机制" §4.2 with the pooled tile
@@ -206,7 +217,8 @@ int sparse_prefill_attn_selected(const void* q, int32_t chunk_len, const void* k
                                  const void* k_cmp_sparse_bf16, const void* v_cmp_sparse_bf16,
                                  const void* k_cmp_dense_bf16, const void* v_cmp_dense_bf16,
                                  const int32_t* sel, const bsa_shape* shape,
-                                 const bsa_prefill_cfg* cfg, float scale, float* out, float* lse3,
+                                 const bsa_prefill_cfg* cfg, float scale,
+                                 const float* sink_logits, float* out, float* lse3,
                                  void* hip_stream);
 
 #ifdef __cplusplus

@@ -39,7 +39,7 @@ class bsa_select_cfg(ctypes.Structure):
 class bsa_prefill_cfg(ctypes.Structure):
     _fields_ = [("m_sparse", ctypes.c_int32), ("top_k_sparse", ctypes.c_int32),
                 ("m_dense", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("q_tile", ctypes.c_int32)]
+                ("q_tile", ctypes.c_int32), ("combine", ctypes.c_int32)]
 
 
 _lib = None
@@ -72,11 +72,12 @@ def lib():
     L.sparse_decode_attn_split.argtypes = [vp, vp, vp, vp, i32, P(bsa_shape), i32, f32, vp, vp,
                                            vp, sz, i32, vp]
     L.sparse_prefill_attn.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, P(bsa_shape),
-                                      P(bsa_prefill_cfg), f32, vp, vp, vp, vp, sz, vp]
+                                      P(bsa_prefill_cfg), f32, vp, vp, vp, vp, vp, sz, vp]
     L.select_prefill_entries.argtypes = [vp, i32, vp, P(bsa_shape), P(bsa_prefill_cfg), vp, vp,
                                          sz, vp]
     L.sparse_prefill_attn_selected.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp,
-                                               P(bsa_shape), P(bsa_prefill_cfg), f32, vp, vp, vp]
+                                               P(bsa_shape), P(bsa_prefill_cfg), f32, vp, vp, vp,
+                                               vp]
     for fn in ("build_block_summaries", "select_blocks", "sparse_decode_attn",
                "sparse_decode_attn_split", "sparse_prefill_attn", "select_prefill_entries",
                "sparse_prefill_attn_selected"):
@@ -116,8 +117,12 @@ def select_cfg(block_size=64, n_sink=1, n_local=2, top_k=-1, keep_ratio=0.0):
     return bsa_select_cfg(block_size, n_sink, n_local, top_k, keep_ratio)
 
 
-def prefill_cfg(m_sparse=4, top_k_sparse=2048, m_dense=128, window=128, q_tile=64):
-    return bsa_prefill_cfg(m_sparse, top_k_sparse, m_dense, window, q_tile)
+COMBINE_AVERAGE, COMBINE_CONCAT = 0, 1
+
+
+def prefill_cfg(m_sparse=4, top_k_sparse=2048, m_dense=128, window=128, q_tile=64,
+                combine=COMBINE_AVERAGE):
+    return bsa_prefill_cfg(m_sparse, top_k_sparse, m_dense, window, q_tile, combine)
 
 
 def num_blocks(n, m):
@@ -219,7 +224,8 @@ def sparse_decode_attn(q, k, v, block_idx, seq_len, block_size=64, scale=0.0, n_
 
 def sparse_prefill_attn(q, k, v, k_cmp_sparse_f32, k_cmp_sparse_bf16, v_cmp_sparse_bf16,
                         k_cmp_dense_bf16, v_cmp_dense_bf16, prior_len, cfg=None, scale=0.0,
-                        want_lse3=False, want_sel=False, out=None, workspace=None):
+                        want_lse3=False, want_sel=False, out=None, workspace=None,
+                        sink_logits=None):
     """Chunked prefill: q bf16 [B][C][Hq][d]; k, v bf16 [B][Hkv][stride][d] with the chunk's
     K/V at [prior_len, prior_len + C).  Returns (out fp32 [B][C][Hq][d], lse3, sel)."""
     import torch
@@ -252,10 +258,22 @@ def sparse_prefill_attn(q, k, v, k_cmp_sparse_f32, k_cmp_sparse_bf16, v_cmp_spar
            lib().sparse_prefill_attn(_ptr(q), C, _ptr(k), _ptr(v), _ptr(k_cmp_sparse_f32),
                                      _ptr(k_cmp_sparse_bf16), _ptr(v_cmp_sparse_bf16),
                                      _ptr(k_cmp_dense_bf16), _ptr(v_cmp_dense_bf16),
-                                     ctypes.byref(shape), ctypes.byref(cfg), scale, _ptr(out),
+                                     ctypes.byref(shape), ctypes.byref(cfg), scale,
+                                     _ptr(_sink(sink_logits, Hq)), _ptr(out),
                                      _ptr(lse3), _ptr(sel), _ptr(workspace), workspace.numel(),
                                      _stream(q.device)))
     return out, lse3, sel
+
+
+def _sink(t, Hq):
+    """Per-head sink logits as a contiguous fp32 device tensor [Hq], or None."""
+    import torch
+    if t is None:
+        return None
+    _need(t, "sink_logits", torch.float32, 1)
+    if t.shape[0] != Hq:
+        raise ValueError(f"sink_logits must have {Hq} entries")
+    return t
 
 
 def _prefill_shape(q, k, prior_len, cfg):
@@ -294,7 +312,7 @@ def select_prefill_entries(q, k, k_cmp_sparse_f32, prior_len, cfg=None, sel=None
 
 def sparse_prefill_attn_selected(q, k, v, k_cmp_sparse_bf16, v_cmp_sparse_bf16, k_cmp_dense_bf16,
                                  v_cmp_dense_bf16, sel, prior_len, cfg=None, scale=0.0,
-                                 want_lse3=False, out=None):
+                                 want_lse3=False, out=None, sink_logits=None):
     """The prefill's three branches and their average over a given selection `sel`."""
     import torch
     cfg = cfg or prefill_cfg()
@@ -316,7 +334,8 @@ def sparse_prefill_attn_selected(q, k, v, k_cmp_sparse_bf16, v_cmp_sparse_bf16, 
                                               _ptr(k_cmp_sparse_bf16), _ptr(v_cmp_sparse_bf16),
                                               _ptr(k_cmp_dense_bf16), _ptr(v_cmp_dense_bf16),
                                               _ptr(sel), ctypes.byref(shape), ctypes.byref(cfg),
-                                              scale, _ptr(out), _ptr(lse3), _stream(q.device)))
+                                              scale, _ptr(_sink(sink_logits, Hq)), _ptr(out),
+                                              _ptr(lse3), _stream(q.device)))
     return out, lse3
 
 
@@ -340,10 +359,10 @@ def build_compressed_streams(k, v, prior_len, cfg=None):
 
 
 def prefill_step(q, k, v, prior_len, cfg=None, scale=0.0, want_lse3=False, want_sel=False,
-                 streams=None):
+                 streams=None, sink_logits=None):
     """Chunked prefill: pooled streams (unless given), then sparse_prefill_attn."""
     cfg = cfg or prefill_cfg()
     if streams is None:
         streams = build_compressed_streams(k, v, prior_len, cfg)
     return sparse_prefill_attn(q, k, v, *streams, prior_len, cfg=cfg, scale=scale,
-                               want_lse3=want_lse3, want_sel=want_sel)
+                               want_lse3=want_lse3, want_sel=want_sel, sink_logits=sink_logits)

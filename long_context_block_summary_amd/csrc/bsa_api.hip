@@ -193,7 +193,7 @@ int prefill_setup(const void* q, int32_t chunk_len, const bsa_shape* shape,
                   const bsa_prefill_cfg* cfg, float scale, bsa::PrefillLaunch* L) {
   if (!q || !shape_ok(shape) || !cfg || chunk_len < 1 || shape->seq_len < 1) return BSA_INVALID_ARG;
   if (cfg->m_sparse < 1 || cfg->m_dense < 1 || cfg->top_k_sparse < 1 || cfg->window < 1 ||
-      cfg->q_tile < 1)
+      cfg->q_tile < 1 || (cfg->combine != BSA_COMBINE_AVERAGE && cfg->combine != BSA_COMBINE_CONCAT))
     return BSA_INVALID_ARG;
   if ((int64_t)shape->seq_len + chunk_len > shape->seq_stride) return BSA_INVALID_ARG;
   if (!aligned16(q)) return BSA_INVALID_ARG;
@@ -219,6 +219,7 @@ int prefill_setup(const void* q, int32_t chunk_len, const bsa_shape* shape,
   L->q_tile = cfg->q_tile;
   L->n_tiles = bsa_num_blocks(chunk_len, cfg->q_tile);
   L->scale = scale == 0.f ? 1.f / sqrtf(128.f) : scale;
+  L->combine = cfg->combine;
   return BSA_OK;
 }
 
@@ -264,7 +265,8 @@ int sparse_prefill_attn_selected(const void* q, int32_t chunk_len, const void* k
                                  const void* k_cmp_sparse_bf16, const void* v_cmp_sparse_bf16,
                                  const void* k_cmp_dense_bf16, const void* v_cmp_dense_bf16,
                                  const int32_t* sel, const bsa_shape* shape,
-                                 const bsa_prefill_cfg* cfg, float scale, float* out, float* lse3,
+                                 const bsa_prefill_cfg* cfg, float scale,
+                                 const float* sink_logits, float* out, float* lse3,
                                  void* hip_stream) {
   bsa::PrefillLaunch L;
   int st = prefill_setup(q, chunk_len, shape, cfg, scale, &L);
@@ -274,6 +276,7 @@ int sparse_prefill_attn_selected(const void* q, int32_t chunk_len, const void* k
   if (st != BSA_OK) return st;
   if (!sel) return BSA_INVALID_ARG;
   L.lse3 = lse3;
+  L.sink = sink_logits;
   if (!bsa::launch_prefill_attend(L, sel, static_cast<hipStream_t>(hip_stream)))
     return BSA_UNSUPPORTED;
   return launch_status();
@@ -283,8 +286,9 @@ int sparse_prefill_attn(const void* q, int32_t chunk_len, const void* k, const v
                         const float* k_cmp_sparse_f32, const void* k_cmp_sparse_bf16,
                         const void* v_cmp_sparse_bf16, const void* k_cmp_dense_bf16,
                         const void* v_cmp_dense_bf16, const bsa_shape* shape,
-                        const bsa_prefill_cfg* cfg, float scale, float* out, float* lse3,
-                        int32_t* sel_out, void* workspace, size_t ws_bytes, void* hip_stream) {
+                        const bsa_prefill_cfg* cfg, float scale, const float* sink_logits,
+                        float* out, float* lse3, int32_t* sel_out, void* workspace,
+                        size_t ws_bytes, void* hip_stream) {
   bsa::PrefillLaunch L;
   int st = prefill_setup(q, chunk_len, shape, cfg, scale, &L);
   if (st != BSA_OK) return st;
@@ -298,6 +302,7 @@ int sparse_prefill_attn(const void* q, int32_t chunk_len, const void* k, const v
     return BSA_WORKSPACE_TOO_SMALL;
   L.k4f = k_cmp_sparse_f32;
   L.lse3 = lse3;
+  L.sink = sink_logits;
   L.workspace = workspace;
   int32_t* sel = sel_out;
   if (!sel) {  // after the pooled queries and the scores

@@ -44,8 +44,10 @@ struct PrefillLaunch {
   const uint16_t* v128b;
   float* out;             // [B][C][Hq][128]
   float* lse3;            // [3][B][C][Hq] or null
+  const float* sink;      // [Hq] sink logits or null
   void* workspace;        // pooled queries + scores (R2 only)
   int B, C, Hq, Hkv, P, stride, E4, E128, ksel, window, q_tile, n_tiles;
+  int combine;            // 0 average, 1 concatenated softmax
   float scale;
 };
 constexpr int PREFILL_MAX_E4 = 131072;  // entries of the selected stream per (b, kv head)

@@ -407,7 +407,9 @@ struct PrefillAttnArgs {
   const int32_t* sel;    // [B][n_tiles][Hkv][ksel]
   float* out;            // [B][C][Hq][D]
   float* lse3;           // [3][B][C][Hq] or null
+  const float* sink;     // [Hq] sink logits (natural log) or null
   int B, C, Hq, Hkv, P, stride, E4, E128, ksel, window, q_tile, n_tiles;
+  int combine;           // 0: average of the branches, 1: one softmax over all of them
   float scale_log2;
 };
 
@@ -444,7 +446,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
   static_assert(PF_CH == 64 && NTH / LPR == 16, "16 groups of 4 entries per chunk");
   __shared__ __align__(16) uint4 k_lds[2][PF_CH * (D / 8)];      // entry rows, 16 B pieces, xor-swizzled
   __shared__ __align__(16) uint16_t vt_lds[2][D * PF_CH];        // V^T fp16 [dim][entry], 8 B groups swizzled
-  __shared__ __align__(16) float xch[NW][2][RW];
+  __shared__ __align__(16) float xch[NW][4][RW];  // alpha, l, lse, running concat lse
   __shared__ int32_t sel_lds[PF_MAX_SEL];                        // the tile's branch-A entries
 
   const int g = a.Hq / a.Hkv;
@@ -679,62 +681,86 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
     // divides by 3), reset
     const bool last = (gc == nA - 1) || (gc == nA + nB - 1) || (gc == total - 1);
     if (last) {
+      // end of a branch: per-row sum l and lse = (m + log2 l) ln 2, then the
+      // branch output O / l is folded into `out`:
+      //   average:  out = (o_A k_A + o_B k_B + o_C k_C) / 3, k = 1 without a sink
+      //             logit z, else 1 / (1 + e^(z - lse)) (the sink joins each softmax);
+      //   concat:   one softmax over all branches' logits: out accumulates
+      //             e^(lse_X - L) o_X with the running L = log sum e^lse_X kept
+      //             in LDS per row; the sink logit scales by 1 / (1 + e^(z - L)).
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         float lt = l_run[nt];
         lt += __shfl_xor(lt, 16);
         lt += __shfl_xor(lt, 32);
         if (j4 == 0) {
+          const float lse = (m_run[nt] + log2f(lt)) * PF_LN2;
           xch[wave][1][16 * nt + l16] = lt;
+          xch[wave][2][16 * nt + l16] = lse;
           const int r = RW * wave + 16 * nt + l16;
           const int i = tile * a.q_tile + r / g;
           if (a.lse3 && i < a.C) {
             const int h = kvh * g + r % g;
-            a.lse3[(((int64_t)br * a.B + b) * a.C + i) * a.Hq + h] = (m_run[nt] + log2f(lt)) * PF_LN2;
+            a.lse3[(((int64_t)br * a.B + b) * a.C + i) * a.Hq + h] = lse;
           }
         }
       }
       wave_lds_sync();
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float4 l4 = *reinterpret_cast<const float4*>(&xch[wave][1][16 * nt + 4 * j4]);
-        const float inv[4] = {__builtin_amdgcn_rcpf(l4.x), __builtin_amdgcn_rcpf(l4.y),
-                              __builtin_amdgcn_rcpf(l4.z), __builtin_amdgcn_rcpf(l4.w)};
         // row addresses from an opaque copy of the lane id: computed here
         // rather than kept live across the chunk loop
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int jo = ln >> 4;
-        float* dst[4];
+        const float4 l4 = *reinterpret_cast<const float4*>(&xch[wave][1][16 * nt + 4 * jo]);
+        const float4 s4 = *reinterpret_cast<const float4*>(&xch[wave][2][16 * nt + 4 * jo]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float lse[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = RW * wave + 16 * nt + 4 * jo + i;
-          const int qi = min(tile * a.q_tile + r / g, a.C - 1);
-          dst[i] = a.out + (((int64_t)b * a.C + qi) * a.Hq + kvh * g + r % g) * D + (ln & 15);
-        }
-        // rows past the chunk's end (qi clamped) belong to no query: skip them
-        bool live[4];
+          const int qi = tile * a.q_tile + r / g;
+          const int h = kvh * g + r % g;
+          // coefficients: out = ca * out + cb * (O / l)
+          float ca = 0.f, cb = 1.f;
+          if (a.combine == 0) {  // uniform
+            if (a.sink) cb = 1.f / (1.f + __expf(a.sink[h] - lse[i]));
+            if (br == 2) {
+              ca = 1.f / 3.f;
+              cb *= 1.f / 3.f;
+            } else {
+              ca = br == 0 ? 0.f : 1.f;
+            }
+          } else {
+            float* Lp = &xch[wave][3][16 * nt + 4 * jo + i];
+            float L = lse[i];
+            if (br > 0) {
+              const float Lo = *Lp, mx = fmaxf(Lo, lse[i]);
+              L = mx + __logf(__expf(Lo - mx) + __expf(lse[i] - mx));
+              ca = __expf(Lo - L);
+              cb = __expf(lse[i] - L);
+            }
+            if ((ln & 15) == 0) *Lp = L;
+            if (br == 2 && a.sink) {
+              const float keep = 1.f / (1.f + __expf(a.sink[h] - L));
+              ca *= keep;
+              cb *= keep;
+            }
+          }
+          cb *= __builtin_amdgcn_rcpf(lv[i]);
+          // rows past the chunk's end belong to no query: skip them
+          if (qi < a.C) {
+            float* dst = a.out + (((int64_t)b * a.C + qi) * a.Hq + h) * D + (ln & 15);
+            if (br == 0) {  // uniform: out holds nothing yet
 #pragma unroll
-        for (int i = 0; i < 4; ++i) live[i] = tile * a.q_tile + (RW * wave + 16 * nt + 4 * jo + i) / g < a.C;
-        if (br == 0) {  // uniform
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (live[i])
-#pragma unroll
-              for (int nd = 0; nd < D / 16; ++nd) dst[i][16 * nd] = O[nt][nd][i] * inv[i];
-        } else if (br == 1) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (live[i])
-#pragma unroll
-              for (int nd = 0; nd < D / 16; ++nd) dst[i][16 * nd] += O[nt][nd][i] * inv[i];
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (live[i])
+              for (int nd = 0; nd < D / 16; ++nd) dst[16 * nd] = O[nt][nd][i] * cb;
+            } else {
 #pragma unroll
               for (int nd = 0; nd < D / 16; ++nd)
-                dst[i][16 * nd] = (dst[i][16 * nd] + O[nt][nd][i] * inv[i]) * (1.f / 3.f);
+                dst[16 * nd] = fmaf(dst[16 * nd], ca, O[nt][nd][i] * cb);
+            }
+          }
         }
 #pragma unroll
         for (int nd = 0; nd < D / 16; ++nd) O[nt][nd] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -808,7 +834,7 @@ bool launch_prefill_attend(const PrefillLaunch& L, const int32_t* sel, hipStream
   const unsigned probs = (unsigned)(L.B * L.n_tiles * L.Hkv);
   PrefillAttnArgs a;
   a.q = L.q; a.k = L.k; a.v = L.v; a.k4 = L.k4b; a.v4 = L.v4b; a.k128 = L.k128b; a.v128 = L.v128b;
-  a.sel = sel; a.out = L.out; a.lse3 = L.lse3;
+  a.sel = sel; a.out = L.out; a.lse3 = L.lse3; a.sink = L.sink; a.combine = L.combine;
   a.B = L.B; a.C = L.C; a.Hq = L.Hq; a.Hkv = L.Hkv; a.P = L.P; a.stride = L.stride;
   a.E4 = L.E4; a.E128 = L.E128; a.ksel = L.ksel; a.window = L.window; a.q_tile = L.q_tile;
   a.n_tiles = L.n_tiles; a.scale_log2 = L.scale * PF_LOG2E;

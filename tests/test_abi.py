@@ -119,20 +119,25 @@ def test_prefill_argument_checks_launch_nothing(L):
     # attention over a given selection: NULL selection, misaligned stream
     args = [fake, 128, fake, fake, fake, fake, fake, fake]
     assert L.sparse_prefill_attn_selected(*args, None, ctypes.byref(sh), ctypes.byref(pc), 0.0,
-                                          fake, None, None) == -1
+                                          None, fake, None, None) == -1
     args[4] = ctypes.c_void_p(0x1004)
     assert L.sparse_prefill_attn_selected(*args, fake, ctypes.byref(sh), ctypes.byref(pc), 0.0,
-                                          fake, None, None) == -1
+                                          None, fake, None, None) == -1
+    # unknown combination mode
+    args[4] = fake
+    bad_mode = bsa.prefill_cfg(combine=2)
+    assert L.sparse_prefill_attn_selected(*args, fake, ctypes.byref(sh), ctypes.byref(bad_mode),
+                                          0.0, None, fake, None, None) == -1
     # more selected entries than the kernel keeps in LDS; compressed stream too long
     big_k = bsa.prefill_cfg(top_k_sparse=8192)
     sh_long = bsa.make_shape(1, 32, 8, 128, 1 << 16, (1 << 16) + 128)
     assert L.sparse_prefill_attn(fake, 128, fake, fake, fake, fake, fake, fake, fake,
-                                 ctypes.byref(sh_long), ctypes.byref(big_k), 0.0, fake, None,
-                                 None, fake, 1 << 40, None) == -2
+                                 ctypes.byref(sh_long), ctypes.byref(big_k), 0.0, None, fake,
+                                 None, None, fake, 1 << 40, None) == -2
     sh_huge = bsa.make_shape(1, 32, 8, 128, 1 << 20, (1 << 20) + 128)
     assert L.sparse_prefill_attn(fake, 128, fake, fake, fake, fake, fake, fake, fake,
-                                 ctypes.byref(sh_huge), ctypes.byref(pc), 0.0, fake, None,
-                                 None, fake, 1 << 40, None) == -2
+                                 ctypes.byref(sh_huge), ctypes.byref(pc), 0.0, None, fake,
+                                 None, None, fake, 1 << 40, None) == -2
 
 
 def test_product_path_has_no_oracle_import():

@@ -46,15 +46,20 @@ def check_tile_selection(g_sel, o_sel, o_scores, rel=TIE_REL):
     return exempt
 
 
-def run_prefill_case(cfg, seed, rows=None):
+def run_prefill_case(cfg, seed, rows=None, combine=0, sink=None):
     import torch
     announce(cfg.name, "seed", seed, "B", cfg.batch, "Hq", cfg.n_q_heads, "Hkv", cfg.n_kv_heads,
              "P", cfg.prior_len, "C", cfg.chunk_len, "m", cfg.m_sparse, cfg.m_dense, "top_k",
-             cfg.top_k_sparse, "window", cfg.window, "q_tile", cfg.q_tile)
+             cfg.top_k_sparse, "window", cfg.window, "q_tile", cfg.q_tile, "combine", combine,
+             "sink", None if sink is None else list(np.round(sink, 3)))
     t = synth.gen_prefill(cfg, seed)
     q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
-    pc = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile)
-    out, lse3, sel = bsa.prefill_step(q, k, v, cfg.prior_len, pc, want_lse3=True, want_sel=True)
+    pc = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile,
+                         combine)
+    sink_dev = None if sink is None else torch.from_numpy(
+        np.asarray(sink, np.float32)).to(q.device)
+    out, lse3, sel = bsa.prefill_step(q, k, v, cfg.prior_len, pc, want_lse3=True, want_sel=True,
+                                      sink_logits=sink_dev)
     torch.cuda.synchronize()
     g_out, g_lse3, g_sel = out.cpu().numpy(), lse3.cpu().numpy(), sel.cpu().numpy()
     common = dict(m_sparse=cfg.m_sparse, top_k=cfg.top_k_sparse, m_dense=cfg.m_dense,
@@ -63,7 +68,10 @@ def run_prefill_case(cfg, seed, rows=None):
                                          want_sel=True, want_sel_scores=True, **common)
     exempt = check_tile_selection(g_sel, ref_sel["sel"], ref_sel["sel_scores"])
     ref = oracle.sparse_prefill_attn(t["q"], t["k"], t["v"], cfg.prior_len, sel_in=g_sel,
-                                     rows=rows, **common)
+                                     rows=rows, combine=combine,
+                                     sink_logits=None if sink is None
+                                     else np.asarray(sink, np.float32).astype(np.float64),
+                                     **common)
     gsub = g_out if rows is None else g_out[:, rows]
     lsub = g_lse3 if rows is None else g_lse3[:, :, rows]
     err = np.abs(gsub - ref["out"]).max()
@@ -98,6 +106,22 @@ def test_prefill_window_and_topk_edges():
     run_prefill_case(small(name="pf_win1", window=1, top_k_sparse=1, chunk_len=70), 72)
     # small prior context (fewer entries than top-k), partial dense entry
     run_prefill_case(small(name="pf_tiny_prior", prior_len=300, chunk_len=64), 73)
+
+
+@pytest.mark.parametrize("combine,with_sink", [(1, False), (0, True), (1, True)])
+def test_prefill_combine_and_sink(combine, with_sink):
+    # concatenated softmax over the branches ("CSA + HCA 混合注意力机制" §4.3) and per-head
+    # sink logits (§5.4); sinks span below, near and above the rows' lse values
+    cfg = small(name=f"pf_comb{combine}{'s' if with_sink else ''}", n_q_heads=8)
+    sink = np.linspace(-4.0, 6.0, cfg.n_q_heads) if with_sink else None
+    run_prefill_case(cfg, 91 + combine, combine=combine, sink=sink)
+
+
+def test_prefill_full_size_concat_sink_sampled_rows():
+    cfg = synth.CONFIGS["prefill256k"]
+    rows = np.array([0, 64, 777, 2047])
+    sink = np.linspace(-2.0, 3.0, cfg.n_q_heads)
+    run_prefill_case(cfg, synth.DEFAULT_SEED["prefill256k"], rows=rows, combine=1, sink=sink)
 
 
 def test_prefill_full_size_sampled_rows():
