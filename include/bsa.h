@@ -52,6 +52,11 @@ typedef struct {
   int32_t head_dim;    /* d: 64 or 128 */
   int32_t seq_len;     /* N: valid tokens in the cache (prefill: prior tokens P) */
   int32_t seq_stride;  /* cache capacity in tokens, >= seq_len (prefill: >= P + C) */
+  int32_t summary_stride; /* blocks between (b, kv head) rows of a block-summary buffer
+                             (build/update_block_summaries, select_blocks); 0 means
+                             ceil(seq_len / block_size).  A fixed stride (e.g.
+                             ceil(seq_stride / block_size)) lets a decode loop keep
+                             one buffer while blocks open.  Prefill streams are dense. */
 } bsa_shape;
 
 typedef struct {
@@ -103,13 +108,35 @@ const char* bsa_status_string(int status);
  * 稀疏注意力与 KV Cache 压缩的工程实现; mean pooling per "CSA + HCA
  * 混合注意力机制" §4.1; also the compressed streams of §4.1 and §5.1).
  *   x         bf16 [B][n_kv_heads][seq_stride][d]
- *   out_f32   fp32 [B][n_kv_heads][nb][d] or NULL    (nb = ceil(seq_len / block_size))
- *   out_bf16  bf16 [B][n_kv_heads][nb][d] or NULL    (the fp32 mean rounded to nearest even)
+ *   out_f32   fp32 [B][n_kv_heads][S][d] or NULL    (S = summary_stride, or nb =
+ *             ceil(seq_len / block_size) when that is 0)
+ *   out_bf16  bf16 [B][n_kv_heads][S][d] or NULL    (the fp32 mean rounded to nearest even)
  * A partial last block is averaged over its valid tokens.  Tokens past
  * seq_len are never read.  Sums are fp32.  At least one output is required.
  * Any block_size >= 1 is supported. */
 int build_block_summaries(const void* x, const bsa_shape* shape, int32_t block_size,
                           float* out_f32, void* out_bf16, void* hip_stream);
+
+/* update_block_summaries -- the per-token part of the decode loop (the block
+ * summary bookkeeping of the hotdry.top post, 稀疏注意力与 KV Cache 压缩的工程实现,
+ * on a growing cache): recomputes the summaries of the blocks holding tokens
+ * [first_token, seq_len) -- the partial last block and any blocks opened
+ * since -- from their tokens, with the same arithmetic and order as
+ * build_block_summaries, so the result is bit-identical to a rebuild.
+ * Other blocks are not touched.  Layout as build_block_summaries (rows
+ * shape->summary_stride blocks apart when non-zero).  0 <= first_token <= seq_len. */
+int update_block_summaries(const void* x, const bsa_shape* shape, int32_t block_size,
+                           int32_t first_token, float* out_f32, void* out_bf16,
+                           void* hip_stream);
+
+/* append_kv -- writes n_new tokens' K and V rows into the caches at positions
+ * [seq_len, seq_len + n_new) of every (b, kv head).
+ *   k_new, v_new      bf16 [B][Hkv][n_new][d]
+ *   k_cache, v_cache  bf16 [B][Hkv][seq_stride][d]
+ * Requires seq_len + n_new <= seq_stride; seq_len in `shape` is the count
+ * before the append. */
+int append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+              const bsa_shape* shape, int32_t n_new, void* hip_stream);
 
 /* select_blocks -- per (batch, kv head): pooled query qbar = sum of the
  * group's query heads (fp32), block scores s_j = qbar . summary_j for the
@@ -118,7 +145,8 @@ int build_block_summaries(const void* x, const bsa_shape* shape, int32_t block_s
  * ascending.  hotdry.top post, 稀疏注意力与 KV Cache 压缩的工程实现;
  * "CSA + HCA 混合注意力机制" §4.4 steps 1-3.
  *   q          bf16 [B][Hq][d]
- *   summaries  fp32 [B][Hkv][nb][d] from build_block_summaries (nb = ceil(seq_len / block_size))
+ *   summaries  fp32 [B][Hkv][S][d] from build_block_summaries (S = summary_stride, or
+ *              nb = ceil(seq_len / block_size) when that is 0)
  *   block_idx  int32 [B][Hkv][n_keep] output, n_keep = bsa_num_kept(nb, cfg)
  *   scores_out fp32 [B][Hkv][nb] or NULL: candidate scores (other entries are not written)
  *   workspace  bsa_select_workspace_size() bytes of device memory (may be NULL if 0)

@@ -27,7 +27,8 @@ class BsaError(RuntimeError):
 class bsa_shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("seq_len", ctypes.c_int32), ("seq_stride", ctypes.c_int32)]
+                ("seq_len", ctypes.c_int32), ("seq_stride", ctypes.c_int32),
+                ("summary_stride", ctypes.c_int32)]
 
 
 class bsa_select_cfg(ctypes.Structure):
@@ -66,6 +67,8 @@ def lib():
     L.bsa_prefill_workspace_size.restype = sz
     L.bsa_status_string.argtypes, L.bsa_status_string.restype = [ctypes.c_int], ctypes.c_char_p
     L.build_block_summaries.argtypes = [vp, P(bsa_shape), i32, vp, vp, vp]
+    L.update_block_summaries.argtypes = [vp, P(bsa_shape), i32, i32, vp, vp, vp]
+    L.append_kv.argtypes = [vp, vp, vp, vp, P(bsa_shape), i32, vp]
     L.select_blocks.argtypes = [vp, vp, P(bsa_shape), P(bsa_select_cfg), vp, vp, vp, sz, vp]
     L.sparse_decode_attn.argtypes = [vp, vp, vp, vp, i32, P(bsa_shape), i32, f32, vp, vp, vp, sz,
                                      vp]
@@ -78,7 +81,8 @@ def lib():
     L.sparse_prefill_attn_selected.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                                P(bsa_shape), P(bsa_prefill_cfg), f32, vp, vp, vp,
                                                vp]
-    for fn in ("build_block_summaries", "select_blocks", "sparse_decode_attn",
+    for fn in ("build_block_summaries", "update_block_summaries", "append_kv",
+               "select_blocks", "sparse_decode_attn",
                "sparse_decode_attn_split", "sparse_prefill_attn", "select_prefill_entries",
                "sparse_prefill_attn_selected"):
         getattr(L, fn).restype = ctypes.c_int
@@ -109,8 +113,8 @@ def _need(t, name, dtype, ndim):
                         f"{t.dtype} {tuple(t.shape)}")
 
 
-def make_shape(batch, n_q_heads, n_kv_heads, head_dim, seq_len, seq_stride):
-    return bsa_shape(batch, n_q_heads, n_kv_heads, head_dim, seq_len, seq_stride)
+def make_shape(batch, n_q_heads, n_kv_heads, head_dim, seq_len, seq_stride, summary_stride=0):
+    return bsa_shape(batch, n_q_heads, n_kv_heads, head_dim, seq_len, seq_stride, summary_stride)
 
 
 def select_cfg(block_size=64, n_sink=1, n_local=2, top_k=-1, keep_ratio=0.0):
@@ -136,21 +140,53 @@ def num_kept(nb, cfg):
 # ------------------------------------------------------------------ entry points
 
 def build_block_summaries(x, seq_len, block_size, want_f32=True, want_bf16=False,
-                          out_f32=None, out_bf16=None):
-    """x bf16 [B][H][stride][d] -> (fp32 [B][H][nb][d] or None, bf16 [B][H][nb][d] or None)."""
+                          out_f32=None, out_bf16=None, summary_stride=0):
+    """x bf16 [B][H][stride][d] -> (fp32 [B][H][S][d] or None, bf16 [B][H][S][d] or None),
+    S = summary_stride or nb = ceil(seq_len / block_size) when that is 0."""
     import torch
     _need(x, "x", torch.bfloat16, 4)
     B, H, stride, d = x.shape
-    nb = num_blocks(seq_len, block_size)
+    S = summary_stride or num_blocks(seq_len, block_size)
     if want_f32 and out_f32 is None:
-        out_f32 = torch.empty((B, H, nb, d), dtype=torch.float32, device=x.device)
+        out_f32 = torch.empty((B, H, S, d), dtype=torch.float32, device=x.device)
     if want_bf16 and out_bf16 is None:
-        out_bf16 = torch.empty((B, H, nb, d), dtype=torch.bfloat16, device=x.device)
-    shape = make_shape(B, H, H, d, seq_len, stride)
+        out_bf16 = torch.empty((B, H, S, d), dtype=torch.bfloat16, device=x.device)
+    shape = make_shape(B, H, H, d, seq_len, stride, summary_stride)
     _check("build_block_summaries",
            lib().build_block_summaries(_ptr(x), ctypes.byref(shape), block_size, _ptr(out_f32),
                                        _ptr(out_bf16), _stream(x.device)))
     return out_f32, out_bf16
+
+
+def update_block_summaries(x, seq_len, block_size, first_token, out_f32=None, out_bf16=None):
+    """Recompute, in place, the summaries of the blocks holding tokens [first_token, seq_len)
+    of x bf16 [B][H][stride][d]; out_* [B][H][S][d] as from build_block_summaries."""
+    import torch
+    _need(x, "x", torch.bfloat16, 4)
+    B, H, stride, d = x.shape
+    ref = out_f32 if out_f32 is not None else out_bf16
+    if ref is None:
+        raise ValueError("an output buffer is required")
+    shape = make_shape(B, H, H, d, seq_len, stride, ref.shape[2])
+    _check("update_block_summaries",
+           lib().update_block_summaries(_ptr(x), ctypes.byref(shape), block_size, first_token,
+                                        _ptr(out_f32), _ptr(out_bf16), _stream(x.device)))
+    return out_f32, out_bf16
+
+
+def append_kv(k_new, v_new, k_cache, v_cache, seq_len):
+    """Write k_new, v_new bf16 [B][Hkv][n][d] into the caches at [seq_len, seq_len + n)."""
+    import torch
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        _need(t, name, torch.bfloat16, 4)
+    B, H, n, d = k_new.shape
+    if tuple(v_new.shape) != (B, H, n, d) or k_cache.shape[:2] != (B, H) or \
+            tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[3] != d:
+        raise ValueError("append_kv: shapes do not match")
+    shape = make_shape(B, H, H, d, seq_len, k_cache.shape[2])
+    _check("append_kv", lib().append_kv(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                        ctypes.byref(shape), n, _stream(k_new.device)))
 
 
 def select_blocks(q, summaries, seq_len, block_size=64, n_sink=1, n_local=2, top_k=-1,
@@ -160,12 +196,15 @@ def select_blocks(q, summaries, seq_len, block_size=64, n_sink=1, n_local=2, top
     _need(q, "q", torch.bfloat16, 3)
     _need(summaries, "summaries", torch.float32, 4)
     B, Hq, d = q.shape
-    Hkv, nb = summaries.shape[1], summaries.shape[2]
+    Hkv, S = summaries.shape[1], summaries.shape[2]
+    nb = num_blocks(seq_len, block_size)
+    if S < nb:
+        raise ValueError(f"summaries hold {S} blocks, {nb} are in use")
     cfg = select_cfg(block_size, n_sink, n_local, top_k, keep_ratio)
     n_keep = num_kept(nb, cfg)
     if n_keep < 0:
         raise ValueError("invalid selection config")
-    shape = make_shape(B, Hq, Hkv, d, seq_len, seq_len)
+    shape = make_shape(B, Hq, Hkv, d, seq_len, seq_len, S)
     if block_idx is None:
         block_idx = torch.empty((B, Hkv, n_keep), dtype=torch.int32, device=q.device)
     scores = None
@@ -344,6 +383,23 @@ def decode_step(q, k, v, summaries, seq_len, block_size=64, n_sink=1, n_local=2,
     """select_blocks then sparse_decode_attn (the per-token hot path)."""
     idx, _ = select_blocks(q, summaries, seq_len, block_size, n_sink, n_local, top_k, keep_ratio)
     out, lse = sparse_decode_attn(q, k, v, idx, seq_len, block_size, scale)
+    return out, lse, idx
+
+
+def decode_loop_step(q, k_new, v_new, k_cache, v_cache, summaries, seq_len, block_size=64,
+                     n_sink=1, n_local=2, top_k=-1, keep_ratio=0.0, scale=0.0, block_idx=None,
+                     out=None, lse=None, sel_workspace=None, dec_workspace=None):
+    """One generated token: append its K/V at seq_len, refresh the summary of the block it
+    lands in (or opens), select, attend over seq_len + n tokens.  summaries fp32
+    [B][Hkv][S][d] with S >= ceil(capacity / block_size).  Returns (out, lse, idx)."""
+    n = k_new.shape[2]
+    append_kv(k_new, v_new, k_cache, v_cache, seq_len)
+    N = seq_len + n
+    update_block_summaries(k_cache, N, block_size, seq_len, out_f32=summaries)
+    idx, _ = select_blocks(q, summaries, N, block_size, n_sink, n_local, top_k, keep_ratio,
+                           block_idx=block_idx, workspace=sel_workspace)
+    out, lse = sparse_decode_attn(q, k_cache, v_cache, idx, N, block_size, scale, out=out,
+                                  lse=lse, workspace=dec_workspace)
     return out, lse, idx
 
 

@@ -14,7 +14,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool shape_ok(const bsa_shape* s) {
   return s && s->batch >= 1 && s->n_q_heads >= 1 && s->n_kv_heads >= 1 &&
          s->n_q_heads % s->n_kv_heads == 0 && s->head_dim >= 1 && s->seq_len >= 0 &&
-         s->seq_stride >= s->seq_len;
+         s->seq_stride >= s->seq_len && s->summary_stride >= 0;
 }
 
 bool dim_supported(int d) { return d == 64 || d == 128; }
@@ -45,6 +45,14 @@ int middle_k(int nb, const bsa_select_cfg* cfg, int n_cand) {
 bool select_cfg_ok(const bsa_select_cfg* c) {
   return c && c->block_size >= 1 && c->n_sink_blocks >= 0 && c->n_local_blocks >= 0 &&
          (c->top_k >= 0 || (c->keep_ratio >= 0.f && c->keep_ratio <= 1.f));
+}
+
+// blocks between consecutive (b, kv head) rows of a summaries buffer, or -1
+// when the shape's summary_stride is below the blocks in use
+int summary_stride(const bsa_shape* s, int bs) {
+  const int nb = bsa_num_blocks(s->seq_len, bs);
+  if (s->summary_stride == 0) return nb;
+  return s->summary_stride >= nb ? s->summary_stride : -1;
 }
 
 int launch_status() {
@@ -93,17 +101,45 @@ const char* bsa_status_string(int status) {
   }
 }
 
-int build_block_summaries(const void* x, const bsa_shape* shape, int32_t block_size,
-                          float* out_f32, void* out_bf16, void* hip_stream) {
+int update_block_summaries(const void* x, const bsa_shape* shape, int32_t block_size,
+                           int32_t first_token, float* out_f32, void* out_bf16,
+                           void* hip_stream) {
   if (!x || !shape_ok(shape) || block_size < 1 || (!out_f32 && !out_bf16)) return BSA_INVALID_ARG;
   if (!aligned16(x) || (out_f32 && !aligned16(out_f32)) || (out_bf16 && !aligned16(out_bf16)))
     return BSA_INVALID_ARG;
   if (!dim_supported(shape->head_dim)) return BSA_UNSUPPORTED;
-  if (shape->seq_len == 0) return BSA_OK;
+  const int nb = bsa_num_blocks(shape->seq_len, block_size);
+  const int ss = summary_stride(shape, block_size);
+  if (ss < 0 || first_token < 0 || first_token > shape->seq_len) return BSA_INVALID_ARG;
+  if (shape->seq_len == 0 || first_token == shape->seq_len) return BSA_OK;
+  const int j0 = first_token / block_size;
+  if (j0 >= nb) return BSA_OK;
   bsa::launch_summaries(static_cast<const uint16_t*>(x),
                         (int64_t)shape->batch * shape->n_kv_heads, shape->seq_len,
-                        shape->seq_stride, shape->head_dim, block_size, out_f32,
+                        shape->seq_stride, shape->head_dim, block_size, j0, ss, out_f32,
                         static_cast<uint16_t*>(out_bf16), static_cast<hipStream_t>(hip_stream));
+  return launch_status();
+}
+
+int build_block_summaries(const void* x, const bsa_shape* shape, int32_t block_size,
+                          float* out_f32, void* out_bf16, void* hip_stream) {
+  return update_block_summaries(x, shape, block_size, 0, out_f32, out_bf16, hip_stream);
+}
+
+int append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+              const bsa_shape* shape, int32_t n_new, void* hip_stream) {
+  if (!k_new || !v_new || !k_cache || !v_cache || !shape_ok(shape) || n_new < 0)
+    return BSA_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return BSA_INVALID_ARG;
+  if (!dim_supported(shape->head_dim)) return BSA_UNSUPPORTED;
+  if ((int64_t)shape->seq_len + n_new > shape->seq_stride) return BSA_INVALID_ARG;
+  const int64_t pairs = (int64_t)shape->batch * shape->n_kv_heads;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  bsa::launch_append(static_cast<const uint16_t*>(k_new), static_cast<uint16_t*>(k_cache), pairs,
+                     n_new, shape->seq_len, shape->seq_stride, shape->head_dim, st);
+  bsa::launch_append(static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(v_cache), pairs,
+                     n_new, shape->seq_len, shape->seq_stride, shape->head_dim, st);
   return launch_status();
 }
 
@@ -117,6 +153,8 @@ int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
     return BSA_INVALID_ARG;
   if (!dim_supported(shape->head_dim)) return BSA_UNSUPPORTED;
   const int nb = bsa_num_blocks(shape->seq_len, cfg->block_size);
+  const int ss = summary_stride(shape, cfg->block_size);
+  if (ss < 0) return BSA_INVALID_ARG;
   int c0, c1, fixed;
   kept_ranges(nb, cfg->n_sink_blocks, cfg->n_local_blocks, &c0, &c1, &fixed);
   const int k = middle_k(nb, cfg, c1 - c0);
@@ -129,7 +167,7 @@ int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
   }
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   bsa::launch_scores(static_cast<const uint16_t*>(q), summaries, shape->batch, shape->n_q_heads,
-                     shape->n_kv_heads, shape->head_dim, nb, c0, c1, scores, st);
+                     shape->n_kv_heads, shape->head_dim, nb, ss, c0, c1, scores, st);
   bsa::launch_topk(scores, (int64_t)shape->batch * shape->n_kv_heads, nb, c0, c1, k, n_keep,
                    block_idx, st);
   return launch_status();

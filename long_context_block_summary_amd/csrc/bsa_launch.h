@@ -7,13 +7,18 @@
 
 namespace bsa {
 
-// mean of every block of `bs` tokens: x [pairs][stride][d] -> [pairs][nb][d]
+// mean of the blocks [j0, nb) of `bs` tokens: x [pairs][stride][d] -> [pairs][ostride][d]
 void launch_summaries(const uint16_t* x, int64_t pairs, int N, int stride, int d, int bs,
-                      float* out_f32, uint16_t* out_bf16, hipStream_t st);
+                      int j0, int ostride, float* out_f32, uint16_t* out_bf16, hipStream_t st);
 
-// candidate scores s[pair][j] = qbar . summary_j for j in [c0, c1)
+// copy src [pairs][n_new][d] to dst [pairs][stride][d] at rows [N, N + n_new)
+void launch_append(const uint16_t* src, uint16_t* dst, int64_t pairs, int n_new, int N,
+                   int stride, int d, hipStream_t st);
+
+// candidate scores s[pair][j] = qbar . summary_j for j in [c0, c1); summaries
+// rows are sstride blocks apart, scores rows nb apart
 void launch_scores(const uint16_t* q, const float* summ, int B, int Hq, int Hkv, int d, int nb,
-                   int c0, int c1, float* scores, hipStream_t st);
+                   int sstride, int c0, int c1, float* scores, hipStream_t st);
 
 // per pair: sink [0,c0) + top-k of scores[c0,c1) + local [c1,nb), ascending
 void launch_topk(const float* scores, int64_t pairs, int nb, int c0, int c1, int k, int n_keep,

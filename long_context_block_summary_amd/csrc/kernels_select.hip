@@ -19,15 +19,16 @@ namespace bsa {
 template <int D>
 __global__ __launch_bounds__(256) void summaries_kernel(const uint16_t* __restrict__ x,
                                                         int64_t items, int N, int stride, int bs,
-                                                        int nb, float* __restrict__ out_f32,
+                                                        int j0, int nbr, int ostride,
+                                                        float* __restrict__ out_f32,
                                                         uint16_t* __restrict__ out_bf16) {
   constexpr int TPR = D / 8;  // threads per row
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t item = gid / TPR;
   const int part = (int)(gid % TPR);
   if (item >= items) return;
-  const int64_t pair = item / nb;
-  const int j = (int)(item % nb);
+  const int64_t pair = item / nbr;          // nbr blocks [j0, j0 + nbr) per pair
+  const int j = j0 + (int)(item % nbr);
   const int t0 = j * bs;
   const int n = min(bs, N - t0);
   const uint4* src = reinterpret_cast<const uint4*>(x + ((int64_t)pair * stride + t0) * D) + part;
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(256) void summaries_kernel(const uint16_t* __restri
   const float fn = (float)n;
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = acc[c] / fn;
-  const int64_t o = item * D + part * 8;
+  const int64_t o = (pair * ostride + j) * D + part * 8;
   if (out_f32) {
     float4* dst = reinterpret_cast<float4*>(out_f32 + o);
     dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -73,16 +74,42 @@ __global__ __launch_bounds__(256) void summaries_kernel(const uint16_t* __restri
 }
 
 void launch_summaries(const uint16_t* x, int64_t pairs, int N, int stride, int d, int bs,
-                      float* out_f32, uint16_t* out_bf16, hipStream_t st) {
+                      int j0, int ostride, float* out_f32, uint16_t* out_bf16, hipStream_t st) {
   const int nb = (N + bs - 1) / bs;
-  const int64_t items = pairs * nb;
+  const int nbr = nb - j0;
+  if (nbr <= 0) return;
+  const int64_t items = pairs * nbr;
   const int64_t threads = items * (d / 8);
   const unsigned grid = (unsigned)((threads + 255) / 256);
-  if (grid == 0) return;
   if (d == 128)
-    summaries_kernel<128><<<grid, 256, 0, st>>>(x, items, N, stride, bs, nb, out_f32, out_bf16);
+    summaries_kernel<128><<<grid, 256, 0, st>>>(x, items, N, stride, bs, j0, nbr, ostride,
+                                                out_f32, out_bf16);
   else
-    summaries_kernel<64><<<grid, 256, 0, st>>>(x, items, N, stride, bs, nb, out_f32, out_bf16);
+    summaries_kernel<64><<<grid, 256, 0, st>>>(x, items, N, stride, bs, j0, nbr, ostride,
+                                               out_f32, out_bf16);
+}
+
+// K/V rows of n_new tokens appended at position N of each (b, kv head)
+__global__ __launch_bounds__(256) void append_kernel(const uint4* __restrict__ src,
+                                                     uint4* __restrict__ dst, int64_t pieces,
+                                                     int n_new, int N, int stride, int ppr) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= pieces) return;
+  const int64_t row = i / ppr;  // [pair][n_new] rows of ppr 16-byte pieces
+  const int part = (int)(i % ppr);
+  const int64_t pair = row / n_new;
+  const int t = (int)(row % n_new);
+  dst[(pair * stride + N + t) * ppr + part] = src[i];
+}
+
+void launch_append(const uint16_t* src, uint16_t* dst, int64_t pairs, int n_new, int N,
+                   int stride, int d, hipStream_t st) {
+  const int ppr = d / 8;
+  const int64_t pieces = pairs * n_new * ppr;
+  if (pieces <= 0) return;
+  append_kernel<<<(unsigned)((pieces + 255) / 256), 256, 0, st>>>(
+      reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), pieces, n_new, N, stride,
+      ppr);
 }
 
 // ---------------------------------------------------------------------------
@@ -96,7 +123,7 @@ constexpr int SCORE_ROWS_PER_WG = 64;
 template <int D>
 __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict__ q,
                                                      const float* __restrict__ summ, int Hq,
-                                                     int Hkv, int nb, int c0, int c1,
+                                                     int Hkv, int nb, int sstride, int c0, int c1,
                                                      float* __restrict__ scores) {
   constexpr int PER = D / 16;  // floats per lane
   __shared__ float qbar[D];
@@ -116,7 +143,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
   for (int c = 0; c < PER; ++c) qv[c] = qbar[l16 * PER + c];
   const int r0 = c0 + blockIdx.x * SCORE_ROWS_PER_WG;
   const int r1 = min(c1, r0 + SCORE_ROWS_PER_WG);
-  const float* base = summ + (int64_t)pair * nb * D;
+  const float* base = summ + (int64_t)pair * sstride * D;
   for (int r = r0 + (tid >> 4); r < r1; r += 16) {
     const float4* row = reinterpret_cast<const float4*>(base + (int64_t)r * D + l16 * PER);
     float s = 0.f;
@@ -134,14 +161,14 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
 }
 
 void launch_scores(const uint16_t* q, const float* summ, int B, int Hq, int Hkv, int d, int nb,
-                   int c0, int c1, float* scores, hipStream_t st) {
+                   int sstride, int c0, int c1, float* scores, hipStream_t st) {
   const int n = c1 - c0;
   if (n <= 0) return;
   dim3 grid((n + SCORE_ROWS_PER_WG - 1) / SCORE_ROWS_PER_WG, B * Hkv);
   if (d == 128)
-    scores_kernel<128><<<grid, 256, 0, st>>>(q, summ, Hq, Hkv, nb, c0, c1, scores);
+    scores_kernel<128><<<grid, 256, 0, st>>>(q, summ, Hq, Hkv, nb, sstride, c0, c1, scores);
   else
-    scores_kernel<64><<<grid, 256, 0, st>>>(q, summ, Hq, Hkv, nb, c0, c1, scores);
+    scores_kernel<64><<<grid, 256, 0, st>>>(q, summ, Hq, Hkv, nb, sstride, c0, c1, scores);
 }
 
 // ---------------------------------------------------------------------------

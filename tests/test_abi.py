@@ -148,3 +148,22 @@ def test_product_path_has_no_oracle_import():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "liboracle" not in text and "oracle.h" not in text, f
+
+
+def test_loop_argument_checks_launch_nothing(L):
+    fake = ctypes.c_void_p(0x1000)
+    sh = bsa.make_shape(1, 4, 4, 128, 100, 128)
+    # append past the capacity; negative count; misaligned cache
+    assert L.append_kv(fake, fake, fake, fake, ctypes.byref(sh), 29, None) == -1
+    assert L.append_kv(fake, fake, fake, fake, ctypes.byref(sh), -1, None) == -1
+    assert L.append_kv(fake, fake, ctypes.c_void_p(0x1008), fake, ctypes.byref(sh), 1,
+                       None) == -1
+    # first token beyond seq_len; summary stride below the blocks in use
+    assert L.update_block_summaries(fake, ctypes.byref(sh), 64, 101, fake, None, None) == -1
+    narrow = bsa.make_shape(1, 4, 4, 128, 100, 128, 1)
+    assert L.update_block_summaries(fake, ctypes.byref(narrow), 64, 0, fake, None, None) == -1
+    cfg = bsa.select_cfg(top_k=1)
+    assert L.select_blocks(fake, fake, ctypes.byref(narrow), ctypes.byref(cfg), fake, None, fake,
+                           1 << 20, None) == -1
+    # nothing to update is a no-op
+    assert L.update_block_summaries(fake, ctypes.byref(sh), 64, 100, fake, None, None) == 0
