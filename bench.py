@@ -192,6 +192,47 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30, inputs=None):
     }
 
 
+def run_decode_loop(cfg, steps, warmup, t, flush_bytes=1 << 30):
+    """Per generated token: append K/V, refresh the summary of its block, select, attend.
+    The cache holds the workload's tokens; the loop starts `warmup + steps` tokens before
+    the end and appends the held tokens one by one (each step reads a cold cache)."""
+    import numpy as np
+    import torch
+
+    import long_context_block_summary_amd as bsa
+
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to(t["q"]), to(t["k"]), to(t["v"])
+    N, bs = cfg.seq_len, cfg.block_size
+    n0 = N - warmup - steps
+    S = -(-N // bs)
+    summ, _ = bsa.build_block_summaries(k, n0, bs, summary_stride=S)
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    ts = []
+    for i in range(warmup + steps):
+        n = n0 + i
+        k_new = k[:, :, n:n + 1].contiguous()
+        v_new = v[:, :, n:n + 1].contiguous()
+        flush.add_(1.0)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        bsa.decode_loop_step(q, k_new, v_new, k, v, summ, n, bs, cfg.n_sink, cfg.n_local,
+                             cfg.top_k, cfg.keep_ratio)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            ts.append(e0.elapsed_time(e1))
+    ms = sum(ts) / len(ts)
+    return {"workload": cfg.name, "ms_per_token": ms,
+            "queries_heads_per_s": cfg.batch * cfg.n_q_heads / (ms / 1e3), **pct(ts),
+            "timed": "decode_loop_step: append_kv + update_block_summaries + select_blocks + "
+                     "sparse_decode_attn per generated token, cold cache, "
+                     f"context {n0 + warmup}..{N}"}
+
+
 def pct(xs):
     """p10 / median / p90 of a list of times."""
     s = sorted(xs)
@@ -257,6 +298,9 @@ def run_prefill(cfg, steps, warmup, flush_bytes=1 << 30):
     ws = torch.empty(bsa.lib().bsa_prefill_workspace_size(ctypes.byref(shape), cfg.chunk_len,
                                                           ctypes.byref(pc)),
                      dtype=torch.uint8, device=dev)
+    pc_cat = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile,
+                             bsa.COMBINE_CONCAT)
+    sink = torch.linspace(-2.0, 3.0, cfg.n_q_heads, dtype=torch.float32, device=dev)
     sel = torch.empty((cfg.batch, -(-cfg.chunk_len // cfg.q_tile), cfg.n_kv_heads,
                        min(cfg.top_k_sparse, -(-cfg.prior_len // cfg.m_sparse))),
                       dtype=torch.int32, device=dev)
@@ -267,6 +311,8 @@ def run_prefill(cfg, steps, warmup, flush_bytes=1 << 30):
             q, k, streams[0], cfg.prior_len, cfg=pc, sel=sel, workspace=ws),
         "sparse_prefill_attn_selected": lambda: bsa.sparse_prefill_attn_selected(
             q, k, v, *streams[1:], sel, cfg.prior_len, cfg=pc, out=out),
+        "concat_sink": lambda: bsa.sparse_prefill_attn_selected(
+            q, k, v, *streams[1:], sel, cfg.prior_len, cfg=pc_cat, out=out, sink_logits=sink),
     }
     times = {}
     for name, fn in calls.items():
@@ -305,6 +351,9 @@ def run_prefill(cfg, steps, warmup, flush_bytes=1 << 30):
                                 "frac_of_bf16_mfma_peak": fl / (att / 1e3) / 1e12
                                 / MFMA_BF16_PEAK_TFLOPS,
                                 "branch_A_gather_GBps_over_call": gather_a / (att / 1e3) / 1e9},
+            "attention_concat_sink": {"call": "sparse_prefill_attn_selected, concatenated "
+                                              "softmax + per-head sink logits",
+                                      "ms": mean(times["concat_sink"])},
             "selection_R2": {"call": "select_prefill_entries", "ms": r2,
                              "stream_GBps": r2_bytes / (r2 / 1e3) / 1e9,
                              "fp32_gflop": r2_flops / 1e9},
@@ -422,6 +471,7 @@ def main():
                        "step_GBps": (s2 + a2) / (r2["step_ms"] / 1e3) / 1e9,
                        "select_us": r2["sel_ms"] * 1e3, "attn_us": r2["att_ms"] * 1e3}
         del r2
+    line["decode_loop"] = run_decode_loop(cfg, max(10, args.steps // 2), 3, r["inputs"])
     if args.prefill and args.prefill != "none":
         line["prefill"] = run_prefill(synth.CONFIGS[args.prefill], max(5, args.steps // 5), 2)
     if extra:
