@@ -130,13 +130,19 @@ int update_block_summaries(const void* x, const bsa_shape* shape, int32_t block_
                            void* hip_stream);
 
 /* append_kv -- writes n_new tokens' K and V rows into the caches at positions
- * [seq_len, seq_len + n_new) of every (b, kv head).
+ * [seq_len, seq_len + n_new) of every (b, kv head), and, when a summaries
+ * buffer is given, refreshes the summaries of the blocks those tokens land in
+ * (the growing partial block, or blocks they open) in the same launch, with
+ * results bit-identical to update_block_summaries / a rebuild.
  *   k_new, v_new      bf16 [B][Hkv][n_new][d]
  *   k_cache, v_cache  bf16 [B][Hkv][seq_stride][d]
+ *   summaries_f32/_bf16  [B][Hkv][S][d] or NULL (both NULL: no refresh, block_size unused);
+ *                     S = summary_stride, or ceil((seq_len + n_new) / block_size) when 0
  * Requires seq_len + n_new <= seq_stride; seq_len in `shape` is the count
  * before the append. */
 int append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-              const bsa_shape* shape, int32_t n_new, void* hip_stream);
+              const bsa_shape* shape, int32_t n_new, int32_t block_size, float* summaries_f32,
+              void* summaries_bf16, void* hip_stream);
 
 /* select_blocks -- per (batch, kv head): pooled query qbar = sum of the
  * group's query heads (fp32), block scores s_j = qbar . summary_j for the

@@ -68,7 +68,7 @@ def lib():
     L.bsa_status_string.argtypes, L.bsa_status_string.restype = [ctypes.c_int], ctypes.c_char_p
     L.build_block_summaries.argtypes = [vp, P(bsa_shape), i32, vp, vp, vp]
     L.update_block_summaries.argtypes = [vp, P(bsa_shape), i32, i32, vp, vp, vp]
-    L.append_kv.argtypes = [vp, vp, vp, vp, P(bsa_shape), i32, vp]
+    L.append_kv.argtypes = [vp, vp, vp, vp, P(bsa_shape), i32, i32, vp, vp, vp]
     L.select_blocks.argtypes = [vp, vp, P(bsa_shape), P(bsa_select_cfg), vp, vp, vp, sz, vp]
     L.sparse_decode_attn.argtypes = [vp, vp, vp, vp, i32, P(bsa_shape), i32, f32, vp, vp, vp, sz,
                                      vp]
@@ -174,8 +174,9 @@ def update_block_summaries(x, seq_len, block_size, first_token, out_f32=None, ou
     return out_f32, out_bf16
 
 
-def append_kv(k_new, v_new, k_cache, v_cache, seq_len):
-    """Write k_new, v_new bf16 [B][Hkv][n][d] into the caches at [seq_len, seq_len + n)."""
+def append_kv(k_new, v_new, k_cache, v_cache, seq_len, block_size=64, summaries=None):
+    """Write k_new, v_new bf16 [B][Hkv][n][d] into the caches at [seq_len, seq_len + n); with
+    `summaries` (fp32 [B][Hkv][S][d]) also refresh the summaries of the blocks they land in."""
     import torch
     for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
                     ("v_cache", v_cache)):
@@ -184,9 +185,14 @@ def append_kv(k_new, v_new, k_cache, v_cache, seq_len):
     if tuple(v_new.shape) != (B, H, n, d) or k_cache.shape[:2] != (B, H) or \
             tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[3] != d:
         raise ValueError("append_kv: shapes do not match")
-    shape = make_shape(B, H, H, d, seq_len, k_cache.shape[2])
+    S = 0
+    if summaries is not None:
+        _need(summaries, "summaries", torch.float32, 4)
+        S = summaries.shape[2]
+    shape = make_shape(B, H, H, d, seq_len, k_cache.shape[2], S)
     _check("append_kv", lib().append_kv(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
-                                        ctypes.byref(shape), n, _stream(k_new.device)))
+                                        ctypes.byref(shape), n, block_size, _ptr(summaries), None,
+                                        _stream(k_new.device)))
 
 
 def select_blocks(q, summaries, seq_len, block_size=64, n_sink=1, n_local=2, top_k=-1,
@@ -393,9 +399,8 @@ def decode_loop_step(q, k_new, v_new, k_cache, v_cache, summaries, seq_len, bloc
     lands in (or opens), select, attend over seq_len + n tokens.  summaries fp32
     [B][Hkv][S][d] with S >= ceil(capacity / block_size).  Returns (out, lse, idx)."""
     n = k_new.shape[2]
-    append_kv(k_new, v_new, k_cache, v_cache, seq_len)
+    append_kv(k_new, v_new, k_cache, v_cache, seq_len, block_size, summaries)
     N = seq_len + n
-    update_block_summaries(k_cache, N, block_size, seq_len, out_f32=summaries)
     idx, _ = select_blocks(q, summaries, N, block_size, n_sink, n_local, top_k, keep_ratio,
                            block_idx=block_idx, workspace=sel_workspace)
     out, lse = sparse_decode_attn(q, k_cache, v_cache, idx, N, block_size, scale, out=out,

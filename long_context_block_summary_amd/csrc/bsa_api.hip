@@ -127,19 +127,46 @@ int build_block_summaries(const void* x, const bsa_shape* shape, int32_t block_s
 }
 
 int append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-              const bsa_shape* shape, int32_t n_new, void* hip_stream) {
+              const bsa_shape* shape, int32_t n_new, int32_t block_size, float* summaries_f32,
+              void* summaries_bf16, void* hip_stream) {
   if (!k_new || !v_new || !k_cache || !v_cache || !shape_ok(shape) || n_new < 0)
     return BSA_INVALID_ARG;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
     return BSA_INVALID_ARG;
   if (!dim_supported(shape->head_dim)) return BSA_UNSUPPORTED;
   if ((int64_t)shape->seq_len + n_new > shape->seq_stride) return BSA_INVALID_ARG;
+  const bool refresh = summaries_f32 || summaries_bf16;
+  bsa_shape after = *shape;
+  after.seq_len = shape->seq_len + n_new;
+  int ss = 0;
+  if (refresh) {
+    if (block_size < 1 || (summaries_f32 && !aligned16(summaries_f32)) ||
+        (summaries_bf16 && !aligned16(summaries_bf16)))
+      return BSA_INVALID_ARG;
+    ss = summary_stride(&after, block_size);
+    if (ss < 0) return BSA_INVALID_ARG;
+  }
+  if (n_new == 0) return BSA_OK;
   const int64_t pairs = (int64_t)shape->batch * shape->n_kv_heads;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (refresh && block_size <= bsa::APPEND_MAX_BS) {
+    bsa::launch_append_update(static_cast<const uint16_t*>(k_new),
+                              static_cast<const uint16_t*>(v_new),
+                              static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                              pairs, n_new, shape->seq_len, shape->seq_stride, shape->head_dim,
+                              block_size, ss, summaries_f32,
+                              static_cast<uint16_t*>(summaries_bf16), st);
+    return launch_status();
+  }
   bsa::launch_append(static_cast<const uint16_t*>(k_new), static_cast<uint16_t*>(k_cache), pairs,
                      n_new, shape->seq_len, shape->seq_stride, shape->head_dim, st);
   bsa::launch_append(static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(v_cache), pairs,
                      n_new, shape->seq_len, shape->seq_stride, shape->head_dim, st);
+  if (refresh)
+    bsa::launch_summaries(static_cast<const uint16_t*>(k_cache), pairs, after.seq_len,
+                          shape->seq_stride, shape->head_dim, block_size,
+                          shape->seq_len / block_size, ss, summaries_f32,
+                          static_cast<uint16_t*>(summaries_bf16), st);
   return launch_status();
 }
 

@@ -15,6 +15,13 @@ void launch_summaries(const uint16_t* x, int64_t pairs, int N, int stride, int d
 void launch_append(const uint16_t* src, uint16_t* dst, int64_t pairs, int n_new, int N,
                    int stride, int d, hipStream_t st);
 
+// append n_new K/V rows at N and refresh the summaries of the blocks they land in
+constexpr int APPEND_MAX_BS = 128;  // block sizes the fused refresh stages in LDS
+void launch_append_update(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
+                          uint16_t* v_cache, int64_t pairs, int n_new, int N, int stride, int d,
+                          int bs, int ostride, float* out_f32, uint16_t* out_bf16,
+                          hipStream_t st);
+
 // candidate scores s[pair][j] = qbar . summary_j for j in [c0, c1); summaries
 // rows are sstride blocks apart, scores rows nb apart
 void launch_scores(const uint16_t* q, const float* summ, int B, int Hq, int Hkv, int d, int nb,

@@ -102,6 +102,71 @@ __global__ __launch_bounds__(256) void append_kernel(const uint4* __restrict__ s
   dst[(pair * stride + N + t) * ppr + part] = src[i];
 }
 
+// Append + summary refresh in one launch: one workgroup per (pair, block
+// holding new tokens).  It writes the block's new K and V rows, stages the
+// block's key rows in LDS (new rows from the source, older ones from the
+// cache), then one thread per column adds them in token order and divides by
+// the count: the same fp32 operations, in the same order, as summaries_kernel,
+// so the result is bit-identical to a rebuild.
+template <int D>
+__global__ __launch_bounds__(256) void append_update_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache, int n_new, int N, int stride,
+    int bs, int j_first, int n_blk, int ostride, float* __restrict__ out_f32,
+    uint16_t* __restrict__ out_bf16) {
+  constexpr int PPR = D / 8;  // 16-byte pieces per row
+  __shared__ uint16_t rows[APPEND_MAX_BS][D];
+  const int64_t pair = blockIdx.x / n_blk;
+  const int j = j_first + (int)(blockIdx.x % n_blk);
+  const int t0 = j * bs, t1 = min(t0 + bs, N + n_new);  // the block's tokens after the append
+  const int n = t1 - t0;
+  const uint4* ksrc = reinterpret_cast<const uint4*>(k_new) + pair * n_new * PPR;
+  const uint4* vsrc = reinterpret_cast<const uint4*>(v_new) + pair * n_new * PPR;
+  uint4* kdst = reinterpret_cast<uint4*>(k_cache) + pair * stride * PPR;
+  uint4* vdst = reinterpret_cast<uint4*>(v_cache) + pair * stride * PPR;
+  for (int i = threadIdx.x; i < n * PPR; i += 256) {
+    const int t = t0 + i / PPR, part = i % PPR;
+    uint4 kv;
+    if (t >= N) {  // a new token: write it and stage it from the source
+      const int64_t si = (int64_t)(t - N) * PPR + part;
+      kv = ksrc[si];
+      kdst[(int64_t)t * PPR + part] = kv;
+      vdst[(int64_t)t * PPR + part] = vsrc[si];
+    } else {
+      kv = kdst[(int64_t)t * PPR + part];
+    }
+    reinterpret_cast<uint4*>(rows[t - t0])[part] = kv;
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int c = threadIdx.x;
+    float acc = 0.f;
+    for (int t = 0; t < n; ++t) acc += __uint_as_float((uint32_t)rows[t][c] << 16);
+    acc = acc / (float)n;
+    const int64_t o = (pair * ostride + j) * D + c;
+    if (out_f32) out_f32[o] = acc;
+    if (out_bf16) out_bf16[o] = (uint16_t)bf16_rne(acc);
+  }
+}
+
+void launch_append_update(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
+                          uint16_t* v_cache, int64_t pairs, int n_new, int N, int stride, int d,
+                          int bs, int ostride, float* out_f32, uint16_t* out_bf16,
+                          hipStream_t st) {
+  if (n_new <= 0 || pairs <= 0) return;
+  const int j_first = N / bs, j_last = (N + n_new - 1) / bs;
+  const int n_blk = j_last - j_first + 1;
+  const unsigned grid = (unsigned)(pairs * n_blk);
+  if (d == 128)
+    append_update_kernel<128><<<grid, 256, 0, st>>>(k_new, v_new, k_cache, v_cache, n_new, N,
+                                                    stride, bs, j_first, n_blk, ostride, out_f32,
+                                                    out_bf16);
+  else
+    append_update_kernel<64><<<grid, 256, 0, st>>>(k_new, v_new, k_cache, v_cache, n_new, N,
+                                                   stride, bs, j_first, n_blk, ostride, out_f32,
+                                                   out_bf16);
+}
+
 void launch_append(const uint16_t* src, uint16_t* dst, int64_t pairs, int n_new, int N,
                    int stride, int d, hipStream_t st) {
   const int ppr = d / 8;

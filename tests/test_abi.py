@@ -154,10 +154,14 @@ def test_loop_argument_checks_launch_nothing(L):
     fake = ctypes.c_void_p(0x1000)
     sh = bsa.make_shape(1, 4, 4, 128, 100, 128)
     # append past the capacity; negative count; misaligned cache
-    assert L.append_kv(fake, fake, fake, fake, ctypes.byref(sh), 29, None) == -1
-    assert L.append_kv(fake, fake, fake, fake, ctypes.byref(sh), -1, None) == -1
-    assert L.append_kv(fake, fake, ctypes.c_void_p(0x1008), fake, ctypes.byref(sh), 1,
-                       None) == -1
+    assert L.append_kv(fake, fake, fake, fake, ctypes.byref(sh), 29, 64, None, None, None) == -1
+    assert L.append_kv(fake, fake, fake, fake, ctypes.byref(sh), -1, 64, None, None, None) == -1
+    assert L.append_kv(fake, fake, ctypes.c_void_p(0x1008), fake, ctypes.byref(sh), 1, 64, None,
+                       None, None) == -1
+    # refresh with a summary stride below the blocks after the append (100 + 29 -> 3 blocks)
+    two = bsa.make_shape(1, 4, 4, 128, 100, 256, 2)
+    assert L.append_kv(fake, fake, fake, fake, ctypes.byref(two), 29, 64, fake, None, None) == -1
+    assert L.append_kv(fake, fake, fake, fake, ctypes.byref(two), 28, 0, fake, None, None) == -1
     # first token beyond seq_len; summary stride below the blocks in use
     assert L.update_block_summaries(fake, ctypes.byref(sh), 64, 101, fake, None, None) == -1
     narrow = bsa.make_shape(1, 4, 4, 128, 100, 128, 1)

@@ -105,3 +105,41 @@ def test_loop_from_an_empty_block():
              top_k=1)
     run_loop("loop_one", 44, B=1, Hq=4, Hkv=2, d=128, n0=1, steps=66, capacity=64 * 3, top_k=2,
              check_every=5)
+
+
+@pytest.mark.parametrize("bs,n_new", [(64, 150), (128, 5), (256, 300), (16, 1)])
+def test_append_refresh_matches_rebuild(bs, n_new):
+    # several tokens per append (several blocks refreshed in one launch), other block sizes
+    # (256 takes the separate append + refresh path), and d = 64
+    import torch
+    B, H, d, cap, n0 = 2, 3, 64, 1200, 333
+    announce("append_refresh", "bs", bs, "n_new", n_new, "B", B, "H", H, "d", d, "start", n0)
+    rng = np.random.default_rng(bs + n_new)
+    kv = synth.bf16_round(rng.standard_normal((2, B, H, cap, d)).astype(np.float32))
+    k_all, v_all = to_dev(kv[0]), to_dev(kv[1])
+    k_cache, v_cache = torch.zeros_like(k_all), torch.zeros_like(v_all)
+    k_cache[:, :, :n0] = k_all[:, :, :n0]
+    v_cache[:, :, :n0] = v_all[:, :, :n0]
+    S = -(-cap // bs)
+    summ, _ = bsa.build_block_summaries(k_cache, n0, bs, summary_stride=S)
+    n = n0
+    while n + n_new <= cap:
+        bsa.append_kv(k_all[:, :, n:n + n_new].contiguous(), v_all[:, :, n:n + n_new].contiguous(),
+                      k_cache, v_cache, n, bs, summ)
+        n += n_new
+        if n > n0 + 4 * n_new:
+            break
+    torch.cuda.synchronize()
+    nb = -(-n // bs)
+    fresh, _ = bsa.build_block_summaries(k_cache, n, bs)
+    assert torch.equal(summ[:, :, :nb], fresh)
+    assert torch.equal(k_cache[:, :, :n], k_all[:, :, :n])
+    assert torch.equal(v_cache[:, :, :n], v_all[:, :, :n])
+    assert not k_cache[:, :, n:].any() and not v_cache[:, :, n:].any()
+    # appending without a summaries buffer only writes the rows
+    m = min(7, cap - n)
+    bsa.append_kv(k_all[:, :, n:n + m].contiguous(), v_all[:, :, n:n + m].contiguous(), k_cache,
+                  v_cache, n)
+    torch.cuda.synchronize()
+    assert torch.equal(k_cache[:, :, :n + m], k_all[:, :, :n + m])
+    assert torch.equal(summ[:, :, :nb], fresh)
