@@ -228,7 +228,7 @@ def run_decode_loop(cfg, steps, warmup, t, flush_bytes=1 << 30):
     ms = sum(ts) / len(ts)
     return {"workload": cfg.name, "ms_per_token": ms,
             "queries_heads_per_s": cfg.batch * cfg.n_q_heads / (ms / 1e3), **pct(ts),
-            "timed": "decode_loop_step: append_kv + update_block_summaries + select_blocks + "
+            "timed": "decode_loop_step: append_kv (with the summary refresh) + select_blocks + "
                      "sparse_decode_attn per generated token, cold cache, "
                      f"context {n0 + warmup}..{N}"}
 
@@ -404,6 +404,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", default="prefill256k",
                     help="prefill workload reported alongside ('none' to skip)")
+    ap.add_argument("--only", choices=["prefill"], default=None,
+                    help="run only the prefill measurement and print its object (for counter "
+                         "passes); the default runs the full bench")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -412,6 +415,10 @@ def main():
         sys.exit(2)
 
     from long_context_block_summary_amd import synth
+    if args.only == "prefill":
+        print(json.dumps(run_prefill(synth.CONFIGS[args.prefill], args.steps, args.warmup)),
+              flush=True)
+        return
     cfg = synth.CONFIGS[args.workload]
     r = run_gpu(cfg, args.steps, args.warmup)
     sel_b, att_b = decode_bytes(cfg, r["n_keep"])
