@@ -1,26 +1,30 @@
 // kernels_prefill.hip -- chunked prefill with compressed-sparse, compressed-dense
-// and sliding-window branches ("CSA + HCA 混合注意力机制" §4.1-4.4, §5.1-5.2).
+// and sliding-window branches ("CSA + HCA 混合注意力机制" §4.1-4.4, §5.1-5.4).
 //
 // A chunk of C new queries at positions P + i attends, per (tile of q_tile
 // consecutive queries, kv head):
 //   A  the top_k entries of the m_sparse mean-pooled stream, chosen with the
 //      tile's pooled query against the fp32 copy of the pooled keys;
 //   B  every entry of the m_dense mean-pooled stream;
-//   C  the raw tokens [p - window + 1, p] of the cache (causal window);
-// each with its own softmax; the three outputs are averaged.
+//   C  the raw tokens [p - window + 1, p] of the cache (causal window).
+// The branches are averaged (each with its own softmax) or joined in one
+// softmax over their concatenated logits (§4.3); an optional per-head sink
+// logit (§5.4) joins the softmax with a zero value.
 //
 // Kernels:
 //   prefill_qbar_kernel    pooled tile queries (fp32)
 //   prefill_scores_kernel  scores = qbar . pooled keys as an fp32 MFMA product
 //                          ([tiles x d] . [d x entries] per kv head)
 //   prefill_topk_kernel    exact top-k per (tile, kv head): MSB-first threshold
-//                          search with wave ballots, then an index-ordered
-//                          compaction (ascending output, lower index on ties)
-//   prefill_attn_kernel    workgroups of 4 waves x 32 (query, head) rows (a
-//                          256-row tile takes two workgroups); the branches' entries
-//                          stream through double-buffered LDS in chunks of 64:
-//                          S^T = K Q^T on bf16 MFMA, online softmax per row,
-//                          O += P V on fp16 MFMA with V transposed in LDS.
+//                          search (full passes, then the undecided keys in LDS),
+//                          then an index-ordered compaction (ascending output,
+//                          lower index on ties)
+//   prefill_attn_kernel    one workgroup of 16*NT*NW (query, head) rows per
+//                          (tile, kv head); the branches' entries stream through
+//                          double-buffered LDS in chunks of 64: S^T = K Q^T on
+//                          bf16 MFMA, online softmax per row, O += P V on fp16
+//                          MFMA with V transposed in LDS; branch ends fold O / l
+//                          into the output.
 #include <math.h>
 
 #include "bsa_device.h"
