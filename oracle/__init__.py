@@ -51,6 +51,11 @@ def load(path=LIB_PATH):
     lib.oracle_select_blocks.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f64,
                                          vp, vp]
     lib.oracle_select_blocks.restype = ctypes.c_int
+    lib.oracle_adaptive_bounds.argtypes = [i32, i32, i32, f64, f64, vp, vp]
+    lib.oracle_adaptive_bounds.restype = ctypes.c_int32
+    lib.oracle_select_blocks_adaptive.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                                  f64, f64, f64, vp, vp, vp]
+    lib.oracle_select_blocks_adaptive.restype = ctypes.c_int
     lib.oracle_sparse_decode_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                               i32, f64, vp, vp, vp]
     lib.oracle_sparse_decode_attn.restype = ctypes.c_int
@@ -119,6 +124,38 @@ def select_blocks(q, summaries, n_kv_heads, n_sink=1, n_local=2, top_k=-1, keep_
     if rc:
         raise ValueError(f"oracle_select_blocks rc={rc}")
     return idx, scores
+
+
+def adaptive_bounds(nb, n_sink, n_local, ratio_min, ratio_max, lib=None):
+    """(width of the kept lists, k_lo, k_hi) of an anchor-adaptive selection."""
+    lib = lib or load()
+    lo, hi = ctypes.c_int32(), ctypes.c_int32()
+    w = lib.oracle_adaptive_bounds(nb, n_sink, n_local, float(ratio_min), float(ratio_max),
+                                   ctypes.byref(lo), ctypes.byref(hi))
+    if w < 0:
+        raise ValueError("invalid adaptive selection bounds")
+    return w, lo.value, hi.value
+
+
+def select_blocks_adaptive(q, summaries, n_kv_heads, n_sink=1, n_local=2, ratio_min=0.1,
+                           ratio_max=0.2, margin=0.0, lib=None):
+    """Anchor-adaptive selection.  Returns (idx int32 [B][Hkv][width] ascending and padded
+    with -1, count int32 [B][Hkv] kept blocks, scores float64 [B][Hkv][nb] of every block)."""
+    lib = lib or load()
+    q = _u16(q)
+    summaries = np.ascontiguousarray(summaries, dtype=np.float64)
+    B, Hq, d = q.shape
+    nb = summaries.shape[2]
+    width, _, _ = adaptive_bounds(nb, n_sink, n_local, ratio_min, ratio_max, lib)
+    idx = np.empty((B, n_kv_heads, width), np.int32)
+    cnt = np.empty((B, n_kv_heads), np.int32)
+    scores = np.empty((B, n_kv_heads, nb), np.float64)
+    rc = lib.oracle_select_blocks_adaptive(_p(q), _p(summaries), B, Hq, n_kv_heads, d, nb,
+                                           n_sink, n_local, float(ratio_min), float(ratio_max),
+                                           float(margin), _p(idx), _p(cnt), _p(scores))
+    if rc:
+        raise ValueError(f"oracle_select_blocks_adaptive rc={rc}")
+    return idx, cnt, scores
 
 
 def sparse_decode_attn(q, k, v, idx, seq_len, block_size=64, scale=0.0, want_weights=False,

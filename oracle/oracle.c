@@ -217,6 +217,93 @@ int oracle_select_blocks(const uint16_t* q, const double* summaries, int32_t B,
   return bad ? -1 : 0;
 }
 
+/* ---- [KV] "锚点动态选择" / "动态重要性选择（Top-P Selection）": the sink and
+ * local blocks are anchors; the threshold is tau = a_max + margin * (a_max -
+ * a_min) over the anchors' scores; k = #(candidates scoring above tau),
+ * clamped so that the kept total lies in [ratio_min * nb, ratio_max * nb]
+ * (rounded as k_of does); the kept list is sink + top-k + local, ascending,
+ * padded with -1 to the widest list. */
+int32_t oracle_adaptive_bounds(int32_t nb, int32_t n_sink, int32_t n_local, double ratio_min,
+                               double ratio_max, int32_t* k_lo, int32_t* k_hi) {
+  if (nb < 0 || n_sink < 0 || n_local < 0 || !(ratio_min >= 0.0) || !(ratio_max >= ratio_min))
+    return -1;
+  int32_t c0, c1, fixed;
+  ranges(nb, n_sink, n_local, &c0, &c1, &fixed);
+  int32_t n_cand = c1 - c0;
+  int64_t lo = (int64_t)floor(ratio_min * (double)nb + 0.5) - fixed;
+  int64_t hi = (int64_t)floor(ratio_max * (double)nb + 0.5) - fixed;
+  if (lo < 0) lo = 0;
+  if (lo > n_cand) lo = n_cand;
+  if (hi < lo) hi = lo;
+  if (hi > n_cand) hi = n_cand;
+  *k_lo = (int32_t)lo;
+  *k_hi = (int32_t)hi;
+  return fixed + (int32_t)hi; /* the widest list */
+}
+
+int oracle_select_blocks_adaptive(const uint16_t* q, const double* summaries, int32_t B,
+                                  int32_t Hq, int32_t Hkv, int32_t d, int32_t nb, int32_t n_sink,
+                                  int32_t n_local, double ratio_min, double ratio_max,
+                                  double margin, int32_t* idx_out, int32_t* count_out,
+                                  double* scores_out) {
+  int32_t k_lo, k_hi;
+  int32_t width = oracle_adaptive_bounds(nb, n_sink, n_local, ratio_min, ratio_max, &k_lo, &k_hi);
+  if (!q || !summaries || !idx_out || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || d <= 0 ||
+      width < 0)
+    return -1;
+  int32_t g = Hq / Hkv;
+  int32_t c0, c1, fixed;
+  ranges(nb, n_sink, n_local, &c0, &c1, &fixed);
+  int64_t npair = (int64_t)B * Hkv;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t p = 0; p < npair; ++p) {
+    int64_t b = p / Hkv, kvh = p % Hkv;
+    double* qbar = (double*)calloc((size_t)d, sizeof(double));
+    double* sc = (double*)malloc(sizeof(double) * ((size_t)nb + 1));
+    scored* cand = (scored*)malloc(sizeof(scored) * (size_t)(c1 - c0 + 1));
+    unsigned char* keep = (unsigned char*)calloc((size_t)nb + 1, 1);
+    for (int32_t h = (int32_t)kvh * g; h < (int32_t)kvh * g + g; ++h)
+      for (int32_t c = 0; c < d; ++c) qbar[c] += bf(q[(b * Hq + h) * (int64_t)d + c]);
+    const double* sm = summaries + p * (int64_t)nb * d;
+    /* every block is scored: the candidates and the anchors */
+    for (int32_t j = 0; j < nb; ++j) {
+      double s = 0.0;
+      for (int32_t c = 0; c < d; ++c) s += qbar[c] * sm[(int64_t)j * d + c];
+      sc[j] = s;
+    }
+    double a_max = -INFINITY, a_min = INFINITY;
+    for (int32_t j = 0; j < nb; ++j)
+      if (j < c0 || j >= c1) {
+        if (sc[j] > a_max) a_max = sc[j];
+        if (sc[j] < a_min) a_min = sc[j];
+      }
+    /* no anchor block: every candidate counts */
+    double tau = fixed > 0 ? a_max + margin * (a_max - a_min) : -INFINITY;
+    int32_t above = 0;
+    for (int32_t j = c0; j < c1; ++j) {
+      cand[j - c0].s = sc[j];
+      cand[j - c0].j = j;
+      if (sc[j] > tau) ++above;
+    }
+    int32_t k = above < k_lo ? k_lo : (above > k_hi ? k_hi : above);
+    top_k_mark(cand, c1 - c0, k, keep);
+    for (int32_t j = 0; j < nb; ++j)
+      if (j < c0 || j >= c1) keep[j] = 1;
+    int32_t w = 0;
+    for (int32_t j = 0; j < nb; ++j)
+      if (keep[j]) idx_out[p * width + w++] = j;
+    for (; w < width; ++w) idx_out[p * width + w] = -1;
+    if (count_out) count_out[p] = fixed + k;
+    if (scores_out)
+      for (int32_t j = 0; j < nb; ++j) scores_out[p * (int64_t)nb + j] = sc[j];
+    free(qbar);
+    free(sc);
+    free(cand);
+    free(keep);
+  }
+  return 0;
+}
+
 /* ---- [CSA] 2.1 / 4.4: exact softmax(q K^T / sqrt(d)) V over a token list.
  * Writes o[d] and returns lse; w (optional) receives the weights. */
 static double attend(const uint16_t* qh, const double* qd, int32_t d, int32_t n,
@@ -262,9 +349,22 @@ int oracle_sparse_decode_attn(const uint16_t* q, const uint16_t* k, const uint16
     return -1;
   int32_t g = Hq / Hkv;
   int32_t nb = oracle_num_blocks(N, bs);
-  for (int64_t i = 0; i < (int64_t)B * Hkv * n_keep; ++i) {
-    if (idx[i] < 0 || idx[i] >= nb) return -1;
-    if (i % n_keep && idx[i] <= idx[i - 1]) return -1; /* ascending, no repeats */
+  /* each list: ascending block indices without repeats, optionally ended by
+   * a run of -1 (the absent entries of an adaptive selection), >= 1 block */
+  for (int64_t p = 0; p < (int64_t)B * Hkv && n_keep > 0; ++p) {
+    const int32_t* li = idx + p * n_keep;
+    int32_t used = n_keep;
+    for (int32_t i = 0; i < n_keep; ++i) {
+      if (li[i] == -1) {
+        used = i;
+        break;
+      }
+      if (li[i] < 0 || li[i] >= nb) return -1;
+      if (i && li[i] <= li[i - 1]) return -1;
+    }
+    if (used == 0) return -1;
+    for (int32_t i = used; i < n_keep; ++i)
+      if (li[i] != -1) return -1;
   }
   if (scale == 0.0) scale = 1.0 / sqrt((double)d);
   int64_t nqh = (int64_t)B * Hq;
@@ -278,7 +378,7 @@ int oracle_sparse_decode_attn(const uint16_t* q, const uint16_t* k, const uint16
     double* wt = (double*)malloc(sizeof(double) * ((size_t)n_keep * bs + 1));
     int32_t n = 0;
     int64_t base = (b * Hkv + kvh) * (int64_t)stride * d;
-    for (int32_t i = 0; i < n_keep; ++i) {
+    for (int32_t i = 0; i < n_keep && list[i] >= 0; ++i) {
       int32_t t0 = list[i] * bs;
       int32_t t1 = t0 + bs < N ? t0 + bs : N;
       for (int32_t t = t0; t < t1; ++t) {

@@ -44,8 +44,25 @@ int oracle_select_blocks(const uint16_t* q, const double* summaries, int32_t B,
                          int32_t n_local, int32_t top_k, double keep_ratio,
                          int32_t* idx_out, double* scores_out);
 
+/* anchor-adaptive selection: tau = a_max + margin * (a_max - a_min) over the
+ * scores of the sink and local (anchor) blocks; k = #(candidates scoring above
+ * tau) clamped to [k_lo, k_hi], where the kept totals ratio_min * nb and
+ * ratio_max * nb are rounded as for keep_ratio; kept = sink + top-k + local,
+ * ascending, padded with -1 to the widest list (returned by
+ * oracle_adaptive_bounds, which also gives k_lo and k_hi; -1 on bad input).
+ * idx_out [B][Hkv][width]; count_out [B][Hkv] or NULL; scores_out [B][Hkv][nb]
+ * (every block) or NULL.  Without anchor blocks every candidate counts. */
+int32_t oracle_adaptive_bounds(int32_t nb, int32_t n_sink, int32_t n_local, double ratio_min,
+                               double ratio_max, int32_t* k_lo, int32_t* k_hi);
+int oracle_select_blocks_adaptive(const uint16_t* q, const double* summaries, int32_t B,
+                                  int32_t Hq, int32_t Hkv, int32_t d, int32_t nb, int32_t n_sink,
+                                  int32_t n_local, double ratio_min, double ratio_max,
+                                  double margin, int32_t* idx_out, int32_t* count_out,
+                                  double* scores_out);
+
 /* exact softmax attention over the tokens of the listed blocks.
- * idx [B][Hkv][n_keep]; out [B][Hq][d]; lse [B][Hq] or NULL;
+ * idx [B][Hkv][n_keep] (a list may end in a run of -1: absent entries);
+ * out [B][Hq][d]; lse [B][Hq] or NULL;
  * weights [B][Hq][n_keep*bs] or NULL (softmax weight of each listed token in
  * list order; slots past the end of a partial block are 0).
  * scale 0 selects 1/sqrt(d). */

@@ -42,6 +42,16 @@ MUTANTS = [
      ": t < src[1] ? (double)k128[rka[t] + c]"),
     ("sink logit sign", "double den = has_sink ? exp(zs - zmax) : 0.0;",
      "double den = has_sink ? exp(zmax - zs) : 0.0;"),
+    ("adaptive threshold from the lowest anchor",
+     "double tau = fixed > 0 ? a_max + margin * (a_max - a_min) : -INFINITY;",
+     "double tau = fixed > 0 ? a_min + margin * (a_max - a_min) : -INFINITY;"),
+    ("adaptive counts scores equal to the threshold", "if (sc[j] > tau) ++above;",
+     "if (sc[j] >= tau) ++above;"),
+    ("adaptive anchors skip the local blocks", "      if (j < c0 || j >= c1) {\n        if (sc[j] > a_max)",
+     "      if (j < c0) {\n        if (sc[j] > a_max)"),
+    ("adaptive k ignores the lower bound",
+     "int32_t k = above < k_lo ? k_lo : (above > k_hi ? k_hi : above);",
+     "int32_t k = above > k_hi ? k_hi : above;"),
     ("branch sink uses the wrong lse", "double keep = has_sink ? 1.0 / (1.0 + exp(zs - l[br])) : 1.0;",
      "double keep = has_sink ? 1.0 / (1.0 + exp(zs - l[0])) : 1.0;"),
     ("bf16 ties away from zero", "double ri = rint(s);", "double ri = floor(s + 0.5);"),

@@ -561,3 +561,84 @@ def test_prefill_combine_rejects_unknown_mode(orc):
     q, k, v = prefill_case(27)
     with pytest.raises(ValueError):
         orc.sparse_prefill_attn(q, k, v, 256, top_k=8, combine=2)
+
+
+# ------------------------------------------------- anchor-adaptive selection
+# hotdry.top post: the sink and local blocks are anchors; blocks whose importance
+# exceeds the anchor point are kept, within a 10-20 % keep range.
+
+def _adaptive_case(cand_scores, anchor_scores, d=4):
+    """Summaries whose column 0 carries the scores (q = e_0, one head): block 0 and the
+    last two blocks are the anchors."""
+    nb = len(cand_scores) + 3
+    summ = np.zeros((1, 1, nb, d))
+    summ[0, 0, 0, 0] = anchor_scores[0]
+    summ[0, 0, 1:nb - 2, 0] = cand_scores
+    summ[0, 0, nb - 2:, 0] = anchor_scores[1:]
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = 1.0
+    return bf(q), summ, nb
+
+
+def test_adaptive_bounds_reproduce_the_keep_range(orc):
+    # 10 % and 20 % of 2048 blocks with sink 1 + local 2: k in [202, 407]
+    assert orc.adaptive_bounds(2048, 1, 2, 0.1, 0.2) == (410, 202, 407)
+    assert orc.adaptive_bounds(512, 1, 2, 0.15, 0.15) == (77, 74, 74)
+    # tiny contexts keep everything; an inverted range is rejected
+    assert orc.adaptive_bounds(3, 1, 2, 0.1, 0.2) == (3, 0, 0)
+    with pytest.raises(ValueError):
+        orc.adaptive_bounds(100, 1, 2, 0.3, 0.2)
+
+
+def test_adaptive_count_above_the_anchor_threshold(orc):
+    rng = np.random.default_rng(31)
+    cand = rng.permutation(np.arange(37, dtype=np.float64)) * 0.25  # 0 .. 9, distinct
+    anchors = [2.0, 1.0, 3.0]                                       # a_max 3, a_min 1
+    q, summ, nb = _adaptive_case(cand, anchors)
+    width, k_lo, k_hi = orc.adaptive_bounds(nb, 1, 2, 0.1, 0.5)
+    assert (k_lo, k_hi) == (1, 17)
+    for margin, tau in ((0.0, 3.0), (1.0, 5.0), (0.5, 4.0), (-0.25, 2.5), (3.0, 9.0)):
+        idx, cnt, sc = orc.select_blocks_adaptive(q, summ, 1, 1, 2, 0.1, 0.5, margin)
+        above = int((cand > tau).sum())              # strictly above: a score equal to tau is out
+        k = min(max(above, k_lo), k_hi)
+        assert cnt[0, 0] == 3 + k
+        expect = sorted([0, nb - 2, nb - 1] + [1 + j for j in np.argsort(-cand, kind="stable")[:k]])
+        assert idx[0, 0, :3 + k].tolist() == expect
+        assert (idx[0, 0, 3 + k:] == -1).all() and idx.shape[2] == width
+        np.testing.assert_allclose(sc[0, 0, 1:nb - 2], cand, atol=0)
+
+
+def test_adaptive_all_equal_scores_keep_the_minimum(orc):
+    q, summ, nb = _adaptive_case(np.full(60, 1.5), [1.5, 1.5, 1.5])
+    _, k_lo, _ = orc.adaptive_bounds(nb, 1, 2, 0.1, 0.2)
+    idx, cnt, _ = orc.select_blocks_adaptive(q, summ, 1, 1, 2, 0.1, 0.2, 0.0)
+    assert cnt[0, 0] == 3 + k_lo
+    # equal scores: the lowest candidate indices
+    assert idx[0, 0, :3 + k_lo].tolist() == [0] + list(range(1, 1 + k_lo)) + [nb - 2, nb - 1]
+
+
+def test_adaptive_anchors_include_the_local_blocks(orc):
+    # raising a local block's score raises the threshold: fewer blocks kept, never more
+    cand = np.linspace(0.0, 10.0, 50)
+    prev = None
+    for local in (0.0, 4.0, 7.0, 9.5):
+        q, summ, nb = _adaptive_case(cand, [1.0, local, 0.5])
+        _, cnt, _ = orc.select_blocks_adaptive(q, summ, 1, 1, 2, 0.0, 1.0, 0.0)
+        assert cnt[0, 0] == 3 + int((cand > max(1.0, local)).sum())
+        assert prev is None or cnt[0, 0] <= prev
+        prev = cnt[0, 0]
+
+
+def test_padded_lists_attend_like_truncated_ones(orc):
+    rng = np.random.default_rng(33)
+    q = bf(rng.standard_normal((1, 2, 16)).astype(np.float32))
+    k = bf(rng.standard_normal((1, 2, 64 * 9, 16)).astype(np.float32))
+    v = bf(rng.standard_normal((1, 2, 64 * 9, 16)).astype(np.float32))
+    full = np.array([[[0, 3, 4, 8, -1, -1], [1, 2, 5, 6, 7, 8]]], np.int32)
+    o_pad, l_pad, _ = orc.sparse_decode_attn(q, k, v, full, 64 * 9 - 5)
+    o_a, l_a, _ = orc.sparse_decode_attn(q[:, :1], k[:, :1], v[:, :1], full[:, :1, :4], 64 * 9 - 5)
+    np.testing.assert_array_equal(o_pad[:, :1], o_a)
+    np.testing.assert_array_equal(l_pad[:, :1], l_a)
+    for bad in ([[[-1, -1]]], [[[2, -1, 3]]], [[[0, -1, -1, 1]]]):
+        with pytest.raises(ValueError):
+            orc.sparse_decode_attn(q[:, :1], k[:, :1], v[:, :1], np.array(bad, np.int32), 128)
