@@ -64,7 +64,11 @@ typedef struct {
   int32_t n_sink_blocks;   /* always-kept leading blocks (1 on the page's table) */
   int32_t n_local_blocks;  /* always-kept trailing blocks (2 on the page's table) */
   int32_t top_k;           /* middle blocks kept by score; < 0: derive from keep_ratio */
-  float keep_ratio;        /* used when top_k < 0: total kept = floor(r * nb + 0.5) */
+  float keep_ratio;        /* used when top_k < 0: total kept = floor(r * nb + 0.5);
+                              adaptive: the smallest kept fraction */
+  int32_t adaptive;        /* 1: anchor-adaptive k per (b, kv head), see select_blocks */
+  float keep_ratio_max;    /* adaptive: the largest kept fraction */
+  float anchor_margin;     /* adaptive: tau = a_max + anchor_margin * (a_max - a_min) */
 } bsa_select_cfg;
 
 typedef struct {
@@ -88,6 +92,7 @@ int32_t bsa_num_blocks(int32_t n, int32_t m);
  * the candidates are the blocks that are neither sink nor local and
  * k = top_k (or floor(keep_ratio*nb + 0.5) - n_sink - n_local when top_k < 0),
  * clamped to [0, #candidates].  With nb <= sink + local every block is kept.
+ * Adaptive selection: the widest list, sink + local + k_hi (see select_blocks).
  * Returns -1 on an invalid cfg. */
 int32_t bsa_num_kept(int32_t nb, const bsa_select_cfg* cfg);
 
@@ -154,8 +159,16 @@ int append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache
  *   summaries  fp32 [B][Hkv][S][d] from build_block_summaries (S = summary_stride, or
  *              nb = ceil(seq_len / block_size) when that is 0)
  *   block_idx  int32 [B][Hkv][n_keep] output, n_keep = bsa_num_kept(nb, cfg)
- *   scores_out fp32 [B][Hkv][nb] or NULL: candidate scores (other entries are not written)
+ *   scores_out fp32 [B][Hkv][nb] or NULL: candidate scores (other entries are not written;
+ *              adaptive: every block's score)
  *   workspace  bsa_select_workspace_size() bytes of device memory (may be NULL if 0)
+ * Anchor-adaptive mode (cfg->adaptive = 1; hotdry.top post, the anchor-point
+ * Top-P selection and 锚点动态选择): the sink and local blocks are anchors;
+ * tau = a_max + anchor_margin * (a_max - a_min) over their scores (fp32); k per
+ * (b, kv head) = #(candidates scoring above tau), clamped so the kept total lies
+ * in [keep_ratio * nb, keep_ratio_max * nb] (each rounded as floor(x + 0.5));
+ * the list holds sink + top-k + local ascending and is padded with -1 to
+ * n_keep.  sparse_decode_attn accepts such padded lists.
  * Requires seq_len >= 1. */
 int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
                   const bsa_select_cfg* cfg, int32_t* block_idx, float* scores_out,
@@ -167,8 +180,10 @@ int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
  * new token's K/V were appended, so no mask is applied).
  *   q          bf16 [B][Hq][d]
  *   k, v       bf16 [B][Hkv][seq_stride][d]
- *   block_idx  int32 [B][Hkv][n_keep], strictly ascending block indices < nb
- *              (not checked on the device: out-of-range entries are the caller's error)
+ *   block_idx  int32 [B][Hkv][n_keep], strictly ascending block indices < nb, each
+ *              list optionally ended by a run of -1 (absent entries, as written by an
+ *              adaptive select_blocks) and holding at least one block (not checked
+ *              on the device: other out-of-range entries are the caller's error)
  *   scale      0 selects 1/sqrt(d)
  *   out        fp32 [B][Hq][d]
  *   lse        fp32 [B][Hq] natural-log log-sum-exp of the scaled logits, or NULL

@@ -34,7 +34,8 @@ class bsa_shape(ctypes.Structure):
 class bsa_select_cfg(ctypes.Structure):
     _fields_ = [("block_size", ctypes.c_int32), ("n_sink_blocks", ctypes.c_int32),
                 ("n_local_blocks", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("keep_ratio", ctypes.c_float)]
+                ("keep_ratio", ctypes.c_float), ("adaptive", ctypes.c_int32),
+                ("keep_ratio_max", ctypes.c_float), ("anchor_margin", ctypes.c_float)]
 
 
 class bsa_prefill_cfg(ctypes.Structure):
@@ -117,8 +118,12 @@ def make_shape(batch, n_q_heads, n_kv_heads, head_dim, seq_len, seq_stride, summ
     return bsa_shape(batch, n_q_heads, n_kv_heads, head_dim, seq_len, seq_stride, summary_stride)
 
 
-def select_cfg(block_size=64, n_sink=1, n_local=2, top_k=-1, keep_ratio=0.0):
-    return bsa_select_cfg(block_size, n_sink, n_local, top_k, keep_ratio)
+def select_cfg(block_size=64, n_sink=1, n_local=2, top_k=-1, keep_ratio=0.0, adaptive=False,
+               keep_ratio_max=0.0, anchor_margin=0.0):
+    """Selection parameters; adaptive=True keeps between keep_ratio and keep_ratio_max of the
+    blocks per (b, kv head), set by the anchors' scores (lists padded with -1)."""
+    return bsa_select_cfg(block_size, n_sink, n_local, top_k, keep_ratio, int(adaptive),
+                          keep_ratio_max, anchor_margin)
 
 
 COMBINE_AVERAGE, COMBINE_CONCAT = 0, 1
@@ -196,7 +201,8 @@ def append_kv(k_new, v_new, k_cache, v_cache, seq_len, block_size=64, summaries=
 
 
 def select_blocks(q, summaries, seq_len, block_size=64, n_sink=1, n_local=2, top_k=-1,
-                  keep_ratio=0.0, want_scores=False, block_idx=None, workspace=None):
+                  keep_ratio=0.0, want_scores=False, block_idx=None, workspace=None,
+                  adaptive=False, keep_ratio_max=0.0, anchor_margin=0.0):
     """q bf16 [B][Hq][d], summaries fp32 [B][Hkv][nb][d] -> (idx int32 [B][Hkv][n_keep], scores)."""
     import torch
     _need(q, "q", torch.bfloat16, 3)
@@ -206,7 +212,8 @@ def select_blocks(q, summaries, seq_len, block_size=64, n_sink=1, n_local=2, top
     nb = num_blocks(seq_len, block_size)
     if S < nb:
         raise ValueError(f"summaries hold {S} blocks, {nb} are in use")
-    cfg = select_cfg(block_size, n_sink, n_local, top_k, keep_ratio)
+    cfg = select_cfg(block_size, n_sink, n_local, top_k, keep_ratio, adaptive, keep_ratio_max,
+                     anchor_margin)
     n_keep = num_kept(nb, cfg)
     if n_keep < 0:
         raise ValueError("invalid selection config")
@@ -385,9 +392,11 @@ def sparse_prefill_attn_selected(q, k, v, k_cmp_sparse_bf16, v_cmp_sparse_bf16, 
 
 
 def decode_step(q, k, v, summaries, seq_len, block_size=64, n_sink=1, n_local=2, top_k=-1,
-                keep_ratio=0.0, scale=0.0):
-    """select_blocks then sparse_decode_attn (the per-token hot path)."""
-    idx, _ = select_blocks(q, summaries, seq_len, block_size, n_sink, n_local, top_k, keep_ratio)
+                keep_ratio=0.0, scale=0.0, **adaptive):
+    """select_blocks then sparse_decode_attn (the per-token hot path); `adaptive` takes the
+    select_blocks keywords adaptive, keep_ratio_max and anchor_margin."""
+    idx, _ = select_blocks(q, summaries, seq_len, block_size, n_sink, n_local, top_k, keep_ratio,
+                           **adaptive)
     out, lse = sparse_decode_attn(q, k, v, idx, seq_len, block_size, scale)
     return out, lse, idx
 

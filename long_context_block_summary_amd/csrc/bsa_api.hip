@@ -2,6 +2,7 @@
 // Every argument check runs before any launch; kernels are only enqueued on
 // the caller's stream.
 #include <math.h>
+#include <cmath>
 #include <stdint.h>
 
 #include "../../include/bsa.h"
@@ -43,8 +44,32 @@ int middle_k(int nb, const bsa_select_cfg* cfg, int n_cand) {
 }
 
 bool select_cfg_ok(const bsa_select_cfg* c) {
-  return c && c->block_size >= 1 && c->n_sink_blocks >= 0 && c->n_local_blocks >= 0 &&
-         (c->top_k >= 0 || (c->keep_ratio >= 0.f && c->keep_ratio <= 1.f));
+  if (!c || c->block_size < 1 || c->n_sink_blocks < 0 || c->n_local_blocks < 0) return false;
+  if (c->adaptive) {
+    return c->adaptive == 1 && c->keep_ratio >= 0.f && c->keep_ratio <= c->keep_ratio_max &&
+           c->keep_ratio_max <= 1.f && std::isfinite(c->anchor_margin);
+  }
+  return c->top_k >= 0 || (c->keep_ratio >= 0.f && c->keep_ratio <= 1.f);
+}
+
+// adaptive selection: the middle-block count lies in [k_lo, k_hi] (the kept
+// totals keep_ratio * nb and keep_ratio_max * nb, rounded as middle_k rounds)
+void adaptive_bounds(int nb, const bsa_select_cfg* cfg, int fixed, int n_cand, int* k_lo,
+                     int* k_hi) {
+  int64_t lo = (int64_t)floor((double)cfg->keep_ratio * (double)nb + 0.5) - fixed;
+  int64_t hi = (int64_t)floor((double)cfg->keep_ratio_max * (double)nb + 0.5) - fixed;
+  lo = lo < 0 ? 0 : (lo > n_cand ? n_cand : lo);
+  hi = hi < lo ? lo : (hi > n_cand ? n_cand : hi);
+  *k_lo = (int)lo;
+  *k_hi = (int)hi;
+}
+
+// middle blocks per list: k (fixed mode) or k_hi (adaptive: the widest list)
+int list_k(int nb, const bsa_select_cfg* cfg, int c0, int c1, int fixed) {
+  if (!cfg->adaptive) return middle_k(nb, cfg, c1 - c0);
+  int lo, hi;
+  adaptive_bounds(nb, cfg, fixed, c1 - c0, &lo, &hi);
+  return hi;
 }
 
 // blocks between consecutive (b, kv head) rows of a summaries buffer, or -1
@@ -72,7 +97,7 @@ int32_t bsa_num_kept(int32_t nb, const bsa_select_cfg* cfg) {
   if (nb < 0 || !select_cfg_ok(cfg)) return -1;
   int c0, c1, fixed;
   kept_ranges(nb, cfg->n_sink_blocks, cfg->n_local_blocks, &c0, &c1, &fixed);
-  return fixed + middle_k(nb, cfg, c1 - c0);
+  return fixed + list_k(nb, cfg, c0, c1, fixed);
 }
 
 size_t bsa_select_workspace_size(const bsa_shape* shape, const bsa_select_cfg* cfg) {
@@ -184,19 +209,23 @@ int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
   if (ss < 0) return BSA_INVALID_ARG;
   int c0, c1, fixed;
   kept_ranges(nb, cfg->n_sink_blocks, cfg->n_local_blocks, &c0, &c1, &fixed);
-  const int k = middle_k(nb, cfg, c1 - c0);
+  const int k = list_k(nb, cfg, c0, c1, fixed);  // adaptive: the widest list
   const int n_keep = fixed + k;
+  int k_lo = k, k_hi = k;
+  if (cfg->adaptive) adaptive_bounds(nb, cfg, fixed, c1 - c0, &k_lo, &k_hi);
   float* scores = scores_out;
   if (!scores) {
     if (ws_bytes < bsa_select_workspace_size(shape, cfg)) return BSA_WORKSPACE_TOO_SMALL;
-    if (c1 > c0 && !workspace) return BSA_INVALID_ARG;
+    if ((c1 > c0 || cfg->adaptive) && !workspace) return BSA_INVALID_ARG;
     scores = static_cast<float*>(workspace);
   }
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  // the adaptive threshold needs the anchors' scores too: score every block
+  const int s0 = cfg->adaptive ? 0 : c0, s1 = cfg->adaptive ? nb : c1;
   bsa::launch_scores(static_cast<const uint16_t*>(q), summaries, shape->batch, shape->n_q_heads,
-                     shape->n_kv_heads, shape->head_dim, nb, ss, c0, c1, scores, st);
+                     shape->n_kv_heads, shape->head_dim, nb, ss, s0, s1, scores, st);
   bsa::launch_topk(scores, (int64_t)shape->batch * shape->n_kv_heads, nb, c0, c1, k, n_keep,
-                   block_idx, st);
+                   block_idx, st, cfg->adaptive != 0, k_lo, k_hi, cfg->anchor_margin);
   return launch_status();
 }
 

@@ -27,9 +27,12 @@ void launch_append_update(const uint16_t* k_new, const uint16_t* v_new, uint16_t
 void launch_scores(const uint16_t* q, const float* summ, int B, int Hq, int Hkv, int d, int nb,
                    int sstride, int c0, int c1, float* scores, hipStream_t st);
 
-// per pair: sink [0,c0) + top-k of scores[c0,c1) + local [c1,nb), ascending
+// per pair: sink [0,c0) + top-k of scores[c0,c1) + local [c1,nb), ascending.
+// adaptive: k per pair from the anchors' scores, clamped to [k_lo, k_hi], the
+// list padded with -1 to n_keep
 void launch_topk(const float* scores, int64_t pairs, int nb, int c0, int c1, int k, int n_keep,
-                 int32_t* idx_out, hipStream_t st);
+                 int32_t* idx_out, hipStream_t st, bool adaptive = false, int k_lo = 0,
+                 int k_hi = 0, float margin = 0.f);
 
 struct DecodePlan {
   int g;           // query heads per kv head

@@ -80,8 +80,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
   }
 
   const int blk0 = split * bps;
-  const int nblk = min(n_keep, blk0 + bps) - blk0;
+  int nblk = min(n_keep, blk0 + bps) - blk0;
   const int32_t* list = idx + (int64_t)pair * n_keep + blk0;
+  // a list may end in -1 (absent entries of an adaptive selection): this
+  // split's blocks are its valid prefix (one scalar load when the run is full)
+  if (nblk > 0 && list[nblk - 1] < 0) {
+    int nv = 0;
+    while (nv < nblk && list[nv] >= 0) ++nv;
+    nblk = nv;
+  }
   const char* kb = reinterpret_cast<const char*>(k + (int64_t)pair * stride * D);
   const char* vb = reinterpret_cast<const char*>(v + (int64_t)pair * stride * D);
   const int tile0 = 16 * wave;  // this wave's 16 tokens of every block

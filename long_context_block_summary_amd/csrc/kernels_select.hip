@@ -267,18 +267,58 @@ __device__ __forceinline__ int block_prefix(bool flag, int* wcnt, int* total) {
   return off + pre;
 }
 
+// ad.on: anchor-adaptive k (the hotdry.top post's anchor selection): the
+// sink and local blocks are anchors, tau = a_max + margin * (a_max - a_min)
+// over their scores (fp32), k = #(candidates > tau) clamped to [k_lo, k_hi];
+// the list is padded with -1 up to n_keep (the widest list).
+struct AdaptiveSel {
+  int on, k_lo, k_hi;
+  float margin;
+};
+
 __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restrict__ scores,
                                                             int nb, int c0, int c1, int k,
-                                                            int n_keep,
+                                                            int n_keep, AdaptiveSel ad,
                                                             int32_t* __restrict__ idx_out) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh_digit, sh_above;
   __shared__ int wcnt[TOPK_WAVES];
+  __shared__ float ext[2][TOPK_WAVES];
   const int pair = blockIdx.x;
   const int tid = threadIdx.x;
   const float* s = scores + (int64_t)pair * nb + c0;
   int32_t* out = idx_out + (int64_t)pair * n_keep;
   const int n = c1 - c0;
+  if (ad.on) {  // uniform
+    const float* all = scores + (int64_t)pair * nb;
+    float amax = -INFINITY, amin = INFINITY;
+    for (int i = tid; i < c0 + (nb - c1); i += TOPK_THREADS) {
+      const float a = all[i < c0 ? i : c1 + (i - c0)];
+      amax = fmaxf(amax, a);
+      amin = fminf(amin, a);
+    }
+    amax = wave_max(amax);
+    amin = -wave_max(-amin);
+    if ((tid & 63) == 0) {
+      ext[0][tid >> 6] = amax;
+      ext[1][tid >> 6] = amin;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < TOPK_WAVES; ++w) {
+      amax = fmaxf(amax, ext[0][w]);
+      amin = fminf(amin, ext[1][w]);
+    }
+    const float tau = (c0 + (nb - c1) > 0) ? amax + ad.margin * (amax - amin) : -INFINITY;
+    int cnt = 0;
+    for (int base = 0; base < n; base += TOPK_THREADS) {
+      int tot;
+      block_prefix(base + tid < n && s[base + tid] > tau, wcnt, &tot);
+      cnt += tot;
+    }
+    k = min(max(cnt, ad.k_lo), ad.k_hi);
+    for (int i = c0 + k + (nb - c1) + tid; i < n_keep; i += TOPK_THREADS) out[i] = -1;  // absent
+  }
   for (int i = tid; i < c0; i += TOPK_THREADS) out[i] = i;                 // sink
   for (int i = tid; i < nb - c1; i += TOPK_THREADS) out[c0 + k + i] = c1 + i;  // local
   if (k <= 0) return;
@@ -350,9 +390,12 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restr
 }
 
 void launch_topk(const float* scores, int64_t pairs, int nb, int c0, int c1, int k, int n_keep,
-                 int32_t* idx_out, hipStream_t st) {
+                 int32_t* idx_out, hipStream_t st, bool adaptive, int k_lo, int k_hi,
+                 float margin) {
   if (pairs <= 0) return;
-  topk_kernel<<<(unsigned)pairs, TOPK_THREADS, 0, st>>>(scores, nb, c0, c1, k, n_keep, idx_out);
+  AdaptiveSel ad{adaptive ? 1 : 0, k_lo, k_hi, margin};
+  topk_kernel<<<(unsigned)pairs, TOPK_THREADS, 0, st>>>(scores, nb, c0, c1, k, n_keep, ad,
+                                                        idx_out);
 }
 
 }  // namespace bsa
