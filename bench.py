@@ -192,6 +192,47 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30, inputs=None):
     }
 
 
+def run_adaptive(cfg, steps, warmup, t, ratio_min=0.10, ratio_max=0.20, margin=0.0,
+                 flush_bytes=1 << 30):
+    """The decode step with anchor-adaptive selection (kept fraction per (b, kv head) between
+    ratio_min and ratio_max, set by the sink/local anchors' scores)."""
+    import numpy as np
+    import torch
+
+    import long_context_block_summary_amd as bsa
+
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to(t["q"]), to(t["k"]), to(t["v"])
+    N, bs = cfg.seq_len, cfg.block_size
+    summ, _ = bsa.build_block_summaries(k, N, bs)
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    kw = dict(adaptive=True, keep_ratio_max=ratio_max, anchor_margin=margin)
+    ts, kept = [], None
+    for i in range(warmup + steps):
+        flush.add_(1.0)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        out, lse, idx = bsa.decode_step(q, k, v, summ, N, bs, cfg.n_sink, cfg.n_local, -1,
+                                        ratio_min, **kw)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            ts.append(e0.elapsed_time(e1))
+        kept = (idx >= 0).sum(dim=2).float()
+    ms = sum(ts) / len(ts)
+    nb = -(-N // bs)
+    return {"workload": cfg.name, "ms_per_step": ms,
+            "queries_heads_per_s": cfg.batch * cfg.n_q_heads / (ms / 1e3), **pct(ts),
+            "keep_range": [ratio_min, ratio_max], "anchor_margin": margin,
+            "kept_pct_mean": float(kept.mean()) / nb * 100,
+            "kept_pct_min": float(kept.min()) / nb * 100,
+            "kept_pct_max": float(kept.max()) / nb * 100,
+            "timed": "select_blocks (adaptive) + sparse_decode_attn, cold cache"}
+
+
 def run_decode_loop(cfg, steps, warmup, t, flush_bytes=1 << 30):
     """Per generated token: append K/V, refresh the summary of its block, select, attend.
     The cache holds the workload's tokens; the loop starts `warmup + steps` tokens before
@@ -479,6 +520,7 @@ def main():
                        "select_us": r2["sel_ms"] * 1e3, "attn_us": r2["att_ms"] * 1e3}
         del r2
     line["decode_loop"] = run_decode_loop(cfg, max(10, args.steps // 2), 3, r["inputs"])
+    line["adaptive_selection"] = run_adaptive(cfg, max(10, args.steps // 2), 3, r["inputs"])
     if args.prefill and args.prefill != "none":
         line["prefill"] = run_prefill(synth.CONFIGS[args.prefill], max(5, args.steps // 5), 2)
     if extra:
