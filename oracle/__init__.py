@@ -51,6 +51,15 @@ def load(path=LIB_PATH):
     lib.oracle_select_blocks.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f64,
                                          vp, vp]
     lib.oracle_select_blocks.restype = ctypes.c_int
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_value.restype = f64
+    lib.oracle_e4m3_encode.argtypes = [f64]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_quantize_fp8.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.oracle_quantize_fp8.restype = ctypes.c_int
+    lib.oracle_sparse_decode_attn_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                  i32, i32, i32, i32, i32, f64, vp, vp]
+    lib.oracle_sparse_decode_attn_fp8.restype = ctypes.c_int
     lib.oracle_adaptive_bounds.argtypes = [i32, i32, i32, f64, f64, vp, vp]
     lib.oracle_adaptive_bounds.restype = ctypes.c_int32
     lib.oracle_select_blocks_adaptive.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32,
@@ -124,6 +133,52 @@ def select_blocks(q, summaries, n_kv_heads, n_sink=1, n_local=2, top_k=-1, keep_
     if rc:
         raise ValueError(f"oracle_select_blocks rc={rc}")
     return idx, scores
+
+
+def e4m3_value(code, lib=None):
+    return (lib or load()).oracle_e4m3_value(int(code))
+
+
+def e4m3_encode(y, lib=None):
+    return int((lib or load()).oracle_e4m3_encode(float(y)))
+
+
+def quantize_fp8(x, seq_len, block_size=64, sstride=0, lib=None):
+    """x uint16 (bf16 bits) [B][H][stride][d] -> (codes uint8 [B][H][stride][d], rows >= seq_len
+    zero; scales float32 [B][H][S], S = sstride or ceil(seq_len / block_size))."""
+    lib = lib or load()
+    x = _u16(x)
+    B, H, stride, d = x.shape
+    S = sstride or -(-seq_len // block_size)
+    out = np.zeros((B, H, stride, d), np.uint8)
+    sc = np.zeros((B, H, S), np.float32)
+    rc = lib.oracle_quantize_fp8(_p(x), B, H, seq_len, stride, d, block_size, S, _p(out), _p(sc))
+    if rc:
+        raise ValueError(f"oracle_quantize_fp8 rc={rc}")
+    return out, sc
+
+
+def sparse_decode_attn_fp8(q, k8, v8, kscales, vscales, idx, seq_len, block_size=64, scale=0.0,
+                           lib=None):
+    """Attention over the dequantized FP8 cache; returns (out [B][Hq][d], lse [B][Hq])."""
+    lib = lib or load()
+    q = _u16(q)
+    k8 = np.ascontiguousarray(k8, dtype=np.uint8)
+    v8 = np.ascontiguousarray(v8, dtype=np.uint8)
+    kscales = np.ascontiguousarray(kscales, dtype=np.float32)
+    vscales = np.ascontiguousarray(vscales, dtype=np.float32)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    B, Hq, d = q.shape
+    Hkv, stride = k8.shape[1], k8.shape[2]
+    out = np.empty((B, Hq, d), np.float64)
+    lse = np.empty((B, Hq), np.float64)
+    rc = lib.oracle_sparse_decode_attn_fp8(_p(q), _p(k8), _p(v8), _p(kscales), _p(vscales),
+                                           _p(idx), idx.shape[2], B, Hq, Hkv, d, seq_len, stride,
+                                           block_size, kscales.shape[2], float(scale), _p(out),
+                                           _p(lse))
+    if rc:
+        raise ValueError(f"oracle_sparse_decode_attn_fp8 rc={rc}")
+    return out, lse
 
 
 def adaptive_bounds(nb, n_sink, n_local, ratio_min, ratio_max, lib=None):

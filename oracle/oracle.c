@@ -304,6 +304,151 @@ int oracle_select_blocks_adaptive(const uint16_t* q, const double* summaries, in
   return 0;
 }
 
+/* ---- FP8 KV cache (aicoding.csdn.net page, 二.2 (3) FP8量化与无损压缩; the
+ * format is not fixed there: OCP E4M3, one fp32 scale per (pair, block)).
+ * E4M3: 1 sign, 4 exponent (bias 7) and 3 mantissa bits, no infinities,
+ * 0x7F / 0xFF are NaN, the largest finite magnitude 448 = 1.75 * 2^8. */
+double oracle_e4m3_value(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -6);
+  return s ? -v : v;
+}
+
+/* the nearest E4M3 code, ties to the even code; magnitudes >= 448 saturate */
+uint8_t oracle_e4m3_encode(double y) {
+  uint8_t s = signbit(y) ? 0x80 : 0;
+  double a = fabs(y);
+  if (a >= 448.0) return s | 0x7E;
+  if (a == 0.0) return s;
+  int e;
+  frexp(a, &e);            /* a in [2^(e-1), 2^e) */
+  int E = e - 1;
+  if (E < -6) E = -6;      /* the subnormal codes share exponent -6's spacing */
+  double r = rint(a / ldexp(1.0, E - 3)); /* spacing 2^(E-3): 3 mantissa bits */
+  int code;
+  if (E == -6 && r < 8.0) {
+    code = (int)r;         /* subnormal: exponent field 0 */
+  } else {
+    if (r >= 16.0) { /* rounded up to the next power of two */
+      r = 8.0;
+      E += 1;
+    }
+    code = ((E + 7) << 3) | ((int)r - 8);
+  }
+  if (code > 0x7E) code = 0x7E;
+  return (uint8_t)(s | code);
+}
+
+/* per (pair, block j): amax = max |x| over the valid tokens; scale = amax /
+ * 448 and inv = 448 / amax in fp32; code = E4M3(clamp(x * inv, +-448)) with
+ * the product in fp32.  out [B][H][stride][d] (rows < N), scales [B][H][sstride] */
+int oracle_quantize_fp8(const uint16_t* x, int32_t B, int32_t H, int32_t N, int32_t stride,
+                        int32_t d, int32_t bs, int32_t sstride, uint8_t* out, float* scales) {
+  if (!x || !out || !scales || B < 0 || H < 0 || N < 0 || d <= 0 || bs <= 0 || stride < N)
+    return -1;
+  int32_t nb = oracle_num_blocks(N, bs);
+  if (sstride < nb) return -1;
+  int64_t np = (int64_t)B * H;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t p = 0; p < np; ++p) {
+    for (int32_t j = 0; j < nb; ++j) {
+      int32_t t0 = j * bs, t1 = t0 + bs < N ? t0 + bs : N;
+      float amax = 0.0f;
+      for (int32_t t = t0; t < t1; ++t)
+        for (int32_t c = 0; c < d; ++c) {
+          float a = (float)fabs(bf(x[(p * stride + t) * (int64_t)d + c]));
+          if (a > amax) amax = a;
+        }
+      float sc = amax / 448.0f;
+      float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+      for (int32_t t = t0; t < t1; ++t)
+        for (int32_t c = 0; c < d; ++c) {
+          int64_t o = (p * stride + t) * (int64_t)d + c;
+          float y = (float)bf(x[o]) * inv;
+          if (y > 448.0f) y = 448.0f;
+          if (y < -448.0f) y = -448.0f;
+          out[o] = oracle_e4m3_encode((double)y);
+        }
+      scales[p * sstride + j] = sc;
+    }
+  }
+  return 0;
+}
+
+/* exact softmax attention over the kept blocks of a quantized cache: each
+ * key / value entry is scale[block] * E4M3(code), in fp64 */
+int oracle_sparse_decode_attn_fp8(const uint16_t* q, const uint8_t* k8, const uint8_t* v8,
+                                  const float* kscales, const float* vscales, const int32_t* idx,
+                                  int32_t n_keep, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                  int32_t N, int32_t stride, int32_t bs, int32_t sstride,
+                                  double scale, double* out, double* lse) {
+  if (!q || !k8 || !v8 || !kscales || !vscales || !idx || !out || B < 0 || Hq <= 0 ||
+      Hkv <= 0 || Hq % Hkv || d <= 0 || N < 1 || stride < N || bs <= 0 || n_keep < 1)
+    return -1;
+  int32_t g = Hq / Hkv;
+  int32_t nb = oracle_num_blocks(N, bs);
+  if (sstride < nb) return -1;
+  for (int64_t p = 0; p < (int64_t)B * Hkv; ++p) {
+    const int32_t* li = idx + p * n_keep;
+    int32_t used = n_keep;
+    for (int32_t i = 0; i < n_keep; ++i) {
+      if (li[i] == -1) {
+        used = i;
+        break;
+      }
+      if (li[i] < 0 || li[i] >= nb || (i && li[i] <= li[i - 1])) return -1;
+    }
+    if (used == 0) return -1;
+    for (int32_t i = used; i < n_keep; ++i)
+      if (li[i] != -1) return -1;
+  }
+  if (scale == 0.0) scale = 1.0 / sqrt((double)d);
+  double lut[256];
+  for (int c = 0; c < 256; ++c) lut[c] = oracle_e4m3_value((uint8_t)c);
+  int64_t nqh = (int64_t)B * Hq;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t bh = 0; bh < nqh; ++bh) {
+    int64_t b = bh / Hq, h = bh % Hq, kvh = h / g, p = b * Hkv + kvh;
+    const int32_t* list = idx + p * n_keep;
+    double* z = (double*)malloc(sizeof(double) * ((size_t)n_keep * bs + 1));
+    int64_t* row = (int64_t*)malloc(sizeof(int64_t) * ((size_t)n_keep * bs + 1));
+    double* vs = (double*)malloc(sizeof(double) * ((size_t)n_keep * bs + 1));
+    int32_t n = 0;
+    double zmax = -INFINITY;
+    for (int32_t i = 0; i < n_keep && list[i] >= 0; ++i) {
+      int32_t blk = list[i], t0 = blk * bs, t1 = t0 + bs < N ? t0 + bs : N;
+      double ks = (double)kscales[p * sstride + blk];
+      for (int32_t t = t0; t < t1; ++t) {
+        const uint8_t* kr = k8 + (p * stride + t) * (int64_t)d;
+        double sdot = 0.0;
+        for (int32_t c = 0; c < d; ++c) sdot += bf(q[bh * d + c]) * (ks * lut[kr[c]]);
+        z[n] = sdot * scale;
+        row[n] = (p * stride + t) * (int64_t)d;
+        vs[n] = (double)vscales[p * sstride + blk];
+        if (z[n] > zmax) zmax = z[n];
+        ++n;
+      }
+    }
+    double l = 0.0;
+    for (int32_t t = 0; t < n; ++t) {
+      z[t] = exp(z[t] - zmax);
+      l += z[t];
+    }
+    double* o = out + bh * d;
+    for (int32_t c = 0; c < d; ++c) o[c] = 0.0;
+    for (int32_t t = 0; t < n; ++t) {
+      double pw = z[t] / l;
+      for (int32_t c = 0; c < d; ++c) o[c] += pw * (vs[t] * lut[v8[row[t] + c]]);
+    }
+    if (lse) lse[bh] = zmax + log(l);
+    free(z);
+    free(row);
+    free(vs);
+  }
+  return 0;
+}
+
 /* ---- [CSA] 2.1 / 4.4: exact softmax(q K^T / sqrt(d)) V over a token list.
  * Writes o[d] and returns lse; w (optional) receives the weights. */
 static double attend(const uint16_t* qh, const double* qd, int32_t d, int32_t n,

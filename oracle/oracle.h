@@ -99,6 +99,24 @@ int oracle_sparse_prefill_attn(const uint16_t* q, int32_t C, const uint16_t* k,
                                const double* sink_logits, double* out, double* branch_out,
                                double* lse3, int32_t* sel_out, double* sel_scores);
 
+/* FP8 KV cache: OCP E4M3 codes with one fp32 scale per (pair, block).
+ * oracle_e4m3_value: the value of a code (NaN for 0x7F / 0xFF);
+ * oracle_e4m3_encode: the nearest code, ties to even, |y| >= 448 saturates;
+ * oracle_quantize_fp8: amax per block, scale = amax / 448 and inv = 448 / amax
+ *   in fp32, code = encode(clamp(x * inv in fp32, +-448)); out [B][H][stride][d]
+ *   for rows < N, scales [B][H][sstride] (sstride >= nb);
+ * oracle_sparse_decode_attn_fp8: exact softmax attention over the kept blocks
+ *   of the dequantized cache (scale * value), lists as oracle_sparse_decode_attn. */
+double oracle_e4m3_value(uint8_t c);
+uint8_t oracle_e4m3_encode(double y);
+int oracle_quantize_fp8(const uint16_t* x, int32_t B, int32_t H, int32_t N, int32_t stride,
+                        int32_t d, int32_t bs, int32_t sstride, uint8_t* out, float* scales);
+int oracle_sparse_decode_attn_fp8(const uint16_t* q, const uint8_t* k8, const uint8_t* v8,
+                                  const float* kscales, const float* vscales, const int32_t* idx,
+                                  int32_t n_keep, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                  int32_t N, int32_t stride, int32_t bs, int32_t sstride,
+                                  double scale, double* out, double* lse);
+
 /* round an fp64 value to the nearest bf16 (ties to even); returns bits */
 uint16_t oracle_round_bf16(double x);
 

@@ -52,6 +52,14 @@ MUTANTS = [
     ("adaptive k ignores the lower bound",
      "int32_t k = above < k_lo ? k_lo : (above > k_hi ? k_hi : above);",
      "int32_t k = above > k_hi ? k_hi : above;"),
+    ("e4m3 ties away from zero", "double r = rint(a / ldexp(1.0, E - 3));",
+     "double r = floor(a / ldexp(1.0, E - 3) + 0.5);"),
+    ("e4m3 exponent bias 8", "double v = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -6);",
+     "double v = e ? ldexp(1.0 + m / 8.0, e - 8) : ldexp(m / 8.0, -7);"),
+    ("fp8 scale for the E4M3 max of the FNUZ variant", "float sc = amax / 448.0f;",
+     "float sc = amax / 240.0f;"),
+    ("fp8 values use the key scale", "vs[n] = (double)vscales[p * sstride + blk];",
+     "vs[n] = (double)kscales[p * sstride + blk];"),
     ("branch sink uses the wrong lse", "double keep = has_sink ? 1.0 / (1.0 + exp(zs - l[br])) : 1.0;",
      "double keep = has_sink ? 1.0 / (1.0 + exp(zs - l[0])) : 1.0;"),
     ("bf16 ties away from zero", "double ri = rint(s);", "double ri = floor(s + 0.5);"),

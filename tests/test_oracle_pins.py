@@ -642,3 +642,88 @@ def test_padded_lists_attend_like_truncated_ones(orc):
     for bad in ([[[-1, -1]]], [[[2, -1, 3]]], [[[0, -1, -1, 1]]]):
         with pytest.raises(ValueError):
             orc.sparse_decode_attn(q[:, :1], k[:, :1], v[:, :1], np.array(bad, np.int32), 128)
+
+
+# ------------------------------------------------------------- FP8 KV cache
+# aicoding.csdn.net page, 二.2 (3): the KV cache stored in FP8.  The format is not
+# fixed there: OCP E4M3 with one scale per (pair, block); torch's float8_e4m3fn is
+# an independent implementation of the same format.
+
+def test_e4m3_values_match_torch(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = np.array([orc.e4m3_value(c) for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+
+
+def test_e4m3_encoding_matches_torch_incl_ties(orc):
+    rng = np.random.default_rng(41)
+    vals = (rng.uniform(-448, 448, 3000) * np.exp2(rng.integers(-12, 1, 3000))).astype(np.float32)
+    # every midpoint between adjacent finite codes (a tie: even code wins)
+    fin = np.array(sorted({orc.e4m3_value(c) for c in range(0, 127)}))
+    mids = ((fin[1:] + fin[:-1]) / 2).astype(np.float32)
+    vals = np.concatenate([vals, mids, -mids, [0.0, -0.0, 448.0, -448.0]]).astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([orc.e4m3_encode(v) for v in vals], np.uint8)
+    np.testing.assert_array_equal(got, ref)
+    # beyond the largest finite value the oracle saturates (torch would give NaN)
+    assert orc.e4m3_encode(449.0) == 0x7E and orc.e4m3_encode(-1e9) == 0xFE
+
+
+def test_quantize_fp8_closed_forms(orc):
+    rng = np.random.default_rng(42)
+    fin = np.array(sorted({orc.e4m3_value(c) for c in range(0, 127)}))
+    d, bs = 16, 64
+    # block 0: E4M3 values whose amax is 448 -> scale 1, codes exact;
+    # block 1: the same times 2^-5 -> scale 2^-5, same codes; block 2: zeros;
+    # block 3 (partial, 10 tokens): general values
+    b0 = rng.choice(np.concatenate([fin, -fin]), (bs, d)).astype(np.float32)
+    b0[3, 5] = 448.0
+    x = np.zeros((1, 1, 4 * bs, d), np.float32)
+    x[0, 0, :bs] = b0
+    x[0, 0, bs:2 * bs] = b0 * 2.0 ** -5
+    x[0, 0, 3 * bs:3 * bs + 10] = rng.standard_normal((10, d))
+    N = 3 * bs + 10
+    codes, sc = orc.quantize_fp8(bf(x), N, bs)
+    assert sc[0, 0, 0] == 1.0 and sc[0, 0, 1] == 2.0 ** -5 and sc[0, 0, 2] == 0.0
+    np.testing.assert_array_equal(codes[0, 0, :bs], codes[0, 0, bs:2 * bs])
+    val = np.vectorize(orc.e4m3_value)
+    np.testing.assert_array_equal(val(codes[0, 0, :bs]), b0)
+    assert not codes[0, 0, 2 * bs:3 * bs].any() and not codes[0, 0, N:].any()
+    # the general block: within half a code spacing, and its amax maps to 448
+    xb = f(bf(x))[0, 0, 3 * bs:N]
+    deq = sc[0, 0, 3] * val(codes[0, 0, 3 * bs:N])
+    assert np.all(np.abs(deq - xb) <= np.maximum(2.0 ** -4 * np.abs(xb), sc[0, 0, 3] * 2.0 ** -10)
+                  * (1 + 1e-6))
+    assert np.abs(val(codes[0, 0, 3 * bs:N])).max() == 448.0
+
+
+def test_fp8_attention_equals_bf16_on_representable_cache(orc):
+    # a cache of E4M3 values with 448 in every block quantizes exactly (scale 1):
+    # attention over it must equal the bf16 path on the same values
+    rng = np.random.default_rng(43)
+    fin = np.array(sorted({orc.e4m3_value(c) for c in range(0, 127)}))
+    pool = np.concatenate([fin[(fin > 0.05) & (fin < 4)], -fin[(fin > 0.05) & (fin < 4)]])
+    B, Hq, Hkv, d, N = 1, 4, 2, 16, 64 * 6 - 7
+    k = rng.choice(pool, (B, Hkv, N, d)).astype(np.float32)
+    v = rng.choice(pool, (B, Hkv, N, d)).astype(np.float32)
+    for j in range(6):
+        k[:, :, j * 64, 0] = 448.0
+        v[:, :, j * 64, 1] = 448.0
+    q = bf(rng.standard_normal((B, Hq, d)).astype(np.float32) * 0.01)
+    k16, v16 = bf(k), bf(v)
+    k8, ks = orc.quantize_fp8(k16, N)
+    v8, vs = orc.quantize_fp8(v16, N)
+    assert (ks == 1.0).all() and (vs == 1.0).all()
+    idx = np.array([[[0, 2, 3, 5], [1, 2, 4, 5]]], np.int32)
+    o8, l8 = orc.sparse_decode_attn_fp8(q, k8, v8, ks, vs, idx, N)
+    o16, l16, _ = orc.sparse_decode_attn(q, k16, v16, idx, N)
+    np.testing.assert_allclose(o8, o16, atol=1e-12)
+    np.testing.assert_allclose(l8, l16, atol=1e-12)
+    # scaling V by 2^-3 scales the output exactly
+    v8b, vsb = orc.quantize_fp8(bf(v * 2.0 ** -3), N)
+    np.testing.assert_array_equal(v8b, v8)
+    o8b, _ = orc.sparse_decode_attn_fp8(q, k8, v8b, ks, vsb, idx, N)
+    np.testing.assert_allclose(o8b, o8 * 2.0 ** -3, atol=1e-12)
