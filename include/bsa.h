@@ -197,6 +197,33 @@ int sparse_decode_attn(const void* q, const void* k, const void* v, const int32_
                        float* out, float* lse, void* workspace, size_t ws_bytes,
                        void* hip_stream);
 
+/* quantize_kv_fp8 -- an FP8 copy of a K or V cache for sparse_decode_attn_fp8
+ * (the FP8 KV cache of the aicoding.csdn.net page, 二.2 KV缓存分层存储, (3)
+ * FP8量化与无损压缩; the pages fix neither the format nor the scale
+ * granularity: this library uses OCP E4M3 with one fp32 scale per (b, kv
+ * head, block)).  Per block:
+ * amax = max |x| over its valid tokens; scale = amax / 448 and
+ * inv = 448 / amax in fp32 (correctly rounded); each value is stored as the
+ * E4M3 code nearest (ties to even) to clamp(x * inv, -448, 448).  A block of
+ * zeros gets scale 0.  The dequantized value is scale * E4M3(code).
+ *   x        bf16 [B][Hkv][seq_stride][d]
+ *   out_fp8  uint8 [B][Hkv][seq_stride][d] (rows past seq_len are not written)
+ *   scales   fp32 [B][Hkv][S], S = summary_stride or ceil(seq_len / block_size) */
+int quantize_kv_fp8(const void* x, const bsa_shape* shape, int32_t block_size, void* out_fp8,
+                    float* scales, void* hip_stream);
+
+/* sparse_decode_attn_fp8 -- sparse_decode_attn over an FP8 cache written by
+ * quantize_kv_fp8: the exact softmax attention of the dequantized keys and
+ * values (E4M3 converts exactly to bf16; the block scales multiply the
+ * logits and the weights).  k_scales / v_scales as quantize_kv_fp8's scales.
+ * Workspace, lists (incl. -1 padding), requirements and errors as
+ * sparse_decode_attn. */
+int sparse_decode_attn_fp8(const void* q, const void* k_fp8, const void* v_fp8,
+                           const float* k_scales, const float* v_scales, const int32_t* block_idx,
+                           int32_t n_keep, const bsa_shape* shape, int32_t block_size,
+                           float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
+                           void* hip_stream);
+
 /* sparse_decode_attn_split -- sparse_decode_attn with an explicit number of
  * kept-block splits per (batch, kv head) (>= 1; 0 = the library's plan).
  * The result equals sparse_decode_attn's up to fp32 rounding of the merge.

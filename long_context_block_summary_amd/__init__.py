@@ -82,7 +82,11 @@ def lib():
     L.sparse_prefill_attn_selected.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                                P(bsa_shape), P(bsa_prefill_cfg), f32, vp, vp, vp,
                                                vp]
-    for fn in ("build_block_summaries", "update_block_summaries", "append_kv",
+    L.quantize_kv_fp8.argtypes = [vp, P(bsa_shape), i32, vp, vp, vp]
+    L.sparse_decode_attn_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, P(bsa_shape), i32, f32, vp,
+                                         vp, vp, sz, vp]
+    for fn in ("quantize_kv_fp8", "sparse_decode_attn_fp8",
+               "build_block_summaries", "update_block_summaries", "append_kv",
                "select_blocks", "sparse_decode_attn",
                "sparse_decode_attn_split", "sparse_prefill_attn", "select_prefill_entries",
                "sparse_prefill_attn_selected"):
@@ -389,6 +393,58 @@ def sparse_prefill_attn_selected(q, k, v, k_cmp_sparse_bf16, v_cmp_sparse_bf16, 
                                               scale, _ptr(_sink(sink_logits, Hq)), _ptr(out),
                                               _ptr(lse3), _stream(q.device)))
     return out, lse3
+
+
+def quantize_kv_fp8(x, seq_len, block_size=64, summary_stride=0, out=None, scales=None):
+    """x bf16 [B][H][stride][d] -> (E4M3 codes uint8 [B][H][stride][d], fp32 scales [B][H][S]),
+    S = summary_stride or ceil(seq_len / block_size); one scale per block."""
+    import torch
+    _need(x, "x", torch.bfloat16, 4)
+    B, H, stride, d = x.shape
+    S = summary_stride or num_blocks(seq_len, block_size)
+    if out is None:
+        out = torch.zeros((B, H, stride, d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, S), dtype=torch.float32, device=x.device)
+    shape = make_shape(B, H, H, d, seq_len, stride, summary_stride)
+    _check("quantize_kv_fp8", lib().quantize_kv_fp8(_ptr(x), ctypes.byref(shape), block_size,
+                                                    _ptr(out), _ptr(scales), _stream(x.device)))
+    return out, scales
+
+
+def sparse_decode_attn_fp8(q, k8, v8, k_scales, v_scales, block_idx, seq_len, block_size=64,
+                           scale=0.0, out=None, lse=None, workspace=None, want_lse=True):
+    """sparse_decode_attn over an E4M3 cache from quantize_kv_fp8 (k8, v8 uint8
+    [B][Hkv][stride][d], scales fp32 [B][Hkv][S])."""
+    import torch
+    _need(q, "q", torch.bfloat16, 3)
+    for name, t in (("k8", k8), ("v8", v8)):
+        _need(t, name, torch.uint8, 4)
+    for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+        _need(t, name, torch.float32, 3)
+    _need(block_idx, "block_idx", torch.int32, 3)
+    B, Hq, d = q.shape
+    Hkv, stride = k8.shape[1], k8.shape[2]
+    if tuple(v8.shape) != tuple(k8.shape) or tuple(v_scales.shape) != tuple(k_scales.shape):
+        raise ValueError("k/v shapes disagree")
+    n_keep = block_idx.shape[2]
+    shape = make_shape(B, Hq, Hkv, d, seq_len, stride, k_scales.shape[2])
+    ws_bytes = lib().bsa_decode_workspace_size(ctypes.byref(shape), n_keep, block_size, 0)
+    if ws_bytes == SIZE_MAX:
+        raise ValueError("invalid decode arguments")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    _check("sparse_decode_attn_fp8",
+           lib().sparse_decode_attn_fp8(_ptr(q), _ptr(k8), _ptr(v8), _ptr(k_scales),
+                                        _ptr(v_scales), _ptr(block_idx), n_keep,
+                                        ctypes.byref(shape), block_size, scale, _ptr(out),
+                                        _ptr(lse), _ptr(workspace), workspace.numel(),
+                                        _stream(q.device)))
+    return out, lse
 
 
 def decode_step(q, k, v, summaries, seq_len, block_size=64, n_sink=1, n_local=2, top_k=-1,

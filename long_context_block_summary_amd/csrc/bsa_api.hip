@@ -258,6 +258,53 @@ int sparse_decode_attn_split(const void* q, const void* k, const void* v,
   return launch_status();
 }
 
+int quantize_kv_fp8(const void* x, const bsa_shape* shape, int32_t block_size, void* out_fp8,
+                    float* scales, void* hip_stream) {
+  if (!x || !out_fp8 || !scales || !shape_ok(shape) || block_size < 1) return BSA_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(out_fp8)) return BSA_INVALID_ARG;
+  if (!dim_supported(shape->head_dim)) return BSA_UNSUPPORTED;
+  const int ss = summary_stride(shape, block_size);
+  if (ss < 0) return BSA_INVALID_ARG;
+  if (shape->seq_len == 0) return BSA_OK;
+  bsa::launch_quantize_fp8(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(out_fp8),
+                           scales, (int64_t)shape->batch * shape->n_kv_heads, shape->seq_len,
+                           shape->seq_stride, shape->head_dim, block_size, ss,
+                           static_cast<hipStream_t>(hip_stream));
+  return launch_status();
+}
+
+int sparse_decode_attn_fp8(const void* q, const void* k_fp8, const void* v_fp8,
+                           const float* k_scales, const float* v_scales, const int32_t* block_idx,
+                           int32_t n_keep, const bsa_shape* shape, int32_t block_size,
+                           float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
+                           void* hip_stream) {
+  if (!q || !k_fp8 || !v_fp8 || !k_scales || !v_scales || !block_idx || !out ||
+      !shape_ok(shape) || n_keep < 1 || shape->seq_len < 1)
+    return BSA_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_fp8) || !aligned16(v_fp8) || !aligned16(out))
+    return BSA_INVALID_ARG;
+  if (block_size < 1) return BSA_INVALID_ARG;
+  if (n_keep > bsa_num_blocks(shape->seq_len, block_size)) return BSA_INVALID_ARG;
+  const int ss = summary_stride(shape, block_size);
+  if (ss < 0) return BSA_INVALID_ARG;
+  const int g = shape->n_q_heads / shape->n_kv_heads;
+  if (block_size != 64 || !dim_supported(shape->head_dim) || !group_supported(g))
+    return BSA_UNSUPPORTED;
+  const int64_t pairs = (int64_t)shape->batch * shape->n_kv_heads;
+  bsa::DecodePlan plan = bsa::plan_decode(pairs, n_keep, g, 0);
+  if (ws_bytes < bsa::decode_workspace_bytes(pairs, shape->head_dim, plan))
+    return BSA_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned16(workspace)) return BSA_INVALID_ARG;
+  if (scale == 0.f) scale = 1.f / sqrtf((float)shape->head_dim);
+  bsa::launch_decode_fp8(static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_fp8),
+                         static_cast<const uint8_t*>(v_fp8), k_scales, v_scales, ss, block_idx,
+                         n_keep, shape->batch, shape->n_q_heads, shape->n_kv_heads,
+                         shape->head_dim, shape->seq_len, shape->seq_stride, scale, plan,
+                         static_cast<float*>(workspace), out, lse,
+                         static_cast<hipStream_t>(hip_stream));
+  return launch_status();
+}
+
 int sparse_decode_attn(const void* q, const void* k, const void* v, const int32_t* block_idx,
                        int32_t n_keep, const bsa_shape* shape, int32_t block_size, float scale,
                        float* out, float* lse, void* workspace, size_t ws_bytes,

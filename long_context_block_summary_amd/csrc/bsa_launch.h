@@ -22,6 +22,10 @@ void launch_append_update(const uint16_t* k_new, const uint16_t* v_new, uint16_t
                           int bs, int ostride, float* out_f32, uint16_t* out_bf16,
                           hipStream_t st);
 
+// OCP E4M3 copy of a cache [pairs][stride][d] with one scale per (pair, block)
+void launch_quantize_fp8(const uint16_t* x, uint8_t* out, float* scales, int64_t pairs, int N,
+                         int stride, int d, int bs, int sstride, hipStream_t st);
+
 // candidate scores s[pair][j] = qbar . summary_j for j in [c0, c1); summaries
 // rows are sstride blocks apart, scores rows nb apart
 void launch_scores(const uint16_t* q, const float* summ, int B, int Hq, int Hkv, int d, int nb,
@@ -46,6 +50,12 @@ size_t decode_workspace_bytes(int64_t pairs, int d, const DecodePlan& p);
 void launch_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
                    int n_keep, int B, int Hq, int Hkv, int d, int N, int stride, float scale,
                    const DecodePlan& plan, float* ws, float* out, float* lse, hipStream_t st);
+// the same over an E4M3 cache with per-(pair, block) K and V scales [pairs][sstride]
+void launch_decode_fp8(const uint16_t* q, const uint8_t* k, const uint8_t* v, const float* ksc,
+                       const float* vsc, int sstride, const int32_t* idx, int n_keep, int B,
+                       int Hq, int Hkv, int d, int N, int stride, float scale,
+                       const DecodePlan& plan, float* ws, float* out, float* lse,
+                       hipStream_t st);
 
 // chunked prefill: pooled queries, scores, top-k, three-branch attention
 struct PrefillLaunch {

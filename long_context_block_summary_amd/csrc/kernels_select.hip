@@ -167,6 +167,66 @@ void launch_append_update(const uint16_t* k_new, const uint16_t* v_new, uint16_t
                                                    out_bf16);
 }
 
+// FP8 (OCP E4M3) quantization of a K or V cache, one scale per (pair, block):
+// amax = max |x| over the block's valid tokens, scale = amax / 448 and
+// inv = 448 / amax (fp32, correctly rounded), code = RNE_E4M3(clamp(x * inv,
+// +-448)) by v_cvt_pk_fp8_f32; an all-zero block gets scale 0 and zero codes.
+template <int D>
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __restrict__ x,
+                                                           uint8_t* __restrict__ out,
+                                                           float* __restrict__ scales, int N,
+                                                           int stride, int bs, int nb,
+                                                           int sstride) {
+  constexpr int PPR = D / 8;  // 8-value pieces per row
+  __shared__ float red[4];
+  const int64_t pair = blockIdx.x / nb;
+  const int j = blockIdx.x % nb;
+  const int t0 = j * bs, n = min(bs, N - t0);
+  const uint4* src = reinterpret_cast<const uint4*>(x + (pair * stride + t0) * D);
+  uint32_t amax_bits = 0;  // |bf16| bit patterns order like the values
+  for (int i = threadIdx.x; i < n * PPR; i += 256) {
+    const uint4 w = src[i];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      amax_bits = max(amax_bits, max(ws[c] & 0x7FFFu, (ws[c] >> 16) & 0x7FFFu));
+  }
+  float amax = __uint_as_float(amax_bits << 16);
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = amax > 0.f ? 448.f / amax : 0.f;
+  if (threadIdx.x == 0) scales[pair * sstride + j] = amax / 448.f;
+  uint2* dst = reinterpret_cast<uint2*>(out + (pair * stride + t0) * D);
+  for (int i = threadIdx.x; i < n * PPR; i += 256) {
+    const uint4 w = src[i];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    float y[8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      y[2 * c] = fminf(fmaxf(bf_lo(ws[c]) * inv, -448.f), 448.f);
+      y[2 * c + 1] = fminf(fmaxf(bf_hi(ws[c]) * inv, -448.f), 448.f);
+    }
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+    dst[i] = make_uint2((uint32_t)lo, (uint32_t)hi);
+  }
+}
+
+void launch_quantize_fp8(const uint16_t* x, uint8_t* out, float* scales, int64_t pairs, int N,
+                         int stride, int d, int bs, int sstride, hipStream_t st) {
+  const int nb = (N + bs - 1) / bs;
+  if (nb <= 0 || pairs <= 0) return;
+  const unsigned grid = (unsigned)(pairs * nb);
+  if (d == 128)
+    quantize_fp8_kernel<128><<<grid, 256, 0, st>>>(x, out, scales, N, stride, bs, nb, sstride);
+  else
+    quantize_fp8_kernel<64><<<grid, 256, 0, st>>>(x, out, scales, N, stride, bs, nb, sstride);
+}
+
 void launch_append(const uint16_t* src, uint16_t* dst, int64_t pairs, int n_new, int N,
                    int stride, int d, hipStream_t st) {
   const int ppr = d / 8;
