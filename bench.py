@@ -233,6 +233,67 @@ def run_adaptive(cfg, steps, warmup, t, ratio_min=0.10, ratio_max=0.20, margin=0
             "timed": "select_blocks (adaptive) + sparse_decode_attn, cold cache"}
 
 
+def run_fp8(cfg, steps, warmup, t, flush_bytes=1 << 30):
+    """The decode step over an FP8 (E4M3) copy of the cache: select_blocks (bf16 summaries) +
+    sparse_decode_attn_fp8.  The quantization runs once at ingest and is timed on its own."""
+    import numpy as np
+    import torch
+
+    import long_context_block_summary_amd as bsa
+
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to(t["q"]), to(t["k"]), to(t["v"])
+    N, bs = cfg.seq_len, cfg.block_size
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    summ, _ = bsa.build_block_summaries(k, N, bs)
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    k8, ks = bsa.quantize_kv_fp8(k, N, bs)
+    v8, vs = bsa.quantize_kv_fp8(v, N, bs)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    quant_ms = e0.elapsed_time(e1)
+    del k, v
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev)
+    idx, _ = bsa.select_blocks(q, summ, N, bs, cfg.n_sink, cfg.n_local, cfg.top_k, cfg.keep_ratio)
+    n_keep = idx.shape[2]
+    ws = torch.empty(max(16, bsa.decode_workspace_size(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads,
+                                                       cfg.head_dim, N, n_keep)),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.batch, cfg.n_q_heads), dtype=torch.float32, device=dev)
+    step_ms, att_ms = [], []
+    for i in range(warmup + steps):
+        flush.add_(1.0)
+        a, b_, c = ev(), ev(), ev()
+        a.record(stream)
+        bsa.select_blocks(q, summ, N, bs, cfg.n_sink, cfg.n_local, cfg.top_k, cfg.keep_ratio,
+                          block_idx=idx)
+        b_.record(stream)
+        bsa.sparse_decode_attn_fp8(q, k8, v8, ks, vs, idx, N, bs, out=out, lse=lse, workspace=ws)
+        c.record(stream)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            step_ms.append(a.elapsed_time(c))
+            att_ms.append(b_.elapsed_time(c))
+    B, Hq, Hkv, d = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    kept_tokens = min(n_keep * bs, N)
+    att_bytes = (B * Hkv * kept_tokens * d * 2 + B * Hkv * n_keep * 2 * 4 + B * Hq * d * 2
+                 + B * Hq * d * 4 + B * Hkv * n_keep * 4)
+    ms, am = sum(step_ms) / len(step_ms), sum(att_ms) / len(att_ms)
+    return {"workload": cfg.name, "ms_per_step": ms,
+            "queries_heads_per_s": B * Hq / (ms / 1e3), **pct(step_ms),
+            "sparse_decode_attn_fp8_us": am * 1e3,
+            "attn_algorithmic_bytes": att_bytes,
+            "attn_GBps": att_bytes / (am / 1e3) / 1e9,
+            "attn_frac_of_8TBps": att_bytes / (am / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "quantize_kv_ms_ingest": quant_ms,
+            "format": "OCP E4M3 codes, one fp32 scale per (b, kv head, 64-token block) for K and V",
+            "timed": "select_blocks + sparse_decode_attn_fp8, cold cache"}
+
+
 def run_decode_loop(cfg, steps, warmup, t, flush_bytes=1 << 30):
     """Per generated token: append K/V, refresh the summary of its block, select, attend.
     The cache holds the workload's tokens; the loop starts `warmup + steps` tokens before
@@ -521,6 +582,7 @@ def main():
         del r2
     line["decode_loop"] = run_decode_loop(cfg, max(10, args.steps // 2), 3, r["inputs"])
     line["adaptive_selection"] = run_adaptive(cfg, max(10, args.steps // 2), 3, r["inputs"])
+    line["fp8_kv"] = run_fp8(cfg, max(10, args.steps // 2), 3, r["inputs"])
     if args.prefill and args.prefill != "none":
         line["prefill"] = run_prefill(synth.CONFIGS[args.prefill], max(5, args.steps // 5), 2)
     if extra:
