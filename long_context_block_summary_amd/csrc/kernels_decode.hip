@@ -2,27 +2,30 @@
 //
 // Exact softmax(q K^T * scale) V over the tokens of the kept blocks only
 // ("CSA + HCA 混合注意力机制" §2.1 and §4.4 step 4).  Decode streams the kept
-// KV once per step; its rate is set by how many bytes each CU keeps in
-// flight, so the kernel is built around a deep per-wave load pipeline:
+// KV once per step, so the kernel keeps a deep per-wave load pipeline and
+// puts both products on the matrix cores (a P.V product on the vector ALU
+// costs ~256 FMAs per lane per tile and made the kernel issue-bound):
 //
 //  * a workgroup of 4 waves owns one split (a contiguous run of one
 //    (batch, kv head) pair's kept-block list); wave w owns tokens
 //    [16w, 16w+16) of every block of the run, i.e. one 16-token tile per
 //    block, and keeps its own online-softmax state;
-//  * per tile a wave needs only 4 KiB of K and 4 KiB of V, so P tiles
-//    (P = 3, or 2 for 16 query heads per kv head) are requested ahead into
-//    registers: the loop always issues the tile P-1 steps ahead (a dummy
-//    broadcast load past the end) and never branches around its loads;
-//  * QK on the matrix cores: the g query heads of the kv group share each
-//    key tile, S^T[16 x 16] = K_tile[16 x d] q^T[d x 16] is d/32
-//    v_mfma_f32_16x16x32_bf16 (heads past g are zero); q stays in
-//    registers as the B operand; K fragments come straight from HBM in the
-//    A-operand layout (lane l: token l%16, 16 bytes at 32*kstep + 8*(l/16));
-//  * online softmax in base 2 per head in the MFMA accumulator layout, the
-//    tile max across the 4 lanes of a head by two cross-lane exchanges;
-//  * PV on the VALU: lane (ts, dq) owns 4 value columns (dq) of every
-//    (64/(d/4))-th token of the tile, so each 8-byte load instruction reads
-//    whole value rows; the weights reach those lanes through LDS;
+//  * P tiles (K tile + V tile) are requested ahead into registers: the loop
+//    always issues the tile P-1 steps ahead (a dummy broadcast load past the
+//    end) and never branches around its loads;
+//  * QK: S^T[16 tok x 16 heads] = K_tile q^T, d/32 v_mfma_f32_16x16x32_bf16
+//    (heads past g are zero); q stays in registers as the B operand and the
+//    K fragments come straight from HBM in the A-operand layout;
+//  * online softmax in base 2 per head in the accumulator layout; the
+//    running max moves only when a logit exceeds it by more than 2^8 (exact:
+//    o and l always share the same reference max);
+//  * PV: O^T[d x 16 heads] += V^T_tile P^T, one 16x16x32 MFMA per 16 value
+//    columns.  The S^T accumulator is already the B-operand layout of P^T; P
+//    enters as a bf16 pair hi + lo (k 0..3 and 4..7 of each lane) so the
+//    product keeps ~16 bits of the fp32 weight.  V rows are loaded
+//    coalesced, transposed 4x4 in registers (v_perm) and staged per wave in
+//    LDS as V^T, from where each lane reads its A fragment with one 8-byte
+//    read;
 //  * the 4 waves merge in LDS into one (o, m, l) partial per head, and a
 //    second small kernel merges the splits exactly with log-sum-exp weights.
 #include <math.h>
@@ -38,385 +41,107 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 constexpr int DEC_WAVES = 4;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr float DEC_RESCALE_LOG2 = 8.f;  // lazy max threshold (weights stay <= 2^8)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-// blocks in flight per wave (register budget: two waves per SIMD)
-template <int G> struct DecStages { static constexpr int value = G >= 16 ? 2 : 3; };
+// V^T staging: per wave D rows (value columns) of 16 bf16 tokens = 4 groups
+// of 4 tokens (8 bytes).  Row r lives at physical row r ^ ((r >> 3) & 7): a
+// bijection within every 16-row group, so the fragment reads (16 consecutive
+// rows) stay one contiguous 512-byte span, while the transposing writes
+// (rows 4 or 8 apart) spread over all banks.
+__device__ __forceinline__ int vt_row(int r) { return r ^ ((r >> 3) & 7); }
 
-template <int D, int G, int P>
-__global__ __launch_bounds__(256, 2) void decode_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, int n_keep, int Hq, int Hkv,
-    int N, int stride, float scale_log2, int bps, int n_splits, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
-  constexpr int KS = D / 32;        // MFMA k-steps over the head dim
-  constexpr int DQ = D / 4;         // 4-column groups per row: lane owns one group
-  constexpr int VT = 64 / DQ;       // token subgroups in the PV layout (2 for d=128)
-  constexpr int TPL = 16 / VT;      // tokens of the tile per lane (PV layout)
-  constexpr int GP = G < 4 ? 4 : G;  // padded weights row
-  __shared__ __align__(16) float p_lds[DEC_WAVES][16 * GP];
-  __shared__ __align__(16) float a_lds[DEC_WAVES][GP];
-  __shared__ __align__(16) float m_lds[DEC_WAVES][G][2];
-  __shared__ __align__(16) float o_lds[DEC_WAVES][G][D];
+// the two 16-bit halves (sel: low halves 0x05040100, high halves 0x07060302)
+// of a and b -> one bf16 pair {a, b}
+__device__ __forceinline__ uint32_t pick16(uint32_t a, uint32_t b, uint32_t sel) {
+  return __builtin_amdgcn_perm(b, a, sel);
+}
 
-  const int split = blockIdx.x;
-  const int pair = blockIdx.y;
-  const int b = pair / Hkv, kvh = pair % Hkv;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int l16 = lane & 15, j4 = lane >> 4;
-  const int dq = lane % DQ, ts = lane / DQ;
-
-  // q^T as the MFMA B operand: lane l holds head l%16, dims 32*ks + 8*(l/16) .. +8
-  uint4 qf[KS];
-  {
-    const uint4* qs = reinterpret_cast<const uint4*>(q + ((int64_t)b * Hq + (int64_t)kvh * G) * D);
+// p (fp32, >= 0) -> bf16 hi part (truncation) and bf16 lo part p - hi; the
+// B fragment of P^T: k 0..3 = hi of the lane's 4 tokens, k 4..7 = lo
+__device__ __forceinline__ uint4 split_weights(const float p[4]) {
+  float lo[4];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = (l16 < G) ? qs[l16 * (D / 8) + ks * 4 + j4] : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < 4; ++i) lo[i] = p[i] - __uint_as_float(__float_as_uint(p[i]) & 0xffff0000u);
+  return make_uint4(pick16(__float_as_uint(p[0]), __float_as_uint(p[1]), 0x07060302u),
+                    pick16(__float_as_uint(p[2]), __float_as_uint(p[3]), 0x07060302u),
+                    pick16(__float_as_uint(lo[0]), __float_as_uint(lo[1]), 0x07060302u),
+                    pick16(__float_as_uint(lo[2]), __float_as_uint(lo[3]), 0x07060302u));
+}
+
+// Per-tile online softmax + PV shared by the bf16 and FP8 kernels.
+// sc: S^T accumulator (lane l: tokens 4*(l/16)+i of the tile, head l%16);
+// zscale: logit scale (log2 units); n_valid: tokens of the tile below seq_len
+// relative to this lane's first token; wscale: factor on the weights PV reads;
+// vt: this wave's V^T rows (already written, wave-synchronised).
+template <int NC>
+__device__ __forceinline__ void softmax_pv(const f32x4v& sc, float zscale, int n_valid,
+                                           float wscale, const uint2* vt, int l16, int j4,
+                                           float& m_run, float& l_run, f32x4v* acc) {
+  float z[4];
+  float bm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    z[i] = (i < n_valid) ? sc[i] * zscale : -INFINITY;
+    bm = fmaxf(bm, z[i]);
   }
-
-  const int blk0 = split * bps;
-  int nblk = min(n_keep, blk0 + bps) - blk0;
-  const int32_t* list = idx + (int64_t)pair * n_keep + blk0;
-  // a list may end in -1 (absent entries of an adaptive selection): this
-  // split's blocks are its valid prefix (one scalar load when the run is full)
-  if (nblk > 0 && list[nblk - 1] < 0) {
-    int nv = 0;
-    while (nv < nblk && list[nv] >= 0) ++nv;
-    nblk = nv;
-  }
-  const char* kb = reinterpret_cast<const char*>(k + (int64_t)pair * stride * D);
-  const char* vb = reinterpret_cast<const char*>(v + (int64_t)pair * stride * D);
-  const int tile0 = 16 * wave;  // this wave's 16 tokens of every block
-
-  float m_run = -INFINITY, l_run = 0.f;  // head l16 over this lane's tokens
-  float acc[G][4];
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  // the 4 lanes of a head agree on bm and m_run, so on grow
+  const bool grow = bm > m_run + DEC_RESCALE_LOG2;
+  if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
+    const float m_new = grow ? bm : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 from -inf, 1 if kept
 #pragma unroll
-  for (int h = 0; h < G; ++h) acc[h][0] = acc[h][1] = acc[h][2] = acc[h][3] = 0.f;
-
-  // register pipeline: P blocks in flight per wave (K tile + V tile)
-  uint4 kbuf[P][KS];
-  uint2 vbuf[P][TPL];
-  // j >= nblk issues a dummy load (every lane reads the pair's first row) so
-  // the pipeline never branches around its loads
-  auto issue = [&](int slot, int j) {
-    const bool real = j < nblk;
-    const int t0 = list[real ? j : 0] * 64 + tile0;
-    const uint32_t koff =
-        real ? (uint32_t)min(t0 + l16, N - 1) * (D * 2) + j4 * 16 : 0u;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kbuf[slot][ks] = ld_stream(reinterpret_cast<const uint4*>(kb + koff + (real ? ks * 64 : 0)));
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      const uint32_t voff =
-          real ? (uint32_t)min(t0 + ts + VT * i, N - 1) * (D * 2) + dq * 8 : 0u;
-      vbuf[slot][i] = ld_stream(reinterpret_cast<const uint2*>(vb + voff));
-    }
-  };
-  float* pl = p_lds[wave];
-  auto compute = [&](int slot, int j) {
-    const int t0 = list[j] * 64 + tile0;
-    // S^T tile: lane l gets tokens 4*(l/16) + i of the tile, head l%16
-    f32x4v sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kbuf[slot][ks]), as_bf16x8(qf[ks]),
-                                                   sc, 0, 0, 0);
-    float z[4];
-    float bm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = (t0 + 4 * j4 + i < N) ? sc[i] * scale_log2 : -INFINITY;
-      bm = fmaxf(bm, z[i]);
-    }
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float m_new = fmaxf(m_run, bm);
-    // a tile past seq_len has no valid token: keep everything at zero
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    for (int c = 0; c < NC; ++c) acc[c] *= alpha;
+    l_run *= alpha;
     m_run = m_new;
-    float ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = __builtin_amdgcn_exp2f(z[i] - m_use);
-      ps += p;
-      if (l16 < G) pl[(4 * j4 + i) * GP + l16] = p;
-    }
-    l_run = l_run * alpha + ps;
-    if (j4 == 0 && l16 < G) a_lds[wave][l16] = alpha;
-    wave_lds_sync();
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float al = a_lds[wave][h];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[h][c] *= al;
-    }
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      const float vv[4] = {bf_lo(vbuf[slot][i].x), bf_hi(vbuf[slot][i].x),
-                           bf_lo(vbuf[slot][i].y), bf_hi(vbuf[slot][i].y)};
-      const float* prow = pl + (ts + VT * i) * GP;
-#pragma unroll
-      for (int h4 = 0; h4 < G; h4 += 4) {
-        const float4 pp = *reinterpret_cast<const float4*>(prow + h4);
-        const float pv[4] = {pp.x, pp.y, pp.z, pp.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (h4 + u < G) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[h4 + u][c] = fmaf(pv[u], vv[c], acc[h4 + u][c]);
-          }
-      }
-    }
-    wave_lds_sync();
-  };
-
-#pragma unroll
-  for (int s = 0; s < P - 1; ++s) issue(s, s);
-  for (int it = 0; it < nblk; it += P) {
-#pragma unroll
-    for (int s = 0; s < P; ++s) {
-      issue((s + P - 1) % P, it + s + P - 1);
-      if (it + s < nblk) compute(s, it + s);
-    }
   }
-
-  // per wave: l over the 4 lanes of a head; acc over the token subgroups
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+  float p[4];
+  float ps = 0.f;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int off = DQ; off < 64; off <<= 1)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[h][c] += __shfl_xor(acc[h][c], off);
-  if (ts == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      *reinterpret_cast<float4*>(&o_lds[wave][h][4 * dq]) =
-          make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+  for (int i = 0; i < 4; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(z[i] - m_use);
+    ps += p[i];
+    p[i] *= wscale;
   }
-  if (j4 == 0 && l16 < G) {
-    m_lds[wave][l16][0] = m_run;
-    m_lds[wave][l16][1] = l_run;
-  }
-  __syncthreads();
-  // merge the 4 waves: each holds a softmax partial over its quarter of every block
-  const int64_t pbase = ((int64_t)pair * n_splits + split) * G;
-  for (int e = tid; e < G * D; e += 256) {
-    const int h = e / D, c = e % D;
-    float M = -INFINITY;
+  l_run += ps;
+  const uint4 pb = split_weights(p);
 #pragma unroll
-    for (int w = 0; w < DEC_WAVES; ++w) M = fmaxf(M, m_lds[w][h][0]);
-    float o = 0.f, L = 0.f;
-#pragma unroll
-    for (int w = 0; w < DEC_WAVES; ++w) {
-      const float mw = m_lds[w][h][0];
-      const float sc = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-      o = fmaf(sc, o_lds[w][h][c], o);
-      L = fmaf(sc, m_lds[w][h][1], L);
-    }
-    part_o[(pbase + h) * D + c] = o;
-    if (c == 0) {
-      part_ml[(pbase + h) * 2 + 0] = M;
-      part_ml[(pbase + h) * 2 + 1] = L;
-    }
+  for (int c = 0; c < NC; ++c) {
+    const uint2 w = vt[vt_row(16 * c + l16) * 4 + j4];
+    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(make_uint4(w.x, w.y, w.x, w.y)),
+                                                     as_bf16x8(pb), acc[c], 0, 0, 0);
   }
 }
 
-// FP8 (OCP E4M3) cache variant of decode_kernel.  K and V rows are one byte
-// per value with one fp32 scale per (b, kv head, 64-token block) each; the
-// E4M3 values convert exactly to bf16 / fp32 (v_cvt_pk_f32_fp8), the K scale
-// multiplies the block's logits and the V scale the weights the PV step
-// reads, so the arithmetic is that of the bf16 kernel on the dequantized
-// cache.  Half the bytes per block, so P (blocks in flight) is one deeper.
-// The MFMA k order is permuted so a lane's 8*KS key bytes are contiguous:
-// lane l holds dims [8*KS*(l/16) + 8*ks, +8) of k-step ks, on both operands.
-template <int G> struct DecStagesFp8 { static constexpr int value = G >= 16 ? 2 : 4; };
-
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  // two E4M3 values (bytes 2*HI, 2*HI + 1 of w) -> two bf16 (exact: E4M3 fits bf16)
-  typedef float f2v __attribute__((ext_vector_type(2)));
-  const f2v f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-  return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xFFFF0000u);
-}
-
-template <int D, int G, int P>
-__global__ __launch_bounds__(256, 2) void decode_fp8_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
-    const float* __restrict__ ksc, const float* __restrict__ vsc, int sstride,
-    const int32_t* __restrict__ idx, int n_keep, int Hq, int Hkv, int N, int stride,
-    float scale_log2, int bps, int n_splits, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
-  constexpr int KS = D / 32;        // MFMA k-steps over the head dim
-  constexpr int KB = KS / 2;        // 16-byte key loads per lane per tile
-  constexpr int DQ = D / 4;         // 4-column groups per row: lane owns one group
-  constexpr int VT = 64 / DQ;       // token subgroups in the PV layout
-  constexpr int TPL = 16 / VT;      // tokens of the tile per lane (PV layout)
-  constexpr int GP = G < 4 ? 4 : G;
-  static_assert(KS % 2 == 0, "head dim a multiple of 64");
-  __shared__ __align__(16) float p_lds[DEC_WAVES][16 * GP];
-  __shared__ __align__(16) float a_lds[DEC_WAVES][GP];
-  __shared__ __align__(16) float m_lds[DEC_WAVES][G][2];
-  __shared__ __align__(16) float o_lds[DEC_WAVES][G][D];
-
-  const int split = blockIdx.x;
-  const int pair = blockIdx.y;
-  const int b = pair / Hkv, kvh = pair % Hkv;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15, j4 = lane >> 4;
-  const int dq = lane % DQ, ts = lane / DQ;
-
-  // q^T fragments in the permuted k order
-  uint4 qf[KS];
-  {
-    const uint4* qs = reinterpret_cast<const uint4*>(q + ((int64_t)b * Hq + (int64_t)kvh * G) * D);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = (l16 < G) ? qs[l16 * (D / 8) + j4 * KS + ks] : make_uint4(0, 0, 0, 0);
-  }
-
-  const int blk0 = split * bps;
-  int nblk = min(n_keep, blk0 + bps) - blk0;
-  const int32_t* list = idx + (int64_t)pair * n_keep + blk0;
-  if (nblk > 0 && list[nblk - 1] < 0) {  // a -1-padded (adaptive) list
-    int nv = 0;
-    while (nv < nblk && list[nv] >= 0) ++nv;
-    nblk = nv;
-  }
-  const uint8_t* kb = k + (int64_t)pair * stride * D;
-  const uint8_t* vb = v + (int64_t)pair * stride * D;
-  const float* ks_row = ksc + (int64_t)pair * sstride;
-  const float* vs_row = vsc + (int64_t)pair * sstride;
-  const int tile0 = 16 * wave;
-
-  float m_run = -INFINITY, l_run = 0.f;
-  float acc[G][4];
-#pragma unroll
-  for (int h = 0; h < G; ++h) acc[h][0] = acc[h][1] = acc[h][2] = acc[h][3] = 0.f;
-
-  uint4 kbuf[P][KB];
-  uint32_t vbuf[P][TPL];
-  float skb[P], svb[P];
-  auto issue = [&](int slot, int j) {
-    const bool real = j < nblk;
-    const int blk = list[real ? j : 0];
-    const int t0 = blk * 64 + tile0;
-    const uint32_t koff = real ? (uint32_t)min(t0 + l16, N - 1) * D + j4 * (8 * KS) : 0u;
-#pragma unroll
-    for (int u = 0; u < KB; ++u)
-      kbuf[slot][u] = ld_stream(reinterpret_cast<const uint4*>(kb + koff) + (real ? u : 0));
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      const uint32_t voff = real ? (uint32_t)min(t0 + ts + VT * i, N - 1) * D + dq * 4 : 0u;
-      vbuf[slot][i] = *reinterpret_cast<const uint32_t*>(vb + voff);
-    }
-    skb[slot] = ks_row[blk];
-    svb[slot] = vs_row[blk];
-  };
-  float* pl = p_lds[wave];
-  auto compute = [&](int slot, int j) {
-    const int t0 = list[j] * 64 + tile0;
-    f32x4v sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 w = kbuf[slot][ks / 2];
-      const uint32_t lo = (ks & 1) ? w.z : w.x, hi = (ks & 1) ? w.w : w.y;
-      const uint4 kk = make_uint4(fp8x2_to_bf16x2<false>(lo), fp8x2_to_bf16x2<true>(lo),
-                                  fp8x2_to_bf16x2<false>(hi), fp8x2_to_bf16x2<true>(hi));
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk), as_bf16x8(qf[ks]), sc, 0, 0, 0);
-    }
-    const float zs = scale_log2 * skb[slot];  // the block's K scale folds into the logits
-    float z[4];
-    float bm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = (t0 + 4 * j4 + i < N) ? sc[i] * zs : -INFINITY;
-      bm = fmaxf(bm, z[i]);
-    }
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float m_new = fmaxf(m_run, bm);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    float ps = 0.f;
-    const float sv = svb[slot];  // the block's V scale folds into the weights PV reads
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = __builtin_amdgcn_exp2f(z[i] - m_use);
-      ps += p;
-      if (l16 < G) pl[(4 * j4 + i) * GP + l16] = p * sv;
-    }
-    l_run = l_run * alpha + ps;
-    if (j4 == 0 && l16 < G) a_lds[wave][l16] = alpha;
-    wave_lds_sync();
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float al = a_lds[wave][h];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[h][c] *= al;
-    }
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      typedef float f2v __attribute__((ext_vector_type(2)));
-      const f2v v01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vbuf[slot][i], false);
-      const f2v v23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vbuf[slot][i], true);
-      const float vv[4] = {v01.x, v01.y, v23.x, v23.y};
-      const float* prow = pl + (ts + VT * i) * GP;
-#pragma unroll
-      for (int h4 = 0; h4 < G; h4 += 4) {
-        const float4 pp = *reinterpret_cast<const float4*>(prow + h4);
-        const float pv[4] = {pp.x, pp.y, pp.z, pp.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (h4 + u < G) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[h4 + u][c] = fmaf(pv[u], vv[c], acc[h4 + u][c]);
-          }
-      }
-    }
-    wave_lds_sync();
-  };
-
-#pragma unroll
-  for (int s = 0; s < P - 1; ++s) issue(s, s);
-  for (int it = 0; it < nblk; it += P) {
-#pragma unroll
-    for (int s = 0; s < P; ++s) {
-      issue((s + P - 1) % P, it + s + P - 1);
-      if (it + s < nblk) compute(s, it + s);
-    }
-  }
-
+// Per wave: (m, l) over the tile lanes of a head, o^T from the accumulators,
+// then the 4 waves merge into the split's partial.
+template <int D, int G>
+__device__ __forceinline__ void decode_finish(float m_run, float l_run, const f32x4v* acc,
+                                              float (*m_lds)[G][2], float (*o_lds)[G][D],
+                                              int wave, int tid, int64_t pbase,
+                                              float* __restrict__ part_o,
+                                              float* __restrict__ part_ml) {
+  constexpr int NC = D / 16;
+  const int lane = tid & 63, l16 = lane & 15, j4 = lane >> 4;
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
+  if (l16 < G) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int off = DQ; off < 64; off <<= 1)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[h][c] += __shfl_xor(acc[h][c], off);
-  if (ts == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      *reinterpret_cast<float4*>(&o_lds[wave][h][4 * dq]) =
-          make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-  }
-  if (j4 == 0 && l16 < G) {
-    m_lds[wave][l16][0] = m_run;
-    m_lds[wave][l16][1] = l_run;
+    for (int c = 0; c < NC; ++c)
+      *reinterpret_cast<float4*>(&o_lds[wave][l16][16 * c + 4 * j4]) =
+          make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+    if (j4 == 0) {
+      m_lds[wave][l16][0] = m_run;
+      m_lds[wave][l16][1] = l_run;
+    }
   }
   __syncthreads();
-  const int64_t pbase = ((int64_t)pair * n_splits + split) * G;
   for (int e = tid; e < G * D; e += 256) {
     const int h = e / D, c = e % D;
     float M = -INFINITY;
@@ -436,6 +161,258 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_kernel(
       part_ml[(pbase + h) * 2 + 1] = L;
     }
   }
+}
+
+// The kept-block run of this split; a list may end in -1 (absent entries of
+// an adaptive selection): the split's blocks are its valid prefix (one scalar
+// load when the run is full).
+__device__ __forceinline__ int split_blocks(const int32_t* list, int n_keep, int blk0, int bps) {
+  int nblk = min(n_keep, blk0 + bps) - blk0;
+  if (nblk > 0 && list[nblk - 1] < 0) {
+    int nv = 0;
+    while (nv < nblk && list[nv] >= 0) ++nv;
+    nblk = nv;
+  }
+  return nblk;
+}
+
+// blocks in flight per wave (register budget: two waves per SIMD)
+constexpr int DEC_STAGES = 3;
+constexpr int DEC_STAGES_FP8 = 4;
+
+template <int D, int G, int P>
+__global__ __launch_bounds__(256, 2) void decode_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, int n_keep, int Hq, int Hkv,
+    int N, int stride, float scale_log2, int bps, int n_splits, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  constexpr int KS = D / 32;  // QK k-steps over the head dim
+  constexpr int NB = D / 64;  // 64-column blocks of a V row (16 lanes x 4 columns)
+  constexpr int NC = D / 16;  // PV column chunks
+  static_assert(G <= 16 && D % 64 == 0, "16 heads per MFMA tile, head dim a multiple of 64");
+  __shared__ __align__(16) uint2 vt_lds[DEC_WAVES][D * 4];
+  __shared__ __align__(16) float m_lds[DEC_WAVES][G][2];
+  __shared__ __align__(16) float o_lds[DEC_WAVES][G][D];
+
+  const int split = blockIdx.x;
+  const int pair = blockIdx.y;
+  const int b = pair / Hkv, kvh = pair % Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int l16 = lane & 15, j4 = lane >> 4;
+
+  // q^T as the MFMA B operand: lane l holds head l%16, dims 32*ks + 8*(l/16) .. +8
+  uint4 qf[KS];
+  {
+    const uint4* qs = reinterpret_cast<const uint4*>(q + ((int64_t)b * Hq + (int64_t)kvh * G) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = (l16 < G) ? qs[l16 * (D / 8) + ks * 4 + j4] : make_uint4(0, 0, 0, 0);
+  }
+
+  const int blk0 = split * bps;
+  const int32_t* list = idx + (int64_t)pair * n_keep + blk0;
+  const int nblk = split_blocks(list, n_keep, blk0, bps);
+  const char* kb = reinterpret_cast<const char*>(k + (int64_t)pair * stride * D);
+  const char* vb = reinterpret_cast<const char*>(v + (int64_t)pair * stride * D);
+  const int tile0 = 16 * wave;  // this wave's 16 tokens of every block
+
+  float m_run = -INFINITY, l_run = 0.f;  // head l16
+  f32x4v acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = f32x4v{0.f, 0.f, 0.f, 0.f};
+
+  // register pipeline: K fragments (lane: token l16, bytes 16*j4 of each
+  // 64-byte k-step) and V rows 4*j4 + r, columns 64*nb + 4*l16 .. +3
+  uint4 kbuf[P][KS];
+  uint2 vbuf[P][NB][4];
+  // j >= nblk issues a dummy load (every lane reads the pair's first row) so
+  // the pipeline never branches around its loads
+  auto issue = [&](int slot, int j) {
+    const bool real = j < nblk;
+    const int t0 = list[real ? j : 0] * 64 + tile0;
+    const uint32_t koff = real ? (uint32_t)min(t0 + l16, N - 1) * (D * 2) + j4 * 16 : 0u;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kbuf[slot][ks] = ld_stream(reinterpret_cast<const uint4*>(kb + koff + (real ? ks * 64 : 0)));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t voff = real ? (uint32_t)min(t0 + 4 * j4 + r, N - 1) * (D * 2) + l16 * 8 : 0u;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        vbuf[slot][nb][r] = ld_stream(reinterpret_cast<const uint2*>(vb + voff + (real ? nb * 128 : 0)));
+    }
+  };
+  uint2* vt = vt_lds[wave];
+  auto compute = [&](int slot, int j) {
+    const int t0 = list[j] * 64 + tile0;
+    f32x4v sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kbuf[slot][ks]), as_bf16x8(qf[ks]),
+                                                   sc, 0, 0, 0);
+    // V^T: lane (j4, l16) holds tokens 4*j4 .. +3 x columns 64*nb + 4*l16 .. +3
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
+        const uint2* rw = vbuf[slot][nb];
+        const uint32_t w0 = (d < 2) ? rw[0].x : rw[0].y, w1 = (d < 2) ? rw[1].x : rw[1].y;
+        const uint32_t w2 = (d < 2) ? rw[2].x : rw[2].y, w3 = (d < 2) ? rw[3].x : rw[3].y;
+        vt[vt_row(64 * nb + 4 * l16 + d) * 4 + j4] = make_uint2(pick16(w0, w1, sel), pick16(w2, w3, sel));
+      }
+    wave_lds_sync();
+    softmax_pv<NC>(sc, scale_log2, N - (t0 + 4 * j4), 1.f, vt, l16, j4, m_run, l_run, acc);
+    wave_lds_sync();  // the next tile's V^T writes follow this tile's reads
+  };
+
+#pragma unroll
+  for (int s = 0; s < P - 1; ++s) issue(s, s);
+  for (int it = 0; it < nblk; it += P) {
+#pragma unroll
+    for (int s = 0; s < P; ++s) {
+      issue((s + P - 1) % P, it + s + P - 1);
+      if (it + s < nblk) compute(s, it + s);
+    }
+  }
+  decode_finish<D, G>(m_run, l_run, acc, m_lds, o_lds, wave, tid,
+                      ((int64_t)pair * n_splits + split) * G, part_o, part_ml);
+}
+
+// FP8 (OCP E4M3) cache variant of decode_kernel.  K and V rows are one byte
+// per value with one fp32 scale per (b, kv head, 64-token block) each; the
+// E4M3 values convert exactly to bf16 (v_cvt_pk_f32_fp8, then the upper
+// halves), the K scale multiplies the block's logits and the V scale the
+// weights PV reads, so the arithmetic is that of the bf16 kernel on the
+// dequantized cache.  Half the bytes per block, so P is one deeper.  The QK
+// k order is permuted so a lane's 8*KS key bytes are contiguous: lane l holds
+// dims [8*KS*(l/16) + 8*ks, +8) of k-step ks, on both operands.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  // two E4M3 values (bytes 2*HI, 2*HI + 1 of w) -> two bf16 (exact: E4M3 fits bf16)
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  const f2v f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  return pick16(__float_as_uint(f.x), __float_as_uint(f.y), 0x07060302u);
+}
+
+template <int D, int G, int P>
+__global__ __launch_bounds__(256, 2) void decode_fp8_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+    const float* __restrict__ ksc, const float* __restrict__ vsc, int sstride,
+    const int32_t* __restrict__ idx, int n_keep, int Hq, int Hkv, int N, int stride,
+    float scale_log2, int bps, int n_splits, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  constexpr int KS = D / 32;  // QK k-steps over the head dim
+  constexpr int KB = KS / 2;  // 16-byte key loads per lane per tile
+  constexpr int VW = D / 64;  // 4-byte words of a V row per lane (16 lanes span the row)
+  constexpr int NC = D / 16;
+  static_assert(G <= 16 && D % 64 == 0, "16 heads per MFMA tile, head dim a multiple of 64");
+  __shared__ __align__(16) uint2 vt_lds[DEC_WAVES][D * 4];
+  __shared__ __align__(16) float m_lds[DEC_WAVES][G][2];
+  __shared__ __align__(16) float o_lds[DEC_WAVES][G][D];
+
+  const int split = blockIdx.x;
+  const int pair = blockIdx.y;
+  const int b = pair / Hkv, kvh = pair % Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, j4 = lane >> 4;
+
+  // q^T fragments in the permuted k order
+  uint4 qf[KS];
+  {
+    const uint4* qs = reinterpret_cast<const uint4*>(q + ((int64_t)b * Hq + (int64_t)kvh * G) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = (l16 < G) ? qs[l16 * (D / 8) + j4 * KS + ks] : make_uint4(0, 0, 0, 0);
+  }
+
+  const int blk0 = split * bps;
+  const int32_t* list = idx + (int64_t)pair * n_keep + blk0;
+  const int nblk = split_blocks(list, n_keep, blk0, bps);
+  const uint8_t* kb = k + (int64_t)pair * stride * D;
+  const uint8_t* vb = v + (int64_t)pair * stride * D;
+  const float* ks_row = ksc + (int64_t)pair * sstride;
+  const float* vs_row = vsc + (int64_t)pair * sstride;
+  const int tile0 = 16 * wave;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4v acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = f32x4v{0.f, 0.f, 0.f, 0.f};
+
+  // K: token l16, bytes 8*KS*j4 .. ; V: rows 4*j4 + r, bytes 4*VW*l16 .. +4*VW
+  uint4 kbuf[P][KB];
+  uint32_t vbuf[P][4][VW];
+  float skb[P], svb[P];
+  auto issue = [&](int slot, int j) {
+    const bool real = j < nblk;
+    const int blk = list[real ? j : 0];
+    const int t0 = blk * 64 + tile0;
+    const uint32_t koff = real ? (uint32_t)min(t0 + l16, N - 1) * D + j4 * (8 * KS) : 0u;
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+      kbuf[slot][u] = ld_stream(reinterpret_cast<const uint4*>(kb + koff) + (real ? u : 0));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t voff = real ? (uint32_t)min(t0 + 4 * j4 + r, N - 1) * D + l16 * (4 * VW) : 0u;
+      if constexpr (VW == 2) {
+        const uint2 w = ld_stream(reinterpret_cast<const uint2*>(vb + voff));
+        vbuf[slot][r][0] = w.x;
+        vbuf[slot][r][1] = w.y;
+      } else {
+        vbuf[slot][r][0] = *reinterpret_cast<const uint32_t*>(vb + voff);
+      }
+    }
+    skb[slot] = ks_row[blk];
+    svb[slot] = vs_row[blk];
+  };
+  uint2* vt = vt_lds[wave];
+  auto compute = [&](int slot, int j) {
+    const int t0 = list[j] * 64 + tile0;
+    f32x4v sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 w = kbuf[slot][ks / 2];
+      const uint32_t lo = (ks & 1) ? w.z : w.x, hi = (ks & 1) ? w.w : w.y;
+      const uint4 kk = make_uint4(fp8x2_to_bf16x2<false>(lo), fp8x2_to_bf16x2<true>(lo),
+                                  fp8x2_to_bf16x2<false>(hi), fp8x2_to_bf16x2<true>(hi));
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk), as_bf16x8(qf[ks]), sc, 0, 0, 0);
+    }
+    // V^T: per pair of columns (2p, 2p+1) of a word, gather the 4 tokens'
+    // bytes (tokens 0,1 and 2,3), then decode each byte pair to a bf16 pair
+#pragma unroll
+    for (int w = 0; w < VW; ++w)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const uint32_t sel = pp ? 0x07030602u : 0x05010400u;
+        const uint32_t t01 = __builtin_amdgcn_perm(vbuf[slot][1][w], vbuf[slot][0][w], sel);
+        const uint32_t t23 = __builtin_amdgcn_perm(vbuf[slot][3][w], vbuf[slot][2][w], sel);
+        const int col = 4 * (VW * l16 + w) + 2 * pp;
+        vt[vt_row(col) * 4 + j4] =
+            make_uint2(fp8x2_to_bf16x2<false>(t01), fp8x2_to_bf16x2<false>(t23));
+        vt[vt_row(col + 1) * 4 + j4] =
+            make_uint2(fp8x2_to_bf16x2<true>(t01), fp8x2_to_bf16x2<true>(t23));
+      }
+    wave_lds_sync();
+    // the block's K scale folds into the logits, its V scale into the weights
+    softmax_pv<NC>(sc, scale_log2 * skb[slot], N - (t0 + 4 * j4), svb[slot], vt, l16, j4, m_run,
+                   l_run, acc);
+    wave_lds_sync();
+  };
+
+#pragma unroll
+  for (int s = 0; s < P - 1; ++s) issue(s, s);
+  for (int it = 0; it < nblk; it += P) {
+#pragma unroll
+    for (int s = 0; s < P; ++s) {
+      issue((s + P - 1) % P, it + s + P - 1);
+      if (it + s < nblk) compute(s, it + s);
+    }
+  }
+  decode_finish<D, G>(m_run, l_run, acc, m_lds, o_lds, wave, tid,
+                      ((int64_t)pair * n_splits + split) * G, part_o, part_ml);
 }
 
 // Exact merge of the splits of one (batch, query head): M = max m_s,
@@ -524,7 +501,7 @@ static void launch_decode_t(const uint16_t* q, const uint16_t* k, const uint16_t
   float* part_ml = ws;
   float* part_o = part_ml + (size_t)pairs * plan.n_splits * G * 2;
   dim3 grid(plan.n_splits, (unsigned)pairs);
-  decode_kernel<D, G, DecStages<G>::value><<<grid, 256, 0, st>>>(
+  decode_kernel<D, G, DEC_STAGES><<<grid, 256, 0, st>>>(
       q, k, v, idx, n_keep, Hq, Hkv, N, stride, scale * LOG2E, plan.bps, plan.n_splits, part_o,
       part_ml);
   decode_merge_kernel<D><<<(unsigned)(B * Hq), D, 0, st>>>(part_o, part_ml, G, Hq, Hkv,
@@ -541,7 +518,7 @@ static void launch_decode_fp8_t(const uint16_t* q, const uint8_t* k, const uint8
   float* part_ml = ws;
   float* part_o = part_ml + (size_t)pairs * plan.n_splits * G * 2;
   dim3 grid(plan.n_splits, (unsigned)pairs);
-  decode_fp8_kernel<D, G, DecStagesFp8<G>::value><<<grid, 256, 0, st>>>(
+  decode_fp8_kernel<D, G, DEC_STAGES_FP8><<<grid, 256, 0, st>>>(
       q, k, v, ksc, vsc, sstride, idx, n_keep, Hq, Hkv, N, stride, scale * LOG2E, plan.bps,
       plan.n_splits, part_o, part_ml);
   decode_merge_kernel<D><<<(unsigned)(B * Hq), D, 0, st>>>(part_o, part_ml, G, Hq, Hkv,
