@@ -228,6 +228,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
   uint2 vbuf[P][NB][4];
   // j >= nblk issues a dummy load (every lane reads the pair's first row) so
   // the pipeline never branches around its loads
+  // j >= nblk issues a dummy load (every lane reads the pair's first row) so
+  // the pipeline never branches around its loads
   auto issue = [&](int slot, int j) {
     const bool real = j < nblk;
     const int t0 = list[real ? j : 0] * 64 + tile0;
@@ -346,17 +348,25 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_kernel(
   uint4 kbuf[P][KB];
   uint32_t vbuf[P][4][VW];
   float skb[P], svb[P];
+  // Dummy loads (j >= nblk) use block 0's scales and a K/V offset masked to
+  // an opaque lane-varying zero, computed without a branch: with a provably
+  // uniform address the compiler turns the dummy into a scalar load on a
+  // path of its own, and the wait counts after the merge then keep too few
+  // tiles in flight.
+  int vzero = 0;
+  asm volatile("" : "+v"(vzero));
   auto issue = [&](int slot, int j) {
-    const bool real = j < nblk;
-    const int blk = list[real ? j : 0];
+    const uint32_t m = (j < nblk) ? 0xffffffffu : 0u;  // uniform
+    const int blk = list[max(min(j, nblk - 1), 0)] & (int)m;
     const int t0 = blk * 64 + tile0;
-    const uint32_t koff = real ? (uint32_t)min(t0 + l16, N - 1) * D + j4 * (8 * KS) : 0u;
+    const uint32_t koff = (((uint32_t)min(t0 + l16, N - 1) * D + j4 * (8 * KS)) & m) + vzero;
 #pragma unroll
     for (int u = 0; u < KB; ++u)
-      kbuf[slot][u] = ld_stream(reinterpret_cast<const uint4*>(kb + koff) + (real ? u : 0));
+      kbuf[slot][u] = ld_stream(reinterpret_cast<const uint4*>(kb + koff + ((u * 16) & m)));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint32_t voff = real ? (uint32_t)min(t0 + 4 * j4 + r, N - 1) * D + l16 * (4 * VW) : 0u;
+      const uint32_t voff =
+          (((uint32_t)min(t0 + 4 * j4 + r, N - 1) * D + l16 * (4 * VW)) & m) + vzero;
       if constexpr (VW == 2) {
         const uint2 w = ld_stream(reinterpret_cast<const uint2*>(vb + voff));
         vbuf[slot][r][0] = w.x;
@@ -365,8 +375,11 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_kernel(
         vbuf[slot][r][0] = *reinterpret_cast<const uint32_t*>(vb + voff);
       }
     }
-    skb[slot] = ks_row[blk];
-    svb[slot] = vs_row[blk];
+    // vector loads (the opaque zero keeps them off the scalar unit): they
+    // retire in order with this tile's K/V loads, whereas a scalar load
+    // would make every later LDS wait also wait for it
+    skb[slot] = ks_row[blk + vzero];
+    svb[slot] = vs_row[blk + vzero];
   };
   uint2* vt = vt_lds[wave];
   auto compute = [&](int slot, int j) {

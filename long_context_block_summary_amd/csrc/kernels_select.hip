@@ -238,11 +238,12 @@ void launch_append(const uint16_t* src, uint16_t* dst, int64_t pairs, int n_new,
 }
 
 // ---------------------------------------------------------------------------
-// Scores.  The pooled query qbar (fp32 sum over the group's query heads, in
-// head order) is built in LDS by each workgroup; 16 lanes share one summary
-// row (512 B for d=128) and reduce their partial dot products with DPP inside
-// the row.  Grid: (row chunks, pairs) so that even 8 pairs spread over the
-// whole chip.
+// Scores.  16 lanes share one summary row (512 B for d=128) and reduce their
+// partial dot products with DPP inside the row; each lane builds the pooled
+// query qbar (fp32 sum over the group's query heads, in head order) for its
+// own dims, so there is no LDS and no barrier, and all of a workgroup's
+// summary loads are issued before anything waits.  Grid: (row chunks,
+// pairs) so that even 8 pairs spread over the whole chip.
 constexpr int SCORE_ROWS_PER_WG = 64;
 
 template <int D>
@@ -250,38 +251,50 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
                                                      const float* __restrict__ summ, int Hq,
                                                      int Hkv, int nb, int sstride, int c0, int c1,
                                                      float* __restrict__ scores) {
-  constexpr int PER = D / 16;  // floats per lane
-  __shared__ float qbar[D];
+  constexpr int PER = D / 16;                       // floats of a row per lane
+  constexpr int PASSES = SCORE_ROWS_PER_WG / 16;    // 16 rows per pass of 256 threads
   const int pair = blockIdx.y;
   const int b = pair / Hkv, kvh = pair % Hkv, g = Hq / Hkv;
-  const int tid = threadIdx.x;
-  if (tid < D) {
-    const uint16_t* qh = q + ((int64_t)b * Hq + (int64_t)kvh * g) * D + tid;
-    float s = 0.f;
-    for (int h = 0; h < g; ++h) s += __uint_as_float((uint32_t)qh[(int64_t)h * D] << 16);
-    qbar[tid] = s;
-  }
-  __syncthreads();
-  const int l16 = tid & 15;
-  float qv[PER];
-#pragma unroll
-  for (int c = 0; c < PER; ++c) qv[c] = qbar[l16 * PER + c];
+  const int tid = threadIdx.x, l16 = tid & 15;
   const int r0 = c0 + blockIdx.x * SCORE_ROWS_PER_WG;
   const int r1 = min(c1, r0 + SCORE_ROWS_PER_WG);
-  const float* base = summ + (int64_t)pair * sstride * D;
-  for (int r = r0 + (tid >> 4); r < r1; r += 16) {
-    const float4* row = reinterpret_cast<const float4*>(base + (int64_t)r * D + l16 * PER);
-    float s = 0.f;
+  const float* base = summ + (int64_t)pair * sstride * D + l16 * PER;
+  // every summary load is in flight before the query is read (rows past r1
+  // re-read row r1 - 1 and are not stored)
+  float4 w[PASSES][PER / 4];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int r = min(r0 + (tid >> 4) + 16 * p, r1 - 1);
+#pragma unroll
+    for (int c = 0; c < PER / 4; ++c)
+      w[p][c] = ld_stream(reinterpret_cast<const float4*>(base + (int64_t)r * D) + c);
+  }
+  // pooled query over the g heads of the group, this lane's PER dims
+  float qv[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) qv[c] = 0.f;
+  const uint16_t* qh = q + ((int64_t)b * Hq + (int64_t)kvh * g) * D + l16 * PER;
+  for (int h = 0; h < g; ++h) {
+#pragma unroll
+    for (int c = 0; c < PER; c += 2) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(qh + (int64_t)h * D + c);
+      qv[c] += bf_lo(u);
+      qv[c + 1] += bf_hi(u);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    float sc = 0.f;
 #pragma unroll
     for (int c = 0; c < PER / 4; ++c) {
-      float4 w = ld_stream(row + c);
-      s = fmaf(qv[4 * c + 0], w.x, s);
-      s = fmaf(qv[4 * c + 1], w.y, s);
-      s = fmaf(qv[4 * c + 2], w.z, s);
-      s = fmaf(qv[4 * c + 3], w.w, s);
+      sc = fmaf(qv[4 * c + 0], w[p][c].x, sc);
+      sc = fmaf(qv[4 * c + 1], w[p][c].y, sc);
+      sc = fmaf(qv[4 * c + 2], w[p][c].z, sc);
+      sc = fmaf(qv[4 * c + 3], w[p][c].w, sc);
     }
-    s = row16_sum(s);
-    if (l16 == 0) scores[(int64_t)pair * nb + r] = s;
+    sc = row16_sum(sc);
+    const int r = r0 + (tid >> 4) + 16 * p;
+    if (l16 == 0 && r < r1) scores[(int64_t)pair * nb + r] = sc;
   }
 }
 
@@ -301,9 +314,14 @@ void launch_scores(const uint16_t* q, const float* summ, int B, int Hq, int Hkv,
 // 1. Radix select over order-preserving uint32 keys, 8 bits per pass with a
 //    256-bin LDS histogram, finds T = the k-th largest key and how many keys
 //    equal to T must be taken (the ones with the lowest block index).
-// 2. An ordered compaction in index order (ballot + mbcnt inside a wave,
-//    wave offsets through LDS) writes the kept candidates ascending, so the
-//    output list (sink, selected, local) is sorted with no extra sort.
+// 2. An ordered compaction in index order writes the kept candidates
+//    ascending, so the output list (sink, selected, local) is sorted with no
+//    extra sort.
+// Up to 16384 candidates (topk_reg_kernel) each thread keeps a contiguous run
+// of KPT candidates in registers for the whole select: one read of the
+// scores, and the compaction is two block-wide scans of per-thread counts.
+// Longer lists use topk_kernel, which re-reads the scores (L2) every pass and
+// compacts in 1024-candidate strides.
 constexpr int TOPK_THREADS = 1024;
 constexpr int TOPK_WAVES = TOPK_THREADS / 64;
 
@@ -449,11 +467,164 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restr
   }
 }
 
+// block-wide exclusive prefix sum of x in thread order; sets *total.  Uses
+// wtot[TOPK_WAVES] of LDS (free again on return).
+__device__ __forceinline__ int block_scan(int x, int* wtot, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
+  }
+  if (lane == 63) wtot[wave] = inc;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < TOPK_WAVES; ++w) {
+    const int c = wtot[w];
+    off += (w < wave) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + inc - x;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(TOPK_THREADS) void topk_reg_kernel(const float* __restrict__ scores,
+                                                                int nb, int c0, int c1, int k,
+                                                                int n_keep, AdaptiveSel ad,
+                                                                int32_t* __restrict__ idx_out) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh_digit, sh_above;
+  __shared__ int wtot[TOPK_WAVES];
+  __shared__ float ext[2][TOPK_WAVES];
+  const int pair = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* s = scores + (int64_t)pair * nb + c0;
+  int32_t* out = idx_out + (int64_t)pair * n_keep;
+  const int n = c1 - c0;
+  const int i0 = tid * KPT;  // this thread's candidates [i0, i0 + KPT)
+  float sv[KPT];
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) sv[e] = (n > 0) ? s[min(i0 + e, n - 1)] : 0.f;
+  if (ad.on) {  // uniform
+    const float* all = scores + (int64_t)pair * nb;
+    float amax = -INFINITY, amin = INFINITY;
+    for (int i = tid; i < c0 + (nb - c1); i += TOPK_THREADS) {
+      const float a = all[i < c0 ? i : c1 + (i - c0)];
+      amax = fmaxf(amax, a);
+      amin = fminf(amin, a);
+    }
+    amax = wave_max(amax);
+    amin = -wave_max(-amin);
+    if ((tid & 63) == 0) {
+      ext[0][tid >> 6] = amax;
+      ext[1][tid >> 6] = amin;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < TOPK_WAVES; ++w) {
+      amax = fmaxf(amax, ext[0][w]);
+      amin = fminf(amin, ext[1][w]);
+    }
+    const float tau = (c0 + (nb - c1) > 0) ? amax + ad.margin * (amax - amin) : -INFINITY;
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) cnt += (i0 + e < n && sv[e] > tau) ? 1 : 0;
+    block_scan(cnt, wtot, &cnt);
+    k = min(max(cnt, ad.k_lo), ad.k_hi);
+    for (int i = c0 + k + (nb - c1) + tid; i < n_keep; i += TOPK_THREADS) out[i] = -1;  // absent
+  }
+  for (int i = tid; i < c0; i += TOPK_THREADS) out[i] = i;                 // sink
+  for (int i = tid; i < nb - c1; i += TOPK_THREADS) out[c0 + k + i] = c1 + i;  // local
+  if (k <= 0) return;
+  if (k >= n) {
+    for (int i = tid; i < n; i += TOPK_THREADS) out[c0 + i] = c0 + i;
+    return;
+  }
+  uint32_t key[KPT];
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) key[e] = order_key(sv[e]);
+  uint32_t prefix = 0;
+  uint32_t remaining = (uint32_t)k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+      const bool match = i0 + e < n && (pass == 0 || ((key[e] ^ prefix) >> (shift + 8)) == 0);
+      if (match) atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns bins 255-4l .. 252-4l (descending order)
+      const int lane = tid;
+      uint32_t c[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = hist[255 - 4 * lane - e];
+      const uint32_t own = c[0] + c[1] + c[2] + c[3];
+      uint32_t inc = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t t = __shfl_up(inc, off);
+        if (lane >= off) inc += t;
+      }
+      const uint32_t exc = inc - own;
+      if (exc < remaining && remaining <= inc) {
+        uint32_t acc = exc;
+        for (int e = 0; e < 4; ++e) {
+          if (acc + c[e] >= remaining) {
+            sh_digit = (uint32_t)(255 - 4 * lane - e);
+            sh_above = acc;
+            break;
+          }
+          acc += c[e];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= sh_digit << shift;
+    remaining -= sh_above;
+  }
+  // T = prefix: keys above T are all taken, plus the first `remaining` keys
+  // equal to T in index order
+  const uint32_t T = prefix;
+  int n_eq = 0;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) n_eq += (i0 + e < n && key[e] == T) ? 1 : 0;
+  int tot;
+  int eq_rank = block_scan(n_eq, wtot, &tot);
+  int n_sel = 0;
+  bool sel[KPT];
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    const bool valid = i0 + e < n;
+    const bool eq = valid && key[e] == T;
+    sel[e] = valid && (key[e] > T || (eq && eq_rank < (int)remaining));
+    eq_rank += eq ? 1 : 0;
+    n_sel += sel[e] ? 1 : 0;
+  }
+  int pos = c0 + block_scan(n_sel, wtot, &tot);
+#pragma unroll
+  for (int e = 0; e < KPT; ++e)
+    if (sel[e]) out[pos++] = c0 + i0 + e;
+}
+
 void launch_topk(const float* scores, int64_t pairs, int nb, int c0, int c1, int k, int n_keep,
                  int32_t* idx_out, hipStream_t st, bool adaptive, int k_lo, int k_hi,
                  float margin) {
   if (pairs <= 0) return;
   AdaptiveSel ad{adaptive ? 1 : 0, k_lo, k_hi, margin};
+  const int n = c1 - c0;
+#define BSA_TOPK_REG(KK)                                                                    \
+  if (n <= TOPK_THREADS * KK)                                                               \
+    return topk_reg_kernel<KK><<<(unsigned)pairs, TOPK_THREADS, 0, st>>>(scores, nb, c0, c1, \
+                                                                        k, n_keep, ad, idx_out);
+  BSA_TOPK_REG(1) BSA_TOPK_REG(2) BSA_TOPK_REG(4) BSA_TOPK_REG(8) BSA_TOPK_REG(16)
+#undef BSA_TOPK_REG
   topk_kernel<<<(unsigned)pairs, TOPK_THREADS, 0, st>>>(scores, nb, c0, c1, k, n_keep, ad,
                                                         idx_out);
 }

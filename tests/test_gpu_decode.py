@@ -105,6 +105,38 @@ def test_edge_cases():
                                  keep_ratio=0.15), 36, capacity=64 * 100)
 
 
+@pytest.mark.parametrize("nb", [700, 1027, 1028, 3000, 6000, 16387, 16388, 20000])
+def test_topk_candidate_counts(nb):
+    """Top-k over 697 .. 19997 candidates: every per-thread run length of the
+    register-resident select (1, 2, 4, 8, 16 candidates per thread, with the
+    1024 / 1025 and 16384 / 16385 edges) and the strided fallback beyond it.
+    Random summaries compare as index sets; integer-valued ones give exact
+    scores with many equal values, where the lower index must win exactly."""
+    import torch
+    B, Hq, Hkv, d, bs = 1, 4, 2, 128, 64
+    N = nb * bs
+    top_k = nb // 7
+    rng = np.random.default_rng(nb)
+    for kind in ("random", "integer_ties"):
+        announce("topk", kind, "nb", nb, "top_k", top_k)
+        if kind == "random":
+            q = synth.bf16_round(rng.standard_normal((B, Hq, d)).astype(np.float32))
+            summ = rng.standard_normal((B, Hkv, nb, d)).astype(np.float32)
+        else:
+            q = synth.bf16_round(rng.integers(-1, 2, (B, Hq, d)).astype(np.float32))
+            summ = rng.integers(-2, 3, (B, Hkv, nb, d)).astype(np.float32)
+        idx, scores = bsa.select_blocks(to_dev(q), torch.from_numpy(summ).cuda(), N, bs, 1, 2,
+                                        top_k, want_scores=True)
+        torch.cuda.synchronize()
+        g_idx = idx.cpu().numpy()
+        o_idx, o_scores = oracle.select_blocks(q, summ.astype(np.float64), Hkv, 1, 2, top_k)
+        assert g_idx.shape == o_idx.shape
+        if kind == "random":
+            check_index_sets(g_idx, o_idx, o_scores, nb, 1, 2)
+        else:
+            assert np.array_equal(g_idx, o_idx)
+
+
 def test_ties_prefer_lower_index():
     import torch
     announce("ties")
