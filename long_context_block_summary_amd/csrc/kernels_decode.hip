@@ -430,53 +430,55 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_kernel(
 
 // Exact merge of the splits of one (batch, query head): M = max m_s,
 // L = sum 2^(m_s - M) l_s, o = sum 2^(m_s - M) o_s / L, lse = (M + log2 L) ln 2.
-// One workgroup of D threads per (batch, query head); the split weights are
-// computed once into LDS, then every column sums its splits with independent
-// loads.  A separate launch: the kernel boundary makes the partials of all
-// workgroups visible (an agent-scope fence per workgroup is far more costly
-// on a multi-XCD part).
+// One workgroup of D threads (one value column each) per (batch, query head).
+// The first MERGE_CHUNK splits' columns are requested together with the
+// (m, l) pairs (lane s of every wave holds split s), so the common case is a
+// single memory round trip; the split weights reach the columns by
+// cross-lane reads, with no LDS and no barrier.  A separate launch: the
+// kernel boundary makes the partials of all workgroups visible (an
+// agent-scope fence per workgroup is far more costly on a multi-XCD part).
+constexpr int MERGE_CHUNK = 16;
+
 template <int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml,
                                                          int G, int Hq, int Hkv, int S,
                                                          float* __restrict__ out,
                                                          float* __restrict__ lse) {
-  constexpr int SMAX = 1024;
-  __shared__ float w_lds[SMAX];
-  __shared__ float red[D / 64][2];
   const int bh = blockIdx.x;
   const int b = bh / Hq, h = bh % Hq;
   const int pair = b * Hkv + h / G, hh = h % G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t r0 = (int64_t)pair * S * G + hh;  // row of split s: r0 + s * G
-  float M = -INFINITY;
-  for (int s2 = tid; s2 < S; s2 += D) M = fmaxf(M, part_ml[(r0 + (int64_t)s2 * G) * 2]);
-  M = wave_max(M);
-  if (lane == 0) red[wave][0] = M;
-  __syncthreads();
+  float ov[MERGE_CHUNK];
 #pragma unroll
-  for (int w = 0; w < D / 64; ++w) M = fmaxf(M, red[w][0]);
+  for (int i = 0; i < MERGE_CHUNK; ++i)
+    ov[i] = (i < S) ? part_o[(r0 + (int64_t)i * G) * D + tid] : 0.f;
+  float M = -INFINITY;
+  for (int s2 = lane; s2 < S; s2 += 64) M = fmaxf(M, part_ml[(r0 + (int64_t)s2 * G) * 2]);
+  M = wave_max(M);
   float L = 0.f, o = 0.f;
-  for (int sb = 0; sb < S; sb += SMAX) {
-    const int se = min(S, sb + SMAX);
-    __syncthreads();
-    for (int s2 = sb + tid; s2 < se; s2 += D) {
-      const int64_t r = r0 + (int64_t)s2 * G;
-      const float ms = part_ml[r * 2];
-      const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      w_lds[s2 - sb] = w;
-      L = fmaf(w, part_ml[r * 2 + 1], L);
+  for (int sb = 0; sb < S; sb += 64) {
+    const int s2 = sb + lane;
+    float w = 0.f;
+    if (s2 < S) {
+      const float ms = part_ml[(r0 + (int64_t)s2 * G) * 2];
+      w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      L = fmaf(w, part_ml[(r0 + (int64_t)s2 * G) * 2 + 1], L);
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int s2 = sb; s2 < se; ++s2) o = fmaf(w_lds[s2 - sb], part_o[(r0 + (int64_t)s2 * G) * D + tid], o);
+    const int ns = min(64, S - sb);
+    for (int cb = 0; cb < ns; cb += MERGE_CHUNK) {
+      if (sb + cb > 0) {  // later chunks (more than MERGE_CHUNK splits)
+#pragma unroll
+        for (int i = 0; i < MERGE_CHUNK; ++i)
+          ov[i] = (cb + i < ns) ? part_o[(r0 + (int64_t)(sb + cb + i) * G) * D + tid] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < MERGE_CHUNK; ++i)
+        o = fmaf(readlane(w, min(cb + i, 63)), ov[i], o);  // ov is 0 past the splits
+    }
   }
   L = wave_sum(L);
-  if (lane == 0) red[wave][1] = L;
-  __syncthreads();
-  L = 0.f;
-#pragma unroll
-  for (int w = 0; w < D / 64; ++w) L += red[w][1];
   out[(int64_t)bh * D + tid] = o / L;
   if (lse && tid == 0) lse[bh] = (M + log2f(L)) * LN2;
 }
