@@ -506,9 +506,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", default="prefill256k",
                     help="prefill workload reported alongside ('none' to skip)")
-    ap.add_argument("--only", choices=["prefill"], default=None,
-                    help="run only the prefill measurement and print its object (for counter "
-                         "passes); the default runs the full bench")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run only the prefill measurement, or only the decode step and its "
+                         "FP8 line, and print their object (for counter passes); the default "
+                         "runs the full bench")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -523,6 +524,13 @@ def main():
         return
     cfg = synth.CONFIGS[args.workload]
     r = run_gpu(cfg, args.steps, args.warmup)
+    if args.only == "decode":
+        print(json.dumps({"workload": cfg.name, "ms_per_step": r["step_ms"],
+                          "breakdown_us": {"select_blocks": r["sel_ms"] * 1e3,
+                                           "sparse_decode_attn": r["att_ms"] * 1e3},
+                          "fp8_kv": run_fp8(cfg, args.steps, args.warmup, r["inputs"])}),
+              flush=True)
+        return
     sel_b, att_b = decode_bytes(cfg, r["n_keep"])
     qh = cfg.batch * cfg.n_q_heads
     step_s = r["step_ms"] / 1e3
