@@ -433,6 +433,13 @@ __device__ __forceinline__ uint32_t piece_word(const uint4& p, int i) {
 // within 16 lanes.
 __device__ __forceinline__ int vt_swz(int dim) { return (dim & 15) ^ ((dim >> 4) & 7); }
 
+// max(a, b) for non-NaN operands as a median with +inf: the compiler emits
+// v_max3 directly, with none of the canonicalising v_max x, x, x that fmaxf
+// puts before every operand
+__device__ __forceinline__ float fmax_nc(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, INFINITY);
+}
+
 // One workgroup per (b, tile, kv head): NW waves of 16*NT (query, head) rows.
 // Per chunk of 64 entries: S^T = K Q^T (bf16 MFMA, Q fragments in registers),
 // online softmax in base 2 with the row maximum raised only when it grows by
@@ -450,7 +457,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
   static_assert(PF_CH == 64 && NTH / LPR == 16, "16 groups of 4 entries per chunk");
   __shared__ __align__(16) uint4 k_lds[2][PF_CH * (D / 8)];      // entry rows, 16 B pieces, xor-swizzled
   __shared__ __align__(16) uint16_t vt_lds[2][D * PF_CH];        // V^T fp16 [dim][entry], 8 B groups swizzled
-  __shared__ __align__(16) float xch[NW][4][RW];  // alpha, l, lse, running concat lse
+  __shared__ __align__(16) float xch[NW][3][RW];  // alpha, row max, running concat lse
   __shared__ int32_t sel_lds[PF_MAX_SEL];                        // the tile's branch-A entries
 
   const int g = a.Hq / a.Hkv;
@@ -550,12 +557,17 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int nd = 0; nd < D / 16; ++nd) O[nt][nd] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float m_run[NT], l_run[NT];
+  // running maximum per row (lane l%16 of the S layout) and row sums of the
+  // weights in the O layout (rows 4(l/16) + i): the sums come from the
+  // matrix cores as P times a B operand of ones
+  float m_run[NT];
+  f32x4_t Lc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
+    Lc[nt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   }
+  const f16x8_t ones = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
   const float c = a.scale_log2;
 
   auto chunk = [&](int gc, int set) {  // set == gc & 1
@@ -619,26 +631,30 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
       float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        mx = fmaxf(mx, fmaxf(fmaxf(s[nt][mt][0], s[nt][mt][1]), fmaxf(s[nt][mt][2], s[nt][mt][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmax_nc(mx, s[nt][mt][i]);
+      mx = fmax_nc(mx, __shfl_xor(mx, 16));
+      mx = fmax_nc(mx, __shfl_xor(mx, 32));
       mc[nt] = mx * c;
       grow = grow || (mc[nt] > m_run[nt] + 8.f);
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // uniform
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float m_new = fmaxf(m_run[nt], mc[nt]);
+        const float m_new = fmax_nc(m_run[nt], mc[nt]);
         const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
         m_run[nt] = m_new;
-        l_run[nt] *= alpha;
         if (j4 == 0) xch[wave][0][16 * nt + l16] = alpha;
       }
       wave_lds_sync();
-      // rescale O rows (lane holds rows 16nt + 4(l/16) + i) by their alpha
+      // rescale O rows and their sums (lane holds rows 16nt + 4(l/16) + i)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const float4 al = *reinterpret_cast<const float4*>(&xch[wave][0][16 * nt + 4 * j4]);
+        Lc[nt][0] *= al.x;
+        Lc[nt][1] *= al.y;
+        Lc[nt][2] *= al.z;
+        Lc[nt][3] *= al.w;
 #pragma unroll
         for (int nd = 0; nd < D / 16; ++nd) {
           O[nt][nd][0] *= al.x;
@@ -653,17 +669,19 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float neg_m = m_run[nt] == -INFINITY ? 0.f : -m_run[nt];
-      float ps = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[nt][mt][i], c, neg_m));
-          ps += p;
-          pa[nt][mt >> 1][4 * (mt & 1) + i] = (_Float16)p;
-        }
-      l_run[nt] += ps;
+        for (int i = 0; i < 4; ++i)
+          pa[nt][mt >> 1][4 * (mt & 1) + i] =
+              (_Float16)__builtin_amdgcn_exp2f(fmaf(s[nt][mt][i], c, neg_m));
     }
+    // row sums of the fp16 weights (the ones PV multiplies)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        Lc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[nt][kk], ones, Lc[nt], 0, 0, 0);
     // O += P V: B operand lane l = dim 16nd + l%16, entries of the P k-slots
 #pragma unroll
     for (int nd = 0; nd < D / 16; ++nd) {
@@ -692,23 +710,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
       //   concat:   one softmax over all branches' logits: out accumulates
       //             e^(lse_X - L) o_X with the running L = log sum e^lse_X kept
       //             in LDS per row; the sink logit scales by 1 / (1 + e^(z - L)).
+      // the row maxima move to the O layout through LDS
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float lt = l_run[nt];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
-        if (j4 == 0) {
-          const float lse = (m_run[nt] + log2f(lt)) * PF_LN2;
-          xch[wave][1][16 * nt + l16] = lt;
-          xch[wave][2][16 * nt + l16] = lse;
-          const int r = RW * wave + 16 * nt + l16;
-          const int i = tile * a.q_tile + r / g;
-          if (a.lse3 && i < a.C) {
-            const int h = kvh * g + r % g;
-            a.lse3[(((int64_t)br * a.B + b) * a.C + i) * a.Hq + h] = lse;
-          }
-        }
-      }
+      for (int nt = 0; nt < NT; ++nt)
+        if (j4 == 0) xch[wave][1][16 * nt + l16] = m_run[nt];
       wave_lds_sync();
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -717,15 +722,21 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int jo = ln >> 4;
-        const float4 l4 = *reinterpret_cast<const float4*>(&xch[wave][1][16 * nt + 4 * jo]);
-        const float4 s4 = *reinterpret_cast<const float4*>(&xch[wave][2][16 * nt + 4 * jo]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float lse[4] = {s4.x, s4.y, s4.z, s4.w};
+        const float4 m4 = *reinterpret_cast<const float4*>(&xch[wave][1][16 * nt + 4 * jo]);
+        const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+        float lv[4], lse[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lv[i] = Lc[nt][i];
+          lse[i] = (mv[i] + log2f(lv[i])) * PF_LN2;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = RW * wave + 16 * nt + 4 * jo + i;
           const int qi = tile * a.q_tile + r / g;
           const int h = kvh * g + r % g;
+          if (a.lse3 && qi < a.C && (ln & 15) == 0)
+            a.lse3[(((int64_t)br * a.B + b) * a.C + qi) * a.Hq + h] = lse[i];
           // coefficients: out = ca * out + cb * (O / l)
           float ca = 0.f, cb = 1.f;
           if (a.combine == 0) {  // uniform
@@ -737,7 +748,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
               ca = br == 0 ? 0.f : 1.f;
             }
           } else {
-            float* Lp = &xch[wave][3][16 * nt + 4 * jo + i];
+            float* Lp = &xch[wave][2][16 * nt + 4 * jo + i];
             float L = lse[i];
             if (br > 0) {
               const float Lo = *Lp, mx = fmaxf(Lo, lse[i]);
@@ -769,7 +780,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
 #pragma unroll
         for (int nd = 0; nd < D / 16; ++nd) O[nt][nd] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
         m_run[nt] = -INFINITY;
-        l_run[nt] = 0.f;
+        Lc[nt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
       }
     }
     // the other buffer was last read in chunk gc - 1, which every wave
