@@ -583,19 +583,24 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
     const int tbase = T0 + (gc - nA - nB) * PF_CH;  // branch C: token of entry 0
     const bool masked = br == 2 || nvalid < PF_CH;   // uniform
     // S^T = K Q^T : lane gets entries 16mt + 4(l/16) + i of row 16nt + l%16
+    // K fragments of entry tile mt + 1 are read while the MFMAs of tile mt run
     f32x4_t s[NT][4];
+    uint4 ka[2][KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ka[0][ks] = k_lds[buf][l16 * (D / 8) + ((4 * ks + j4) ^ l16)];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      uint4 ka[KS];
+      if (mt + 1 < 4) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ka[ks] = k_lds[buf][(16 * mt + l16) * (D / 8) + ((4 * ks + j4) ^ l16)];
+        for (int ks = 0; ks < KS; ++ks)
+          ka[(mt + 1) & 1][ks] = k_lds[buf][(16 * (mt + 1) + l16) * (D / 8) + ((4 * ks + j4) ^ l16)];
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[mt & 1][ks]),
                                                         __builtin_bit_cast(bf16x8_t, qf[nt][ks]),
                                                         acc, 0, 0, 0);
         s[nt][mt] = acc;
@@ -682,17 +687,28 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         Lc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[nt][kk], ones, Lc[nt], 0, 0, 0);
-    // O += P V: B operand lane l = dim 16nd + l%16, entries of the P k-slots
-#pragma unroll
-    for (int nd = 0; nd < D / 16; ++nd) {
+    // O += P V: B operand lane l = dim 16nd + l%16, entries of the P k-slots;
+    // the fragments of column tile nd + 1 are read while the MFMAs of nd run
+    auto vfrag = [&](int nd, int kk) {
       const int dim = 16 * nd + l16;
       const uint2* vrow = reinterpret_cast<const uint2*>(&vt_lds[buf][dim * PF_CH]);
       const int sw = vt_swz(dim);
+      const uint2 lo = vrow[(8 * kk + j4) ^ sw];
+      const uint2 hi = vrow[(8 * kk + 4 + j4) ^ sw];
+      return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    };
+    uint4 vf[2][2];
+    vf[0][0] = vfrag(0, 0);
+    vf[0][1] = vfrag(0, 1);
+#pragma unroll
+    for (int nd = 0; nd < D / 16; ++nd) {
+      if (nd + 1 < D / 16) {
+        vf[(nd + 1) & 1][0] = vfrag(nd + 1, 0);
+        vf[(nd + 1) & 1][1] = vfrag(nd + 1, 1);
+      }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const uint2 lo = vrow[(8 * kk + j4) ^ sw];
-        const uint2 hi = vrow[(8 * kk + 4 + j4) ^ sw];
-        const f16x8_t vb = __builtin_bit_cast(f16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const f16x8_t vb = __builtin_bit_cast(f16x8_t, vf[nd & 1][kk]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           O[nt][nd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[nt][kk], vb, O[nt][nd], 0, 0, 0);
