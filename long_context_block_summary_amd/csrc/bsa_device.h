@@ -90,6 +90,30 @@ __device__ __forceinline__ float wave_sum(float x) {
   return (readlane(x, 0) + readlane(x, 16)) + (readlane(x, 32) + readlane(x, 48));
 }
 
+// max(a, b) for non-NaN operands as a median with +inf: the compiler emits
+// v_max3 directly, with none of the canonicalising v_max x, x, x that fmaxf
+// puts before every operand
+__device__ __forceinline__ float fmax_nc(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, INFINITY);
+}
+
+// max of x over the lane pair (l, l ^ 16), resp. (l, l ^ 32), in both lanes:
+// v_permlane16_swap exchanges the odd 16-lane rows of its first operand with
+// the even rows of its second, v_permlane32_swap the upper half of the first
+// with the lower half of the second; with x in both operands the two results
+// hold x of the two partners.  VALU only (no LDS round trip as for a
+// ds_bpermute shuffle).
+__device__ __forceinline__ float pair16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return fmax_nc(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return fmax_nc(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // order LDS traffic between the lanes of one wave (no cross-wave barrier)
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

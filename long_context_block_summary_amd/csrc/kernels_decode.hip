@@ -86,10 +86,9 @@ __device__ __forceinline__ void softmax_pv(const f32x4v& sc, float zscale, int n
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     z[i] = (i < n_valid) ? sc[i] * zscale : -INFINITY;
-    bm = fmaxf(bm, z[i]);
+    bm = fmax_nc(bm, z[i]);
   }
-  bm = fmaxf(bm, __shfl_xor(bm, 16));
-  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  bm = pair32_max(pair16_max(bm));
   // the 4 lanes of a head agree on bm and m_run, so on grow
   const bool grow = bm > m_run + DEC_RESCALE_LOG2;
   if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform

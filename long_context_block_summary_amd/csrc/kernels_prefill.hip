@@ -433,12 +433,6 @@ __device__ __forceinline__ uint32_t piece_word(const uint4& p, int i) {
 // within 16 lanes.
 __device__ __forceinline__ int vt_swz(int dim) { return (dim & 15) ^ ((dim >> 4) & 7); }
 
-// max(a, b) for non-NaN operands as a median with +inf: the compiler emits
-// v_max3 directly, with none of the canonicalising v_max x, x, x that fmaxf
-// puts before every operand
-__device__ __forceinline__ float fmax_nc(float a, float b) {
-  return __builtin_amdgcn_fmed3f(a, b, INFINITY);
-}
 
 // One workgroup per (b, tile, kv head): NW waves of 16*NT (query, head) rows.
 // Per chunk of 64 entries: S^T = K Q^T (bf16 MFMA, Q fragments in registers),
@@ -638,8 +632,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmax_nc(mx, s[nt][mt][i]);
-      mx = fmax_nc(mx, __shfl_xor(mx, 16));
-      mx = fmax_nc(mx, __shfl_xor(mx, 32));
+      mx = pair32_max(pair16_max(mx));
       mc[nt] = mx * c;
       grow = grow || (mc[nt] > m_run[nt] + 8.f);
     }
