@@ -42,9 +42,19 @@ def decode_bytes(cfg, n_keep):
     return sel, att
 
 
-def measured_traffic(workload):
-    """HBM bytes per sparse_decode_attn call from the committed counter summary, or None when
-    the summary is for another workload or the decode kernel source changed since it was taken."""
+def partials_bytes(cfg, n_keep):
+    """Algorithmic bytes of step S4 alone (the split-K partials kernel): 64 * d * 2 * 2 bytes of
+    K and V per (batch, kv head, kept block), plus q and the index list.  The fp32 output is
+    S5's; the partials are scratch."""
+    B, Hq, Hkv, d = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    kept_tokens = min(n_keep * cfg.block_size, cfg.seq_len)
+    return B * Hkv * kept_tokens * d * 2 * 2 + B * Hq * d * 2 + B * Hkv * n_keep * 4
+
+
+def measured_traffic(workload, field="traffic_bytes_per_launch"):
+    """HBM bytes per launch from the committed counter summary (`field`: the whole
+    sparse_decode_attn call, or the S4 kernel alone), or None when the summary is for another
+    workload or the decode kernel source changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_traffic.md")
     src = os.path.join(ROOT, "long_context_block_summary_amd", "csrc", "kernels_decode.hip")
@@ -58,7 +68,7 @@ def measured_traffic(workload):
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     if fields.get("kernel_source_sha256_prefix") != sha:
         return None
-    return float(fields["traffic_bytes_per_launch"])
+    return float(fields[field]) if field in fields else None
 
 
 def kv_bytes_per_token(n_layers, width, elem_bytes):
@@ -111,7 +121,7 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30, inputs=None):
                                                            n_keep)),
                          dtype=torch.uint8, device=dev)
 
-    def step(e0=None, e1=None, e2=None):
+    def step(e0=None, e1=None, e2=None, e3=None):
         st = torch.cuda.current_stream(dev)
         if e0 is not None:
             e0.record(st)
@@ -119,9 +129,16 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30, inputs=None):
                           block_idx=idx, workspace=ws_sel)
         if e1 is not None:
             e1.record(st)
-        bsa.sparse_decode_attn(q, k, v, idx, N, bs, out=out, lse=lse, workspace=ws_dec)
-        if e2 is not None:
+        if e3 is None:
+            bsa.sparse_decode_attn(q, k, v, idx, N, bs, out=out, lse=lse, workspace=ws_dec)
+            if e2 is not None:
+                e2.record(st)
+        else:  # the attention as its two steps, S4 (partials) and S5 (merge), timed apart
+            bsa.sparse_decode_partials(q, k, v, idx, N, bs, workspace=ws_dec)
             e2.record(st)
+            bsa.sparse_decode_merge(ws_dec, cfg.batch, cfg.n_q_heads, cfg.n_kv_heads,
+                                    cfg.head_dim, N, n_keep, bs, out=out, lse=lse)
+            e3.record(st)
 
     for _ in range(warmup):
         flush.add_(1.0)
@@ -138,7 +155,8 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30, inputs=None):
     wall = time.perf_counter() - w0
     step_ms = [a.elapsed_time(b) for a, b in events]
 
-    # per-call breakdown (separate pass with an event between the calls)
+    # per-call breakdown (separate passes with events between the calls): select + the
+    # attention call; select + its two steps S4 and S5 as separate calls
     bevents = [(ev(), ev(), ev()) for _ in range(steps)]
     for e in bevents:
         flush.add_(1.0)
@@ -146,6 +164,13 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30, inputs=None):
     torch.cuda.synchronize()
     sel_ms = [a.elapsed_time(b) for a, b, _ in bevents]
     att_ms = [b.elapsed_time(c) for _, b, c in bevents]
+    sevents = [(ev(), ev(), ev(), ev()) for _ in range(steps)]
+    for e in sevents:
+        flush.add_(1.0)
+        step(*e)
+    torch.cuda.synchronize()
+    s4_ms = [b.elapsed_time(c) for _, b, c, _ in sevents]
+    s5_ms = [c.elapsed_time(d) for _, _, c, d in sevents]
 
     # the same step captured once in a HIP graph and replayed (flush outside the graph)
     graph_ms = None
@@ -183,6 +208,8 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30, inputs=None):
         "sum_ms": sorted(sum_ms)[len(sum_ms) // 2],
         "sel_ms": sum(sel_ms) / len(sel_ms),
         "att_ms": sum(att_ms) / len(att_ms),
+        "s4_ms": sum(s4_ms) / len(s4_ms),
+        "s5_ms": sum(s5_ms) / len(s5_ms),
         "step_ms": sum(step_ms) / len(step_ms),
         "step_pct": pct(step_ms),
         "graph_ms": graph_ms,
@@ -532,9 +559,11 @@ def main():
               flush=True)
         return
     sel_b, att_b = decode_bytes(cfg, r["n_keep"])
+    s4_b = partials_bytes(cfg, r["n_keep"])
     qh = cfg.batch * cfg.n_q_heads
     step_s = r["step_ms"] / 1e3
     att_gbs = att_b / (r["att_ms"] / 1e3) / 1e9
+    s4_gbs = s4_b / (r["s4_ms"] / 1e3) / 1e9
     line = {
         "metric": METRIC,
         "value": qh / step_s,
@@ -555,12 +584,20 @@ def main():
                    "top_k": cfg.top_k, "n_keep": r["n_keep"],
                    "keep_pct": round(100.0 * r["n_keep"] / -(-cfg.seq_len // cfg.block_size), 2)},
         "step_GBps": (sel_b + att_b) / step_s / 1e9,
-        "roofline": {"bound": "hbm", "kernel": "sparse_decode_attn",
-                     "achieved": att_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": att_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(cfg.name),
-                     "algorithmic_bytes": att_b, "avg_us": r["att_ms"] * 1e3},
+        "roofline": {"bound": "hbm",
+                     "kernel": "decode_kernel (step S4, the sparse_decode_partials call)",
+                     "achieved": s4_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": s4_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(cfg.name, "s4_traffic_bytes_per_launch"),
+                     "algorithmic_bytes": s4_b, "avg_us": r["s4_ms"] * 1e3},
+        "attention_call": {"call": "sparse_decode_attn (S4 + S5)", "avg_us": r["att_ms"] * 1e3,
+                           "algorithmic_bytes": att_b, "GBps": att_gbs,
+                           "frac": att_gbs / HBM_PEAK_GBS,
+                           "traffic": measured_traffic(cfg.name)},
         "breakdown_us": {"select_blocks": r["sel_ms"] * 1e3,
                          "sparse_decode_attn": r["att_ms"] * 1e3,
+                         "sparse_decode_partials": r["s4_ms"] * 1e3,
+                         "sparse_decode_merge": r["s5_ms"] * 1e3,
                          "build_block_summaries_ingest": r["sum_ms"] * 1e3},
         "select_GBps": sel_b / (r["sel_ms"] / 1e3) / 1e9,
         "warm_cache_ms_per_step": r["warm_step_ms"],

@@ -234,6 +234,32 @@ int sparse_decode_attn_split(const void* q, const void* k, const void* v,
                              void* workspace, size_t ws_bytes, int32_t n_splits,
                              void* hip_stream);
 
+/* The two steps of sparse_decode_attn_split as calls of their own (same
+ * kernels, same arguments; calling them in order on one stream with one
+ * workspace gives sparse_decode_attn_split's result bit for bit).
+ *
+ * sparse_decode_partials -- the kept tokens of each (batch, kv head) are cut
+ * into runs of kept blocks (splits); per split and query head it writes the
+ * unnormalised partial softmax state of "CSA + HCA 混合注意力机制" §2.1 /
+ * §4.4 step 4 restricted to the split: m = max of the base-2 scaled logits,
+ * l = sum 2^(z - m), o = sum 2^(z - m) V.  Into the workspace (16-byte
+ * aligned, bsa_decode_workspace_size(shape, n_keep, block_size, n_splits)
+ * bytes): fp32 (m, l) [B*Hkv][splits][g][2], then fp32 o [B*Hkv][splits][g][d].
+ * Arguments, lists, requirements and errors as sparse_decode_attn_split. */
+int sparse_decode_partials(const void* q, const void* k, const void* v, const int32_t* block_idx,
+                           int32_t n_keep, const bsa_shape* shape, int32_t block_size,
+                           float scale, void* workspace, size_t ws_bytes, int32_t n_splits,
+                           void* hip_stream);
+
+/* sparse_decode_merge -- the exact log-sum-exp merge of the partials that
+ * sparse_decode_partials wrote into `workspace` with the same shape, n_keep,
+ * block_size and n_splits: M = max_s m_s, L = sum_s 2^(m_s - M) l_s,
+ * out = sum_s 2^(m_s - M) o_s / L (fp32 [B][Hq][d]), lse = (M + log2 L) ln 2
+ * (fp32 [B][Hq], or NULL).  Errors as sparse_decode_attn_split. */
+int sparse_decode_merge(const bsa_shape* shape, int32_t n_keep, int32_t block_size,
+                        int32_t n_splits, const void* workspace, size_t ws_bytes, float* out,
+                        float* lse, void* hip_stream);
+
 /* sparse_prefill_attn -- chunked prefill of C new queries at positions
  * P + i (P = shape->seq_len prior tokens), three branches averaged:
  *   A ("CSA + HCA 混合注意力机制" §4.1-4.2, §4.4): per (tile of q_tile

@@ -75,6 +75,9 @@ def lib():
                                      vp]
     L.sparse_decode_attn_split.argtypes = [vp, vp, vp, vp, i32, P(bsa_shape), i32, f32, vp, vp,
                                            vp, sz, i32, vp]
+    L.sparse_decode_partials.argtypes = [vp, vp, vp, vp, i32, P(bsa_shape), i32, f32, vp, sz, i32,
+                                         vp]
+    L.sparse_decode_merge.argtypes = [P(bsa_shape), i32, i32, i32, vp, sz, vp, vp, vp]
     L.sparse_prefill_attn.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, P(bsa_shape),
                                       P(bsa_prefill_cfg), f32, vp, vp, vp, vp, vp, sz, vp]
     L.select_prefill_entries.argtypes = [vp, i32, vp, P(bsa_shape), P(bsa_prefill_cfg), vp, vp,
@@ -88,7 +91,8 @@ def lib():
     for fn in ("quantize_kv_fp8", "sparse_decode_attn_fp8",
                "build_block_summaries", "update_block_summaries", "append_kv",
                "select_blocks", "sparse_decode_attn",
-               "sparse_decode_attn_split", "sparse_prefill_attn", "select_prefill_entries",
+               "sparse_decode_attn_split", "sparse_decode_partials", "sparse_decode_merge",
+               "sparse_prefill_attn", "select_prefill_entries",
                "sparse_prefill_attn_selected"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
@@ -275,6 +279,53 @@ def sparse_decode_attn(q, k, v, block_idx, seq_len, block_size=64, scale=0.0, n_
                                           ctypes.byref(shape), block_size, scale, _ptr(out),
                                           _ptr(lse), _ptr(workspace), workspace.numel(),
                                           n_splits, _stream(q.device)))
+    return out, lse
+
+
+def sparse_decode_partials(q, k, v, block_idx, seq_len, block_size=64, scale=0.0, n_splits=0,
+                           workspace=None):
+    """Step S4 alone: the split-K partial softmax states of sparse_decode_attn, written into
+    `workspace` (uint8, allocated when None).  Returns the workspace."""
+    import torch
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(block_idx, "block_idx", torch.int32, 3)
+    B, Hq, d = q.shape
+    Hkv, stride = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or block_idx.shape[:2] != (B, Hkv):
+        raise ValueError("k, v and block_idx shapes disagree")
+    n_keep = block_idx.shape[2]
+    shape = make_shape(B, Hq, Hkv, d, seq_len, stride)
+    ws_bytes = lib().bsa_decode_workspace_size(ctypes.byref(shape), n_keep, block_size, n_splits)
+    if ws_bytes == SIZE_MAX:
+        raise ValueError("invalid decode arguments")
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    _check("sparse_decode_partials",
+           lib().sparse_decode_partials(_ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), n_keep,
+                                        ctypes.byref(shape), block_size, scale, _ptr(workspace),
+                                        workspace.numel(), n_splits, _stream(q.device)))
+    return workspace
+
+
+def sparse_decode_merge(workspace, batch, n_q_heads, n_kv_heads, head_dim, seq_len, n_keep,
+                        block_size=64, n_splits=0, seq_stride=None, out=None, lse=None,
+                        want_lse=True):
+    """Step S5 alone: the exact merge of the partials sparse_decode_partials wrote with the
+    same sizes.  Returns (out fp32 [B][Hq][d], lse fp32 [B][Hq] or None)."""
+    import torch
+    shape = make_shape(batch, n_q_heads, n_kv_heads, head_dim, seq_len,
+                       seq_len if seq_stride is None else seq_stride)
+    if out is None:
+        out = torch.empty((batch, n_q_heads, head_dim), dtype=torch.float32,
+                          device=workspace.device)
+    if lse is None and want_lse:
+        lse = torch.empty((batch, n_q_heads), dtype=torch.float32, device=workspace.device)
+    _check("sparse_decode_merge",
+           lib().sparse_decode_merge(ctypes.byref(shape), n_keep, block_size, n_splits,
+                                     _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
+                                     _stream(workspace.device)))
     return out, lse
 
 

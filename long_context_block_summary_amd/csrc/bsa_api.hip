@@ -229,32 +229,77 @@ int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
   return launch_status();
 }
 
-int sparse_decode_attn_split(const void* q, const void* k, const void* v,
-                             const int32_t* block_idx, int32_t n_keep, const bsa_shape* shape,
-                             int32_t block_size, float scale, float* out, float* lse,
-                             void* workspace, size_t ws_bytes, int32_t n_splits,
-                             void* hip_stream) {
-  if (!q || !k || !v || !block_idx || !out || !shape_ok(shape) || n_keep < 1 || n_splits < 0 ||
-      shape->seq_len < 1)
+// checks shared by the decode calls (shape, list length, block size, splits,
+// workspace); fills the plan.  Nothing is launched when a check fails.
+static int decode_checks(const bsa_shape* shape, int32_t n_keep, int32_t block_size,
+                         int32_t n_splits, const void* workspace, size_t ws_bytes,
+                         bsa::DecodePlan* plan) {
+  if (!shape_ok(shape) || n_keep < 1 || n_splits < 0 || shape->seq_len < 1 || block_size < 1)
     return BSA_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return BSA_INVALID_ARG;
-  if (block_size < 1) return BSA_INVALID_ARG;
   if (n_keep > bsa_num_blocks(shape->seq_len, block_size)) return BSA_INVALID_ARG;
   const int g = shape->n_q_heads / shape->n_kv_heads;
   if (block_size != 64 || !dim_supported(shape->head_dim) || !group_supported(g))
     return BSA_UNSUPPORTED;
   const int64_t pairs = (int64_t)shape->batch * shape->n_kv_heads;
-  bsa::DecodePlan plan = bsa::plan_decode(pairs, n_keep, g, n_splits);
-  if (ws_bytes < bsa::decode_workspace_bytes(pairs, shape->head_dim, plan))
+  *plan = bsa::plan_decode(pairs, n_keep, g, n_splits);
+  if (ws_bytes < bsa::decode_workspace_bytes(pairs, shape->head_dim, *plan))
     return BSA_WORKSPACE_TOO_SMALL;
   if (!workspace || !aligned16(workspace)) return BSA_INVALID_ARG;
+  return BSA_OK;
+}
+
+int sparse_decode_partials(const void* q, const void* k, const void* v, const int32_t* block_idx,
+                           int32_t n_keep, const bsa_shape* shape, int32_t block_size,
+                           float scale, void* workspace, size_t ws_bytes, int32_t n_splits,
+                           void* hip_stream) {
+  if (!q || !k || !v || !block_idx) return BSA_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return BSA_INVALID_ARG;
+  bsa::DecodePlan plan;
+  const int rc = decode_checks(shape, n_keep, block_size, n_splits, workspace, ws_bytes, &plan);
+  if (rc != BSA_OK) return rc;
   if (scale == 0.f) scale = 1.f / sqrtf((float)shape->head_dim);
-  bsa::launch_decode(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), block_idx, n_keep, shape->batch,
-                     shape->n_q_heads, shape->n_kv_heads, shape->head_dim, shape->seq_len,
-                     shape->seq_stride, scale, plan, static_cast<float*>(workspace), out, lse,
-                     static_cast<hipStream_t>(hip_stream));
+  bsa::launch_decode_partials(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                              static_cast<const uint16_t*>(v), block_idx, n_keep, shape->batch,
+                              shape->n_q_heads, shape->n_kv_heads, shape->head_dim,
+                              shape->seq_len, shape->seq_stride, scale, plan,
+                              static_cast<float*>(workspace),
+                              static_cast<hipStream_t>(hip_stream));
+  return launch_status();
+}
+
+int sparse_decode_merge(const bsa_shape* shape, int32_t n_keep, int32_t block_size,
+                        int32_t n_splits, const void* workspace, size_t ws_bytes, float* out,
+                        float* lse, void* hip_stream) {
+  if (!out || !aligned16(out)) return BSA_INVALID_ARG;
+  bsa::DecodePlan plan;
+  const int rc = decode_checks(shape, n_keep, block_size, n_splits, workspace, ws_bytes, &plan);
+  if (rc != BSA_OK) return rc;
+  bsa::launch_decode_merge(shape->batch, shape->n_q_heads, shape->n_kv_heads, shape->head_dim,
+                           plan, static_cast<const float*>(workspace), out, lse,
+                           static_cast<hipStream_t>(hip_stream));
+  return launch_status();
+}
+
+int sparse_decode_attn_split(const void* q, const void* k, const void* v,
+                             const int32_t* block_idx, int32_t n_keep, const bsa_shape* shape,
+                             int32_t block_size, float scale, float* out, float* lse,
+                             void* workspace, size_t ws_bytes, int32_t n_splits,
+                             void* hip_stream) {
+  if (!q || !k || !v || !block_idx || !out) return BSA_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return BSA_INVALID_ARG;
+  bsa::DecodePlan plan;
+  const int rc = decode_checks(shape, n_keep, block_size, n_splits, workspace, ws_bytes, &plan);
+  if (rc != BSA_OK) return rc;
+  if (scale == 0.f) scale = 1.f / sqrtf((float)shape->head_dim);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  bsa::launch_decode_partials(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                              static_cast<const uint16_t*>(v), block_idx, n_keep, shape->batch,
+                              shape->n_q_heads, shape->n_kv_heads, shape->head_dim,
+                              shape->seq_len, shape->seq_stride, scale, plan,
+                              static_cast<float*>(workspace), st);
+  bsa::launch_decode_merge(shape->batch, shape->n_q_heads, shape->n_kv_heads, shape->head_dim,
+                           plan, static_cast<const float*>(workspace), out, lse, st);
   return launch_status();
 }
 
@@ -278,30 +323,26 @@ int sparse_decode_attn_fp8(const void* q, const void* k_fp8, const void* v_fp8,
                            int32_t n_keep, const bsa_shape* shape, int32_t block_size,
                            float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
                            void* hip_stream) {
-  if (!q || !k_fp8 || !v_fp8 || !k_scales || !v_scales || !block_idx || !out ||
-      !shape_ok(shape) || n_keep < 1 || shape->seq_len < 1)
+  if (!q || !k_fp8 || !v_fp8 || !k_scales || !v_scales || !block_idx || !out)
     return BSA_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_fp8) || !aligned16(v_fp8) || !aligned16(out))
     return BSA_INVALID_ARG;
-  if (block_size < 1) return BSA_INVALID_ARG;
-  if (n_keep > bsa_num_blocks(shape->seq_len, block_size)) return BSA_INVALID_ARG;
+  bsa::DecodePlan plan;
+  const int rc = decode_checks(shape, n_keep, block_size, 0, workspace, ws_bytes, &plan);
+  if (rc != BSA_OK) return rc;
   const int ss = summary_stride(shape, block_size);
   if (ss < 0) return BSA_INVALID_ARG;
-  const int g = shape->n_q_heads / shape->n_kv_heads;
-  if (block_size != 64 || !dim_supported(shape->head_dim) || !group_supported(g))
-    return BSA_UNSUPPORTED;
-  const int64_t pairs = (int64_t)shape->batch * shape->n_kv_heads;
-  bsa::DecodePlan plan = bsa::plan_decode(pairs, n_keep, g, 0);
-  if (ws_bytes < bsa::decode_workspace_bytes(pairs, shape->head_dim, plan))
-    return BSA_WORKSPACE_TOO_SMALL;
-  if (!workspace || !aligned16(workspace)) return BSA_INVALID_ARG;
   if (scale == 0.f) scale = 1.f / sqrtf((float)shape->head_dim);
-  bsa::launch_decode_fp8(static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_fp8),
-                         static_cast<const uint8_t*>(v_fp8), k_scales, v_scales, ss, block_idx,
-                         n_keep, shape->batch, shape->n_q_heads, shape->n_kv_heads,
-                         shape->head_dim, shape->seq_len, shape->seq_stride, scale, plan,
-                         static_cast<float*>(workspace), out, lse,
-                         static_cast<hipStream_t>(hip_stream));
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  bsa::launch_decode_partials_fp8(static_cast<const uint16_t*>(q),
+                                  static_cast<const uint8_t*>(k_fp8),
+                                  static_cast<const uint8_t*>(v_fp8), k_scales, v_scales, ss,
+                                  block_idx, n_keep, shape->batch, shape->n_q_heads,
+                                  shape->n_kv_heads, shape->head_dim, shape->seq_len,
+                                  shape->seq_stride, scale, plan,
+                                  static_cast<float*>(workspace), st);
+  bsa::launch_decode_merge(shape->batch, shape->n_q_heads, shape->n_kv_heads, shape->head_dim,
+                           plan, static_cast<const float*>(workspace), out, lse, st);
   return launch_status();
 }
 

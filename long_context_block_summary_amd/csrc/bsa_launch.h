@@ -46,16 +46,21 @@ struct DecodePlan {
 DecodePlan plan_decode(int64_t pairs, int n_keep, int g, int n_splits_req);
 size_t decode_workspace_bytes(int64_t pairs, int d, const DecodePlan& p);
 
-// split-K partials + merge.  ws holds [pairs][splits][g][d] o and [pairs][splits][g][2] (m, l)
-void launch_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
-                   int n_keep, int B, int Hq, int Hkv, int d, int N, int stride, float scale,
-                   const DecodePlan& plan, float* ws, float* out, float* lse, hipStream_t st);
+// S4: split-K partials into the workspace: [pairs][splits][g][2] (m, l), then
+// [pairs][splits][g][d] o
+void launch_decode_partials(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const int32_t* idx, int n_keep, int B, int Hq, int Hkv, int d, int N,
+                            int stride, float scale, const DecodePlan& plan, float* ws,
+                            hipStream_t st);
 // the same over an E4M3 cache with per-(pair, block) K and V scales [pairs][sstride]
-void launch_decode_fp8(const uint16_t* q, const uint8_t* k, const uint8_t* v, const float* ksc,
-                       const float* vsc, int sstride, const int32_t* idx, int n_keep, int B,
-                       int Hq, int Hkv, int d, int N, int stride, float scale,
-                       const DecodePlan& plan, float* ws, float* out, float* lse,
-                       hipStream_t st);
+void launch_decode_partials_fp8(const uint16_t* q, const uint8_t* k, const uint8_t* v,
+                                const float* ksc, const float* vsc, int sstride,
+                                const int32_t* idx, int n_keep, int B, int Hq, int Hkv, int d,
+                                int N, int stride, float scale, const DecodePlan& plan, float* ws,
+                                hipStream_t st);
+// S5: exact log-sum-exp merge of the partials -> out [B][Hq][d], lse [B][Hq] (or null)
+void launch_decode_merge(int B, int Hq, int Hkv, int d, const DecodePlan& plan, const float* ws,
+                         float* out, float* lse, hipStream_t st);
 
 // chunked prefill: pooled queries, scores, top-k, three-branch attention
 struct PrefillLaunch {

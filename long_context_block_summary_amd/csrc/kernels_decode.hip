@@ -506,60 +506,76 @@ size_t decode_workspace_bytes(int64_t pairs, int d, const DecodePlan& p) {
   return (size_t)pairs * p.n_splits * p.g * (size_t)(d + 2) * sizeof(float);
 }
 
-template <int D, int G>
-static void launch_decode_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                            const int32_t* idx, int n_keep, int B, int Hq, int Hkv, int N,
-                            int stride, float scale, const DecodePlan& plan, float* ws,
-                            float* out, float* lse, hipStream_t st) {
-  const int64_t pairs = (int64_t)B * Hkv;
-  float* part_ml = ws;
-  float* part_o = part_ml + (size_t)pairs * plan.n_splits * G * 2;
-  dim3 grid(plan.n_splits, (unsigned)pairs);
-  decode_kernel<D, G, DEC_STAGES><<<grid, 256, 0, st>>>(
-      q, k, v, idx, n_keep, Hq, Hkv, N, stride, scale * LOG2E, plan.bps, plan.n_splits, part_o,
-      part_ml);
-  decode_merge_kernel<D><<<(unsigned)(B * Hq), D, 0, st>>>(part_o, part_ml, G, Hq, Hkv,
-                                                           plan.n_splits, out, lse);
+// partials at the front of the workspace: [pairs][splits][g][2] (m, l), then
+// [pairs][splits][g][d] o
+struct DecodeWs {
+  float* ml;
+  float* o;
+};
+static DecodeWs decode_ws(float* ws, int64_t pairs, int d, const DecodePlan& p) {
+  return {ws, ws + (size_t)pairs * p.n_splits * p.g * 2};
 }
 
 template <int D, int G>
-static void launch_decode_fp8_t(const uint16_t* q, const uint8_t* k, const uint8_t* v,
-                                const float* ksc, const float* vsc, int sstride,
-                                const int32_t* idx, int n_keep, int B, int Hq, int Hkv, int N,
-                                int stride, float scale, const DecodePlan& plan, float* ws,
-                                float* out, float* lse, hipStream_t st) {
+static void launch_partials_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* idx, int n_keep, int B, int Hq, int Hkv, int N,
+                              int stride, float scale, const DecodePlan& plan, float* ws,
+                              hipStream_t st) {
   const int64_t pairs = (int64_t)B * Hkv;
-  float* part_ml = ws;
-  float* part_o = part_ml + (size_t)pairs * plan.n_splits * G * 2;
+  const DecodeWs w = decode_ws(ws, pairs, D, plan);
+  dim3 grid(plan.n_splits, (unsigned)pairs);
+  decode_kernel<D, G, DEC_STAGES><<<grid, 256, 0, st>>>(
+      q, k, v, idx, n_keep, Hq, Hkv, N, stride, scale * LOG2E, plan.bps, plan.n_splits, w.o,
+      w.ml);
+}
+
+template <int D, int G>
+static void launch_partials_fp8_t(const uint16_t* q, const uint8_t* k, const uint8_t* v,
+                                  const float* ksc, const float* vsc, int sstride,
+                                  const int32_t* idx, int n_keep, int B, int Hq, int Hkv, int N,
+                                  int stride, float scale, const DecodePlan& plan, float* ws,
+                                  hipStream_t st) {
+  const int64_t pairs = (int64_t)B * Hkv;
+  const DecodeWs w = decode_ws(ws, pairs, D, plan);
   dim3 grid(plan.n_splits, (unsigned)pairs);
   decode_fp8_kernel<D, G, DEC_STAGES_FP8><<<grid, 256, 0, st>>>(
       q, k, v, ksc, vsc, sstride, idx, n_keep, Hq, Hkv, N, stride, scale * LOG2E, plan.bps,
-      plan.n_splits, part_o, part_ml);
-  decode_merge_kernel<D><<<(unsigned)(B * Hq), D, 0, st>>>(part_o, part_ml, G, Hq, Hkv,
-                                                           plan.n_splits, out, lse);
+      plan.n_splits, w.o, w.ml);
 }
 
-void launch_decode_fp8(const uint16_t* q, const uint8_t* k, const uint8_t* v, const float* ksc,
-                       const float* vsc, int sstride, const int32_t* idx, int n_keep, int B,
-                       int Hq, int Hkv, int d, int N, int stride, float scale,
-                       const DecodePlan& plan, float* ws, float* out, float* lse,
-                       hipStream_t st) {
-#define BSA_DEC(DD, GG)                                                                        \
-  if (d == DD && plan.g == GG)                                                                 \
-    return launch_decode_fp8_t<DD, GG>(q, k, v, ksc, vsc, sstride, idx, n_keep, B, Hq, Hkv, N, \
-                                       stride, scale, plan, ws, out, lse, st);
+void launch_decode_merge(int B, int Hq, int Hkv, int d, const DecodePlan& plan, const float* ws,
+                         float* out, float* lse, hipStream_t st) {
+  const DecodeWs w = decode_ws(const_cast<float*>(ws), (int64_t)B * Hkv, d, plan);
+  if (d == 128)
+    decode_merge_kernel<128><<<(unsigned)(B * Hq), 128, 0, st>>>(w.o, w.ml, plan.g, Hq, Hkv,
+                                                                 plan.n_splits, out, lse);
+  else
+    decode_merge_kernel<64><<<(unsigned)(B * Hq), 64, 0, st>>>(w.o, w.ml, plan.g, Hq, Hkv,
+                                                               plan.n_splits, out, lse);
+}
+
+void launch_decode_partials(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const int32_t* idx, int n_keep, int B, int Hq, int Hkv, int d, int N,
+                            int stride, float scale, const DecodePlan& plan, float* ws,
+                            hipStream_t st) {
+#define BSA_DEC(DD, GG)                                                                       \
+  if (d == DD && plan.g == GG)                                                                \
+    return launch_partials_t<DD, GG>(q, k, v, idx, n_keep, B, Hq, Hkv, N, stride, scale, plan, \
+                                     ws, st);
   BSA_DEC(128, 1) BSA_DEC(128, 2) BSA_DEC(128, 4) BSA_DEC(128, 8) BSA_DEC(128, 16)
   BSA_DEC(64, 1) BSA_DEC(64, 2) BSA_DEC(64, 4) BSA_DEC(64, 8) BSA_DEC(64, 16)
 #undef BSA_DEC
 }
 
-void launch_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
-                   int n_keep, int B, int Hq, int Hkv, int d, int N, int stride, float scale,
-                   const DecodePlan& plan, float* ws, float* out, float* lse, hipStream_t st) {
+void launch_decode_partials_fp8(const uint16_t* q, const uint8_t* k, const uint8_t* v,
+                                const float* ksc, const float* vsc, int sstride,
+                                const int32_t* idx, int n_keep, int B, int Hq, int Hkv, int d,
+                                int N, int stride, float scale, const DecodePlan& plan, float* ws,
+                                hipStream_t st) {
 #define BSA_DEC(DD, GG)                                                                        \
   if (d == DD && plan.g == GG)                                                                 \
-    return launch_decode_t<DD, GG>(q, k, v, idx, n_keep, B, Hq, Hkv, N, stride, scale, plan,  \
-                                   ws, out, lse, st);
+    return launch_partials_fp8_t<DD, GG>(q, k, v, ksc, vsc, sstride, idx, n_keep, B, Hq, Hkv, \
+                                         N, stride, scale, plan, ws, st);
   BSA_DEC(128, 1) BSA_DEC(128, 2) BSA_DEC(128, 4) BSA_DEC(128, 8) BSA_DEC(128, 16)
   BSA_DEC(64, 1) BSA_DEC(64, 2) BSA_DEC(64, 4) BSA_DEC(64, 8) BSA_DEC(64, 16)
 #undef BSA_DEC

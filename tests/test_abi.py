@@ -102,6 +102,32 @@ def test_argument_checks_launch_nothing(L):
                                 None, fake, 1 << 20, None) == -1
 
 
+def test_decode_step_calls_check_arguments(L):
+    """S4 (sparse_decode_partials) and S5 (sparse_decode_merge) alone: the checks of
+    sparse_decode_attn_split, and their own NULL / alignment checks."""
+    sh = bsa.make_shape(1, 4, 4, 128, 1024, 1024)
+    fake = ctypes.c_void_p(0x1000)
+    ws = 1 << 20
+    P, M = L.sparse_decode_partials, L.sparse_decode_merge
+    assert P(None, fake, fake, fake, 4, ctypes.byref(sh), 64, 0.0, fake, ws, 0, None) == -1
+    assert P(fake, fake, fake, None, 4, ctypes.byref(sh), 64, 0.0, fake, ws, 0, None) == -1
+    assert P(ctypes.c_void_p(0x1004), fake, fake, fake, 4, ctypes.byref(sh), 64, 0.0, fake, ws, 0,
+             None) == -1
+    assert P(fake, fake, fake, fake, 4, ctypes.byref(sh), 32, 0.0, fake, ws, 0, None) == -2
+    assert P(fake, fake, fake, fake, 17, ctypes.byref(sh), 64, 0.0, fake, ws, 0, None) == -1
+    assert P(fake, fake, fake, fake, 4, ctypes.byref(sh), 64, 0.0, fake, 16, 0, None) == -3
+    assert P(fake, fake, fake, fake, 4, ctypes.byref(sh), 64, 0.0, None, ws, 0, None) == -1
+    assert P(fake, fake, fake, fake, 4, ctypes.byref(sh), 64, 0.0, fake, ws, -1, None) == -1
+    assert M(ctypes.byref(sh), 4, 64, 0, fake, ws, None, None, None) == -1
+    assert M(ctypes.byref(sh), 4, 64, 0, fake, ws, ctypes.c_void_p(0x1008), None, None) == -1
+    assert M(ctypes.byref(sh), 4, 64, 0, fake, 16, fake, None, None) == -3
+    assert M(ctypes.byref(sh), 4, 64, 0, None, ws, fake, None, None) == -1
+    assert M(ctypes.byref(sh), 0, 64, 0, fake, ws, fake, None, None) == -1
+    g32 = bsa.make_shape(1, 32, 1, 128, 1024, 1024)
+    assert M(ctypes.byref(g32), 4, 64, 0, fake, ws, fake, None, None) == -2
+    assert M(None, 4, 64, 0, fake, ws, fake, None, None) == -1
+
+
 def test_prefill_argument_checks_launch_nothing(L):
     fake = ctypes.c_void_p(0x1000)
     pc = bsa.prefill_cfg()

@@ -137,6 +137,33 @@ def test_topk_candidate_counts(nb):
             assert np.array_equal(g_idx, o_idx)
 
 
+def test_partials_then_merge_equal_the_call():
+    """S4 then S5 as separate calls give sparse_decode_attn_split's result bit for bit, for
+    the library's split plan and explicit split counts; the merged output is within the
+    bound of the oracle."""
+    import torch
+    cfg = synth.scaled(synth.CONFIGS["gqa32k"], name="s4s5", batch=2, seq_len=64 * 300 + 17,
+                       top_k=41)
+    announce("s4s5", "B", cfg.batch, "N", cfg.seq_len)
+    t = synth.gen_decode(cfg, 61)
+    N, bs = cfg.seq_len, cfg.block_size
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    summ, _ = bsa.build_block_summaries(k, N, bs)
+    idx, _ = bsa.select_blocks(q, summ, N, bs, cfg.n_sink, cfg.n_local, cfg.top_k)
+    n_keep = idx.shape[2]
+    o_out, o_lse, _ = oracle.sparse_decode_attn(t["q"], t["k"], t["v"], idx.cpu().numpy(), N, bs)
+    for splits in (0, 1, 3, n_keep):
+        ref, ref_lse = bsa.sparse_decode_attn(q, k, v, idx, N, bs, n_splits=splits)
+        ws = bsa.sparse_decode_partials(q, k, v, idx, N, bs, n_splits=splits)
+        out, lse = bsa.sparse_decode_merge(ws, cfg.batch, cfg.n_q_heads, cfg.n_kv_heads,
+                                           cfg.head_dim, N, n_keep, bs, n_splits=splits,
+                                           seq_stride=k.shape[2])
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(lse, ref_lse), splits
+        assert np.abs(out.cpu().numpy() - o_out).max() <= OUT_ATOL
+        assert np.abs(lse.cpu().numpy() - o_lse).max() <= 1e-3
+
+
 def test_ties_prefer_lower_index():
     import torch
     announce("ties")
