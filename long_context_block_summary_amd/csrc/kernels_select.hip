@@ -324,6 +324,9 @@ void launch_scores(const uint16_t* q, const float* summ, int B, int Hq, int Hkv,
 // compacts in 1024-candidate strides.
 constexpr int TOPK_THREADS = 1024;
 constexpr int TOPK_WAVES = TOPK_THREADS / 64;
+// histogram copies of the register-resident select: 8 from 8 candidates per
+// thread on (where the first passes' same-address atomics dominate), else 1
+template <int KPT> struct TopkCopies { static constexpr int value = KPT >= 8 ? 8 : 1; };
 
 // block-wide exclusive prefix count of `flag` in thread order; returns the
 // thread's prefix and sets *total.  Uses wcnt[TOPK_WAVES] of LDS.
@@ -496,7 +499,12 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_reg_kernel(const float* __r
                                                                 int nb, int c0, int c1, int k,
                                                                 int n_keep, AdaptiveSel ad,
                                                                 int32_t* __restrict__ idx_out) {
-  __shared__ uint32_t hist[256];
+  // HC copies of the histogram (lane l counts into copy l % HC, rows padded
+  // by one word so the copies of a bin sit in different banks): keys of one
+  // pass mostly share a few digits, and same-address atomics of a wave
+  // serialise
+  constexpr int HC = TopkCopies<KPT>::value;
+  __shared__ uint32_t hist[HC][257];
   __shared__ uint32_t sh_digit, sh_above;
   __shared__ int wtot[TOPK_WAVES];
   __shared__ float ext[2][TOPK_WAVES];
@@ -551,12 +559,12 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_reg_kernel(const float* __r
   uint32_t remaining = (uint32_t)k;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
+    for (int i = tid; i < HC * 257; i += TOPK_THREADS) (&hist[0][0])[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
       const bool match = i0 + e < n && (pass == 0 || ((key[e] ^ prefix) >> (shift + 8)) == 0);
-      if (match) atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
+      if (match) atomicAdd(&hist[tid % HC][(key[e] >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (tid < 64) {
@@ -564,7 +572,11 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_reg_kernel(const float* __r
       const int lane = tid;
       uint32_t c[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) c[e] = hist[255 - 4 * lane - e];
+      for (int e = 0; e < 4; ++e) {
+        c[e] = 0;
+#pragma unroll
+        for (int cp = 0; cp < HC; ++cp) c[e] += hist[cp][255 - 4 * lane - e];
+      }
       const uint32_t own = c[0] + c[1] + c[2] + c[3];
       uint32_t inc = own;
 #pragma unroll
