@@ -352,21 +352,55 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
     wcnt[1][wave] = n_eq;
   }
   __syncthreads();
-  int gt_before = 0, eq_before = 0, tot_gt = 0;
+  int gt_before = 0, eq_before = 0, tot_gt = 0, tot_eq = 0;
 #pragma unroll
   for (int w = 0; w < PTK_WAVES; ++w) {
     const int cg = wcnt[0][w], ce = wcnt[1][w];
     tot_gt += cg;
+    tot_eq += ce;
     gt_before += w < wave ? cg : 0;
     eq_before += w < wave ? ce : 0;
   }
   const int need_eq = k - tot_gt;  // >= 1 by the choice of T
-  int pos = gt_before + min(eq_before, need_eq);  // selected keys of the earlier waves
-  int eq_rank = eq_before;                        // equal keys before this group
   // entry indices from an opaque copy of the lane id: computed here instead of
   // being kept live from the loads on
   int ln = lane;
   asm volatile("" : "+v"(ln));
+  // (not in the 1024-thread variant, whose 128 keys per thread already exceed
+  // its registers)
+  if (PTK_THREADS <= 512 && tot_eq == need_eq) {  // uniform: every key equal to T is taken
+    // per lane and group counts of three groups packed in 10-bit fields (a
+    // group's wave total is at most 256), one wave scan for the three
+    int pos = gt_before + eq_before;
+#pragma unroll
+    for (int v0 = 0; v0 < NV; v0 += 3) {
+      int packed = 0;
+#pragma unroll
+      for (int jg = 0; jg < 3; ++jg)
+        if (v0 + jg < NV) {
+          int ns = 0;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) ns += key[v0 + jg][c] >= T ? 1 : 0;
+          packed |= ns << (10 * jg);
+        }
+      int tot;
+      const int pre = wave_exscan(packed, &tot);
+#pragma unroll
+      for (int jg = 0; jg < 3; ++jg)
+        if (v0 + jg < NV) {
+          int p = pos + ((pre >> (10 * jg)) & 1023);
+          const int j = wbase + 256 * (v0 + jg) + 4 * ln;
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (key[v0 + jg][c] >= T) out[p++] = j + c;
+          pos += (tot >> (10 * jg)) & 1023;
+        }
+    }
+    return;
+  }
+  // ties at T: the first need_eq equal keys in index order are taken
+  int pos = gt_before + min(eq_before, need_eq);  // selected keys of the earlier waves
+  int eq_rank = eq_before;                        // equal keys before this group
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     // keys of group v in index order: lane-major, then c

@@ -171,3 +171,32 @@ def test_prefill_split_entry_points_compose():
     o_t, _ = bsa.sparse_prefill_attn_selected(q, k, v, *st[1:], tame, cfg.prior_len, cfg=pc)
     torch.cuda.synchronize()
     assert torch.equal(o_w, o_t)
+
+
+@pytest.mark.parametrize("prior_len", [64 * 40 + 16, 160_000, 270_000])
+def test_prefill_selection_exact_ties(prior_len):
+    """Integer keys constant over every 4-token group and integer queries: the pooled m = 4
+    keys are exact, the fp32 scores exact integers with many equal values, so the tile
+    selection must equal the oracle's exactly (lower entry index first at the k-th score).
+    Covers the top-k's tie path at 4 (644 entries) and 128 keys per thread with 512 threads
+    (40,000 entries) and with 1024 threads (67,500 entries); random scores (the other tests)
+    take the path without ties."""
+    import torch
+    B, Hq, Hkv, d, C, top_k = 1, 4, 1, 128, 64, 96
+    announce("pf_ties", "P", prior_len, "top_k", top_k)
+    rng = np.random.default_rng(prior_len)
+    n_tok = prior_len + C
+    groups = rng.integers(-2, 3, (B, Hkv, -(-n_tok // 4), d)).astype(np.float32)
+    k = synth.bf16_round(np.repeat(groups, 4, axis=2)[:, :, :n_tok])
+    v = synth.bf16_round(rng.standard_normal((B, Hkv, n_tok, d)).astype(np.float32))
+    q = synth.bf16_round(rng.integers(-1, 2, (B, C, Hq, d)).astype(np.float32))
+    pc = bsa.prefill_cfg(4, top_k, 128, 128, 64)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    st = bsa.build_compressed_streams(kd, vd, prior_len, pc)
+    sel = bsa.select_prefill_entries(qd, kd, st[0], prior_len, cfg=pc)
+    torch.cuda.synchronize()
+    o_sel = oracle.sparse_prefill_attn(q, k, v, prior_len, m_sparse=4, top_k=top_k, m_dense=128,
+                                       window=128, q_tile=64, rows=[0], want_sel=True)["sel"]
+    g_sel = sel.cpu().numpy()
+    assert g_sel.shape == o_sel.shape
+    assert np.array_equal(g_sel, o_sel)
