@@ -54,10 +54,11 @@ def partials_bytes(cfg, n_keep):
 def measured_traffic(workload, field="traffic_bytes_per_launch"):
     """HBM bytes per launch from the committed counter summary (`field`: the whole
     sparse_decode_attn call, or the S4 kernel alone), or None when the summary is for another
-    workload or the decode kernel source changed since it was taken."""
+    workload or the decode kernel's sources (kernels_decode.hip, then the device helpers
+    bsa_device.h, hashed as one byte string) changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_traffic.md")
-    src = os.path.join(ROOT, "long_context_block_summary_amd", "csrc", "kernels_decode.hip")
+    csrc = os.path.join(ROOT, "long_context_block_summary_amd", "csrc")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -65,7 +66,9 @@ def measured_traffic(workload, field="traffic_bytes_per_launch"):
         if ":" in line and not line.startswith(("|", "#", "`")):
             key, _, val = line.partition(":")
             fields[key.strip()] = val.strip()
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    src = b"".join(open(os.path.join(csrc, f), "rb").read()
+                   for f in ("kernels_decode.hip", "bsa_device.h"))
+    sha = hashlib.sha256(src).hexdigest()[:16]
     if fields.get("kernel_source_sha256_prefix") != sha:
         return None
     return float(fields[field]) if field in fields else None

@@ -102,16 +102,23 @@ __device__ __forceinline__ float fmax_nc(float a, float b) {
 // the even rows of its second, v_permlane32_swap the upper half of the first
 // with the lower half of the second; with x in both operands the two results
 // hold x of the two partners.  VALU only (no LDS round trip as for a
-// ds_bpermute shuffle).
+// ds_bpermute shuffle).  The maximum is a v_med3 against +inf held in an SGPR
+// the compiler cannot see into: with the constant it would fold the median to
+// a plain max and canonicalise both swap results first.
+__device__ __forceinline__ float opaque_inf() {
+  float x;
+  asm("s_mov_b32 %0, 0x7f800000" : "=s"(x));
+  return x;
+}
 __device__ __forceinline__ float pair16_max(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                    false);
-  return fmax_nc(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]), opaque_inf());
 }
 __device__ __forceinline__ float pair32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                    false);
-  return fmax_nc(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]), opaque_inf());
 }
 
 // order LDS traffic between the lanes of one wave (no cross-wave barrier)

@@ -486,7 +486,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
   __shared__ __align__(16) uint4 k_lds[2][PF_CH * (D / 8)];      // entry rows, 16 B pieces, xor-swizzled
   __shared__ __align__(16) uint16_t vt_lds[2][D * PF_CH];        // V^T fp16 [dim][entry], 8 B groups swizzled
   __shared__ __align__(16) float xch[NW][3][RW];  // alpha, row max, running concat lse
-  __shared__ int32_t sel_lds[PF_MAX_SEL];                        // the tile's branch-A entries
+  __shared__ __align__(16) uint32_t sel_lds[PF_MAX_SEL];         // the tile's branch-A row offsets
 
   const int g = a.Hq / a.Hkv;
   const int prob = blockIdx.x;
@@ -518,43 +518,61 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
   const int T1 = min(a.P + a.C, a.P + tile * a.q_tile + a.q_tile);
   const int nC = (T1 - T0 + PF_CH - 1) / PF_CH;
   const int total = nA + nB + nC;
+  // rows are addressed as a uniform base (the pair's stream; for the window,
+  // its first token) plus a 32-bit byte offset: every stream a pair reads
+  // spans less than 4 GiB, and the loads take the offset in one VGPR
+  constexpr uint32_t RB = D * 2;  // bytes per entry row
+  const int eg = tid / LPR, pc = tid % LPR;
+  const uint32_t pcb = (uint32_t)(PB * pc);  // the thread's piece within a row
   {
+    // the tile's branch-A entries as row offsets, padded to whole chunks with
+    // the last entry; clamped: a caller's out-of-range index never leaves the stream
     const int32_t* sel = a.sel + ((int64_t)(b * a.n_tiles + tile) * a.Hkv + kvh) * a.ksel;
-    // clamped: a caller's out-of-range entry index never leaves the stream
-    for (int j = tid; j < a.ksel; j += NTH) sel_lds[j] = min(max(sel[j], 0), a.E4 - 1);
+    for (int j = tid; j < nA * PF_CH; j += NTH)
+      sel_lds[j] = (uint32_t)min(max(sel[min(j, a.ksel - 1)], 0), a.E4 - 1) * RB;
   }
   __syncthreads();
+  const char* const kA = reinterpret_cast<const char*>(a.k4 + pair * a.E4 * D);
+  const char* const vA = reinterpret_cast<const char*>(a.v4 + pair * a.E4 * D);
+  const char* const kB = reinterpret_cast<const char*>(a.k128 + pair * a.E128 * D);
+  const char* const vB = reinterpret_cast<const char*>(a.v128 + pair * a.E128 * D);
+  const char* const kC = reinterpret_cast<const char*>(a.k + (pair * a.stride + T0) * D);
+  const char* const vC = reinterpret_cast<const char*>(a.v + (pair * a.stride + T0) * D);
+  const uint32_t lastB = (uint32_t)(a.E128 - 1) * RB + pcb, lastC = (uint32_t)(T1 - T0 - 1) * RB + pcb;
 
   // global -> registers two chunks ahead (two register sets), stored to LDS
   // after the compute of the chunk before it.  Thread t moves bytes
   // [PB*(t % LPR), +PB) of the four consecutive entries 4*(t / LPR) + u: one
   // load instruction reads whole rows.
-  const int eg = tid / LPR, pc = tid % LPR;
   Piece kreg[2][4], vreg[2][4];
   auto load_chunk = [&](int set, int gc) {
-    const uint16_t *kb, *vb;
-    int64_t row[4];
+    const char *kb, *vb;
+    uint32_t off[4];
     if (gc < nA) {  // uniform
-#pragma unroll
-      for (int u = 0; u < 4; ++u) row[u] = pair * a.E4 + sel_lds[min(gc * PF_CH + 4 * eg + u, a.ksel - 1)];
-      kb = a.k4;
-      vb = a.v4;
+      const uint4 o = *reinterpret_cast<const uint4*>(&sel_lds[gc * PF_CH + 4 * eg]);
+      off[0] = o.x + pcb;
+      off[1] = o.y + pcb;
+      off[2] = o.z + pcb;
+      off[3] = o.w + pcb;
+      kb = kA;
+      vb = vA;
     } else if (gc < nA + nB) {
+      const uint32_t r0 = (uint32_t)((gc - nA) * PF_CH + 4 * eg) * RB + pcb;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) row[u] = pair * a.E128 + min((gc - nA) * PF_CH + 4 * eg + u, a.E128 - 1);
-      kb = a.k128;
-      vb = a.v128;
+      for (int u = 0; u < 4; ++u) off[u] = min(r0 + u * RB, lastB);
+      kb = kB;
+      vb = vB;
     } else {
+      const uint32_t r0 = (uint32_t)((gc - nA - nB) * PF_CH + 4 * eg) * RB + pcb;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        row[u] = pair * a.stride + min(T0 + (gc - nA - nB) * PF_CH + 4 * eg + u, T1 - 1);
-      kb = a.k;
-      vb = a.v;
+      for (int u = 0; u < 4; ++u) off[u] = min(r0 + u * RB, lastC);
+      kb = kC;
+      vb = vC;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      kreg[set][u] = ld_stream(reinterpret_cast<const Piece*>(kb + row[u] * D) + pc);
-      vreg[set][u] = ld_stream(reinterpret_cast<const Piece*>(vb + row[u] * D) + pc);
+      kreg[set][u] = ld_stream(reinterpret_cast<const Piece*>(kb + off[u]));
+      vreg[set][u] = ld_stream(reinterpret_cast<const Piece*>(vb + off[u]));
     }
   };
   auto store_chunk = [&](int set, int buf) {
