@@ -48,6 +48,8 @@ def load(path=LIB_PATH):
     lib.oracle_round_bf16.restype = ctypes.c_uint16
     lib.oracle_block_summaries.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp]
     lib.oracle_block_summaries.restype = ctypes.c_int
+    lib.oracle_block_summaries_f32.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.oracle_block_summaries_f32.restype = ctypes.c_int
     lib.oracle_select_blocks.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f64,
                                          vp, vp]
     lib.oracle_select_blocks.restype = ctypes.c_int
@@ -111,6 +113,20 @@ def block_summaries(x, seq_len, block_size, lib=None):
     rc = lib.oracle_block_summaries(_p(x), B, H, seq_len, stride, d, block_size, _p(out))
     if rc:
         raise ValueError(f"oracle_block_summaries rc={rc}")
+    return out
+
+
+def block_summaries_f32(x, seq_len, block_size, lib=None):
+    """x: uint16 [B][H][stride][d] -> float32 [B][H][nb][d]: the fp32 running sum in token
+    order, then one fp32 division by the block's token count."""
+    lib = lib or load()
+    x = _u16(x)
+    B, H, stride, d = x.shape
+    nb = -(-seq_len // block_size)
+    out = np.empty((B, H, nb, d), np.float32)
+    rc = lib.oracle_block_summaries_f32(_p(x), B, H, seq_len, stride, d, block_size, _p(out))
+    if rc:
+        raise ValueError(f"oracle_block_summaries_f32 rc={rc}")
     return out
 
 

@@ -141,6 +141,34 @@ int oracle_block_summaries(const uint16_t* x, int32_t B, int32_t H, int32_t N,
   return 0;
 }
 
+/* ---- the fp32 summary: [KV] block-level evaluation unit; [CSA] 4.1 mean
+ * pool.  The pages fix the mean, not its fp32 evaluation; the reading taken
+ * here is the plainest loop: an fp32 running sum in token order, then an fp32
+ * division by the count (C on x86-64 evaluates float expressions in float,
+ * and the build disables contraction). */
+int oracle_block_summaries_f32(const uint16_t* x, int32_t B, int32_t H, int32_t N,
+                               int32_t stride, int32_t d, int32_t bs, float* out) {
+  if (!x || !out || B < 0 || H < 0 || N < 0 || d <= 0 || bs <= 0 || stride < N) return -1;
+  int32_t nb = oracle_num_blocks(N, bs);
+  int64_t nbh = (int64_t)B * H;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t bh = 0; bh < nbh; ++bh) {
+    const uint16_t* xs = x + bh * (int64_t)stride * d;
+    for (int32_t j = 0; j < nb; ++j) {
+      int32_t t0 = j * bs;
+      int32_t t1 = t0 + bs < N ? t0 + bs : N;
+      float* o = out + (bh * nb + j) * (int64_t)d;
+      for (int32_t c = 0; c < d; ++c) {
+        float s = 0.0f;
+        for (int32_t t = t0; t < t1; ++t)
+          s = s + (float)bf(xs[(int64_t)t * d + c]); /* the conversion is exact */
+        o[c] = s / (float)(t1 - t0);
+      }
+    }
+  }
+  return 0;
+}
+
 /* ---- selection order: higher score first, lower index on equal scores */
 typedef struct {
   double s;

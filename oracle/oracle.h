@@ -7,7 +7,8 @@
  * the HIP library.
  *
  * Inputs are bf16 bit patterns (uint16_t); every computation is carried out in
- * fp64; outputs are fp64.  Layouts (row-major):
+ * fp64 (except oracle_block_summaries_f32, which states its fp32 steps);
+ * outputs are fp64.  Layouts (row-major):
  *   q (decode)   [B][Hq][d]
  *   q (prefill)  [B][C][Hq][d]
  *   K, V         [B][Hkv][stride][d]   (stride = cache capacity in tokens)
@@ -36,6 +37,13 @@ int32_t oracle_num_threads(void);
 /* block summaries: out[b][h][j][c] = mean of x over the tokens of block j */
 int oracle_block_summaries(const uint16_t* x, int32_t B, int32_t H, int32_t N,
                            int32_t stride, int32_t d, int32_t bs, double* out);
+
+/* the same mean as a stored fp32 summary: the block's values added one token
+ * at a time in fp32 (ascending token order, from 0), then one correctly
+ * rounded fp32 division by the token count.  The one place the oracle works
+ * in fp32: it fixes the fp32 summary bit for bit. */
+int oracle_block_summaries_f32(const uint16_t* x, int32_t B, int32_t H, int32_t N,
+                               int32_t stride, int32_t d, int32_t bs, float* out);
 
 /* per (b, kv head) block selection; idx_out [B][Hkv][n_keep] ascending,
  * scores_out [B][Hkv][nb] (candidates only; others set to NaN) or NULL */

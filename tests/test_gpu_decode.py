@@ -58,6 +58,8 @@ def run_decode_case(cfg, seed, capacity=None, n_splits=0):
     o_summ = oracle.block_summaries(t["k"], N, bs)
     tol = summary_tolerance(t["k"], N, bs)
     assert np.all(np.abs(g_summ - o_summ) <= tol), "summaries out of bound"
+    # and bit for bit the fp32 running sum in token order divided by the count
+    assert np.array_equal(g_summ, oracle.block_summaries_f32(t["k"], N, bs)), "fp32 summaries"
     # selection
     o_idx, o_scores = oracle.select_blocks(t["q"], o_summ, cfg.n_kv_heads, cfg.n_sink,
                                            cfg.n_local, cfg.top_k, cfg.keep_ratio)
@@ -202,6 +204,11 @@ def test_split_invariance_and_determinism():
         assert (l - ref_lse).abs().max().item() <= 1e-5, s
 
 
+def rne_bf16(x32):
+    """bf16 bits of fp32 values, rounded by the oracle (nearest, ties to even)."""
+    return np.vectorize(oracle.round_bf16, otypes=[np.uint16])(x32.astype(np.float64))
+
+
 def test_summaries_bf16_and_compressed_block_sizes():
     import torch
     for m, N in ((4, 64 * 50 + 2), (128, 128 * 20 + 5), (64, 64 * 33)):
@@ -215,8 +222,11 @@ def test_summaries_bf16_and_compressed_block_sizes():
         gb = from_dev_bf16(b16)
         ref = oracle.block_summaries(t["k"], N, m)
         assert np.all(np.abs(g32 - ref) <= summary_tolerance(t["k"], N, m))
-        # bf16 copy = the fp32 mean rounded to nearest even
-        assert np.array_equal(gb, synth.bf16_round(g32))
+        # bit for bit: the fp32 running sum in token order / count, and its bf16 rounding
+        # (nearest, ties to even)
+        o32 = oracle.block_summaries_f32(t["k"], N, m)
+        assert np.array_equal(g32, o32)
+        assert np.array_equal(gb, rne_bf16(o32))
         # and within one bf16 step of the exact mean rounded directly
         rb = synth.bf16_to_f32(gb).astype(np.float64)
         assert np.all(np.abs(rb - ref) <= np.abs(ref) * 2.0 ** -7 + summary_tolerance(t["k"], N, m))

@@ -90,6 +90,30 @@ def small(**kw):
     return synth.PrefillConfig(**base)
 
 
+def test_compressed_streams_bit_exact():
+    """The pooled streams (m = 4 fp32 + bf16 keys, bf16 values; m = 128 bf16 keys and values)
+    over a ragged prior length equal the oracle's fp32 token-order means and their bf16
+    roundings bit for bit."""
+    import torch
+    cfg = small(name="pf_streams", prior_len=64 * 37 + 22)
+    announce(cfg.name, "seed", 71, "P", cfg.prior_len, "streams")
+    t = synth.gen_prefill(cfg, 71)
+    k, v = to_dev(t["k"]), to_dev(t["v"])
+    pc = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile)
+    k4f, k4b, v4b, k128b, v128b = bsa.build_compressed_streams(k, v, cfg.prior_len, pc)
+    torch.cuda.synchronize()
+    bits = lambda a: a.view(torch.int16).cpu().numpy().view(np.uint16)
+    rne = np.vectorize(oracle.round_bf16, otypes=[np.uint16])
+    P = cfg.prior_len
+    o_k4 = oracle.block_summaries_f32(t["k"], P, cfg.m_sparse)
+    assert np.array_equal(k4f.cpu().numpy(), o_k4)
+    assert np.array_equal(bits(k4b), rne(o_k4.astype(np.float64)))
+    for got, x, m in ((v4b, t["v"], cfg.m_sparse), (k128b, t["k"], cfg.m_dense),
+                      (v128b, t["v"], cfg.m_dense)):
+        o = oracle.block_summaries_f32(x, P, m)
+        assert np.array_equal(bits(got), rne(o.astype(np.float64))), m
+
+
 def test_prefill_small_ragged_g4():
     run_prefill_case(small(), 61)
 

@@ -67,6 +67,12 @@ MUTANTS = [
      "E128, rk, rk, NULL, NULL, k128, k128,"),
     ("lse drops the max", "return zmax + log(l);", "return log(l);"),
     ("weights not normalised", "double p = z[t] / l;", "double p = z[t];"),
+    ("fp32 summary accumulates in fp64", "        float s = 0.0f;\n        for (int32_t t = t0; t < t1; ++t)\n          s = s + (float)bf(",
+     "        double s = 0.0;\n        for (int32_t t = t0; t < t1; ++t)\n          s = s + (float)bf("),
+    ("fp32 summary adds the tokens last to first", "        for (int32_t t = t0; t < t1; ++t)\n          s = s + (float)bf(",
+     "        for (int32_t t = t1 - 1; t >= t0; --t)\n          s = s + (float)bf("),
+    ("fp32 summary multiplies by a rounded reciprocal", "o[c] = s / (float)(t1 - t0);",
+     "o[c] = s * (1.0f / (float)(t1 - t0));"),
     ("pooled query skips a dimension", "for (int32_t c = 0; c < d; ++c) qbar[c] += bf(q[(b * Hq + h)",
      "for (int32_t c = 1; c < d; ++c) qbar[c] += bf(q[(b * Hq + h)"),
 ]

@@ -158,6 +158,79 @@ def test_summaries_ignore_tokens_past_seq_len(orc):
     assert np.array_equal(orc.block_summaries(x, 130, 64), orc.block_summaries(x2, 130, 64))
 
 
+def nearest_f32(fr):
+    """The fp32 value nearest to the rational fr, ties to the even significand (IEEE
+    round-to-nearest-even), found by exact rational comparison of the neighbours."""
+    from fractions import Fraction
+    c = np.float32(float(fr))
+    cands = [np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))]
+    best = min(abs(Fraction(float(x)) - fr) for x in cands)
+    tied = [x for x in cands if abs(Fraction(float(x)) - fr) == best]
+    return min(tied, key=lambda x: int(np.float32(x).view(np.uint32)) & 1)
+
+
+def test_summaries_f32_within_the_summation_bound(orc):
+    # the fp32 running sum of n values errs by at most (n - 1) u sum|x| (u = 2^-24), the
+    # division adds one rounding of the quotient
+    rng = np.random.default_rng(4)
+    N, bs = 64 * 6 + 23, 64
+    x = bf(rng.standard_normal((1, 3, N, 32)) * 5 + 2)
+    s32 = orc.block_summaries_f32(x, N, bs).astype(np.float64)
+    ref = orc.block_summaries(x, N, bs)
+    xf = np.abs(f(x))
+    for j in range(-(-N // bs)):
+        n = min(bs, N - j * bs)
+        bound = (n - 1) * 2.0 ** -24 * xf[:, :, j * bs:j * bs + n].sum(axis=2) / n
+        bound += 2.0 ** -24 * np.abs(ref[:, :, j]) * (1 + 2.0 ** -20)
+        assert np.all(np.abs(s32[:, :, j] - ref[:, :, j]) <= bound)
+
+
+def test_summaries_f32_exact_on_exact_sums(orc):
+    # multiples of 1/8 in [-64, 64] (bf16 keeps them multiples of 1/8): every partial sum of up
+    # to 64 of them is exact in fp32,
+    # so with a power-of-two count the stored mean is the exact mean
+    rng = np.random.default_rng(5)
+    x = grid(rng, (2, 2, 256, 16), -64, 64)
+    s32 = orc.block_summaries_f32(bf(x), 256, 64)
+    assert s32.dtype == np.float32
+    assert np.array_equal(s32.astype(np.float64), orc.block_summaries(bf(x), 256, 64))
+
+
+def test_summaries_f32_add_in_token_order(orc):
+    # 2^24 then 63 ones: in fp32, 2^24 + 1 rounds back to 2^24 (ties to even), so the
+    # running sum stays 2^24 and the mean is 2^18 exactly.  Ones first: 63, then
+    # 63 + 2^24 = 16777279 lies halfway between 16777278 and 16777280 and rounds to the
+    # even significand, 16777280; / 64 = 262145.  The exact mean, 262144.984375, is neither.
+    big = 2.0 ** 24
+    fwd = np.ones((1, 1, 64, 2), np.float32)
+    fwd[0, 0, 0] = big
+    rev = np.ones((1, 1, 64, 2), np.float32)
+    rev[0, 0, 63] = big
+    assert np.all(orc.block_summaries_f32(bf(fwd), 64, 64) == np.float32(262144.0))
+    assert np.all(orc.block_summaries_f32(bf(rev), 64, 64) == np.float32(262145.0))
+    assert np.all(orc.block_summaries(bf(fwd), 64, 64) == 262144.984375)
+
+
+def test_summaries_f32_divide_once_correctly_rounded(orc):
+    # partial last blocks of 3, 5, 7 and 11 tokens: the stored value is the fp32 rounding of
+    # (exact integer sum) / n, not a product with a rounded reciprocal
+    from fractions import Fraction
+    rng = np.random.default_rng(6)
+    for n in (3, 5, 7, 11):
+        N = 64 + n
+        x = rng.integers(-40, 41, size=(1, 1, N, 64)).astype(np.float32)
+        s32 = orc.block_summaries_f32(bf(x), N, 64)
+        sums = x[0, 0, 64:].astype(np.int64).sum(axis=0)
+        want = np.array([nearest_f32(Fraction(int(t), n)) for t in sums], np.float32)
+        assert np.array_equal(s32[0, 0, 1], want), n
+    # a case where the product with the rounded reciprocal 1/3 rounds differently
+    t = next(t for t in range(1, 4000)
+             if np.float32(t) * np.float32(1 / 3) != nearest_f32(Fraction(t, 3)))
+    x = np.zeros((1, 1, 67, 1), np.float32)
+    x[0, 0, 64] = t
+    assert orc.block_summaries_f32(bf(x), 67, 64)[0, 0, 1, 0] == nearest_f32(Fraction(t, 3))
+
+
 # ---------------------------------------------------------------- selection
 
 def tiny_inputs(seed=11):
