@@ -132,6 +132,14 @@ def test_prefill_window_and_topk_edges():
     run_prefill_case(small(name="pf_tiny_prior", prior_len=300, chunk_len=64), 73)
 
 
+@pytest.mark.parametrize("g", [4, 2])
+def test_prefill_largest_selection(g):
+    """The largest branch-A selection the attention keeps in LDS (4,096 entries) out of 5,003,
+    for 256- and 128-row tiles."""
+    run_prefill_case(small(name=f"pf_maxsel_g{g}", n_q_heads=2 * g, prior_len=4 * 5003,
+                           chunk_len=90, top_k_sparse=4096), 74 + g)
+
+
 @pytest.mark.parametrize("combine,with_sink", [(1, False), (0, True), (1, True)])
 def test_prefill_combine_and_sink(combine, with_sink):
     # concatenated softmax over the branches ("CSA + HCA 混合注意力机制" §4.3) and per-head
