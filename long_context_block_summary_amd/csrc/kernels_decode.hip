@@ -283,18 +283,19 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
 
 // FP8 (OCP E4M3) cache variant of decode_kernel.  K and V rows are one byte
 // per value with one fp32 scale per (b, kv head, 64-token block) each; the
-// E4M3 values convert exactly to bf16 (v_cvt_pk_f32_fp8, then the upper
-// halves), the K scale multiplies the block's logits and the V scale the
+// E4M3 values convert exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8 with a
+// unit scale, two values per instruction), the K scale multiplies the block's logits and the V scale the
 // weights PV reads, so the arithmetic is that of the bf16 kernel on the
 // dequantized cache.  Half the bytes per block, so P is one deeper.  The QK
 // k order is permuted so a lane's 8*KS key bytes are contiguous: lane l holds
 // dims [8*KS*(l/16) + 8*ks, +8) of k-step ks, on both operands.
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  // two E4M3 values (bytes 2*HI, 2*HI + 1 of w) -> two bf16 (exact: E4M3 fits bf16)
-  typedef float f2v __attribute__((ext_vector_type(2)));
-  const f2v f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-  return pick16(__float_as_uint(f.x), __float_as_uint(f.y), 0x07060302u);
+  // two E4M3 values (bytes 2*HI, 2*HI + 1 of w) -> two bf16 in one instruction
+  // (v_cvt_scalef32_pk_bf16_fp8 with scale 1: exact, E4M3 fits bf16)
+  typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+  const b2v r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 template <int D, int G, int P>
