@@ -492,7 +492,7 @@ def run_prefill(cfg, steps, warmup, flush_bytes=1 << 30):
             "streams_ingest_ms": sorted(r1)[1]}
 
 
-def run_cpu_baseline(cfg, t, budget_s=20.0, min_s=10.0):
+def run_cpu_baseline(cfg, t, budget_s=20.0, min_s=10.0, one_thread_s=4.0):
     """Oracle select + attend (given its fp64 summaries) on a bounded sample."""
     import numpy as np
 
@@ -518,11 +518,38 @@ def run_cpu_baseline(cfg, t, budget_s=20.0, min_s=10.0):
         elapsed += one(slice(0, nb_used))
         reps += 1
     qh = reps * nb_used * cfg.n_q_heads
-    return {"value": qh / elapsed, "unit": "queries*heads/s", "cores": oracle.num_threads(),
+    cores = oracle.num_threads()
+    # the same oracle on one thread, over one batch entry (bounded to a few seconds)
+    oracle.set_threads(1)
+    try:
+        reps1, el1 = 0, 0.0
+        while reps1 == 0 or el1 < one_thread_s:
+            el1 += one(slice(0, 1))
+            reps1 += 1
+    finally:
+        oracle.set_threads(cores)
+    return {"value": qh / elapsed, "unit": "queries*heads/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{cfg.name}: select + attend (fp64 oracle, summaries precomputed) for "
                       f"{nb_used} of {B} batch entries ({nb_used * cfg.n_q_heads} query heads), "
-                      f"{reps} passes, {elapsed:.2f} s"}
+                      f"{reps} passes, {elapsed:.2f} s",
+            "one_thread": {"value": reps1 * cfg.n_q_heads / el1, "unit": "queries*heads/s",
+                           "sample": f"{cfg.name}: 1 of {B} batch entries, {reps1} passes, "
+                                     f"{el1:.2f} s"},
+            "host": host_description()}
+
+
+def host_description():
+    """Logical CPUs and the CPU model of the host the oracle ran on."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
 
 
 def main():

@@ -44,6 +44,8 @@ def load(path=LIB_PATH):
     lib.oracle_num_kept.restype = i32
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
+    lib.oracle_set_threads.argtypes = [i32]
+    lib.oracle_set_threads.restype = None
     lib.oracle_round_bf16.argtypes = [f64]
     lib.oracle_round_bf16.restype = ctypes.c_uint16
     lib.oracle_block_summaries.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp]
@@ -97,6 +99,10 @@ def num_kept(nb, n_sink, n_local, top_k, keep_ratio=0.0, lib=None):
 
 def num_threads(lib=None):
     return (lib or load()).oracle_num_threads()
+
+
+def set_threads(n, lib=None):
+    (lib or load()).oracle_set_threads(int(n))
 
 
 def round_bf16(x, lib=None):

@@ -88,6 +88,14 @@ int32_t oracle_num_threads(void) {
 #endif
 }
 
+void oracle_set_threads(int32_t n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* candidate range [c0, c1) and |sink U local| for nb blocks */
 static void ranges(int32_t nb, int32_t n_sink, int32_t n_local, int32_t* c0, int32_t* c1,
                    int32_t* fixed) {

@@ -31,8 +31,9 @@ int32_t oracle_num_blocks(int32_t n, int32_t m);
 int32_t oracle_num_kept(int32_t nb, int32_t n_sink, int32_t n_local, int32_t top_k,
                         double keep_ratio);
 
-/* threads the oracle's parallel loops use */
+/* threads the oracle's parallel loops use, and a way to change it (n >= 1) */
 int32_t oracle_num_threads(void);
+void oracle_set_threads(int32_t n);
 
 /* block summaries: out[b][h][j][c] = mean of x over the tokens of block j */
 int oracle_block_summaries(const uint16_t* x, int32_t B, int32_t H, int32_t N,
