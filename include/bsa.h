@@ -41,7 +41,8 @@ extern "C" {
 /* status codes */
 #define BSA_OK 0
 #define BSA_INVALID_ARG (-1)       /* NULL pointer, bad shape, misalignment, n_keep mismatch */
-#define BSA_UNSUPPORTED (-2)       /* head_dim not in {64, 128}, unsupported block size or group */
+#define BSA_UNSUPPORTED (-2)       /* head_dim not in {64, 128}, unsupported block size or group,
+                                      or a size beyond a documented limit */
 #define BSA_WORKSPACE_TOO_SMALL (-3)
 #define BSA_HIP_ERROR (-4)         /* a launch failed (hipGetLastError after launch) */
 
@@ -191,7 +192,11 @@ int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
  *              aligned: split partials (o, m, l); contents on entry are irrelevant.
  *              Calls that overlap in time must not share a workspace.
  * block_size must be 64; n_keep >= 1; Hq/Hkv in {1, 2, 4, 8, 16}.  A partial
- * last block contributes only its tokens below seq_len. */
+ * last block contributes only its tokens below seq_len.  seq_len * d * 2 must not
+ * exceed 2^32 (a kv head's rows are addressed by 32-bit byte offsets; 16,777,216
+ * tokens at d = 128), else BSA_UNSUPPORTED; the same holds for
+ * sparse_decode_attn_split and sparse_decode_partials, and for
+ * sparse_decode_attn_fp8 with seq_len * d. */
 int sparse_decode_attn(const void* q, const void* k, const void* v, const int32_t* block_idx,
                        int32_t n_keep, const bsa_shape* shape, int32_t block_size, float scale,
                        float* out, float* lse, void* workspace, size_t ws_bytes,

@@ -231,14 +231,18 @@ int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
 
 // checks shared by the decode calls (shape, list length, block size, splits,
 // workspace); fills the plan.  Nothing is launched when a check fails.
+// elem_bytes: bytes per cached value (2 bf16, 1 FP8); the kernels address a
+// kv head's rows by 32-bit byte offsets from the head's base.
 static int decode_checks(const bsa_shape* shape, int32_t n_keep, int32_t block_size,
                          int32_t n_splits, const void* workspace, size_t ws_bytes,
-                         bsa::DecodePlan* plan) {
+                         bsa::DecodePlan* plan, int elem_bytes = 2) {
   if (!shape_ok(shape) || n_keep < 1 || n_splits < 0 || shape->seq_len < 1 || block_size < 1)
     return BSA_INVALID_ARG;
   if (n_keep > bsa_num_blocks(shape->seq_len, block_size)) return BSA_INVALID_ARG;
   const int g = shape->n_q_heads / shape->n_kv_heads;
   if (block_size != 64 || !dim_supported(shape->head_dim) || !group_supported(g))
+    return BSA_UNSUPPORTED;
+  if ((int64_t)shape->seq_len * shape->head_dim * elem_bytes > (int64_t(1) << 32))
     return BSA_UNSUPPORTED;
   const int64_t pairs = (int64_t)shape->batch * shape->n_kv_heads;
   *plan = bsa::plan_decode(pairs, n_keep, g, n_splits);
@@ -328,7 +332,7 @@ int sparse_decode_attn_fp8(const void* q, const void* k_fp8, const void* v_fp8,
   if (!aligned16(q) || !aligned16(k_fp8) || !aligned16(v_fp8) || !aligned16(out))
     return BSA_INVALID_ARG;
   bsa::DecodePlan plan;
-  const int rc = decode_checks(shape, n_keep, block_size, 0, workspace, ws_bytes, &plan);
+  const int rc = decode_checks(shape, n_keep, block_size, 0, workspace, ws_bytes, &plan, 1);
   if (rc != BSA_OK) return rc;
   const int ss = summary_stride(shape, block_size);
   if (ss < 0) return BSA_INVALID_ARG;

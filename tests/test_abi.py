@@ -126,6 +126,15 @@ def test_decode_step_calls_check_arguments(L):
     g32 = bsa.make_shape(1, 32, 1, 128, 1024, 1024)
     assert M(ctypes.byref(g32), 4, 64, 0, fake, ws, fake, None, None) == -2
     assert M(None, 4, 64, 0, fake, ws, fake, None, None) == -1
+    # a kv head's rows beyond 32-bit byte offsets: bf16 from 2^24 + 1 tokens at d = 128,
+    # FP8 from 2^25 + 1
+    for n, code in ((1 << 24, -3), ((1 << 24) + 64, -2)):
+        big = bsa.make_shape(1, 4, 4, 128, n, n)
+        assert P(fake, fake, fake, fake, 4, ctypes.byref(big), 64, 0.0, fake, 16, 0, None) == code
+    for n, code in ((1 << 25, -3), ((1 << 25) + 64, -2)):
+        big = bsa.make_shape(1, 4, 4, 128, n, n)
+        assert L.sparse_decode_attn_fp8(fake, fake, fake, fake, fake, fake, 4, ctypes.byref(big),
+                                        64, 0.0, fake, None, fake, 16, None) == code
 
 
 def test_prefill_argument_checks_launch_nothing(L):
