@@ -324,6 +324,43 @@ def run_fp8(cfg, steps, warmup, t, flush_bytes=1 << 30):
             "timed": "select_blocks + sparse_decode_attn_fp8, cold cache"}
 
 
+def run_fused_step(cfg, steps, warmup, t, flush_bytes=1 << 30):
+    """The same decode step as one sparse_decode_step call (block scores, then the top-k
+    done by every attention workgroup for its own pair inside the attention launch, then
+    the merge); block_idx and outputs equal the two calls' bit for bit."""
+    import numpy as np
+    import torch
+
+    import long_context_block_summary_amd as bsa
+
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to(t["q"]), to(t["k"]), to(t["v"])
+    N, bs = cfg.seq_len, cfg.block_size
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    summ, _ = bsa.build_block_summaries(k, N, bs)
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev)
+    out, lse, idx = bsa.sparse_decode_step(q, k, v, summ, N, bs, cfg.n_sink, cfg.n_local,
+                                           cfg.top_k, cfg.keep_ratio)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    step_ms = []
+    for i in range(warmup + steps):
+        flush.add_(1.0)
+        a, c = ev(), ev()
+        a.record(stream)
+        bsa.sparse_decode_step(q, k, v, summ, N, bs, cfg.n_sink, cfg.n_local, cfg.top_k,
+                               cfg.keep_ratio, block_idx=idx, out=out, lse=lse, workspace=ws)
+        c.record(stream)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            step_ms.append(a.elapsed_time(c))
+    ms = sum(step_ms) / len(step_ms)
+    return {"workload": cfg.name, "ms_per_step": ms,
+            "queries_heads_per_s": cfg.batch * cfg.n_q_heads / (ms / 1e3), **pct(step_ms),
+            "timed": "sparse_decode_step (select fused into the attention launch), cold cache"}
+
+
 def run_decode_loop(cfg, steps, warmup, t, flush_bytes=1 << 30):
     """Per generated token: append K/V, refresh the summary of its block, select, attend.
     The cache holds the workload's tokens; the loop starts `warmup + steps` tokens before
@@ -655,6 +692,7 @@ def main():
                        "step_GBps": (s2 + a2) / (r2["step_ms"] / 1e3) / 1e9,
                        "select_us": r2["sel_ms"] * 1e3, "attn_us": r2["att_ms"] * 1e3}
         del r2
+    line["fused_step"] = run_fused_step(cfg, max(10, args.steps // 2), 3, r["inputs"])
     line["decode_loop"] = run_decode_loop(cfg, max(10, args.steps // 2), 3, r["inputs"])
     line["adaptive_selection"] = run_adaptive(cfg, max(10, args.steps // 2), 3, r["inputs"])
     line["fp8_kv"] = run_fp8(cfg, max(10, args.steps // 2), 3, r["inputs"])

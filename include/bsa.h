@@ -101,6 +101,7 @@ int32_t bsa_num_kept(int32_t nb, const bsa_select_cfg* cfg);
  * sparse_prefill_attn for these arguments (0 if none is needed; SIZE_MAX on
  * invalid arguments).  n_splits = 0 selects the library's own split plan. */
 size_t bsa_select_workspace_size(const bsa_shape* shape, const bsa_select_cfg* cfg);
+size_t bsa_decode_step_workspace_size(const bsa_shape* shape, const bsa_select_cfg* cfg);
 size_t bsa_decode_workspace_size(const bsa_shape* shape, int32_t n_keep, int32_t block_size,
                                  int32_t n_splits);
 size_t bsa_prefill_workspace_size(const bsa_shape* shape, int32_t chunk_len,
@@ -174,6 +175,24 @@ int append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache
 int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
                   const bsa_select_cfg* cfg, int32_t* block_idx, float* scores_out,
                   void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* sparse_decode_step -- select_blocks followed by sparse_decode_attn, as one call:
+ * block scores (the hotdry.top post's block-level evaluation; "CSA + HCA 混合注意力机制"
+ * §4.4 steps 1-3), then, for d = 128 and up to 4,096 candidate blocks per (b, kv head),
+ * one attention launch whose workgroups each select their pair's kept blocks from the
+ * scores before attending (§2.1, §4.4 step 4), then the merge; other shapes run the
+ * same steps as separate launches.  block_idx and out/lse are those of the two calls
+ * (the same list, the same outputs bit for bit).
+ *   q, k, v, out, lse, scale  as for sparse_decode_attn
+ *   summaries   fp32 as for select_blocks
+ *   cfg         as for select_blocks; adaptive selection is BSA_UNSUPPORTED here
+ *   block_idx   int32 [B][Hkv][bsa_num_kept(nb, cfg)], written
+ *   workspace   bsa_decode_step_workspace_size(shape, cfg) bytes, 16-byte aligned
+ *               (block scores, then the split partials); contents on entry irrelevant */
+int sparse_decode_step(const void* q, const void* k, const void* v, const float* summaries,
+                       const bsa_shape* shape, const bsa_select_cfg* cfg, int32_t* block_idx,
+                       float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
+                       void* hip_stream);
 
 /* sparse_decode_attn -- exact softmax(q K^T * scale) V for every query head
  * over the tokens of its kv head's kept blocks ("CSA + HCA 混合注意力机制"

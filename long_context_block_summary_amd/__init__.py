@@ -64,6 +64,8 @@ def lib():
     L.bsa_select_workspace_size.restype = sz
     L.bsa_decode_workspace_size.argtypes = [P(bsa_shape), i32, i32, i32]
     L.bsa_decode_workspace_size.restype = sz
+    L.bsa_decode_step_workspace_size.argtypes = [P(bsa_shape), P(bsa_select_cfg)]
+    L.bsa_decode_step_workspace_size.restype = sz
     L.bsa_prefill_workspace_size.argtypes = [P(bsa_shape), i32, P(bsa_prefill_cfg)]
     L.bsa_prefill_workspace_size.restype = sz
     L.bsa_status_string.argtypes, L.bsa_status_string.restype = [ctypes.c_int], ctypes.c_char_p
@@ -78,6 +80,8 @@ def lib():
     L.sparse_decode_partials.argtypes = [vp, vp, vp, vp, i32, P(bsa_shape), i32, f32, vp, sz, i32,
                                          vp]
     L.sparse_decode_merge.argtypes = [P(bsa_shape), i32, i32, i32, vp, sz, vp, vp, vp]
+    L.sparse_decode_step.argtypes = [vp, vp, vp, vp, P(bsa_shape), P(bsa_select_cfg), vp, f32, vp,
+                                     vp, vp, sz, vp]
     L.sparse_prefill_attn.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, P(bsa_shape),
                                       P(bsa_prefill_cfg), f32, vp, vp, vp, vp, vp, sz, vp]
     L.select_prefill_entries.argtypes = [vp, i32, vp, P(bsa_shape), P(bsa_prefill_cfg), vp, vp,
@@ -93,7 +97,7 @@ def lib():
                "select_blocks", "sparse_decode_attn",
                "sparse_decode_attn_split", "sparse_decode_partials", "sparse_decode_merge",
                "sparse_prefill_attn", "select_prefill_entries",
-               "sparse_prefill_attn_selected"):
+               "sparse_prefill_attn_selected", "sparse_decode_step"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -242,6 +246,48 @@ def select_blocks(q, summaries, seq_len, block_size=64, n_sink=1, n_local=2, top
                                workspace.numel() if workspace is not None else 0,
                                _stream(q.device)))
     return block_idx, scores
+
+
+def sparse_decode_step(q, k, v, summaries, seq_len, block_size=64, n_sink=1, n_local=2, top_k=-1,
+                       keep_ratio=0.0, scale=0.0, block_idx=None, out=None, lse=None,
+                       workspace=None, want_lse=True):
+    """select_blocks then sparse_decode_attn in one call (the selection fused into the
+    attention launch where it fits).  Returns (out, lse or None, block_idx)."""
+    import torch
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(summaries, "summaries", torch.float32, 4)
+    B, Hq, d = q.shape
+    Hkv, stride = k.shape[1], k.shape[2]
+    S = summaries.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or summaries.shape[:2] != (B, Hkv):
+        raise ValueError("k, v and summaries shapes disagree")
+    nb = num_blocks(seq_len, block_size)
+    if S < nb:
+        raise ValueError(f"summaries hold {S} blocks, {nb} are in use")
+    cfg = select_cfg(block_size, n_sink, n_local, top_k, keep_ratio)
+    n_keep = num_kept(nb, cfg)
+    if n_keep < 1:
+        raise ValueError("invalid selection config")
+    shape = make_shape(B, Hq, Hkv, d, seq_len, stride, S)
+    ws_bytes = lib().bsa_decode_step_workspace_size(ctypes.byref(shape), ctypes.byref(cfg))
+    if ws_bytes == SIZE_MAX:
+        raise ValueError("invalid decode step arguments")
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if block_idx is None:
+        block_idx = torch.empty((B, Hkv, n_keep), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check("sparse_decode_step",
+           lib().sparse_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(summaries),
+                                    ctypes.byref(shape), ctypes.byref(cfg), _ptr(block_idx), scale,
+                                    _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                    _stream(q.device)))
+    return out, lse, block_idx
 
 
 def decode_workspace_size(B, Hq, Hkv, d, seq_len, n_keep, block_size=64, n_splits=0):

@@ -106,6 +106,13 @@ size_t bsa_select_workspace_size(const bsa_shape* shape, const bsa_select_cfg* c
   return (size_t)shape->batch * shape->n_kv_heads * (size_t)nb * sizeof(float);
 }
 
+size_t bsa_decode_step_workspace_size(const bsa_shape* shape, const bsa_select_cfg* cfg) {
+  if (!shape_ok(shape) || !select_cfg_ok(cfg)) return SIZE_MAX;
+  const int n_keep = bsa_num_kept(bsa_num_blocks(shape->seq_len, cfg->block_size), cfg);
+  const size_t dec = bsa_decode_workspace_size(shape, n_keep < 1 ? 1 : n_keep, cfg->block_size, 0);
+  if (dec == SIZE_MAX) return SIZE_MAX;
+  return (bsa_select_workspace_size(shape, cfg) + 255) / 256 * 256 + dec;
+}
 size_t bsa_decode_workspace_size(const bsa_shape* shape, int32_t n_keep, int32_t block_size,
                                  int32_t n_splits) {
   if (!shape_ok(shape) || n_keep < 1 || block_size < 1 || n_splits < 0) return SIZE_MAX;
@@ -229,13 +236,69 @@ int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
   return launch_status();
 }
 
+static int decode_checks(const bsa_shape* shape, int32_t n_keep, int32_t block_size,
+                         int32_t n_splits, const void* workspace, size_t ws_bytes,
+                         bsa::DecodePlan* plan, int elem_bytes = 2);
+
+int sparse_decode_step(const void* q, const void* k, const void* v, const float* summaries,
+                       const bsa_shape* shape, const bsa_select_cfg* cfg, int32_t* block_idx,
+                       float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
+                       void* hip_stream) {
+  if (!q || !k || !v || !summaries || !block_idx || !out || !shape_ok(shape) ||
+      !select_cfg_ok(cfg) || shape->seq_len < 1)
+    return BSA_INVALID_ARG;
+  if (cfg->adaptive) return BSA_UNSUPPORTED;  // the list length varies: use the two calls
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(summaries) || !aligned16(out))
+    return BSA_INVALID_ARG;
+  if (!dim_supported(shape->head_dim)) return BSA_UNSUPPORTED;
+  const int nb = bsa_num_blocks(shape->seq_len, cfg->block_size);
+  const int ss = summary_stride(shape, cfg->block_size);
+  if (ss < 0) return BSA_INVALID_ARG;
+  int c0, c1, fixed;
+  kept_ranges(nb, cfg->n_sink_blocks, cfg->n_local_blocks, &c0, &c1, &fixed);
+  const int top_k = list_k(nb, cfg, c0, c1, fixed);
+  const int n_keep = fixed + top_k;
+  if (ws_bytes < bsa_decode_step_workspace_size(shape, cfg)) return BSA_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned16(workspace)) return BSA_INVALID_ARG;
+  const size_t sel_bytes = (bsa_select_workspace_size(shape, cfg) + 255) / 256 * 256;
+  bsa::DecodePlan plan;
+  const int rc = decode_checks(shape, n_keep, cfg->block_size, 0,
+                               static_cast<char*>(workspace) + sel_bytes, ws_bytes - sel_bytes,
+                               &plan, 2);
+  if (rc != BSA_OK) return rc;
+  if (scale == 0.f) scale = 1.f / sqrtf((float)shape->head_dim);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  float* scores = static_cast<float*>(workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + sel_bytes);
+  const auto* qb = static_cast<const uint16_t*>(q);
+  const auto* kb = static_cast<const uint16_t*>(k);
+  const auto* vb = static_cast<const uint16_t*>(v);
+  if (c1 > c0)
+    bsa::launch_scores(qb, summaries, shape->batch, shape->n_q_heads, shape->n_kv_heads,
+                       shape->head_dim, nb, ss, c0, c1, scores, st);
+  if (bsa::decode_select_fusable(shape->head_dim, plan.g, c1 - c0, n_keep)) {
+    bsa::launch_decode_select_partials(qb, kb, vb, scores, nb, c0, c1, top_k, block_idx, n_keep,
+                                       shape->batch, shape->n_q_heads, shape->n_kv_heads,
+                                       shape->seq_len, shape->seq_stride, scale, plan, part, st);
+  } else {  // the same steps as separate launches
+    bsa::launch_topk(scores, (int64_t)shape->batch * shape->n_kv_heads, nb, c0, c1, top_k, n_keep,
+                     block_idx, st, false, top_k, top_k, 0.f);
+    bsa::launch_decode_partials(qb, kb, vb, block_idx, n_keep, shape->batch, shape->n_q_heads,
+                                shape->n_kv_heads, shape->head_dim, shape->seq_len,
+                                shape->seq_stride, scale, plan, part, st);
+  }
+  bsa::launch_decode_merge(shape->batch, shape->n_q_heads, shape->n_kv_heads, shape->head_dim,
+                           plan, part, out, lse, st);
+  return launch_status();
+}
+
 // checks shared by the decode calls (shape, list length, block size, splits,
 // workspace); fills the plan.  Nothing is launched when a check fails.
 // elem_bytes: bytes per cached value (2 bf16, 1 FP8); the kernels address a
 // kv head's rows by 32-bit byte offsets from the head's base.
 static int decode_checks(const bsa_shape* shape, int32_t n_keep, int32_t block_size,
                          int32_t n_splits, const void* workspace, size_t ws_bytes,
-                         bsa::DecodePlan* plan, int elem_bytes = 2) {
+                         bsa::DecodePlan* plan, int elem_bytes) {
   if (!shape_ok(shape) || n_keep < 1 || n_splits < 0 || shape->seq_len < 1 || block_size < 1)
     return BSA_INVALID_ARG;
   if (n_keep > bsa_num_blocks(shape->seq_len, block_size)) return BSA_INVALID_ARG;

@@ -48,6 +48,15 @@ size_t decode_workspace_bytes(int64_t pairs, int d, const DecodePlan& p);
 
 // S4: split-K partials into the workspace: [pairs][splits][g][2] (m, l), then
 // [pairs][splits][g][d] o
+// S3 + S4 in one launch: each workgroup selects its pair's kept blocks from the
+// block scores (candidates [c0, c1)) before it attends; split 0 writes the list
+// to idx_out.  Fusable for d = 128, up to 4096 candidates and 4160 kept blocks.
+bool decode_select_fusable(int d, int g, int n_cand, int n_keep);
+void launch_decode_select_partials(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const float* scores, int nb, int c0, int c1, int top_k,
+                                   int32_t* idx_out, int n_keep, int B, int Hq, int Hkv, int N,
+                                   int stride, float scale, const DecodePlan& plan, float* ws,
+                                   hipStream_t st);
 void launch_decode_partials(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const int32_t* idx, int n_keep, int B, int Hq, int Hkv, int d, int N,
                             int stride, float scale, const DecodePlan& plan, float* ws,

@@ -30,8 +30,11 @@
 //    second small kernel merges the splits exactly with log-sum-exp weights.
 #include <math.h>
 
+#include <type_traits>
+
 #include "bsa_device.h"
 #include "bsa_launch.h"
+#include "topk_device.h"
 
 namespace bsa {
 
@@ -179,12 +182,24 @@ __device__ __forceinline__ int split_blocks(const int32_t* list, int n_keep, int
 constexpr int DEC_STAGES = 3;
 constexpr int DEC_STAGES_FP8 = 4;
 
-template <int D, int G, int P>
+// SEL: the workgroup first selects its pair's kept blocks from the block
+// scores itself (the same list select_blocks writes; split 0 also writes it
+// to sel.idx_out) instead of reading idx: no separate top-k launch.
+struct FusedSelect {
+  const float* scores;  // [pairs][nb] block scores (candidates [c0, c1) written)
+  int nb, c0, c1, k;    // sink blocks [0, c0), candidates [c0, c1), local [c1, nb); top-k
+  int32_t* idx_out;     // [pairs][n_keep] kept list, written by split 0
+};
+constexpr int DEC_SEL_KPT = 16;                 // candidates per thread: up to 4096
+constexpr int DEC_SEL_MAX_CAND = 256 * DEC_SEL_KPT;
+constexpr int DEC_SEL_MAX_KEEP = DEC_SEL_MAX_CAND + 64;
+
+template <int D, int G, int P, int SELK = 0>
 __global__ __launch_bounds__(256, 2) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, int n_keep, int Hq, int Hkv,
     int N, int stride, float scale_log2, int bps, int n_splits, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    float* __restrict__ part_ml, FusedSelect fs = {}) {
   constexpr int KS = D / 32;  // QK k-steps over the head dim
   constexpr int NB = D / 64;  // 64-column blocks of a V row (16 lanes x 4 columns)
   constexpr int NC = D / 16;  // PV column chunks
@@ -209,8 +224,27 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
       qf[ks] = (l16 < G) ? qs[l16 * (D / 8) + ks * 4 + j4] : make_uint4(0, 0, 0, 0);
   }
 
+  constexpr bool SEL = SELK > 0;
+  using SelShared = std::conditional_t<SEL, TopkShared<256, 8>, char>;
+  __shared__ SelShared sel_sh;
+  __shared__ int32_t list_lds[SEL ? DEC_SEL_MAX_KEEP : 1];
+  if constexpr (SEL) {
+    // the pair's kept list into LDS: sink, the top-k of the candidates, local
+    const int n = fs.c1 - fs.c0;
+    for (int i = tid; i < fs.c0; i += 256) list_lds[i] = i;
+    for (int i = tid; i < fs.nb - fs.c1; i += 256) list_lds[fs.c0 + fs.k + i] = fs.c1 + i;
+    if (fs.k >= n) {  // uniform
+      for (int i = tid; i < n; i += 256) list_lds[fs.c0 + i] = fs.c0 + i;
+    } else if (fs.k > 0) {
+      topk_into_list<256, (SEL ? SELK : 1), 8>(fs.scores + (int64_t)pair * fs.nb + fs.c0, n,
+                                                fs.k, fs.c0, list_lds, sel_sh);
+    }
+    __syncthreads();
+    if (split == 0)
+      for (int i = tid; i < n_keep; i += 256) fs.idx_out[(int64_t)pair * n_keep + i] = list_lds[i];
+  }
   const int blk0 = split * bps;
-  const int32_t* list = idx + (int64_t)pair * n_keep + blk0;
+  const int32_t* list = SEL ? list_lds + blk0 : idx + (int64_t)pair * n_keep + blk0;
   const int nblk = split_blocks(list, n_keep, blk0, bps);
   const char* kb = reinterpret_cast<const char*>(k + (int64_t)pair * stride * D);
   const char* vb = reinterpret_cast<const char*>(v + (int64_t)pair * stride * D);
@@ -225,8 +259,6 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
   // 64-byte k-step) and V rows 4*j4 + r, columns 64*nb + 4*l16 .. +3
   uint4 kbuf[P][KS];
   uint2 vbuf[P][NB][4];
-  // j >= nblk issues a dummy load (every lane reads the pair's first row) so
-  // the pipeline never branches around its loads
   // j >= nblk issues a dummy load (every lane reads the pair's first row) so
   // the pipeline never branches around its loads
   auto issue = [&](int slot, int j) {
@@ -531,6 +563,24 @@ static void launch_partials_t(const uint16_t* q, const uint16_t* k, const uint16
 }
 
 template <int D, int G>
+static void launch_select_partials_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const FusedSelect& fs, int n_keep, int B, int Hq, int Hkv,
+                                     int N, int stride, float scale, const DecodePlan& plan,
+                                     float* ws, hipStream_t st) {
+  const int64_t pairs = (int64_t)B * Hkv;
+  const DecodeWs w = decode_ws(ws, pairs, D, plan);
+  dim3 grid(plan.n_splits, (unsigned)pairs);
+  if (fs.c1 - fs.c0 <= 256 * 8)  // 8 candidates per thread, else 16
+    decode_kernel<D, G, DEC_STAGES, 8><<<grid, 256, 0, st>>>(
+        q, k, v, nullptr, n_keep, Hq, Hkv, N, stride, scale * LOG2E, plan.bps, plan.n_splits,
+        w.o, w.ml, fs);
+  else
+    decode_kernel<D, G, DEC_STAGES, DEC_SEL_KPT><<<grid, 256, 0, st>>>(
+        q, k, v, nullptr, n_keep, Hq, Hkv, N, stride, scale * LOG2E, plan.bps, plan.n_splits,
+        w.o, w.ml, fs);
+}
+
+template <int D, int G>
 static void launch_partials_fp8_t(const uint16_t* q, const uint8_t* k, const uint8_t* v,
                                   const float* ksc, const float* vsc, int sstride,
                                   const int32_t* idx, int n_keep, int B, int Hq, int Hkv, int N,
@@ -553,6 +603,25 @@ void launch_decode_merge(int B, int Hq, int Hkv, int d, const DecodePlan& plan, 
   else
     decode_merge_kernel<64><<<(unsigned)(B * Hq), 64, 0, st>>>(w.o, w.ml, plan.g, Hq, Hkv,
                                                                plan.n_splits, out, lse);
+}
+
+bool decode_select_fusable(int d, int g, int n_cand, int n_keep) {
+  return d == 128 && n_cand <= DEC_SEL_MAX_CAND && n_keep <= DEC_SEL_MAX_KEEP &&
+         (g == 1 || g == 2 || g == 4 || g == 8 || g == 16);
+}
+
+void launch_decode_select_partials(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const float* scores, int nb, int c0, int c1, int top_k,
+                                   int32_t* idx_out, int n_keep, int B, int Hq, int Hkv, int N,
+                                   int stride, float scale, const DecodePlan& plan, float* ws,
+                                   hipStream_t st) {
+  const FusedSelect fs{scores, nb, c0, c1, top_k, idx_out};
+#define BSA_DEC(GG)                                                                            \
+  if (plan.g == GG)                                                                            \
+    return launch_select_partials_t<128, GG>(q, k, v, fs, n_keep, B, Hq, Hkv, N, stride, scale, \
+                                             plan, ws, st);
+  BSA_DEC(1) BSA_DEC(2) BSA_DEC(4) BSA_DEC(8) BSA_DEC(16)
+#undef BSA_DEC
 }
 
 void launch_decode_partials(const uint16_t* q, const uint16_t* k, const uint16_t* v,

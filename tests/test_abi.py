@@ -137,6 +137,27 @@ def test_decode_step_calls_check_arguments(L):
                                         64, 0.0, fake, None, fake, 16, None) == code
 
 
+def test_decode_step_checks_arguments(L):
+    """sparse_decode_step: NULL / alignment, adaptive selection refused, workspace size."""
+    sh = bsa.make_shape(1, 4, 4, 128, 1024, 1024)
+    cfg = bsa.select_cfg(64, 1, 2, 4)
+    fake = ctypes.c_void_p(0x1000)
+    ws = L.bsa_decode_step_workspace_size(ctypes.byref(sh), ctypes.byref(cfg))
+    assert 0 < ws < 1 << 30
+    S = L.sparse_decode_step
+    args = lambda **kw: [kw.get("q", fake), fake, fake, fake, ctypes.byref(sh),
+                         ctypes.byref(kw.get("cfg", cfg)), kw.get("idx", fake), 0.0,
+                         kw.get("out", fake), None, kw.get("ws", fake), kw.get("ws_bytes", ws),
+                         None]
+    assert S(*args(q=None)) == -1
+    assert S(*args(idx=None)) == -1
+    assert S(*args(out=ctypes.c_void_p(0x1004))) == -1
+    assert S(*args(ws=None)) == -1
+    assert S(*args(ws_bytes=ws - 1)) == -3
+    adaptive = bsa.select_cfg(64, 1, 2, -1, 0.1, True, 0.2, 0.0)
+    assert S(*args(cfg=adaptive)) == -2
+
+
 def test_prefill_argument_checks_launch_nothing(L):
     fake = ctypes.c_void_p(0x1000)
     pc = bsa.prefill_cfg()

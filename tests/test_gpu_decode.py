@@ -166,6 +166,39 @@ def test_partials_then_merge_equal_the_call():
         assert np.abs(lse.cpu().numpy() - o_lse).max() <= 1e-3
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("long128k_15", {}),                                      # the headline shape, fused
+    ("gqa32k", dict(batch=3, seq_len=64 * 300 + 17)),         # ragged, fused
+    ("gqa32k", dict(batch=1, seq_len=64 * 40, top_k=0)),      # sink + local only
+    ("gqa32k", dict(batch=1, seq_len=64 * 40, top_k=500)),    # every block
+    ("gqa32k", dict(batch=1, seq_len=100, top_k=5)),          # fewer blocks than sink + local
+    ("gqa32k", dict(batch=1, seq_len=64 * 4103, top_k=400)),  # 4,100 candidates: separate launches
+    ("gqa32k", dict(batch=2, n_q_heads=32, head_dim=64, seq_len=64 * 200, top_k=30)),  # d = 64
+    ("gqa32k", dict(batch=2, n_kv_heads=2, n_q_heads=32, seq_len=64 * 200, top_k=30)),  # g = 16
+])
+def test_decode_step_equals_the_two_calls(name, kw):
+    """sparse_decode_step (the selection fused into the attention launch where it fits)
+    writes the list select_blocks writes and the outputs of sparse_decode_attn, bit for bit."""
+    import torch
+    cfg = synth.scaled(synth.CONFIGS[name], **kw)
+    seed = synth.DEFAULT_SEED.get(name, 0) + 5
+    announce("decode step", cfg.name, kw, "seed", seed)
+    t = synth.gen_decode(cfg, seed)
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    N, bs = cfg.seq_len, cfg.block_size
+    summ, _ = bsa.build_block_summaries(k, N, bs)
+    idx, _ = bsa.select_blocks(q, summ, N, bs, cfg.n_sink, cfg.n_local, cfg.top_k,
+                               cfg.keep_ratio)
+    out, lse = bsa.sparse_decode_attn(q, k, v, idx, N, bs)
+    for _ in range(2):  # twice: the workspace and outputs hold the previous call's values
+        out2, lse2, idx2 = bsa.sparse_decode_step(q, k, v, summ, N, bs, cfg.n_sink, cfg.n_local,
+                                                  cfg.top_k, cfg.keep_ratio)
+        torch.cuda.synchronize()
+        assert torch.equal(idx2, idx)
+        assert torch.equal(out2, out)
+        assert torch.equal(lse2, lse)
+
+
 def test_ties_prefer_lower_index():
     import torch
     announce("ties")
