@@ -237,6 +237,7 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
   __shared__ int red[2][PTK_MAX_WAVES];
   __shared__ int wcnt[2][PTK_WAVES];
   __shared__ uint32_t und[PTK_CAP + 64];  // undecided keys (+ a dummy slot per lane)
+  __shared__ uint32_t dhist[4][256];      // one histogram per digit of the last bits
   const int prob = blockIdx.x;  // sel order: [b][tile][kvh]
   const int b = prob / (n_tiles * Hkv), tile = (prob / Hkv) % n_tiles, kvh = prob % Hkv;
   const float* s = scores + (((int64_t)b * Hkv + kvh) * n_tiles + tile) * Es;
@@ -248,19 +249,39 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
     return;
   }
   const int wbase = wave * 64 * KPT;
+  // All loads are issued before any key is formed: the raw bits land in the
+  // key registers themselves, so every load of the row is in flight at once
+  // (with the keys formed load by load, the compiler issued the loads one
+  // memory latency apart).
   uint32_t key[NV][4];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    // branch-free: the load is clamped into the (padded) row, keys past E are 0
+    // branch-free: the load is clamped into the (padded) row
     const int j = wbase + 256 * v + 4 * lane;
-    const float4 f = *reinterpret_cast<const float4*>(s + min(j, Es - 4));
-    // all-ones where j + c < E (sign of j + c - E), else 0: no compare masks
-    // held across the load
-    auto keep = [&](int c) { return (uint32_t)((j + c - E) >> 31); };
-    key[v][0] = order_key(f.x) & keep(0);  // 0: below any real key
-    key[v][1] = order_key(f.y) & keep(1);
-    key[v][2] = order_key(f.z) & keep(2);
-    key[v][3] = order_key(f.w) & keep(3);
+    const uint4 r = *reinterpret_cast<const uint4*>(s + min(j, Es - 4));
+    key[v][0] = r.x;
+    key[v][1] = r.y;
+    key[v][2] = r.z;
+    key[v][3] = r.w;
+  }
+  // the empty asm statements are ordered after the barrier, and each key is
+  // formed from its statement's output: no key work moves between the loads
+  // (only where the compiler serialized them: the wide 512-thread variants;
+  // the 1024-thread variant's keys exceed its registers anyway)
+  if constexpr (PTK_THREADS <= 512 && KPT >= 64) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      asm volatile("" : "+v"(key[v][0]), "+v"(key[v][1]), "+v"(key[v][2]), "+v"(key[v][3]));
+  }
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int j = wbase + 256 * v + 4 * lane;
+    // all-ones where j + c < E (sign of j + c - E), else 0: keys past E are 0,
+    // below any real key
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      key[v][c] = order_key(__uint_as_float(key[v][c])) & (uint32_t)((j + c - E) >> 31);
   }
   // Threshold search.  Before each bit the undecided keys are those in
   // [T, T + 2^(bit+1)); n_ge counts keys >= T and n_top keys above the range.
@@ -317,22 +338,57 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
         und[((uint32_t)at & ~m) | ((uint32_t)dummy & m)] = key[v][c];
         at += 1 - (int)o;
       }
+    for (int i = tid; i < 4 * 256; i += PTK_THREADS) (&dhist[0][0])[i] = 0u;
     __syncthreads();
     uint32_t lk[PTK_CAP / PTK_THREADS];
 #pragma unroll
     for (int r = 0; r < PTK_CAP / PTK_THREADS; ++r) {
       const int j = tid + PTK_THREADS * r;
-      lk[r] = j < n_und ? und[j] : 0u;  // 0 never reaches a candidate (>= 1)
+      // padding 0: below every real key (the k-th largest key is a real one)
+      lk[r] = j < n_und ? und[j] : 0u;
     }
-    const int n_above = n_top;
-    for (; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      int cnt = 0;
+    // The last sh bits of T, in digits of up to 8 bits from the top: a
+    // histogram of the digit over the undecided keys that share T's bits above
+    // it, then the digit whose bin reaches the remaining rank counting from
+    // the top.  The histograms were cleared up front and every wave scans the
+    // bins itself, so each digit costs one barrier.
+    uint32_t remaining = (uint32_t)(k - n_top);  // rank of T among the undecided keys
+    int lo = sh;
+    for (int p = 0; lo > 0; ++p) {  // uniform, at most 4 digits
+      const int w = min(8, lo);
+      lo -= w;
+      const int hi = lo + w;  // bits [lo, hi) are this digit
 #pragma unroll
-      for (int r = 0; r < PTK_CAP / PTK_THREADS; ++r) cnt += lk[r] >= cand ? 1 : 0;
-      cnt = n_above + ptk_block_sum<PTK_WAVES>((int)wave_sum((float)cnt), red, parity);
-      parity ^= 1;
-      if (cnt >= k) T = cand;
+      for (int r = 0; r < PTK_CAP / PTK_THREADS; ++r) {
+        const uint32_t kv = lk[r];
+        const bool same = hi == 32 || ((kv ^ T) >> hi) == 0u;
+        if (same) atomicAdd(&dhist[p][(kv >> lo) & ((1u << w) - 1u)], 1u);
+      }
+      __syncthreads();
+      // lane l owns bins 255-4l .. 252-4l (descending order)
+      uint32_t c4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c4[e] = dhist[p][255 - 4 * lane - e];
+      const uint32_t own = c4[0] + c4[1] + c4[2] + c4[3];
+      uint32_t inc = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t t = __shfl_up(inc, off);
+        if (lane >= off) inc += t;
+      }
+      const uint32_t exc = inc - own;
+      const bool here = exc < remaining && remaining <= inc;  // exactly one lane
+      uint32_t dg = 0u, above = exc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool take = dg == 0u && above + c4[e] >= remaining;
+        dg = take ? (uint32_t)(256 - 4 * lane - e) : dg;  // digit + 1
+        above = (dg == 0u) ? above + c4[e] : above;
+      }
+      const int src = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(here));
+      const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)dg, src) - 1u;
+      remaining -= (uint32_t)__builtin_amdgcn_readlane((int)above, src);
+      T |= d << lo;
     }
   }
   // per-wave counts above and equal to T, prefixes over the waves
@@ -369,33 +425,28 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
   // (not in the 1024-thread variant, whose 128 keys per thread already exceed
   // its registers)
   if (PTK_THREADS <= 512 && tot_eq == need_eq) {  // uniform: every key equal to T is taken
-    // per lane and group counts of three groups packed in 10-bit fields (a
-    // group's wave total is at most 256), one wave scan for the three
+    // Per group of 256 keys, the lane's count (0..4) as three ballots of its
+    // bits: the lane's position is their weighted mbcnt, the group total their
+    // weighted popcount.  The indices are staged in LDS (und is free: its last
+    // reads precede the barriers since) and written out as whole rows.
     int pos = gt_before + eq_before;
 #pragma unroll
-    for (int v0 = 0; v0 < NV; v0 += 3) {
-      int packed = 0;
+    for (int v = 0; v < NV; ++v) {
+      int ns = 0;
 #pragma unroll
-      for (int jg = 0; jg < 3; ++jg)
-        if (v0 + jg < NV) {
-          int ns = 0;
+      for (int c = 0; c < 4; ++c) ns += key[v][c] >= T ? 1 : 0;
+      const uint64_t b0 = __builtin_amdgcn_ballot_w64((ns & 1) != 0);
+      const uint64_t b1 = __builtin_amdgcn_ballot_w64((ns & 2) != 0);
+      const uint64_t b2 = __builtin_amdgcn_ballot_w64((ns & 4) != 0);
+      int p = pos + (int)(lane_prefix(b0) + 2 * lane_prefix(b1) + 4 * lane_prefix(b2));
+      const int j = wbase + 256 * v + 4 * ln;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) ns += key[v0 + jg][c] >= T ? 1 : 0;
-          packed |= ns << (10 * jg);
-        }
-      int tot;
-      const int pre = wave_exscan(packed, &tot);
-#pragma unroll
-      for (int jg = 0; jg < 3; ++jg)
-        if (v0 + jg < NV) {
-          int p = pos + ((pre >> (10 * jg)) & 1023);
-          const int j = wbase + 256 * (v0 + jg) + 4 * ln;
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (key[v0 + jg][c] >= T) out[p++] = j + c;
-          pos += (tot >> (10 * jg)) & 1023;
-        }
+      for (int c = 0; c < 4; ++c)
+        if (key[v][c] >= T) und[p++] = (uint32_t)(j + c);
+      pos += __builtin_popcountll(b0) + 2 * __builtin_popcountll(b1) + 4 * __builtin_popcountll(b2);
     }
+    __syncthreads();
+    for (int i = tid; i < k; i += PTK_THREADS) out[i] = (int32_t)und[i];
     return;
   }
   // ties at T: the first need_eq equal keys in index order are taken
