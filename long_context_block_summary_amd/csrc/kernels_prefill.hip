@@ -59,13 +59,27 @@ __global__ __launch_bounds__(256) void prefill_qbar_kernel(const uint16_t* __res
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.f;
-#pragma unroll 4
-  for (int r = rg; r < rows; r += 16) {
-    const int i = i0 + r / g, h = kvh * g + r % g;
-    float f[8];
-    unpack8(reinterpret_cast<const uint4*>(q + (((int64_t)b * C + i) * Hq + h) * D)[col], f);
+  // rows in batches of 16 per thread, each batch's loads issued together
+  // (a batch slot past the tile's end reads row 0 and adds nothing); the
+  // rows are still added in order
+  constexpr int RB = 16;
+  for (int r0 = rg; r0 < rows; r0 += 16 * RB) {
+    uint4 piece[RB];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] += f[c];
+    for (int u = 0; u < RB; ++u) {
+      const int r = r0 + 16 * u < rows ? r0 + 16 * u : 0;
+      const int i = i0 + r / g, h = kvh * g + r % g;
+      piece[u] = reinterpret_cast<const uint4*>(q + (((int64_t)b * C + i) * Hq + h) * D)[col];
+    }
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      float f[8];
+      unpack8(piece[u], f);
+      if (r0 + 16 * u < rows) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] += f[c];
+      }
+    }
   }
 #pragma unroll
   for (int c = 0; c < 8; ++c) part[rg][8 * col + c] = acc[c];
@@ -89,7 +103,7 @@ __global__ __launch_bounds__(256) void prefill_qbar_kernel(const uint16_t* __res
 constexpr int PSC_GROUPS = 8;     // 16-entry groups per wave
 constexpr int PSC_MAX_TILES = 64; // pooled queries held in LDS per workgroup
 
-template <int D>
+template <int D, int NTB>
 __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __restrict__ ks,
                                                              const float* __restrict__ qbar,
                                                              int n_tiles, int Hkv, int E, int Es,
@@ -100,7 +114,10 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __rest
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, j4 = lane >> 4;
-  const int ntb = (n_tiles + 15) / 16;  // tile blocks of 16
+  // NTB = ceil(n_tiles / 16) tile blocks of 16, a compile-time count: with
+  // the stores in a loop of run-time length the compiler waited for every
+  // load (the next group's prefetch included) before each group's MFMAs
+  constexpr int ntb = NTB;
   for (int c = tid; c < ntb * 16 * D; c += 256) {
     const int tl = c / D, dd = c % D;
     qs[tl][dd] = tl < n_tiles ? qbar[(((int64_t)b * n_tiles + tl) * Hkv + kvh) * D + dd] : 0.f;
@@ -118,6 +135,7 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __rest
   };
   auto group = [&](int set, int gi) {
     const int e = e_first + 16 * gi + 4 * j4;  // lane's first entry of the output tile
+#pragma unroll
     for (int tb = 0; tb < ntb; ++tb) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -166,7 +184,7 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __rest
 constexpr int PTK_MAX_WAVES = 16;  // 1024 threads
 static_assert(PTK_MAX_WAVES * 64 * 128 >= PREFILL_MAX_E4, "largest key count per thread is 128");
 
-constexpr int PTK_CAP = 4096;  // undecided keys moved to LDS for the last bits
+constexpr int PTK_UND = 16384;  // undecided keys staged in LDS for the open bits
 
 // block sum of one value per wave (lane 0's), through LDS slot set `parity`
 template <int NWV>
@@ -236,8 +254,14 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
   constexpr int PTK_WAVES = PTK_THREADS / 64;
   __shared__ int red[2][PTK_MAX_WAVES];
   __shared__ int wcnt[2][PTK_WAVES];
-  __shared__ uint32_t und[PTK_CAP + 64];  // undecided keys (+ a dummy slot per lane)
-  __shared__ uint32_t dhist[4][256];      // one histogram per digit of the last bits
+  // staged keys (the bracket path: in index order, their indices in und_idx);
+  // a dummy slot per lane past PTK_UND takes the writes of unstaged keys
+  __shared__ uint32_t und[PTK_UND + 64];
+  __shared__ uint32_t und_idx[PTK_UND + 64];
+  __shared__ uint32_t dhist[4][256];      // one histogram per digit of the open bits
+  __shared__ uint32_t samp[PTK_THREADS];  // the bracket's sample
+  __shared__ int bsum[PTK_WAVES];
+  __shared__ uint32_t bmax[PTK_WAVES];
   const int prob = blockIdx.x;  // sel order: [b][tile][kvh]
   const int b = prob / (n_tiles * Hkv), tile = (prob / Hkv) % n_tiles, kvh = prob % Hkv;
   const float* s = scores + (((int64_t)b * Hkv + kvh) * n_tiles + tile) * Es;
@@ -283,84 +307,195 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
     for (int c = 0; c < 4; ++c)
       key[v][c] = order_key(__uint_as_float(key[v][c])) & (uint32_t)((j + c - E) >> 31);
   }
-  // Threshold search.  Before each bit the undecided keys are those in
-  // [T, T + 2^(bit+1)); n_ge counts keys >= T and n_top keys above the range.
-  // Full passes over the registers run until at most PTK_CAP keys are
-  // undecided; those are then copied to LDS and the remaining bits count only
-  // them (plus the n_top keys above them).
+  // Threshold search: T = the k-th largest key.
+  //
+  // First a bracket from a sample.  Each thread contributes one key, from its
+  // register group lane % NV so that the sample spreads over the row; with
+  // mu = k * samples / E the expected number of samples at or above T, the
+  // r-th largest sample, r = mu + 7 sqrt(mu) + 4, lies below T with a wide
+  // margin.  One pass counts the keys at or above it (n_lo) and finds the
+  // row's largest key; when k <= n_lo <= PTK_UND those keys are staged in LDS
+  // and T lies between the bracket and the maximum, sharing their common
+  // leading bits.  Otherwise (a sample that misses: heavy ties, tiny rows)
+  // full passes over the registers fix T bit by bit from the MSB until at
+  // most PTK_UND keys remain undecided, and those are staged.  The open low
+  // bits of T are then found as 8-bit radix digits over the staged keys.
   uint32_t T = 0;
-  int parity = 0;
-  int bit = 31;
-  int n_ge = PTK_THREADS * KPT, n_top = 0;
-  for (; bit >= 0 && n_ge - n_top > PTK_CAP; --bit) {  // uniform
-    const uint32_t cand = T | (1u << bit);
-    int cnt = 0;
+  int n_top = 0;  // keys above the undecided range (all among the top k)
+  int n_und = 0;  // undecided keys staged in und
+  int sh = 32;    // the bits of T below sh are open
+  bool staged = false;
+  {
+    uint32_t t[NV];
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
+    for (int v = 0; v < NV; ++v) t[v] = key[v][0];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) cnt = add_ge(cnt, key[v][c], cand);
-    cnt = ptk_block_sum<PTK_WAVES>((int)wave_sum((float)cnt), red, parity);  // exact: < 2^24
-    parity ^= 1;
-    if (cnt >= k) {
-      T = cand;
-      n_ge = cnt;
-    } else {
-      n_top = cnt;
+    for (int step = 1; step < NV; step <<= 1)
+#pragma unroll
+      for (int v = 0; v + step < NV; v += 2 * step) t[v] = (lane & step) ? t[v + step] : t[v];
+    samp[tid] = t[0];  // keys past E are 0: below every candidate
+  }
+  __syncthreads();
+  const float mu = (float)k * (float)PTK_THREADS / (float)E;
+  const int r_s = __builtin_amdgcn_readfirstlane((int)ceilf(mu + 7.f * sqrtf(mu) + 4.f));
+  if (r_s <= PTK_THREADS / 2) {  // uniform
+    // every wave finds the r_s-th largest sample itself (no barrier)
+    constexpr int NS = PTK_THREADS / 64;
+    uint32_t sm[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) sm[i] = samp[NS * lane + i];
+    uint32_t ts = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = ts | (1u << b);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(sm[i] >= cand));
+      if (cnt >= r_s) ts = cand;
+    }
+    if (ts != 0u) {  // uniform
+      int mine = 0;
+      uint32_t kmx = 0;
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          mine = add_ge(mine, key[v][c], ts);
+          kmx = max(kmx, key[v][c]);
+        }
+      int inc = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int x = __shfl_up(inc, off);
+        if (lane >= off) inc += x;
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, off));
+      if (lane == 63) bsum[wave] = inc;
+      if (lane == 0) bmax[wave] = kmx;
+      __syncthreads();
+      int before = 0, n_lo = 0;
+      uint32_t mx = 0;
+#pragma unroll
+      for (int w = 0; w < PTK_WAVES; ++w) {
+        const int cw = bsum[w];
+        before += w < wave ? cw : 0;
+        n_lo += cw;
+        mx = max(mx, bmax[w]);
+      }
+      if (n_lo >= k && n_lo <= PTK_UND) {  // uniform
+        // The keys at or above the bracket, with their indices, in index
+        // order: the wave's block starts after the earlier waves' keys; per
+        // group of 256 keys the lane's count (0..4) as three ballots of its
+        // bits gives its position (weighted mbcnt) and the group's total
+        // (weighted popcount).  Branch-free: unstaged keys write a dummy slot.
+        int pos = 0;
+#pragma unroll
+        for (int w = 0; w < PTK_WAVES; ++w) pos += w < wave ? bsum[w] : 0;
+        const int dummy = PTK_UND + lane;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          int ns = 0;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) ns += key[v][c] >= ts ? 1 : 0;
+          const uint64_t b0 = __builtin_amdgcn_ballot_w64((ns & 1) != 0);
+          const uint64_t b1 = __builtin_amdgcn_ballot_w64((ns & 2) != 0);
+          const uint64_t b2 = __builtin_amdgcn_ballot_w64((ns & 4) != 0);
+          int p = pos + (int)(lane_prefix(b0) + 2 * lane_prefix(b1) + 4 * lane_prefix(b2));
+          // the group's indices from an opaque copy of the lane id: formed
+          // here, not ahead of time for every group
+          int lnv = lane;
+          asm volatile("" : "+v"(lnv));
+          const int j = wbase + 256 * v + 4 * lnv;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const bool in = key[v][c] >= ts;
+            // separate arrays: a 64-bit write would need each key in a
+            // register pair with its index
+            const int a = in ? p : dummy;
+            und[a] = key[v][c];
+            und_idx[a] = (uint32_t)(j + c);
+            p += in ? 1 : 0;
+          }
+          pos += __builtin_popcountll(b0) + 2 * __builtin_popcountll(b1) +
+                 4 * __builtin_popcountll(b2);
+          __builtin_amdgcn_sched_barrier(0);  // one group's masks live at a time
+        }
+        n_und = n_lo;
+        sh = ts == mx ? 0 : 32 - __builtin_clz(ts ^ mx);
+        T = sh == 32 ? 0u : (ts >> sh) << sh;
+        staged = true;
+      }
     }
   }
-  if (bit >= 0) {
-    // undecided: key in [T, T + 2^sh), T a multiple of 2^sh.  Branch-free:
-    // out-of-range keys go to a per-lane dummy slot past PTK_CAP.
-    const int sh = bit + 1;  // uniform, 1..32
-    const uint32_t pre = sh == 32 ? 0u : (T >> sh);
-    auto outside_p = [&](uint32_t kv, uint32_t p) -> uint32_t {  // 1 when kv is decided
-      const uint32_t x = sh == 32 ? 0u : ((kv >> sh) ^ p);
-      return (x | (0u - x)) >> 31;
-    };
-    auto outside = [&](uint32_t kv) { return outside_p(kv, pre); };
-    int mine = 0;
+  if (!staged) {  // uniform
+    // Before each bit the undecided keys are those in [T, T + 2^(bit+1));
+    // n_ge counts keys >= T and n_top keys above the range.
+    int parity = 0;
+    int bit = 31;
+    int n_ge = PTK_THREADS * KPT;
+    for (; bit >= 0 && n_ge - n_top > PTK_UND; --bit) {  // uniform
+      const uint32_t cand = T | (1u << bit);
+      int cnt = 0;
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
+      for (int v = 0; v < NV; ++v)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) mine += 1 - (int)outside(key[v][c]);
-    int n_und;
-    int at = ptk_block_exscan<PTK_WAVES>(mine, red[0], &n_und);
-    const int dummy = PTK_CAP + lane;
-    // recomputed from an opaque copy of the prefix: not kept live across the scan
-    uint32_t pre2 = pre;
-    asm volatile("" : "+v"(pre2));
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t o = outside_p(key[v][c], pre2);
-        const uint32_t m = 0u - o;  // all ones when decided
-        und[((uint32_t)at & ~m) | ((uint32_t)dummy & m)] = key[v][c];
-        at += 1 - (int)o;
+        for (int c = 0; c < 4; ++c) cnt = add_ge(cnt, key[v][c], cand);
+      cnt = ptk_block_sum<PTK_WAVES>((int)wave_sum((float)cnt), red, parity);  // exact: < 2^24
+      parity ^= 1;
+      if (cnt >= k) {
+        T = cand;
+        n_ge = cnt;
+      } else {
+        n_top = cnt;
       }
-    for (int i = tid; i < 4 * 256; i += PTK_THREADS) (&dhist[0][0])[i] = 0u;
-    __syncthreads();
-    uint32_t lk[PTK_CAP / PTK_THREADS];
-#pragma unroll
-    for (int r = 0; r < PTK_CAP / PTK_THREADS; ++r) {
-      const int j = tid + PTK_THREADS * r;
-      // padding 0: below every real key (the k-th largest key is a real one)
-      lk[r] = j < n_und ? und[j] : 0u;
     }
-    // The last sh bits of T, in digits of up to 8 bits from the top: a
-    // histogram of the digit over the undecided keys that share T's bits above
+    sh = bit + 1;
+    if (sh > 0) {  // uniform
+      // undecided: key in [T, T + 2^sh), T a multiple of 2^sh.  Branch-free:
+      // out-of-range keys go to a per-lane dummy slot past PTK_UND.
+      const uint32_t pre = sh == 32 ? 0u : (T >> sh);
+      auto outside_p = [&](uint32_t kv, uint32_t p) -> uint32_t {  // 1 when kv is decided
+        const uint32_t x = sh == 32 ? 0u : ((kv >> sh) ^ p);
+        return (x | (0u - x)) >> 31;
+      };
+      int mine = 0;
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mine += 1 - (int)outside_p(key[v][c], pre);
+      int at = ptk_block_exscan<PTK_WAVES>(mine, red[0], &n_und);
+      const int dummy = PTK_UND + lane;
+      // recomputed from an opaque copy of the prefix: not kept live across the scan
+      uint32_t pre2 = pre;
+      asm volatile("" : "+v"(pre2));
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t o = outside_p(key[v][c], pre2);
+          const uint32_t m = 0u - o;  // all ones when decided
+          und[((uint32_t)at & ~m) | ((uint32_t)dummy & m)] = key[v][c];
+          at += 1 - (int)o;
+        }
+    }
+  }
+  for (int i = tid; i < 4 * 256; i += PTK_THREADS) (&dhist[0][0])[i] = 0u;
+  __syncthreads();
+  {
+    // The open sh bits of T, in digits of up to 8 bits from the top: a
+    // histogram of the digit over the staged keys that share T's bits above
     // it, then the digit whose bin reaches the remaining rank counting from
     // the top.  The histograms were cleared up front and every wave scans the
-    // bins itself, so each digit costs one barrier.
-    uint32_t remaining = (uint32_t)(k - n_top);  // rank of T among the undecided keys
+    // bins itself, so each digit costs one barrier.  Staged padding keys (0,
+    // past E) lie below the k-th largest key, which is a real one.
+    uint32_t remaining = (uint32_t)(k - n_top);  // rank of T among the staged keys
     int lo = sh;
     for (int p = 0; lo > 0; ++p) {  // uniform, at most 4 digits
       const int w = min(8, lo);
       lo -= w;
       const int hi = lo + w;  // bits [lo, hi) are this digit
-#pragma unroll
-      for (int r = 0; r < PTK_CAP / PTK_THREADS; ++r) {
-        const uint32_t kv = lk[r];
+      for (int j = tid; j < n_und; j += PTK_THREADS) {
+        const uint32_t kv = und[j];
         const bool same = hi == 32 || ((kv ^ T) >> hi) == 0u;
         if (same) atomicAdd(&dhist[p][(kv >> lo) & ((1u << w) - 1u)], 1u);
       }
@@ -390,6 +525,32 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
       remaining -= (uint32_t)__builtin_amdgcn_readlane((int)above, src);
       T |= d << lo;
     }
+  }
+  if (staged) {  // uniform
+    // The top k are the staged keys above T and the first k - #(> T) keys
+    // equal to T in index order.  Thread t walks the staged entries
+    // [t ch, (t + 1) ch), contiguous in index order; one workgroup scan of its
+    // two counts (packed: each total is below 2^15) places its selections.
+    const int ch = (n_und + PTK_THREADS - 1) / PTK_THREADS;
+    const int e0 = min(tid * ch, n_und), e1 = min(e0 + ch, n_und);
+    int ng = 0, nq = 0;
+    for (int e = e0; e < e1; ++e) {
+      const uint32_t kv = und[e];
+      ng += kv > T ? 1 : 0;
+      nq += kv == T ? 1 : 0;
+    }
+    int tot;
+    const int pre = ptk_block_exscan<PTK_WAVES>(ng | (nq << 16), red[0], &tot);
+    const int need_eq = k - (tot & 0xFFFF);  // >= 1 by the choice of T
+    int qr = pre >> 16;
+    int p = (pre & 0xFFFF) + min(qr, need_eq);
+    for (int e = e0; e < e1; ++e) {
+      const uint32_t kv = und[e];
+      const bool eq = kv == T;
+      if ((kv > T || (eq && qr < need_eq)) && p < k) out[p++] = (int32_t)und_idx[e];
+      qr += eq ? 1 : 0;
+    }
+    return;
   }
   // per-wave counts above and equal to T, prefixes over the waves
   int n_gt = 0, n_eq = 0;
@@ -940,7 +1101,13 @@ bool launch_prefill_select(const PrefillLaunch& L, int32_t* sel, hipStream_t st)
   prefill_qbar_kernel<<<probs, 256, 0, st>>>(L.q, L.C, L.Hq, L.Hkv, L.q_tile, L.n_tiles, qbar);
   dim3 sg((L.E4 + 64 * PSC_GROUPS - 1) / (64 * PSC_GROUPS), L.Hkv, L.B);
   if (L.n_tiles > PSC_MAX_TILES) return false;
-  prefill_scores_kernel<128><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores);
+  switch ((L.n_tiles + 15) / 16) {
+    case 1: prefill_scores_kernel<128, 1><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
+    case 2: prefill_scores_kernel<128, 2><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
+    case 3: prefill_scores_kernel<128, 3><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
+    case 4: prefill_scores_kernel<128, 4><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
+    default: return false;
+  }
   int nthr;
   const int kpt = prefill_topk_kpt(L.E4, &nthr);
 #define BSA_PTK(KK, NT)                                                                         \
