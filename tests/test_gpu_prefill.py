@@ -232,3 +232,44 @@ def test_prefill_selection_exact_ties(prior_len):
     g_sel = sel.cpu().numpy()
     assert g_sel.shape == o_sel.shape
     assert np.array_equal(g_sel, o_sel)
+
+
+@pytest.mark.parametrize("prior_len,top_k,keys", [
+    (80_000, 96, "equal"),    # 20,000 equal scores: the sample's bracket holds more keys than
+                              # the top-k stages, so the bit passes run
+    (40_000, 96, "equal"),    # 10,000 equal scores: staged, the bracket is the largest key
+    (8_192, 1_024, "normal"),  # k / entries = 1/2: no sample rank brackets it, bit passes
+    (64 * 700, 600, "normal"),  # 11,200 entries, a bracketed sample
+])
+def test_prefill_selection_threshold_paths(prior_len, top_k, keys):
+    """The tile selection equals the oracle's on inputs that steer the top-k's threshold
+    search down each of its paths (sample bracket, bit passes) and through all-equal scores,
+    where the lowest entry indices are taken."""
+    import torch
+    B, Hq, Hkv, d, C = 1, 4, 1, 128, 64
+    announce("pf_thr", "P", prior_len, "top_k", top_k, keys)
+    rng = np.random.default_rng(prior_len + top_k)
+    n_tok = prior_len + C
+    if keys == "equal":
+        k = synth.bf16_round(np.ones((B, Hkv, n_tok, d), np.float32))
+        q = synth.bf16_round(rng.integers(-1, 2, (B, C, Hq, d)).astype(np.float32))
+    else:
+        k = synth.bf16_round(rng.standard_normal((B, Hkv, n_tok, d)).astype(np.float32))
+        q = synth.bf16_round(rng.standard_normal((B, C, Hq, d)).astype(np.float32))
+    v = synth.bf16_round(rng.standard_normal((B, Hkv, n_tok, d)).astype(np.float32))
+    pc = bsa.prefill_cfg(4, top_k, 128, 128, 64)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    st = bsa.build_compressed_streams(kd, vd, prior_len, pc)
+    sel = bsa.select_prefill_entries(qd, kd, st[0], prior_len, cfg=pc)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_prefill_attn(q, k, v, prior_len, m_sparse=4, top_k=top_k, m_dense=128,
+                                     window=128, q_tile=64, rows=[0], want_sel=True,
+                                     want_sel_scores=True)
+    o_sel = ref["sel"]
+    g_sel = sel.cpu().numpy()
+    assert g_sel.shape == o_sel.shape
+    if keys == "equal":
+        assert np.array_equal(o_sel.reshape(-1, top_k)[0], np.arange(top_k))
+        assert np.array_equal(g_sel, o_sel)
+    else:
+        announce("  exempt ties", check_tile_selection(g_sel, o_sel, ref["sel_scores"]))
