@@ -255,9 +255,12 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
   __shared__ int red[2][PTK_MAX_WAVES];
   __shared__ int wcnt[2][PTK_WAVES];
   // staged keys (the bracket path: in index order, their indices in und_idx);
-  // a dummy slot per lane past PTK_UND takes the writes of unstaged keys
-  __shared__ uint32_t und[PTK_UND + 64];
-  __shared__ uint32_t und_idx[PTK_UND + 64];
+  // a dummy slot per lane past UND takes the writes of unstaged keys.  A row
+  // never stages more keys than a workgroup holds, so the small variants keep
+  // small arrays (and room for more workgroups per CU).
+  constexpr int UND = PTK_THREADS * KPT < PTK_UND ? PTK_THREADS * KPT : PTK_UND;
+  __shared__ uint32_t und[UND + 64];
+  __shared__ uint32_t und_idx[UND + 64];
   __shared__ uint32_t dhist[4][256];      // one histogram per digit of the open bits
   __shared__ uint32_t samp[PTK_THREADS];  // the bracket's sample
   __shared__ int bsum[PTK_WAVES];
@@ -314,11 +317,11 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
   // mu = k * samples / E the expected number of samples at or above T, the
   // r-th largest sample, r = mu + 7 sqrt(mu) + 4, lies below T with a wide
   // margin.  One pass counts the keys at or above it (n_lo) and finds the
-  // row's largest key; when k <= n_lo <= PTK_UND those keys are staged in LDS
+  // row's largest key; when k <= n_lo <= UND those keys are staged in LDS
   // and T lies between the bracket and the maximum, sharing their common
   // leading bits.  Otherwise (a sample that misses: heavy ties, tiny rows)
   // full passes over the registers fix T bit by bit from the MSB until at
-  // most PTK_UND keys remain undecided, and those are staged.  The open low
+  // most UND keys remain undecided, and those are staged.  The open low
   // bits of T are then found as 8-bit radix digits over the staged keys.
   uint32_t T = 0;
   int n_top = 0;  // keys above the undecided range (all among the top k)
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
         n_lo += cw;
         mx = max(mx, bmax[w]);
       }
-      if (n_lo >= k && n_lo <= PTK_UND) {  // uniform
+      if (n_lo >= k && n_lo <= UND) {  // uniform
         // The keys at or above the bracket, with their indices, in index
         // order: the wave's block starts after the earlier waves' keys; per
         // group of 256 keys the lane's count (0..4) as three ballots of its
@@ -391,7 +394,7 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
         int pos = 0;
 #pragma unroll
         for (int w = 0; w < PTK_WAVES; ++w) pos += w < wave ? bsum[w] : 0;
-        const int dummy = PTK_UND + lane;
+        const int dummy = UND + lane;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
           int ns = 0;
@@ -433,7 +436,7 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
     int parity = 0;
     int bit = 31;
     int n_ge = PTK_THREADS * KPT;
-    for (; bit >= 0 && n_ge - n_top > PTK_UND; --bit) {  // uniform
+    for (; bit >= 0 && n_ge - n_top > UND; --bit) {  // uniform
       const uint32_t cand = T | (1u << bit);
       int cnt = 0;
 #pragma unroll
@@ -452,7 +455,7 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
     sh = bit + 1;
     if (sh > 0) {  // uniform
       // undecided: key in [T, T + 2^sh), T a multiple of 2^sh.  Branch-free:
-      // out-of-range keys go to a per-lane dummy slot past PTK_UND.
+      // out-of-range keys go to a per-lane dummy slot past UND.
       const uint32_t pre = sh == 32 ? 0u : (T >> sh);
       auto outside_p = [&](uint32_t kv, uint32_t p) -> uint32_t {  // 1 when kv is decided
         const uint32_t x = sh == 32 ? 0u : ((kv >> sh) ^ p);
@@ -464,7 +467,7 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
 #pragma unroll
         for (int c = 0; c < 4; ++c) mine += 1 - (int)outside_p(key[v][c], pre);
       int at = ptk_block_exscan<PTK_WAVES>(mine, red[0], &n_und);
-      const int dummy = PTK_UND + lane;
+      const int dummy = UND + lane;
       // recomputed from an opaque copy of the prefix: not kept live across the scan
       uint32_t pre2 = pre;
       asm volatile("" : "+v"(pre2));
