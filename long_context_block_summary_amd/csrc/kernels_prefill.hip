@@ -15,10 +15,11 @@
 //   prefill_qbar_kernel    pooled tile queries (fp32)
 //   prefill_scores_kernel  scores = qbar . pooled keys as an fp32 MFMA product
 //                          ([tiles x d] . [d x entries] per kv head)
-//   prefill_topk_kernel    exact top-k per (tile, kv head): MSB-first threshold
-//                          search (full passes, then the undecided keys in LDS),
-//                          then an index-ordered compaction (ascending output,
-//                          lower index on ties)
+//   prefill_topk_kernel    exact top-k per (tile, kv head): the k-th largest
+//                          key bracketed from a sample (else fixed by MSB-first
+//                          bit passes), its open bits as radix digits over the
+//                          keys staged in LDS, then an index-ordered output
+//                          (ascending, lower index on ties)
 //   prefill_attn_kernel    one workgroup of 16*NT*NW (query, head) rows per
 //                          (tile, kv head); the branches' entries stream through
 //                          double-buffered LDS in chunks of 64: S^T = K Q^T on
@@ -176,11 +177,10 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __rest
 // top-k per (b, tile, kvh) over the E scores of a row (row stride Es, a
 // multiple of 4).  Wave w owns the keys [64*KPT*w, 64*KPT*(w+1)); lane l holds
 // keys 256v + 4l + c (v < KPT/4, c < 4) of that range, so each float4 load of
-// a wave reads 1 KB of consecutive scores.  T = the k-th largest key is built
-// bit by bit from the MSB: keep bit b set if at least k keys are >= (T | bit).
-// Then every key > T is taken, and the first k - #(> T) keys equal to T in
-// index order; the output is written in index order (prefix over the waves,
-// then a lane scan inside the wave).
+// a wave reads 1 KB of consecutive scores.  T = the k-th largest key; every
+// key > T is taken, and the first k - #(> T) keys equal to T in index order;
+// the output is written in index order.  How T is found is described at the
+// threshold search below.
 constexpr int PTK_MAX_WAVES = 16;  // 1024 threads
 static_assert(PTK_MAX_WAVES * 64 * 128 >= PREFILL_MAX_E4, "largest key count per thread is 128");
 
