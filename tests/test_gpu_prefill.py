@@ -240,6 +240,7 @@ def test_prefill_selection_exact_ties(prior_len):
     (40_000, 96, "equal"),    # 10,000 equal scores: staged, the bracket is the largest key
     (8_192, 1_024, "normal"),  # k / entries = 1/2: no sample rank brackets it, bit passes
     (64 * 700, 600, "normal"),  # 11,200 entries, a bracketed sample
+    (64 * 700 + 12, 600, "normal"),  # 11,203 entries: a ragged last float4 of the row
 ])
 def test_prefill_selection_threshold_paths(prior_len, top_k, keys):
     """The tile selection equals the oracle's on inputs that steer the top-k's threshold
