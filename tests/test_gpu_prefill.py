@@ -246,10 +246,22 @@ def test_prefill_selection_threshold_paths(prior_len, top_k, keys):
     """The tile selection equals the oracle's on inputs that steer the top-k's threshold
     search down each of its paths (sample bracket, bit passes) and through all-equal scores,
     where the lowest entry indices are taken."""
+    _threshold_case(prior_len, top_k, keys)
+
+
+@pytest.mark.parametrize("prior_len,top_k,keys", [(64 * 700 + 12, 600, "normal"),
+                                                  (40_000, 96, "equal")])
+def test_prefill_selection_threshold_batched(prior_len, top_k, keys):
+    """The same over 2 batch entries x 2 kv heads x 2 tiles: every (batch, tile, kv head)
+    row finds its own threshold and writes its own selection."""
+    _threshold_case(prior_len, top_k, keys, B=2, Hkv=2, Hq=8, C=128)
+
+
+def _threshold_case(prior_len, top_k, keys, B=1, Hkv=1, Hq=4, C=64):
     import torch
-    B, Hq, Hkv, d, C = 1, 4, 1, 128, 64
-    announce("pf_thr", "P", prior_len, "top_k", top_k, keys)
-    rng = np.random.default_rng(prior_len + top_k)
+    d = 128
+    announce("pf_thr", "B", B, "Hkv", Hkv, "P", prior_len, "top_k", top_k, keys)
+    rng = np.random.default_rng(prior_len + top_k + B)
     n_tok = prior_len + C
     if keys == "equal":
         k = synth.bf16_round(np.ones((B, Hkv, n_tok, d), np.float32))
