@@ -73,6 +73,18 @@ MUTANTS = [
      "        for (int32_t t = t1 - 1; t >= t0; --t)\n          s = s + (float)bf("),
     ("fp32 summary multiplies by a rounded reciprocal", "o[c] = s / (float)(t1 - t0);",
      "o[c] = s * (1.0f / (float)(t1 - t0));"),
+    ("fp8 attention ignores the key scale",
+     "sdot += bf(q[bh * d + c]) * (ks * lut[kr[c]]);", "sdot += bf(q[bh * d + c]) * (lut[kr[c]]);"),
+    ("fp8 keys take the first block's scale", "double ks = (double)kscales[p * sstride + blk];",
+     "double ks = (double)kscales[p * sstride];"),
+    ("branch A keys are the unrounded means",
+     "k4[i] = (float)bf(oracle_round_bf16(ks_exact[i]));", "k4[i] = (float)ks_exact[i];"),
+    ("branch A values are the unrounded means",
+     "v4[i] = (float)bf(oracle_round_bf16(tmp4[i]));", "v4[i] = (float)tmp4[i];"),
+    ("branch B keys are the unrounded means",
+     "k128[i] = (float)bf(oracle_round_bf16(tmp128[i]));", "k128[i] = (float)tmp128[i];"),
+    ("branch B values are the unrounded means",
+     "v128[i] = (float)bf(oracle_round_bf16(tmp128[i]));", "v128[i] = (float)tmp128[i];"),
     ("pooled query skips a dimension", "for (int32_t c = 0; c < d; ++c) qbar[c] += bf(q[(b * Hq + h)",
      "for (int32_t c = 1; c < d; ++c) qbar[c] += bf(q[(b * Hq + h)"),
 ]

@@ -482,6 +482,45 @@ def test_prefill_branch_a_all_entries_is_dense_over_pooled(orc):
         np.testing.assert_allclose(r["branches"][0, 0, :, h], ref, atol=1e-12)
 
 
+def test_prefill_compressed_operands_are_bf16_rounded_means(orc):
+    # "CSA + HCA 混合注意力机制" §4.1 / §5.1: an entry is the mean of m consecutive rows;
+    # the attention copies of the entries are a bf16 cache (round to nearest even of the
+    # mean).  Values n/64 with |n| <= 255 are bf16-exact, and the mean of 4 of them,
+    # (sum of n)/256, has up to 10 significant bits: exact in fp32 but mostly not in bf16,
+    # so the rounding (ties included) decides both branches' operands.  torch's fp32 ->
+    # bf16 conversion rounds them independently of the oracle.
+    rng = np.random.default_rng(28)
+    P, C, Hq, Hkv, d, m = 256, 40, 4, 2, 16, 4
+    k = rng.integers(-255, 256, (1, Hkv, P + C, d)).astype(np.float32) / 64
+    v = rng.integers(-255, 256, (1, Hkv, P + C, d)).astype(np.float32) / 64
+    q = rng.standard_normal((1, C, Hq, d)).astype(np.float32)
+    qb, kb, vb = bf(q), bf(k), bf(v)
+    assert np.array_equal(f(kb), k) and np.array_equal(f(vb), v)
+    kp = k[0, :, :P].astype(np.float64).reshape(Hkv, P // m, m, d).mean(2)
+    vp = v[0, :, :P].astype(np.float64).reshape(Hkv, P // m, m, d).mean(2)
+    assert np.array_equal(kp.astype(np.float32), kp) and np.array_equal(vp.astype(np.float32), vp)
+
+    def rne(a):
+        return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).double().numpy()
+
+    kr, vr = rne(kp), rne(vp)
+    assert (kr != kp).mean() > 0.15 and (vr != vp).mean() > 0.15
+    # some means lie exactly halfway between two bf16 values (the 16 fp32 bits that bf16
+    # drops are 0x8000)
+    half = lambda a: (a.astype(np.float32).view(np.uint32) & 0xFFFF) == 0x8000
+    assert half(kp).sum() > 10 and half(vp).sum() > 10
+    # branch A over every m=4 entry and branch B with m_dense = 4 attend the same stream
+    r = orc.sparse_prefill_attn(qb, kb, vb, P, m_sparse=m, top_k=10 ** 6, m_dense=m, window=4,
+                                q_tile=16, want_branches=True)
+    qf = f(qb)
+    for h in range(Hq):
+        ref = sdpa(qf[0, :, h], kr[h // 2], vr[h // 2])
+        np.testing.assert_allclose(r["branches"][0, 0, :, h], ref, atol=1e-12)
+        np.testing.assert_allclose(r["branches"][1, 0, :, h], ref, atol=1e-12)
+        # the unrounded means give a visibly different result
+        assert np.abs(sdpa(qf[0, :, h], kp[h // 2], vp[h // 2]) - ref).max() > 1e-5
+
+
 def test_prefill_branch_c_window(orc):
     q, k, v = prefill_case(22, exact=False)
     P, C = 256, 40
@@ -800,3 +839,40 @@ def test_fp8_attention_equals_bf16_on_representable_cache(orc):
     np.testing.assert_array_equal(v8b, v8)
     o8b, _ = orc.sparse_decode_attn_fp8(q, k8, v8b, ks, vsb, idx, N)
     np.testing.assert_allclose(o8b, o8 * 2.0 ** -3, atol=1e-12)
+
+
+def test_fp8_attention_applies_each_blocks_scales(orc):
+    # the representable cache above with block j's keys times 2^-(j+1) and its values times
+    # 2^(j-2): each block quantizes to exactly that scale and the same codes, so the
+    # attention of the FP8 cache must equal the bf16 attention of the scaled values
+    # (the key scale enters every logit of its block, the value scale every value row)
+    rng = np.random.default_rng(44)
+    fin = np.array(sorted({orc.e4m3_value(c) for c in range(0, 127)}))
+    pool = np.concatenate([fin[(fin > 0.05) & (fin < 4)], -fin[(fin > 0.05) & (fin < 4)]])
+    B, Hq, Hkv, d, nb = 1, 4, 2, 16, 6
+    N = 64 * nb - 9
+    k = rng.choice(pool, (B, Hkv, N, d)).astype(np.float32)
+    v = rng.choice(pool, (B, Hkv, N, d)).astype(np.float32)
+    for j in range(nb):
+        k[:, :, j * 64, 0] = 448.0
+        v[:, :, j * 64, 1] = 448.0
+        k[:, :, j * 64:(j + 1) * 64] *= 2.0 ** -(j + 1)
+        v[:, :, j * 64:(j + 1) * 64] *= 2.0 ** (j - 2)
+    q = bf(rng.standard_normal((B, Hq, d)).astype(np.float32) * 0.5)
+    k16, v16 = bf(k), bf(v)
+    assert np.array_equal(f(k16), k) and np.array_equal(f(v16), v)
+    k8, ks = orc.quantize_fp8(k16, N)
+    v8, vs = orc.quantize_fp8(v16, N)
+    np.testing.assert_array_equal(ks[0, 0], 2.0 ** -(np.arange(nb) + 1))
+    np.testing.assert_array_equal(vs[0, 1], 2.0 ** (np.arange(nb) - 2))
+    idx = np.array([[[0, 1, 3, 5], [0, 2, 4, 5]]], np.int32)
+    o8, l8 = orc.sparse_decode_attn_fp8(q, k8, v8, ks, vs, idx, N)
+    o16, l16, _ = orc.sparse_decode_attn(q, k16, v16, idx, N)
+    np.testing.assert_allclose(o8, o16, atol=1e-12)
+    np.testing.assert_allclose(l8, l16, atol=1e-12)
+    # the scales differ enough that a dropped or misplaced key scale would show
+    ku, _ = orc.quantize_fp8(bf(k * (2.0 ** (np.arange(N) // 64 + 1))[None, None, :, None]), N)
+    np.testing.assert_array_equal(ku, k8)
+    o_unscaled, _, _ = orc.sparse_decode_attn(
+        q, bf(k * (2.0 ** (np.arange(N) // 64 + 1))[None, None, :, None]), v16, idx, N)
+    assert np.abs(o_unscaled - o16).max() > 1e-3
