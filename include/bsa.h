@@ -65,11 +65,12 @@ typedef struct {
   int32_t n_sink_blocks;   /* always-kept leading blocks (1 on the page's table) */
   int32_t n_local_blocks;  /* always-kept trailing blocks (2 on the page's table) */
   int32_t top_k;           /* middle blocks kept by score; < 0: derive from keep_ratio */
-  float keep_ratio;        /* used when top_k < 0: total kept = floor(r * nb + 0.5);
-                              adaptive: the smallest kept fraction */
+  double keep_ratio;       /* used when top_k < 0: total kept = floor(r * nb + 0.5), evaluated
+                              in double on this value; adaptive: the smallest kept fraction */
   int32_t adaptive;        /* 1: anchor-adaptive k per (b, kv head), see select_blocks */
-  float keep_ratio_max;    /* adaptive: the largest kept fraction */
-  float anchor_margin;     /* adaptive: tau = a_max + anchor_margin * (a_max - a_min) */
+  double keep_ratio_max;   /* adaptive: the largest kept fraction (rounded as keep_ratio) */
+  double anchor_margin;    /* adaptive: tau = a_max + anchor_margin * (a_max - a_min); the
+                              kernels form tau in fp32 from (float)anchor_margin */
 } bsa_select_cfg;
 
 typedef struct {
@@ -202,8 +203,10 @@ int sparse_decode_step(const void* q, const void* k, const void* v, const float*
  *   k, v       bf16 [B][Hkv][seq_stride][d]
  *   block_idx  int32 [B][Hkv][n_keep], strictly ascending block indices < nb, each
  *              list optionally ended by a run of -1 (absent entries, as written by an
- *              adaptive select_blocks) and holding at least one block (not checked
- *              on the device: other out-of-range entries are the caller's error)
+ *              adaptive select_blocks) and holding at least one block.  Not checked
+ *              on the device: any other entry outside [0, nb) is the caller's error;
+ *              the kernels clamp it to a valid block, so every read stays inside the
+ *              cache (and the scales), but the result is then unspecified
  *   scale      0 selects 1/sqrt(d)
  *   out        fp32 [B][Hq][d]
  *   lse        fp32 [B][Hq] natural-log log-sum-exp of the scaled logits, or NULL
@@ -309,7 +312,9 @@ int sparse_decode_merge(const bsa_shape* shape, int32_t n_keep, int32_t block_si
  *   sel_out              int32 [B][ceil(C / q_tile)][Hkv][min(top_k_sparse, E_s)] ascending, or NULL
  *   workspace            bsa_prefill_workspace_size() bytes, 16-byte aligned
  * Requires P >= 1, head_dim 128, q_tile * Hq/Hkv in {64, 128, 256},
- * E_s <= 131072, min(top_k_sparse, E_s) <= 4096 and, for the selection,
+ * E_s <= 131072, min(top_k_sparse, E_s) <= 4096, E_d <= 16,777,216 and
+ * min(window + q_tile, P + C) <= 16,777,216 (a pair's dense-stream rows and a tile's
+ * window rows are addressed by 32-bit byte offsets) and, for the selection,
  * ceil(C / q_tile) <= 64 (else BSA_UNSUPPORTED).
  * Equals select_prefill_entries followed by sparse_prefill_attn_selected. */
 int sparse_prefill_attn(const void* q, int32_t chunk_len, const void* k, const void* v,

@@ -34,8 +34,8 @@ class bsa_shape(ctypes.Structure):
 class bsa_select_cfg(ctypes.Structure):
     _fields_ = [("block_size", ctypes.c_int32), ("n_sink_blocks", ctypes.c_int32),
                 ("n_local_blocks", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("keep_ratio", ctypes.c_float), ("adaptive", ctypes.c_int32),
-                ("keep_ratio_max", ctypes.c_float), ("anchor_margin", ctypes.c_float)]
+                ("keep_ratio", ctypes.c_double), ("adaptive", ctypes.c_int32),
+                ("keep_ratio_max", ctypes.c_double), ("anchor_margin", ctypes.c_double)]
 
 
 class bsa_prefill_cfg(ctypes.Structure):

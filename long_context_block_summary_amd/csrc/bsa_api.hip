@@ -2,6 +2,7 @@
 // Every argument check runs before any launch; kernels are only enqueued on
 // the caller's stream.
 #include <math.h>
+#include <algorithm>
 #include <cmath>
 #include <stdint.h>
 
@@ -36,7 +37,7 @@ int middle_k(int nb, const bsa_select_cfg* cfg, int n_cand) {
   if (cfg->top_k >= 0)
     k = cfg->top_k;
   else
-    k = (int64_t)floor((double)cfg->keep_ratio * (double)nb + 0.5) - cfg->n_sink_blocks -
+    k = (int64_t)floor(cfg->keep_ratio * (double)nb + 0.5) - cfg->n_sink_blocks -
         cfg->n_local_blocks;
   if (k < 0) k = 0;
   if (k > n_cand) k = n_cand;
@@ -46,18 +47,18 @@ int middle_k(int nb, const bsa_select_cfg* cfg, int n_cand) {
 bool select_cfg_ok(const bsa_select_cfg* c) {
   if (!c || c->block_size < 1 || c->n_sink_blocks < 0 || c->n_local_blocks < 0) return false;
   if (c->adaptive) {
-    return c->adaptive == 1 && c->keep_ratio >= 0.f && c->keep_ratio <= c->keep_ratio_max &&
-           c->keep_ratio_max <= 1.f && std::isfinite(c->anchor_margin);
+    return c->adaptive == 1 && c->keep_ratio >= 0.0 && c->keep_ratio <= c->keep_ratio_max &&
+           c->keep_ratio_max <= 1.0 && std::isfinite((float)c->anchor_margin);
   }
-  return c->top_k >= 0 || (c->keep_ratio >= 0.f && c->keep_ratio <= 1.f);
+  return c->top_k >= 0 || (c->keep_ratio >= 0.0 && c->keep_ratio <= 1.0);
 }
 
 // adaptive selection: the middle-block count lies in [k_lo, k_hi] (the kept
 // totals keep_ratio * nb and keep_ratio_max * nb, rounded as middle_k rounds)
 void adaptive_bounds(int nb, const bsa_select_cfg* cfg, int fixed, int n_cand, int* k_lo,
                      int* k_hi) {
-  int64_t lo = (int64_t)floor((double)cfg->keep_ratio * (double)nb + 0.5) - fixed;
-  int64_t hi = (int64_t)floor((double)cfg->keep_ratio_max * (double)nb + 0.5) - fixed;
+  int64_t lo = (int64_t)floor(cfg->keep_ratio * (double)nb + 0.5) - fixed;
+  int64_t hi = (int64_t)floor(cfg->keep_ratio_max * (double)nb + 0.5) - fixed;
   lo = lo < 0 ? 0 : (lo > n_cand ? n_cand : lo);
   hi = hi < lo ? lo : (hi > n_cand ? n_cand : hi);
   *k_lo = (int)lo;
@@ -232,7 +233,7 @@ int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
   bsa::launch_scores(static_cast<const uint16_t*>(q), summaries, shape->batch, shape->n_q_heads,
                      shape->n_kv_heads, shape->head_dim, nb, ss, s0, s1, scores, st);
   bsa::launch_topk(scores, (int64_t)shape->batch * shape->n_kv_heads, nb, c0, c1, k, n_keep,
-                   block_idx, st, cfg->adaptive != 0, k_lo, k_hi, cfg->anchor_margin);
+                   block_idx, st, cfg->adaptive != 0, k_lo, k_hi, (float)cfg->anchor_margin);
   return launch_status();
 }
 
@@ -452,6 +453,13 @@ int prefill_setup(const void* q, int32_t chunk_len, const bsa_shape* shape,
   const int ksel = cfg->top_k_sparse < E4 ? cfg->top_k_sparse : E4;
   if (shape->head_dim != 128 || (rows != 64 && rows != 128 && rows != 256) ||
       E4 > bsa::PREFILL_MAX_E4 || ksel > bsa::PREFILL_MAX_SEL)
+    return BSA_UNSUPPORTED;
+  // the attention addresses a pair's dense-stream rows and a tile's window rows
+  // by 32-bit byte offsets from one base (256-byte rows at d = 128)
+  const int64_t e_dense = bsa_num_blocks(shape->seq_len, cfg->m_dense);
+  const int64_t win_rows =
+      std::min<int64_t>((int64_t)cfg->window + cfg->q_tile, (int64_t)shape->seq_len + chunk_len);
+  if (e_dense * 256 > (int64_t(1) << 32) || win_rows * 256 > (int64_t(1) << 32))
     return BSA_UNSUPPORTED;
   *L = bsa::PrefillLaunch{};
   L->q = static_cast<const uint16_t*>(q);

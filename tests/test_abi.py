@@ -227,3 +227,53 @@ def test_loop_argument_checks_launch_nothing(L):
                            1 << 20, None) == -1
     # nothing to update is a no-op
     assert L.update_block_summaries(fake, ctypes.byref(sh), 64, 100, fake, None, None) == 0
+
+
+def test_keep_ratio_counts_equal_the_oracle(L, orc):
+    """The kept count and the adaptive bounds follow the oracle's rounding of the ratio as
+    given (floor(r * nb + 0.5) in double), including ratios whose float value would round
+    the other way: (5, 0.7), (10, 0.35), (10, 0.45), (5, 0.9)."""
+    import numpy as np
+    for nb, r, kept in ((5, 0.7, 4), (10, 0.35, 4), (10, 0.45, 5), (5, 0.9, 5)):
+        assert orc.num_kept(nb, 1, 2, -1, r) == kept
+        assert bsa.num_kept(nb, bsa.select_cfg(keep_ratio=r)) == kept
+        w, _, _ = orc.adaptive_bounds(nb, 1, 2, r, r)
+        assert bsa.num_kept(nb, bsa.select_cfg(keep_ratio=r, adaptive=True,
+                                               keep_ratio_max=r)) == w == kept
+    ratios = [round(0.05 * i, 2) for i in range(1, 20)]
+    for sink, local in ((1, 2), (0, 1), (2, 0)):
+        for r in ratios:
+            want = np.array([orc.num_kept(nb, sink, local, -1, r) for nb in range(1, 5001)])
+            cfg = bsa.select_cfg(n_sink=sink, n_local=local, keep_ratio=r)
+            got = np.array([L.bsa_num_kept(nb, ctypes.byref(cfg)) for nb in range(1, 5001)])
+            assert np.array_equal(got, want), (sink, local, r)
+        for lo, hi in zip(ratios[:-3], ratios[3:]):
+            cfg = bsa.select_cfg(n_sink=sink, n_local=local, keep_ratio=lo, adaptive=True,
+                                 keep_ratio_max=hi)
+            lo_cfg = bsa.select_cfg(n_sink=sink, n_local=local, keep_ratio=lo, adaptive=True,
+                                    keep_ratio_max=lo)
+            for nb in range(1, 5001, 7):
+                w, k_lo, k_hi = orc.adaptive_bounds(nb, sink, local, lo, hi)
+                assert L.bsa_num_kept(nb, ctypes.byref(cfg)) == w, (nb, lo, hi)
+                assert L.bsa_num_kept(nb, ctypes.byref(lo_cfg)) == w - k_hi + k_lo, (nb, lo)
+
+
+def test_prefill_rejects_rows_beyond_32bit_offsets(L):
+    """The attention addresses the dense stream's rows and a tile's window rows by 32-bit
+    byte offsets (256-byte rows): E_d and min(window + q_tile, P + C) are bounded by 2^24."""
+    fake = ctypes.c_void_p(0x1000)
+    S = L.select_prefill_entries
+
+    def call(P, C, **kw):
+        sh = bsa.make_shape(1, 32, 8, 128, P, P + C)
+        pc = bsa.prefill_cfg(**kw)
+        return S(fake, C, fake, ctypes.byref(sh), ctypes.byref(pc), fake, fake, 64, None)
+
+    # dense stream: 2^24 entries pass the checks (then the workspace is too small), one more
+    # is unsupported
+    assert call(1 << 24, 128, m_sparse=256, m_dense=1) == -3
+    assert call((1 << 24) + 1, 128, m_sparse=256, m_dense=1) == -2
+    # window rows: min(window + q_tile, P + C)
+    assert call(1 << 24, 128, m_sparse=256, window=(1 << 24) - 64) == -3
+    assert call(1 << 24, 128, m_sparse=256, window=(1 << 24) - 63) == -2
+    assert call(1 << 20, 128, m_sparse=256, window=1 << 30) == -3  # capped by P + C
