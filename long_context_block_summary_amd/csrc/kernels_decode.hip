@@ -263,7 +263,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
   // the pipeline never branches around its loads
   auto issue = [&](int slot, int j) {
     const bool real = j < nblk;
-    const int t0 = list[real ? j : 0] * 64 + tile0;
+    // a caller's entry outside [0, nb) is clamped to a valid block: every
+    // read stays inside the pair's rows (the result is then unspecified)
+    const int t0 = min(max(list[real ? j : 0], 0), (N - 1) >> 6) * 64 + tile0;
     const uint32_t koff = real ? (uint32_t)min(t0 + l16, N - 1) * (D * 2) + j4 * 16 : 0u;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -389,7 +391,8 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_kernel(
   asm volatile("" : "+v"(vzero));
   auto issue = [&](int slot, int j) {
     const uint32_t m = (j < nblk) ? 0xffffffffu : 0u;  // uniform
-    const int blk = list[max(min(j, nblk - 1), 0)] & (int)m;
+    // clamped to a valid block as in the bf16 kernel (rows and scales)
+    const int blk = min(max(list[max(min(j, nblk - 1), 0)], 0), (N - 1) >> 6) & (int)m;
     const int t0 = blk * 64 + tile0;
     const uint32_t koff = (((uint32_t)min(t0 + l16, N - 1) * D + j4 * (8 * KS)) & m) + vzero;
 #pragma unroll
