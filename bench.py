@@ -28,18 +28,31 @@ METRIC = "sparse-decode attn queries·heads/s + achieved HBM GB/s at 128K ctx, 1
 HBM_PEAK_GBS = 8000.0
 
 
-def decode_bytes(cfg, n_keep):
-    """Algorithmic bytes of one decode step (select + attend), split by call.
+def kv_bytes_per_token(n_layers, width, elem_bytes):
+    """K and V bytes of one token: layers x (heads * head_dim) x bytes x 2."""
+    return n_layers * width * elem_bytes * 2
 
-    select: summaries (fp32) of every block + q; attend: kept K and V (bf16),
-    q, fp32 output and the index list.  Unselected KV and implementation
-    scratch (scores, split partials) are not counted."""
+
+def decode_bytes(cfg, n_keep):
+    """Algorithmic bytes of the two calls of one decode step.
+
+    select: the fp32 summaries of every block + q; attend: the kept K and V (bf16), q, the
+    fp32 output and lse, and the index list.  Unselected KV and implementation scratch
+    (scores, split partials) are not counted."""
     B, Hq, Hkv, d = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     nb = -(-cfg.seq_len // cfg.block_size)
     kept_tokens = min(n_keep * cfg.block_size, cfg.seq_len)
-    sel = B * Hkv * nb * d * 4 + B * Hq * d * 2
-    att = B * Hkv * kept_tokens * d * 2 * 2 + B * Hq * d * 2 + B * Hq * d * 4 + B * Hkv * n_keep * 4
+    q_bytes = B * Hq * d * 2
+    sel = B * Hkv * nb * d * 4 + q_bytes
+    att = (B * Hkv * kept_tokens * kv_bytes_per_token(1, d, 2) + q_bytes + B * Hq * d * 4
+           + B * Hq * 4 + B * Hkv * n_keep * 4)
     return sel, att
+
+
+def step_bytes(cfg, n_keep):
+    """Algorithmic bytes of one step: both calls' bytes with q counted once."""
+    sel, att = decode_bytes(cfg, n_keep)
+    return sel + att - cfg.batch * cfg.n_q_heads * cfg.head_dim * 2
 
 
 def partials_bytes(cfg, n_keep):
@@ -48,7 +61,7 @@ def partials_bytes(cfg, n_keep):
     S5's; the partials are scratch."""
     B, Hq, Hkv, d = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     kept_tokens = min(n_keep * cfg.block_size, cfg.seq_len)
-    return B * Hkv * kept_tokens * d * 2 * 2 + B * Hq * d * 2 + B * Hkv * n_keep * 4
+    return B * Hkv * kept_tokens * kv_bytes_per_token(1, d, 2) + B * Hq * d * 2 + B * Hkv * n_keep * 4
 
 
 def measured_traffic(workload, field="traffic_bytes_per_launch"):
@@ -72,11 +85,6 @@ def measured_traffic(workload, field="traffic_bytes_per_launch"):
     if fields.get("kernel_source_sha256_prefix") != sha:
         return None
     return float(fields[field]) if field in fields else None
-
-
-def kv_bytes_per_token(n_layers, width, elem_bytes):
-    """K and V bytes of one token: layers x (heads*head_dim) x bytes x 2."""
-    return n_layers * width * elem_bytes * 2
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -526,43 +534,57 @@ def run_prefill(cfg, steps, warmup, flush_bytes=1 << 30):
             "selection_R2": {"call": "select_prefill_entries", "ms": r2,
                              "stream_GBps": r2_bytes / (r2 / 1e3) / 1e9,
                              "fp32_gflop": r2_flops / 1e9},
-            "streams_ingest_ms": sorted(r1)[1]}
+            "streams_ingest_ms": sorted(r1)[1], "inputs": t}
 
 
-def run_cpu_baseline(cfg, t, budget_s=20.0, min_s=10.0, one_thread_s=4.0):
-    """Oracle select + attend (given its fp64 summaries) on a bounded sample."""
-    import numpy as np
-
+def run_cpu_baseline(cfg, t, budget_s=20.0, min_s=10.0, one_thread_s=4.0, others=None):
+    """Oracle select + attend (given its fp64 summaries) on a bounded sample, on every host
+    thread and on one; the oracle's summaries alone; and one-thread select + attend on other
+    decode workloads (`others`: name -> (config, inputs))."""
     import oracle
     B = cfg.batch
+    t0 = time.perf_counter()
     summ = oracle.block_summaries(t["k"], cfg.seq_len, cfg.block_size)
+    summ_s = time.perf_counter() - t0
 
-    def one(bsl):
+    def one(c, inp, sm, bsl):
         t0 = time.perf_counter()
-        idx, _ = oracle.select_blocks(t["q"][bsl], summ[bsl], cfg.n_kv_heads, cfg.n_sink,
-                                      cfg.n_local, cfg.top_k, cfg.keep_ratio)
-        oracle.sparse_decode_attn(t["q"][bsl], t["k"][bsl], t["v"][bsl], idx, cfg.seq_len,
-                                  cfg.block_size)
+        idx, _ = oracle.select_blocks(inp["q"][bsl], sm[bsl], c.n_kv_heads, c.n_sink,
+                                      c.n_local, c.top_k, c.keep_ratio)
+        oracle.sparse_decode_attn(inp["q"][bsl], inp["k"][bsl], inp["v"][bsl], idx, c.seq_len,
+                                  c.block_size)
         return time.perf_counter() - t0
 
-    first = one(slice(0, 1))
+    first = one(cfg, t, summ, slice(0, 1))
     nb_used = 1
     if first * B <= budget_s and B > 1:
         nb_used = B
     # repeat the pass until about min_s of CPU time has been spent (bounded by budget_s)
     reps, elapsed = 0, 0.0
     while reps == 0 or (elapsed < min_s and elapsed + elapsed / reps <= budget_s):
-        elapsed += one(slice(0, nb_used))
+        elapsed += one(cfg, t, summ, slice(0, nb_used))
         reps += 1
     qh = reps * nb_used * cfg.n_q_heads
     cores = oracle.num_threads()
-    # the same oracle on one thread, over one batch entry (bounded to a few seconds)
+    k_bytes = cfg.batch * cfg.n_kv_heads * cfg.seq_len * cfg.head_dim * 2
+
+    def one_thread(c, inp, sm, limit_s):
+        reps1, el1 = 0, 0.0
+        while reps1 == 0 or el1 < limit_s:
+            el1 += one(c, inp, sm, slice(0, 1))
+            reps1 += 1
+        return {"value": reps1 * c.n_q_heads / el1, "unit": "queries*heads/s",
+                "sample": f"{c.name}: 1 of {c.batch} batch entries, {reps1} passes, {el1:.2f} s"}
+
+    # the same oracle on one thread, over one batch entry (bounded to a few seconds each)
+    others = others or {}
+    other_summ = {name: oracle.block_summaries(inp["k"], c.seq_len, c.block_size)
+                  for name, (c, inp) in others.items()}
     oracle.set_threads(1)
     try:
-        reps1, el1 = 0, 0.0
-        while reps1 == 0 or el1 < one_thread_s:
-            el1 += one(slice(0, 1))
-            reps1 += 1
+        one_t = one_thread(cfg, t, summ, one_thread_s)
+        one_t_others = {name: one_thread(c, inp, other_summ[name], one_thread_s / 2)
+                        for name, (c, inp) in others.items()}
     finally:
         oracle.set_threads(cores)
     return {"value": qh / elapsed, "unit": "queries*heads/s", "cores": cores,
@@ -570,9 +592,52 @@ def run_cpu_baseline(cfg, t, budget_s=20.0, min_s=10.0, one_thread_s=4.0):
             "sample": f"{cfg.name}: select + attend (fp64 oracle, summaries precomputed) for "
                       f"{nb_used} of {B} batch entries ({nb_used * cfg.n_q_heads} query heads), "
                       f"{reps} passes, {elapsed:.2f} s",
-            "one_thread": {"value": reps1 * cfg.n_q_heads / el1, "unit": "queries*heads/s",
-                           "sample": f"{cfg.name}: 1 of {B} batch entries, {reps1} passes, "
-                                     f"{el1:.2f} s"},
+            "one_thread": one_t,
+            "one_thread_other_workloads": one_t_others,
+            "summaries_alone": {"s": summ_s, "key_GBps": k_bytes / summ_s / 1e9, "cores": cores,
+                                "sample": f"{cfg.name}: fp64 means of every 64-token block of "
+                                          f"K ({k_bytes / 1e9:.2f} GB of bf16 keys), once"},
+            "host": host_description()}
+
+
+def run_cpu_prefill_baseline(cfg, t, big_tiles=4):
+    """The oracle's prefill on sampled query rows.  Its call builds the compressed streams from
+    the raw cache every time (a fixed cost), so the select + attend rate given the streams is
+    taken as the difference between a call over `big_tiles` whole tiles and a call over one
+    tile; the streams alone (fp64 means, no rounding) and the whole larger call are reported
+    beside it."""
+    import numpy as np
+
+    import oracle
+    P = cfg.prior_len
+    common = dict(m_sparse=cfg.m_sparse, top_k=cfg.top_k_sparse, m_dense=cfg.m_dense,
+                  window=cfg.window, q_tile=cfg.q_tile)
+    rows_small = np.arange(cfg.q_tile, dtype=np.int32)
+    rows_big = np.arange(big_tiles * cfg.q_tile, dtype=np.int32)
+    t0 = time.perf_counter()
+    for x in (t["k"], t["v"]):
+        for m in (cfg.m_sparse, cfg.m_dense):
+            oracle.block_summaries(x, P, m)
+    streams_s = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.sparse_prefill_attn(t["q"], t["k"], t["v"], P, rows=rows_small, **common)
+    small_s = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.sparse_prefill_attn(t["q"], t["k"], t["v"], P, rows=rows_big, **common)
+    big_s = time.perf_counter() - t0
+    e4 = -(-P // cfg.m_sparse)
+    n_ent = min(cfg.top_k_sparse, e4) + -(-P // cfg.m_dense) + cfg.window
+    d_rows = len(rows_big) - len(rows_small)
+    marg = max(big_s - small_s, 1e-9)
+    qh = d_rows * cfg.n_q_heads
+    return {"value": qh / marg, "unit": "queries*heads/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "gflops_fp64": 4 * cfg.head_dim * n_ent * qh / marg / 1e9,
+            "sample": f"{cfg.name}: oracle calls over {len(rows_big)} and {len(rows_small)} "
+                      f"query rows ({big_tiles} and 1 tiles, {cfg.n_q_heads} heads each) took "
+                      f"{big_s:.2f} s and {small_s:.2f} s; the rate is the {d_rows} extra rows "
+                      f"over the difference (both calls build the same streams)",
+            "whole_call_s": big_s, "streams_alone_s": streams_s,
             "host": host_description()}
 
 
@@ -595,7 +660,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long128k_15")
-    ap.add_argument("--also", default="long128k",
+    ap.add_argument("--also", default="long128k,gqa32k,ctx1m",
                     help="comma list of extra decode workloads reported alongside ('none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", default="prefill256k",
@@ -613,8 +678,9 @@ def main():
 
     from long_context_block_summary_amd import synth
     if args.only == "prefill":
-        print(json.dumps(run_prefill(synth.CONFIGS[args.prefill], args.steps, args.warmup)),
-              flush=True)
+        pr = run_prefill(synth.CONFIGS[args.prefill], args.steps, args.warmup)
+        pr.pop("inputs")
+        print(json.dumps(pr), flush=True)
         return
     cfg = synth.CONFIGS[args.workload]
     r = run_gpu(cfg, args.steps, args.warmup)
@@ -650,7 +716,9 @@ def main():
                    "n_sink_blocks": cfg.n_sink, "n_local_blocks": cfg.n_local,
                    "top_k": cfg.top_k, "n_keep": r["n_keep"],
                    "keep_pct": round(100.0 * r["n_keep"] / -(-cfg.seq_len // cfg.block_size), 2)},
-        "step_GBps": (sel_b + att_b) / step_s / 1e9,
+        "step_bytes": step_bytes(cfg, r["n_keep"]),
+        "step_GBps": step_bytes(cfg, r["n_keep"]) / step_s / 1e9,
+        "step_frac": step_bytes(cfg, r["n_keep"]) / step_s / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm",
                      "kernel": "decode_kernel (step S4, the sparse_decode_partials call)",
                      "achieved": s4_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -677,31 +745,46 @@ def main():
         "timed_wall_s": r["wall_s"],
         "cache_flush": "1 GiB read+write before every step (untimed)",
     }
-    extra = {}
+    extra, keep_inputs = {}, {}
     for name in [s for s in args.also.split(",") if s and s != "none"]:
         c2 = synth.CONFIGS[name]
         same = (c2.batch, c2.n_q_heads, c2.n_kv_heads, c2.head_dim, c2.seq_len) == \
             (cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len) and \
             synth.DEFAULT_SEED.get(name) == synth.DEFAULT_SEED.get(cfg.name)
         r2 = run_gpu(c2, max(10, args.steps // 2), 3, inputs=r["inputs"] if same else None)
-        s2, a2 = decode_bytes(c2, r2["n_keep"])
+        _, a2 = decode_bytes(c2, r2["n_keep"])
+        st2 = step_bytes(c2, r2["n_keep"])
+        p2 = partials_bytes(c2, r2["n_keep"])
         extra[name] = {"queries_heads_per_s": c2.batch * c2.n_q_heads / (r2["step_ms"] / 1e3),
                        "ms_per_step": r2["step_ms"], "n_keep": r2["n_keep"],
+                       "step_bytes": st2,
+                       "step_GBps": st2 / (r2["step_ms"] / 1e3) / 1e9,
+                       "step_frac": st2 / (r2["step_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
                        "attn_GBps": a2 / (r2["att_ms"] / 1e3) / 1e9,
                        "attn_frac": a2 / (r2["att_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
-                       "step_GBps": (s2 + a2) / (r2["step_ms"] / 1e3) / 1e9,
+                       "s4_us": r2["s4_ms"] * 1e3,
+                       "s4_frac": p2 / (r2["s4_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
                        "select_us": r2["sel_ms"] * 1e3, "attn_us": r2["att_ms"] * 1e3}
+        if name in ("tiny", "gqa32k", "long128k"):
+            keep_inputs[name] = (c2, r2["inputs"])
         del r2
     line["fused_step"] = run_fused_step(cfg, max(10, args.steps // 2), 3, r["inputs"])
     line["decode_loop"] = run_decode_loop(cfg, max(10, args.steps // 2), 3, r["inputs"])
     line["adaptive_selection"] = run_adaptive(cfg, max(10, args.steps // 2), 3, r["inputs"])
     line["fp8_kv"] = run_fp8(cfg, max(10, args.steps // 2), 3, r["inputs"])
+    pf_inputs = None
     if args.prefill and args.prefill != "none":
         line["prefill"] = run_prefill(synth.CONFIGS[args.prefill], max(5, args.steps // 5), 2)
+        pf_inputs = line["prefill"].pop("inputs")
     if extra:
         line["also"] = extra
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = run_cpu_baseline(cfg, r["inputs"])
+        if "tiny" not in keep_inputs:
+            keep_inputs["tiny"] = (synth.CONFIGS["tiny"], synth.gen_decode(synth.CONFIGS["tiny"]))
+        line["cpu_baseline"] = run_cpu_baseline(cfg, r["inputs"], others=keep_inputs)
+        if pf_inputs is not None:
+            line["cpu_baseline_prefill"] = run_cpu_prefill_baseline(
+                synth.CONFIGS[args.prefill], pf_inputs)
     print(json.dumps(line), flush=True)
 
 
