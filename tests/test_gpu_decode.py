@@ -273,3 +273,18 @@ def test_full_size_workloads(name):
 
 def test_full_size_1m():
     run_decode_case(synth.CONFIGS["ctx1m"], synth.DEFAULT_SEED["ctx1m"])
+
+
+@pytest.mark.parametrize("name", ["gqa32k", "long128k", "long128k_15", "ctx1m"])
+def test_full_size_second_seed(name):
+    run_decode_case(synth.CONFIGS[name], 101)
+
+
+@pytest.mark.parametrize("nb,ratio", [(5, 0.7), (10, 0.35), (10, 0.45), (5, 0.9), (2048, 0.15)])
+def test_keep_ratio_half_way_counts(nb, ratio):
+    """Keep ratios whose product with nb sits at a rounding half-way point in double (and
+    would round down from the ratio's float value): the list width and the lists equal the
+    oracle's."""
+    cfg = synth.scaled(synth.CONFIGS["gqa32k"], name=f"ratio{ratio}_nb{nb}", batch=2,
+                       seq_len=64 * nb, top_k=-1, keep_ratio=ratio)
+    run_decode_case(cfg, 200 + nb)

@@ -71,6 +71,10 @@ def run_loop(name, seed, B, Hq, Hkv, d, n0, steps, capacity, top_k=-1, keep_rati
         # the incremental summaries equal a rebuild of the whole cache, bit for bit
         fresh, _ = bsa.build_block_summaries(k_cache, n1, bs)
         assert torch.equal(summ[:, :, :nb], fresh), f"step {s}: incremental summaries differ"
+        # and the oracle's fp32 token-order means, bit for bit
+        assert np.array_equal(summ[:, :, :nb].cpu().numpy(),
+                              oracle.block_summaries_f32(k_host, n1, bs)), \
+            f"step {s}: summaries differ from the oracle's"
         # the cache holds exactly the appended tokens
         assert torch.equal(k_cache[:, :, :n1], k_all[:, :, :n1])
         assert torch.equal(v_cache[:, :, :n1], v_all[:, :, :n1])
@@ -143,3 +147,10 @@ def test_append_refresh_matches_rebuild(bs, n_new):
     torch.cuda.synchronize()
     assert torch.equal(k_cache[:, :, :n + m], k_all[:, :, :n + m])
     assert torch.equal(summ[:, :, :nb], fresh)
+
+
+def test_loop_at_the_128k_workload_shape():
+    # the 128K / 15 % workload's shapes, 10 tokens before the end of its last full block:
+    # the loop fills that block and opens the next one
+    run_loop("loop_128k", 45, B=4, Hq=64, Hkv=8, d=128, n0=131062, steps=14,
+             capacity=131072 + 64, top_k=304)

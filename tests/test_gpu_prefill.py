@@ -35,6 +35,8 @@ def check_tile_selection(g_sel, o_sel, o_scores, rel=TIE_REL):
         for t in range(T):
             for h in range(H):
                 g, o = g_sel[b, t, h], o_sel[b, t, h]
+                assert len(g) == len(o) == k, (b, t, h)
+                assert g.min() >= 0 and g.max() < o_scores.shape[-1], (b, t, h)
                 assert np.all(np.diff(g) > 0), (b, t, h)
                 if np.array_equal(g, o):
                     continue
@@ -160,6 +162,50 @@ def test_prefill_full_size_sampled_rows():
     cfg = synth.CONFIGS["prefill256k"]
     rows = np.array([0, 1, 63, 64, 500, 1023, 1024, 1500, 2046, 2047])
     run_prefill_case(cfg, synth.DEFAULT_SEED["prefill256k"], rows=rows)
+
+
+def test_prefill_full_size_two_whole_tiles():
+    """Every query row and head of the first and the last tile (64 queries x 32 heads each)
+    of the 262K workload."""
+    cfg = synth.CONFIGS["prefill256k"]
+    rows = np.r_[0:64, 1984:2048]
+    run_prefill_case(cfg, synth.DEFAULT_SEED["prefill256k"], rows=rows)
+
+
+def test_prefill_full_size_second_seed():
+    cfg = synth.CONFIGS["prefill256k"]
+    rows = np.array([0, 5, 63, 64, 130, 999, 1024, 1535, 1536, 2047])
+    run_prefill_case(cfg, 105, rows=rows)
+
+
+def test_prefill_values_near_the_fp16_limit():
+    """P V runs on the fp16 matrix cores, so values must lie inside fp16's range (|v| <=
+    65504).  V times 2^13 (|v| up to ~37,000, every bf16 value still exact) stays in range: the
+    outputs scale by 2^13 and the error bound with them (it is relative to the values)."""
+    import torch
+    cfg = small(name="pf_bigv", chunk_len=70)
+    seed = 77
+    scale = 2.0 ** 13
+    announce(cfg.name, "seed", seed, "V x", scale)
+    t = synth.gen_prefill(cfg, seed)
+    v_big = synth.bf16_round(synth.bf16_to_f32(t["v"]) * np.float32(scale))
+    assert np.array_equal(synth.bf16_to_f32(v_big), synth.bf16_to_f32(t["v"]) * scale)
+    vmax = float(np.abs(synth.bf16_to_f32(v_big)).max())
+    assert 30000 < vmax <= 65504, vmax
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(v_big)
+    pc = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile)
+    out, lse3, sel = bsa.prefill_step(q, k, v, cfg.prior_len, pc, want_lse3=True, want_sel=True)
+    torch.cuda.synchronize()
+    common = dict(m_sparse=cfg.m_sparse, top_k=cfg.top_k_sparse, m_dense=cfg.m_dense,
+                  window=cfg.window, q_tile=cfg.q_tile)
+    ref = oracle.sparse_prefill_attn(t["q"], t["k"], v_big, cfg.prior_len,
+                                     sel_in=sel.cpu().numpy(), **common)
+    g = out.cpu().numpy()
+    err = np.abs(g - ref["out"]).max()
+    announce("  max|out err|", err, "max|out|", np.abs(ref["out"]).max())
+    assert np.isfinite(g).all()
+    assert err <= OUT_ATOL * scale, err
+    assert np.abs(lse3.cpu().numpy() - ref["lse3"]).max() <= 1e-3
 
 
 def test_prefill_split_entry_points_compose():
