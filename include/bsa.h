@@ -195,6 +195,22 @@ int sparse_decode_step(const void* q, const void* k, const void* v, const float*
                        float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
                        void* hip_stream);
 
+/* sparse_decode_step_noalloc -- sparse_decode_step for callers that cannot allocate
+ * device memory: code under HIP stream capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The workspace is a static array inside the library, one copy per
+ * GPU of BSA_NOALLOC_SCRATCH_BYTES, held until the process ends; no call allocates.
+ * Arguments, outputs (bit-identical to sparse_decode_step's) and errors as
+ * sparse_decode_step without the workspace; BSA_UNSUPPORTED when
+ * bsa_decode_step_workspace_size(shape, cfg) exceeds BSA_NOALLOC_SCRATCH_BYTES.
+ * hip_stream must belong to the current device.  Every call on one GPU uses the same
+ * array: calls that overlap in time on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller. */
+#define BSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int sparse_decode_step_noalloc(const void* q, const void* k, const void* v,
+                               const float* summaries, const bsa_shape* shape,
+                               const bsa_select_cfg* cfg, int32_t* block_idx, float scale,
+                               float* out, float* lse, void* hip_stream);
+
 /* sparse_decode_attn -- exact softmax(q K^T * scale) V for every query head
  * over the tokens of its kv head's kept blocks ("CSA + HCA 混合注意力机制"
  * §2.1 and §4.4 step 4; the decode step of §2.3 reads the cache after the
