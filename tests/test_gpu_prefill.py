@@ -282,16 +282,18 @@ def test_prefill_selection_exact_ties(prior_len):
 
 @pytest.mark.parametrize("prior_len,top_k,keys", [
     (80_000, 96, "equal"),    # 20,000 equal scores: the sample's bracket holds more keys than
-                              # the top-k stages, so the bit passes run
+                              # the top-k stages, so the bit passes run (nothing above the
+                              # undecided range)
     (40_000, 96, "equal"),    # 10,000 equal scores: staged, the bracket is the largest key
-    (8_192, 1_024, "normal"),  # k / entries = 1/2: no sample rank brackets it, bit passes
+    (8_192, 1_024, "normal"),  # k / entries = 1/2: no sample rank brackets it; all 2,048 keys
+                              # fit the staging, so no bit pass runs and the radix digits fix T
     (64 * 700, 600, "normal"),  # 11,200 entries, a bracketed sample
     (64 * 700 + 12, 600, "normal"),  # 11,203 entries: a ragged last float4 of the row
 ])
 def test_prefill_selection_threshold_paths(prior_len, top_k, keys):
     """The tile selection equals the oracle's on inputs that steer the top-k's threshold
-    search down each of its paths (sample bracket, bit passes) and through all-equal scores,
-    where the lowest entry indices are taken."""
+    search down each of its paths (sample bracket, every key staged, bit passes) and through
+    all-equal scores, where the lowest entry indices are taken."""
     _threshold_case(prior_len, top_k, keys)
 
 
@@ -301,6 +303,57 @@ def test_prefill_selection_threshold_batched(prior_len, top_k, keys):
     """The same over 2 batch entries x 2 kv heads x 2 tiles: every (batch, tile, kv head)
     row finds its own threshold and writes its own selection."""
     _threshold_case(prior_len, top_k, keys, B=2, Hkv=2, Hq=8, C=128)
+
+
+@pytest.mark.parametrize("n_entries", [30_000, 70_000])
+def test_prefill_selection_distinct_tops_over_ties(n_entries):
+    """40 distinct high scores above tens of thousands of equal ones, k = 96: the sample's
+    bracket is the common value and holds more keys than the top-k stages, so the bit passes
+    run with the 40 distinct keys above the undecided range, then the digits and the
+    emission from the registers.  30,000 entries take the 512-thread variant, 70,000 the
+    1024-thread one.  Exact scores: the selection must equal the oracle's (the 40, then the
+    56 lowest indices of the equal entries)."""
+    _distinct_over_ties(4 * n_entries, 96, n_high=40, seed=n_entries)
+
+
+def test_prefill_selection_sparse_high_scores_over_ties():
+    """512 high scores on every 40th of 20,480 entries and equal low scores elsewhere,
+    k = 1,024: the threshold lies among the equal scores, so the selection is the 512 high
+    entries and the 512 lowest-index low ones (the bit passes run with the high keys above
+    the undecided range)."""
+    E = 20_480
+    high = (np.arange(512) * E) // 512
+    _distinct_over_ties(4 * E, 1_024, high_at=high, seed=5)
+
+
+def _distinct_over_ties(prior_len, top_k, n_high=0, high_at=None, seed=0):
+    import torch
+    d, C, Hq = 128, 64, 4
+    E = prior_len // 4
+    announce("pf_tops", "P", prior_len, "E", E, "top_k", top_k, "high", n_high,
+             "high_at", None if high_at is None else len(high_at))
+    rng = np.random.default_rng(seed)
+    n_tok = prior_len + C
+    # every 4-token group pools to ones (score 256 * 128 with q = ones), except the high
+    # entries, whose dim 0 is 2 + r / 4 (distinct, exact in bf16)
+    k = np.ones((1, 1, n_tok, d), np.float32)
+    pos = rng.choice(E, n_high, replace=False) if high_at is None else np.asarray(high_at)
+    for r, j in enumerate(pos):
+        k[0, 0, 4 * j:4 * j + 4, 0] = 2.0 + 0.25 * (r % 40) + 16.0 * (r // 40)
+    k = synth.bf16_round(k)
+    v = synth.bf16_round(rng.standard_normal((1, 1, n_tok, d)).astype(np.float32))
+    q = synth.bf16_round(np.ones((1, C, Hq, d), np.float32))
+    pc = bsa.prefill_cfg(4, top_k, 128, 128, 64)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    st = bsa.build_compressed_streams(kd, vd, prior_len, pc)
+    sel = bsa.select_prefill_entries(qd, kd, st[0], prior_len, cfg=pc)
+    torch.cuda.synchronize()
+    o_sel = oracle.sparse_prefill_attn(q, k, v, prior_len, m_sparse=4, top_k=top_k, m_dense=128,
+                                       window=128, q_tile=64, rows=[0], want_sel=True)["sel"]
+    g_sel = sel.cpu().numpy()
+    assert g_sel.shape == o_sel.shape
+    assert np.array_equal(g_sel, o_sel)
+    assert set(pos.tolist()) <= set(o_sel.reshape(-1).tolist())
 
 
 def _threshold_case(prior_len, top_k, keys, B=1, Hkv=1, Hq=4, C=64):
