@@ -327,6 +327,12 @@ int sparse_decode_merge(const bsa_shape* shape, int32_t n_keep, int32_t block_si
  *   lse3                 fp32 [3][B][C][Hq] per-branch log-sum-exp, or NULL
  *   sel_out              int32 [B][ceil(C / q_tile)][Hkv][min(top_k_sparse, E_s)] ascending, or NULL
  *   workspace            bsa_prefill_workspace_size() bytes, 16-byte aligned
+ * Values: P V runs on the fp16 matrix cores (fp16 weights, V converted to fp16), so every
+ * value attended -- both value streams and the window rows of v -- must lie within fp16's
+ * range, |v| <= 65504; larger values give infinite or NaN outputs.  The conversion is
+ * exact for bf16 values of magnitude 2^-14 and above (smaller ones keep an absolute error
+ * below 2^-25), and the output error, from the fp16 weights, scales with the values'
+ * magnitude (about 2e-4 for N(0,1) values).
  * Requires P >= 1, head_dim 128, q_tile * Hq/Hkv in {64, 128, 256},
  * E_s <= 131072, min(top_k_sparse, E_s) <= 4096, E_d <= 16,777,216 and
  * min(window + q_tile, P + C) <= 16,777,216 (a pair's dense-stream rows and a tile's
