@@ -25,7 +25,8 @@
 //                          double-buffered LDS in chunks of 64: S^T = K Q^T on
 //                          bf16 MFMA, online softmax per row, O += P V on fp16
 //                          MFMA with V transposed in LDS; branch ends fold O / l
-//                          into the output.
+//                          into a partial sum kept in LDS (fp16), written to the
+//                          output once, at the last branch.
 #include <math.h>
 
 #include "bsa_device.h"
@@ -688,7 +689,8 @@ __device__ __forceinline__ int vt_swz(int dim) { return (dim & 15) ^ ((dim >> 4)
 // online softmax in base 2 with the row maximum raised only when it grows by
 // more than 2^8 (exact: the weights and their sum share the stale maximum),
 // P in fp16, O += P V (fp16 MFMA, V^T staged in LDS).  At the end of a branch
-// the normalised rows are added into `out` by the lanes that own them.
+// the normalised rows are added into a partial sum in LDS (fp16, each lane's
+// own values), which the last branch folds into `out` with one write.
 template <int NW, int NT>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArgs a) {
   constexpr int D = 128, KS = D / 32, NTH = NW * 64;
@@ -702,6 +704,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
   __shared__ __align__(16) uint16_t vt_lds[2][D * PF_CH];        // V^T fp16 [dim][entry], 8 B groups swizzled
   __shared__ __align__(16) float xch[NW][3][RW];  // alpha, row max, running concat lse
   __shared__ __align__(16) uint32_t sel_lds[PF_MAX_SEL];         // the tile's branch-A row offsets
+  // the output's partial sum over the branches done so far, fp16, in each
+  // lane's own accumulator layout [wave][nt][nd][lane] x 4 rows: only that
+  // lane reads it back, so no barrier; out is written once, at the last branch
+  __shared__ __align__(16) uint2 part_lds[NW][NT][D / 16][64];
 
   const int g = a.Hq / a.Hkv;
   const int prob = blockIdx.x;
@@ -975,17 +981,19 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // end of a branch: normalise, add into out (A writes, B adds, C adds and
-    // divides by 3), reset
+    // end of a branch: normalise, fold into the LDS partial sum (A writes it, B
+    // adds, C adds and writes out), reset
     const bool last = (gc == nA - 1) || (gc == nA + nB - 1) || (gc == total - 1);
     if (last) {
       // end of a branch: per-row sum l and lse = (m + log2 l) ln 2, then the
-      // branch output O / l is folded into `out`:
-      //   average:  out = (o_A k_A + o_B k_B + o_C k_C) / 3, k = 1 without a sink
+      // branch output O / l is folded into the sum (sum = ca sum + cb O / l):
+      //   average:  sum = (o_A k_A + o_B k_B + o_C k_C) / 3, k = 1 without a sink
       //             logit z, else 1 / (1 + e^(z - lse)) (the sink joins each softmax);
-      //   concat:   one softmax over all branches' logits: out accumulates
+      //   concat:   one softmax over all branches' logits: the sum accumulates
       //             e^(lse_X - L) o_X with the running L = log sum e^lse_X kept
       //             in LDS per row; the sink logit scales by 1 / (1 + e^(z - L)).
+      // The partial sums stay within the values' range, so fp16 holds them
+      // (rounding each by at most 2^-11 relative).
       // the row maxima move to the O layout through LDS
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -1006,6 +1014,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
           lv[i] = Lc[nt][i];
           lse[i] = (mv[i] + log2f(lv[i])) * PF_LN2;
         }
+        float ca[4], cb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = RW * wave + 16 * nt + 4 * jo + i;
@@ -1013,43 +1022,60 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_attn_kernel(PrefillAttnArg
           const int h = kvh * g + r % g;
           if (a.lse3 && qi < a.C && (ln & 15) == 0)
             a.lse3[(((int64_t)br * a.B + b) * a.C + qi) * a.Hq + h] = lse[i];
-          // coefficients: out = ca * out + cb * (O / l)
-          float ca = 0.f, cb = 1.f;
+          // coefficients: sum = ca * sum + cb * (O / l)
+          ca[i] = 0.f;
+          cb[i] = 1.f;
           if (a.combine == 0) {  // uniform
-            if (a.sink) cb = 1.f / (1.f + __expf(a.sink[h] - lse[i]));
-            if (br == 2) {
-              ca = 1.f / 3.f;
-              cb *= 1.f / 3.f;
-            } else {
-              ca = br == 0 ? 0.f : 1.f;
-            }
+            // the sum holds (k_A o_A + k_B o_B) / 3 so far: |sum| <= 2/3 max |v|
+            if (a.sink) cb[i] = 1.f / (1.f + __expf(a.sink[h] - lse[i]));
+            cb[i] *= 1.f / 3.f;
+            ca[i] = br == 0 ? 0.f : 1.f;
           } else {
             float* Lp = &xch[wave][2][16 * nt + 4 * jo + i];
             float L = lse[i];
             if (br > 0) {
               const float Lo = *Lp, mx = fmaxf(Lo, lse[i]);
               L = mx + __logf(__expf(Lo - mx) + __expf(lse[i] - mx));
-              ca = __expf(Lo - L);
-              cb = __expf(lse[i] - L);
+              ca[i] = __expf(Lo - L);
+              cb[i] = __expf(lse[i] - L);
             }
             if ((ln & 15) == 0) *Lp = L;
             if (br == 2 && a.sink) {
               const float keep = 1.f / (1.f + __expf(a.sink[h] - L));
-              ca *= keep;
-              cb *= keep;
+              ca[i] *= keep;
+              cb[i] *= keep;
             }
           }
-          cb *= __builtin_amdgcn_rcpf(lv[i]);
-          // rows past the chunk's end belong to no query: skip them
-          if (qi < a.C) {
-            float* dst = a.out + (((int64_t)b * a.C + qi) * a.Hq + h) * D + (ln & 15);
-            if (br == 0) {  // uniform: out holds nothing yet
+          cb[i] *= __builtin_amdgcn_rcpf(lv[i]);
+        }
+        const int r0 = RW * wave + 16 * nt + 4 * jo;
 #pragma unroll
-              for (int nd = 0; nd < D / 16; ++nd) dst[16 * nd] = O[nt][nd][i] * cb;
-            } else {
+        for (int nd = 0; nd < D / 16; ++nd) {
+          float v[4];
 #pragma unroll
-              for (int nd = 0; nd < D / 16; ++nd)
-                dst[16 * nd] = fmaf(dst[16 * nd], ca, O[nt][nd][i] * cb);
+          for (int i = 0; i < 4; ++i) v[i] = O[nt][nd][i] * cb[i];
+          uint2* pp = &part_lds[wave][nt][nd][ln];
+          if (br > 0) {  // uniform
+            const uint2 w = *pp;
+            const f16x2_t p01 = __builtin_bit_cast(f16x2_t, w.x), p23 = __builtin_bit_cast(f16x2_t, w.y);
+            v[0] = fmaf((float)p01[0], ca[0], v[0]);
+            v[1] = fmaf((float)p01[1], ca[1], v[1]);
+            v[2] = fmaf((float)p23[0], ca[2], v[2]);
+            v[3] = fmaf((float)p23[1], ca[3], v[3]);
+          }
+          if (br < 2) {  // uniform
+            *pp = make_uint2(__builtin_bit_cast(uint32_t, (f16x2_t){(_Float16)v[0], (_Float16)v[1]}),
+                             __builtin_bit_cast(uint32_t, (f16x2_t){(_Float16)v[2], (_Float16)v[3]}));
+          } else {
+            // the last branch: out is written once; rows past the chunk's end
+            // belong to no query
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = r0 + i;
+              const int qi = tile * a.q_tile + r / g;
+              const int h = kvh * g + r % g;
+              if (qi < a.C)
+                a.out[(((int64_t)b * a.C + qi) * a.Hq + h) * D + 16 * nd + (ln & 15)] = v[i];
             }
           }
         }
