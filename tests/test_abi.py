@@ -277,3 +277,29 @@ def test_prefill_rejects_rows_beyond_32bit_offsets(L):
     assert call(1 << 24, 128, m_sparse=256, window=(1 << 24) - 64) == -3
     assert call(1 << 24, 128, m_sparse=256, window=(1 << 24) - 63) == -2
     assert call(1 << 20, 128, m_sparse=256, window=1 << 30) == -3  # capped by P + C
+
+
+def test_noalloc_step_checks_before_any_device_call(L):
+    """sparse_decode_step_noalloc checks its arguments (and the scratch limit) before it
+    touches the device: an invalid shape or config is BSA_INVALID_ARG, a step whose
+    workspace exceeds the static scratch BSA_UNSUPPORTED."""
+    fake = ctypes.c_void_p(0x1000)
+    F = L.sparse_decode_step_noalloc
+    F.argtypes = [ctypes.c_void_p] * 4 + [ctypes.POINTER(bsa.bsa_shape),
+                                          ctypes.POINTER(bsa.bsa_select_cfg), ctypes.c_void_p,
+                                          ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    F.restype = ctypes.c_int
+    cfg = bsa.select_cfg(top_k=304)
+    bad = bsa.make_shape(1, 6, 4, 128, 1024, 1024)        # Hq % Hkv != 0
+    assert F(fake, fake, fake, fake, ctypes.byref(bad), ctypes.byref(cfg), fake, 0.0, fake, None,
+             None) == -1
+    assert F(fake, fake, fake, fake, None, ctypes.byref(cfg), fake, 0.0, fake, None, None) == -1
+    neg = bsa.select_cfg(n_sink=-1)
+    ok = bsa.make_shape(1, 4, 4, 128, 1024, 1024)
+    assert F(fake, fake, fake, fake, ctypes.byref(ok), ctypes.byref(neg), fake, 0.0, fake, None,
+             None) == -1
+    big = bsa.make_shape(256, 64, 8, 128, 131072, 131072)
+    assert L.bsa_decode_step_workspace_size(ctypes.byref(big), ctypes.byref(cfg)) > 16 << 20
+    assert F(fake, fake, fake, fake, ctypes.byref(big), ctypes.byref(cfg), fake, 0.0, fake, None,
+             None) == -2
