@@ -236,8 +236,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
     if (fs.k >= n) {  // uniform
       for (int i = tid; i < n; i += 256) list_lds[fs.c0 + i] = fs.c0 + i;
     } else if (fs.k > 0) {
-      topk_into_list<256, (SEL ? SELK : 1), 8>(fs.scores + (int64_t)pair * fs.nb + fs.c0, n,
-                                                fs.k, fs.c0, list_lds, sel_sh);
+      topk_into_list<256, (SEL ? SELK : 1), 8>(fs.scores + (int64_t)pair * fs.nb, fs.nb, fs.c0,
+                                                fs.c1, fs.k, list_lds, sel_sh);
     }
     __syncthreads();
     if (split == 0)

@@ -8,6 +8,7 @@
 // page: every block gets a score, the highest-scoring ones are kept.
 #include "bsa_device.h"
 #include "bsa_launch.h"
+#include "topk_device.h"
 
 namespace bsa {
 
@@ -241,10 +242,11 @@ void launch_append(const uint16_t* src, uint16_t* dst, int64_t pairs, int n_new,
 // Scores.  16 lanes share one summary row (512 B for d=128) and reduce their
 // partial dot products with DPP inside the row; each lane builds the pooled
 // query qbar (fp32 sum over the group's query heads, in head order) for its
-// own dims, so there is no LDS and no barrier, and all of a workgroup's
-// summary loads are issued before anything waits.  Grid: (row chunks,
-// pairs) so that even 8 pairs spread over the whole chip.
+// own dims from the query rows staged in LDS.  All of a workgroup's summary
+// loads are issued before anything waits.  Grid: (row chunks, pairs) so that
+// even 8 pairs spread over the whole chip.
 constexpr int SCORE_ROWS_PER_WG = 64;
+constexpr int SCORE_QH = 16;  // query heads staged in LDS at a time
 
 template <int D>
 __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict__ q,
@@ -269,18 +271,34 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
     for (int c = 0; c < PER / 4; ++c)
       w[p][c] = ld_stream(reinterpret_cast<const float4*>(base + (int64_t)r * D) + c);
   }
-  // pooled query over the g heads of the group, this lane's PER dims
+  // pooled query over the g heads of the group, this lane's PER dims: up to
+  // SCORE_QH heads at a time are read with one 16-byte load per thread into
+  // LDS (all requested together), then each lane sums its dims in head order
+  __shared__ __align__(16) float qs[SCORE_QH][D];
   float qv[PER];
 #pragma unroll
   for (int c = 0; c < PER; ++c) qv[c] = 0.f;
-  const uint16_t* qh = q + ((int64_t)b * Hq + (int64_t)kvh * g) * D + l16 * PER;
-  for (int h = 0; h < g; ++h) {
-#pragma unroll
-    for (int c = 0; c < PER; c += 2) {
-      const uint32_t u = *reinterpret_cast<const uint32_t*>(qh + (int64_t)h * D + c);
-      qv[c] += bf_lo(u);
-      qv[c + 1] += bf_hi(u);
+  const uint16_t* qg = q + ((int64_t)b * Hq + (int64_t)kvh * g) * D;
+  for (int h0 = 0; h0 < g; h0 += SCORE_QH) {
+    const int hn = min(SCORE_QH, g - h0);
+    for (int i = tid; i < hn * (D / 8); i += 256) {
+      const int h = i / (D / 8), c8 = (i % (D / 8)) * 8;
+      const uint4 u = *reinterpret_cast<const uint4*>(qg + (int64_t)(h0 + h) * D + c8);
+      *reinterpret_cast<float4*>(&qs[h][c8]) = make_float4(bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y));
+      *reinterpret_cast<float4*>(&qs[h][c8 + 4]) = make_float4(bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w));
     }
+    __syncthreads();
+    for (int h = 0; h < hn; ++h) {
+#pragma unroll
+      for (int c = 0; c < PER; c += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(&qs[h][l16 * PER + c]);
+        qv[c] += x.x;
+        qv[c + 1] += x.y;
+        qv[c + 2] += x.z;
+        qv[c + 3] += x.w;
+      }
+    }
+    __syncthreads();
   }
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
@@ -311,17 +329,18 @@ void launch_scores(const uint16_t* q, const float* summ, int B, int Hq, int Hkv,
 
 // ---------------------------------------------------------------------------
 // Top-k.  One workgroup of 1024 threads per (batch, kv head).
-// 1. Radix select over order-preserving uint32 keys, 8 bits per pass with a
-//    256-bin LDS histogram, finds T = the k-th largest key and how many keys
+// 1. T = the k-th largest order-preserving uint32 key, and how many keys
 //    equal to T must be taken (the ones with the lowest block index).
 // 2. An ordered compaction in index order writes the kept candidates
 //    ascending, so the output list (sink, selected, local) is sorted with no
 //    extra sort.
 // Up to 16384 candidates (topk_reg_kernel) each thread keeps a contiguous run
-// of KPT candidates in registers for the whole select: one read of the
-// scores, and the compaction is two block-wide scans of per-thread counts.
-// Longer lists use topk_kernel, which re-reads the scores (L2) every pass and
-// compacts in 1024-candidate strides.
+// of KPT candidates in registers for the whole select (one read of the
+// scores), T comes from a value-bucket pass and a rank inside the bucket
+// holding it (topk_select_regs), and the compaction is two block-wide scans
+// of per-thread counts.  Longer lists use topk_kernel: radix passes of 8 bits
+// with a 256-bin LDS histogram that re-read the scores (L2) every pass, and a
+// compaction in 1024-candidate strides.
 constexpr int TOPK_THREADS = 1024;
 constexpr int TOPK_WAVES = TOPK_THREADS / 64;
 // histogram copies of the register-resident select: 8 from 8 candidates per
@@ -499,24 +518,20 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_reg_kernel(const float* __r
                                                                 int nb, int c0, int c1, int k,
                                                                 int n_keep, AdaptiveSel ad,
                                                                 int32_t* __restrict__ idx_out) {
-  // HC copies of the histogram (lane l counts into copy l % HC, rows padded
-  // by one word so the copies of a bin sit in different banks): keys of one
-  // pass mostly share a few digits, and same-address atomics of a wave
-  // serialise
-  constexpr int HC = TopkCopies<KPT>::value;
-  __shared__ uint32_t hist[HC][257];
-  __shared__ uint32_t sh_digit, sh_above;
+  __shared__ TopkShared<TOPK_THREADS, TopkCopies<KPT>::value> sh;
   __shared__ int wtot[TOPK_WAVES];
   __shared__ float ext[2][TOPK_WAVES];
   const int pair = blockIdx.x;
   const int tid = threadIdx.x;
-  const float* s = scores + (int64_t)pair * nb + c0;
+  const float* row = scores + (int64_t)pair * nb;
   int32_t* out = idx_out + (int64_t)pair * n_keep;
   const int n = c1 - c0;
-  const int i0 = tid * KPT;  // this thread's candidates [i0, i0 + KPT)
+  // this thread's slots: row positions [p0, p0 + KPT), an aligned run of the
+  // row when it fits the slots, else a run of the candidates
+  const int base = (nb <= TOPK_THREADS * KPT) ? 0 : c0;
+  const int p0 = base + tid * KPT;
   float sv[KPT];
-#pragma unroll
-  for (int e = 0; e < KPT; ++e) sv[e] = (n > 0) ? s[min(i0 + e, n - 1)] : 0.f;
+  load_slots<KPT>(row, base, nb, sv);
   if (ad.on) {  // uniform
     const float* all = scores + (int64_t)pair * nb;
     float amax = -INFINITY, amin = INFINITY;
@@ -540,7 +555,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_reg_kernel(const float* __r
     const float tau = (c0 + (nb - c1) > 0) ? amax + ad.margin * (amax - amin) : -INFINITY;
     int cnt = 0;
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) cnt += (i0 + e < n && sv[e] > tau) ? 1 : 0;
+    for (int e = 0; e < KPT; ++e) cnt += (p0 + e >= c0 && p0 + e < c1 && sv[e] > tau) ? 1 : 0;
     block_scan(cnt, wtot, &cnt);
     k = min(max(cnt, ad.k_lo), ad.k_hi);
     for (int i = c0 + k + (nb - c1) + tid; i < n_keep; i += TOPK_THREADS) out[i] = -1;  // absent
@@ -552,77 +567,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_reg_kernel(const float* __r
     for (int i = tid; i < n; i += TOPK_THREADS) out[c0 + i] = c0 + i;
     return;
   }
-  uint32_t key[KPT];
-#pragma unroll
-  for (int e = 0; e < KPT; ++e) key[e] = order_key(sv[e]);
-  uint32_t prefix = 0;
-  uint32_t remaining = (uint32_t)k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < HC * 257; i += TOPK_THREADS) (&hist[0][0])[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-      const bool match = i0 + e < n && (pass == 0 || ((key[e] ^ prefix) >> (shift + 8)) == 0);
-      if (match) atomicAdd(&hist[tid % HC][(key[e] >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // lane l owns bins 255-4l .. 252-4l (descending order)
-      const int lane = tid;
-      uint32_t c[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c[e] = 0;
-#pragma unroll
-        for (int cp = 0; cp < HC; ++cp) c[e] += hist[cp][255 - 4 * lane - e];
-      }
-      const uint32_t own = c[0] + c[1] + c[2] + c[3];
-      uint32_t inc = own;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t t = __shfl_up(inc, off);
-        if (lane >= off) inc += t;
-      }
-      const uint32_t exc = inc - own;
-      if (exc < remaining && remaining <= inc) {
-        uint32_t acc = exc;
-        for (int e = 0; e < 4; ++e) {
-          if (acc + c[e] >= remaining) {
-            sh_digit = (uint32_t)(255 - 4 * lane - e);
-            sh_above = acc;
-            break;
-          }
-          acc += c[e];
-        }
-      }
-    }
-    __syncthreads();
-    prefix |= sh_digit << shift;
-    remaining -= sh_above;
-  }
-  // T = prefix: keys above T are all taken, plus the first `remaining` keys
-  // equal to T in index order
-  const uint32_t T = prefix;
-  int n_eq = 0;
-#pragma unroll
-  for (int e = 0; e < KPT; ++e) n_eq += (i0 + e < n && key[e] == T) ? 1 : 0;
-  int tot;
-  int eq_rank = block_scan(n_eq, wtot, &tot);
-  int n_sel = 0;
-  bool sel[KPT];
-#pragma unroll
-  for (int e = 0; e < KPT; ++e) {
-    const bool valid = i0 + e < n;
-    const bool eq = valid && key[e] == T;
-    sel[e] = valid && (key[e] > T || (eq && eq_rank < (int)remaining));
-    eq_rank += eq ? 1 : 0;
-    n_sel += sel[e] ? 1 : 0;
-  }
-  int pos = c0 + block_scan(n_sel, wtot, &tot);
-#pragma unroll
-  for (int e = 0; e < KPT; ++e)
-    if (sel[e]) out[pos++] = c0 + i0 + e;
+  topk_select_regs<TOPK_THREADS, KPT, TopkCopies<KPT>::value>(sv, base, c0, c1, k, c0, out, sh);
 }
 
 void launch_topk(const float* scores, int64_t pairs, int nb, int c0, int c1, int k, int n_keep,
