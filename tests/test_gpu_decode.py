@@ -139,6 +139,70 @@ def test_topk_candidate_counts(nb):
             assert np.array_equal(g_idx, o_idx)
 
 
+def _path_summaries(kind, B, Hkv, nb, d, rng):
+    """Summaries that steer the top-k down each of its paths (q is all ones, so
+    every score is 2 x the row sum, an exact integer in fp32 for small rows):
+    equal: every candidate score equal (zero range: radix over all keys);
+    outlier: one block far above integer-valued rows (the k-th score's value
+    bucket holds nearly every candidate: radix inside that bucket);
+    overflow: three blocks whose fp32 scores overflow to +inf (not finite:
+    radix over all keys); the oracle's fp64 scores stay finite and highest."""
+    summ = rng.integers(-2, 3, (B, Hkv, nb, d)).astype(np.float32)
+    if kind == "equal":
+        summ[:] = 1.0
+    elif kind == "outlier":
+        summ[:, :, nb // 3, :] = 8192.0
+    elif kind == "overflow":
+        for j in (5, nb // 2, nb - 4):
+            summ[:, :, j, :] = 3.0e38
+    return summ
+
+
+@pytest.mark.parametrize("nb", [3000, 16003])
+@pytest.mark.parametrize("kind", ["equal", "outlier", "overflow"])
+def test_topk_paths(kind, nb):
+    """Each path of the top-k's threshold search gives the oracle's list exactly."""
+    import torch
+    B, Hq, Hkv, d, bs = 1, 4, 2, 128, 64
+    top_k = nb // 9
+    announce("topk path", kind, "nb", nb, "top_k", top_k)
+    q = synth.bf16_round(np.ones((B, Hq, d), np.float32))
+    summ = _path_summaries(kind, B, Hkv, nb, d, np.random.default_rng(nb))
+    idx, scores = bsa.select_blocks(to_dev(q), torch.from_numpy(summ).cuda(), nb * bs, bs, 1, 2,
+                                    top_k, want_scores=True)
+    torch.cuda.synchronize()
+    if kind == "overflow":
+        assert np.isposinf(scores.cpu().numpy()[..., nb // 2]).all()
+    o_idx, _ = oracle.select_blocks(q, summ.astype(np.float64), Hkv, 1, 2, top_k)
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+
+
+@pytest.mark.parametrize("kind", ["equal", "outlier"])
+def test_topk_paths_fused_step(kind):
+    """The same paths inside the attention launch (sparse_decode_step): the key
+    rows of a block all equal its target summary, so the block means are it."""
+    import torch
+    B, Hq, Hkv, d, bs, nb = 1, 4, 2, 128, 64, 2000
+    top_k = nb // 9
+    announce("topk path fused", kind, "nb", nb, "top_k", top_k)
+    rng = np.random.default_rng(7)
+    summ = _path_summaries(kind, B, Hkv, nb, d, rng)
+    k = np.repeat(summ, bs, axis=2)
+    v = rng.standard_normal((B, Hkv, nb * bs, d)).astype(np.float32)
+    q = synth.bf16_round(np.ones((B, Hq, d), np.float32) / 64.0)
+    qd = to_dev(q)
+    kd, vd = (to_dev(synth.bf16_round(a)) for a in (k, v))
+    N = nb * bs
+    summ_d, _ = bsa.build_block_summaries(kd, N, bs)
+    idx, _ = bsa.select_blocks(qd, summ_d, N, bs, 1, 2, top_k)
+    out, lse = bsa.sparse_decode_attn(qd, kd, vd, idx, N, bs)
+    out2, lse2, idx2 = bsa.sparse_decode_step(qd, kd, vd, summ_d, N, bs, 1, 2, top_k, 0.0)
+    torch.cuda.synchronize()
+    o_idx, _ = oracle.select_blocks(q, summ.astype(np.float64), Hkv, 1, 2, top_k)
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+    assert torch.equal(idx2, idx) and torch.equal(out2, out) and torch.equal(lse2, lse)
+
+
 def test_partials_then_merge_equal_the_call():
     """S4 then S5 as separate calls give sparse_decode_attn_split's result bit for bit, for
     the library's split plan and explicit split counts; the merged output is within the
