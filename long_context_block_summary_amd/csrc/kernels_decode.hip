@@ -178,9 +178,12 @@ __device__ __forceinline__ int split_blocks(const int32_t* list, int n_keep, int
   return nblk;
 }
 
-// blocks in flight per wave (register budget: two waves per SIMD)
+// blocks in flight per wave.  The bf16 kernel keeps the register budget of
+// two waves per SIMD (deeper pipelines at one wave per SIMD, 4-6 stages,
+// measured slower); the FP8 kernel, with half the bytes per tile, takes 5
+// stages at one wave per SIMD (one workgroup per CU is what the plan launches)
 constexpr int DEC_STAGES = 3;
-constexpr int DEC_STAGES_FP8 = 4;
+constexpr int DEC_STAGES_FP8 = 5;
 
 // SEL: the workgroup first selects its pair's kept blocks from the block
 // scores itself (the same list select_blocks writes; split 0 also writes it
@@ -333,7 +336,7 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 }
 
 template <int D, int G, int P>
-__global__ __launch_bounds__(256, 2) void decode_fp8_kernel(
+__global__ __launch_bounds__(256, 1) void decode_fp8_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const float* __restrict__ ksc, const float* __restrict__ vsc, int sstride,
     const int32_t* __restrict__ idx, int n_keep, int Hq, int Hkv, int N, int stride,
@@ -518,11 +521,15 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
   if (lse && tid == 0) lse[bh] = (M + log2f(L)) * LN2;
 }
 
-// Two workgroups of 4 waves fit per CU (two waves per SIMD), so the plan aims
-// at one full round of 512 workgroups over the MI355X's 256 CUs: splits per
-// pair = round(512 / pairs), each split a contiguous run of the kept-block
-// list.  More pairs than that: one split per pair.
-constexpr int DEC_TARGET_WGS = 512;
+// The plan aims at one round of 256 workgroups, one per CU of the MI355X:
+// splits per pair = round(256 / pairs), each split a contiguous run of the
+// kept-block list; more pairs than that, one split per pair.  Two workgroups
+// of 4 waves would fit per CU, but measured, one longer split per CU is
+// faster at every shape (128K: 40.1 against 41.7 us for S4; 1M: 72.6 against
+// 74.2): each workgroup pays its start-up (list, then first-tile latency) and
+// its epilogue once over twice the blocks, and the merge reads half the
+// partials.  A round that is not whole (384 or 640 workgroups) is slower still.
+constexpr int DEC_TARGET_WGS = 256;
 
 DecodePlan plan_decode(int64_t pairs, int n_keep, int g, int n_splits_req) {
   DecodePlan p;
