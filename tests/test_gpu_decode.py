@@ -105,6 +105,9 @@ def test_edge_cases():
     # cache capacity beyond seq_len, keep ratio instead of top-k
     run_decode_case(synth.scaled(base, name="cap", batch=2, seq_len=64 * 90 + 1, top_k=-1,
                                  keep_ratio=0.15), 36, capacity=64 * 100)
+    # more (batch, kv head) pairs than the plan's 256 workgroups: one split per pair
+    run_decode_case(synth.scaled(base, name="manypairs", batch=40, seq_len=64 * 30 + 5, top_k=6),
+                    37)
 
 
 @pytest.mark.parametrize("nb", [700, 1027, 1028, 3000, 6000, 16387, 16388, 20000])
