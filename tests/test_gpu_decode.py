@@ -239,6 +239,8 @@ def test_partials_then_merge_equal_the_call():
     ("gqa32k", dict(batch=1, seq_len=64 * 40, top_k=0)),      # sink + local only
     ("gqa32k", dict(batch=1, seq_len=64 * 40, top_k=500)),    # every block
     ("gqa32k", dict(batch=1, seq_len=100, top_k=5)),          # fewer blocks than sink + local
+    ("gqa32k", dict(batch=1, seq_len=64 * 3000, top_k=300)),  # 16 candidates per thread, float4 rows
+    ("gqa32k", dict(batch=1, seq_len=64 * 3000 + 7, top_k=300)),  # the same, rows not float4-aligned
     ("gqa32k", dict(batch=1, seq_len=64 * 4103, top_k=400)),  # 4,100 candidates: separate launches
     ("gqa32k", dict(batch=2, n_q_heads=32, head_dim=64, seq_len=64 * 200, top_k=30)),  # d = 64
     ("gqa32k", dict(batch=2, n_kv_heads=2, n_q_heads=32, seq_len=64 * 200, top_k=30)),  # g = 16
