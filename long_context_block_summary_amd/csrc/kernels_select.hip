@@ -331,7 +331,8 @@ void launch_scores(const uint16_t* q, const float* summ, int B, int Hq, int Hkv,
 }
 
 // ---------------------------------------------------------------------------
-// Top-k.  One workgroup of 1024 threads per (batch, kv head).
+// Top-k.  One workgroup per (batch, kv head): 256, 512 or 1024 threads by the
+// candidate count (the strided kernel: 1024).
 // 1. T = the k-th largest order-preserving uint32 key, and how many keys
 //    equal to T must be taken (the ones with the lowest block index).
 // 2. An ordered compaction in index order writes the kept candidates
@@ -492,38 +493,14 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const float* __restr
   }
 }
 
-// block-wide exclusive prefix sum of x in thread order; sets *total.  Uses
-// wtot[TOPK_WAVES] of LDS (free again on return).
-__device__ __forceinline__ int block_scan(int x, int* wtot, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(inc, off);
-    if (lane >= off) inc += t;
-  }
-  if (lane == 63) wtot[wave] = inc;
-  __syncthreads();
-  int off = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < TOPK_WAVES; ++w) {
-    const int c = wtot[w];
-    off += (w < wave) ? c : 0;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return off + inc - x;
-}
-
-template <int KPT>
-__global__ __launch_bounds__(TOPK_THREADS) void topk_reg_kernel(const float* __restrict__ scores,
+template <int NTH, int KPT>
+__global__ __launch_bounds__(NTH) void topk_reg_kernel(const float* __restrict__ scores,
                                                                 int nb, int c0, int c1, int k,
                                                                 int n_keep, AdaptiveSel ad,
                                                                 int32_t* __restrict__ idx_out) {
-  __shared__ TopkShared<TOPK_THREADS, TopkCopies<KPT>::value> sh;
-  __shared__ int wtot[TOPK_WAVES];
-  __shared__ float ext[2][TOPK_WAVES];
+  constexpr int NW = NTH / 64;
+  __shared__ TopkShared<NTH, TopkCopies<KPT>::value> sh;
+  __shared__ float ext[2][NW];
   const int pair = blockIdx.x;
   const int tid = threadIdx.x;
   const float* row = scores + (int64_t)pair * nb;
@@ -531,14 +508,14 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_reg_kernel(const float* __r
   const int n = c1 - c0;
   // this thread's slots: row positions [p0, p0 + KPT), an aligned run of the
   // row when it fits the slots, else a run of the candidates
-  const int base = (nb <= TOPK_THREADS * KPT) ? 0 : c0;
+  const int base = (nb <= NTH * KPT) ? 0 : c0;
   const int p0 = base + tid * KPT;
   float sv[KPT];
   load_slots<KPT>(row, base, nb, sv);
   if (ad.on) {  // uniform
     const float* all = scores + (int64_t)pair * nb;
     float amax = -INFINITY, amin = INFINITY;
-    for (int i = tid; i < c0 + (nb - c1); i += TOPK_THREADS) {
+    for (int i = tid; i < c0 + (nb - c1); i += NTH) {
       const float a = all[i < c0 ? i : c1 + (i - c0)];
       amax = fmaxf(amax, a);
       amin = fminf(amin, a);
@@ -551,7 +528,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_reg_kernel(const float* __r
     }
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < TOPK_WAVES; ++w) {
+    for (int w = 0; w < NW; ++w) {
       amax = fmaxf(amax, ext[0][w]);
       amin = fminf(amin, ext[1][w]);
     }
@@ -559,18 +536,18 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_reg_kernel(const float* __r
     int cnt = 0;
 #pragma unroll
     for (int e = 0; e < KPT; ++e) cnt += (p0 + e >= c0 && p0 + e < c1 && sv[e] > tau) ? 1 : 0;
-    block_scan(cnt, wtot, &cnt);
+    wg_exscan<NTH>(cnt, sh.wtot, &cnt);
     k = min(max(cnt, ad.k_lo), ad.k_hi);
-    for (int i = c0 + k + (nb - c1) + tid; i < n_keep; i += TOPK_THREADS) out[i] = -1;  // absent
+    for (int i = c0 + k + (nb - c1) + tid; i < n_keep; i += NTH) out[i] = -1;  // absent
   }
-  for (int i = tid; i < c0; i += TOPK_THREADS) out[i] = i;                 // sink
-  for (int i = tid; i < nb - c1; i += TOPK_THREADS) out[c0 + k + i] = c1 + i;  // local
+  for (int i = tid; i < c0; i += NTH) out[i] = i;                 // sink
+  for (int i = tid; i < nb - c1; i += NTH) out[c0 + k + i] = c1 + i;  // local
   if (k <= 0) return;
   if (k >= n) {
-    for (int i = tid; i < n; i += TOPK_THREADS) out[c0 + i] = c0 + i;
+    for (int i = tid; i < n; i += NTH) out[c0 + i] = c0 + i;
     return;
   }
-  topk_select_regs<TOPK_THREADS, KPT, TopkCopies<KPT>::value>(sv, base, c0, c1, k, c0, out, sh);
+  topk_select_regs<NTH, KPT, TopkCopies<KPT>::value>(sv, base, c0, c1, k, c0, out, sh);
 }
 
 void launch_topk(const float* scores, int64_t pairs, int nb, int c0, int c1, int k, int n_keep,
@@ -579,11 +556,21 @@ void launch_topk(const float* scores, int64_t pairs, int nb, int c0, int c1, int
   if (pairs <= 0) return;
   AdaptiveSel ad{adaptive ? 1 : 0, k_lo, k_hi, margin};
   const int n = c1 - c0;
-#define BSA_TOPK_REG(KK)                                                                    \
-  if (n <= TOPK_THREADS * KK)                                                               \
-    return topk_reg_kernel<KK><<<(unsigned)pairs, TOPK_THREADS, 0, st>>>(scores, nb, c0, c1, \
-                                                                        k, n_keep, ad, idx_out);
-  BSA_TOPK_REG(1) BSA_TOPK_REG(2) BSA_TOPK_REG(4) BSA_TOPK_REG(8) BSA_TOPK_REG(16)
+  // workgroup size by candidate count (measured: 509 candidates 12.7 us per
+  // select with 256 threads against 13.1 / 14.3 with 512 / 1024; 2,045
+  // candidates 16.5 us with 512 against 16.7 / 17.5), then the fewest
+  // candidates per thread that hold them
+#define BSA_TOPK_REG(NT, KK)                                                                    \
+  if (n <= NT * KK)                                                                             \
+    return topk_reg_kernel<NT, KK><<<(unsigned)pairs, NT, 0, st>>>(scores, nb, c0, c1, k, n_keep, \
+                                                                   ad, idx_out);
+  if (n <= 1024) {
+    BSA_TOPK_REG(256, 1) BSA_TOPK_REG(256, 2) BSA_TOPK_REG(256, 4)
+  } else if (n <= 4096) {
+    BSA_TOPK_REG(512, 4) BSA_TOPK_REG(512, 8)
+  } else {
+    BSA_TOPK_REG(1024, 8) BSA_TOPK_REG(1024, 16)
+  }
 #undef BSA_TOPK_REG
   topk_kernel<<<(unsigned)pairs, TOPK_THREADS, 0, st>>>(scores, nb, c0, c1, k, n_keep, ad,
                                                         idx_out);
