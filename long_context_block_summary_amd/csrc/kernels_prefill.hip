@@ -61,6 +61,10 @@ __global__ __launch_bounds__(256) void prefill_qbar_kernel(const uint16_t* __res
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+  // r / g as (r * gm) >> 24 with gm = ceil(2^24 / g): exact for r, g <= 256
+  // (a tile holds at most 256 rows), and one multiply instead of an integer
+  // division per row
+  const uint32_t gm = (1u << 24) / (uint32_t)g + ((1u << 24) % (uint32_t)g != 0u ? 1u : 0u);
   // rows in batches of 16 per thread, each batch's loads issued together
   // (a batch slot past the tile's end reads row 0 and adds nothing); the
   // rows are still added in order
@@ -70,7 +74,8 @@ __global__ __launch_bounds__(256) void prefill_qbar_kernel(const uint16_t* __res
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
       const int r = r0 + 16 * u < rows ? r0 + 16 * u : 0;
-      const int i = i0 + r / g, h = kvh * g + r % g;
+      const int rq = (int)(((uint32_t)r * gm) >> 24);
+      const int i = i0 + rq, h = kvh * g + (r - rq * g);
       piece[u] = reinterpret_cast<const uint4*>(q + (((int64_t)b * C + i) * Hq + h) * D)[col];
     }
 #pragma unroll
@@ -186,6 +191,8 @@ constexpr int PTK_MAX_WAVES = 16;  // 1024 threads
 static_assert(PTK_MAX_WAVES * 64 * 128 >= PREFILL_MAX_E4, "largest key count per thread is 128");
 
 constexpr int PTK_UND = 16384;  // undecided keys staged in LDS for the open bits
+constexpr int PTK_BUCKETS = 2048;  // value buckets over the staged keys' range
+constexpr int PTK_RANK_MAX = 256;  // keys of the threshold bucket ranked directly
 
 // block sum of one value per wave (lane 0's), through LDS slot set `parity`
 template <int NWV>
@@ -266,6 +273,10 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
   __shared__ uint32_t samp[PTK_THREADS];  // the bracket's sample
   __shared__ int bsum[PTK_WAVES];
   __shared__ uint32_t bmax[PTK_WAVES];
+  __shared__ uint32_t bhist[PTK_BUCKETS];  // value buckets of the staged keys
+  __shared__ uint2 bcand[PTK_RANK_MAX];    // (key, staged position) of the bucket holding T
+  __shared__ int bk_sel, bk_cnt, bk_n;
+  __shared__ uint32_t bk_above, bk_T;
   const int prob = blockIdx.x;  // sel order: [b][tile][kvh]
   const int b = prob / (n_tiles * Hkv), tile = (prob / Hkv) % n_tiles, kvh = prob % Hkv;
   const float* s = scores + (((int64_t)b * Hkv + kvh) * n_tiles + tile) * Es;
@@ -329,6 +340,7 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
   int n_und = 0;  // undecided keys staged in und
   int sh = 32;    // the bits of T below sh are open
   bool staged = false;
+  uint32_t b_lo = 0u, b_hi = 0u;  // the staged keys' range [bracket, row maximum]
   {
     uint32_t t[NV];
 #pragma unroll
@@ -428,6 +440,8 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
         sh = ts == mx ? 0 : 32 - __builtin_clz(ts ^ mx);
         T = sh == 32 ? 0u : (ts >> sh) << sh;
         staged = true;
+        b_lo = ts;
+        b_hi = mx;
       }
     }
   }
@@ -483,6 +497,73 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
         }
     }
   }
+  // Staged keys, all in [ts, mx]: T by value buckets first.  PTK_BUCKETS
+  // equal-width buckets over [ts, mx] of the order keys (a key's bucket is a
+  // monotone function of it: a subtraction, a conversion, a product and a
+  // truncation), one histogram pass over the staged keys, a scan from the top
+  // for the bucket holding the k-th largest key; when that bucket holds at
+  // most PTK_RANK_MAX keys, T is the key of the remaining rank among them
+  // (key descending, staged position ascending).  Otherwise the radix digits
+  // below fix T.
+  bool found = false;
+  if (staged && sh > 0) {  // uniform
+    const float bscale = (float)PTK_BUCKETS / ((float)(b_hi - b_lo) + 1.f);
+    auto bucket_of = [&](uint32_t kv) {
+      return min((int)((float)(kv - b_lo) * bscale), PTK_BUCKETS - 1);
+    };
+    for (int i = tid; i < PTK_BUCKETS; i += PTK_THREADS) bhist[i] = 0u;
+    __syncthreads();
+    for (int j = tid; j < n_und; j += PTK_THREADS) atomicAdd(&bhist[bucket_of(und[j])], 1u);
+    __syncthreads();
+    // thread t owns buckets top - PER t .. top - PER t - PER + 1 (descending)
+    constexpr int PER = PTK_BUCKETS / PTK_THREADS;
+    uint32_t c[PER];
+    uint32_t own = 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      c[j] = bhist[PTK_BUCKETS - 1 - (tid * PER + j)];
+      own += c[j];
+    }
+    int tot;
+    const uint32_t exc = (uint32_t)ptk_block_exscan<PTK_WAVES>((int)own, red[0], &tot);
+    const uint32_t rem = (uint32_t)k;  // no key lies above the staged range here
+    if (exc < rem && rem <= exc + own) {
+      uint32_t acc = exc;
+      for (int j = 0; j < PER; ++j) {
+        if (acc + c[j] >= rem) {
+          bk_sel = PTK_BUCKETS - 1 - (tid * PER + j);
+          bk_above = acc;
+          bk_cnt = (int)c[j];
+          bk_n = 0;
+          break;
+        }
+        acc += c[j];
+      }
+    }
+    __syncthreads();
+    const int tbk = bk_sel, cnt = bk_cnt;
+    if (cnt <= PTK_RANK_MAX) {  // uniform
+      for (int j = tid; j < n_und; j += PTK_THREADS) {
+        const uint32_t kv = und[j];
+        if (bucket_of(kv) == tbk) bcand[atomicAdd(&bk_n, 1)] = make_uint2(kv, (uint32_t)j);
+      }
+      __syncthreads();
+      const uint32_t want = rem - bk_above - 1u;  // T's rank in the bucket, from 0
+      for (int i = tid; i < cnt; i += PTK_THREADS) {
+        const uint2 me = bcand[i];
+        uint32_t rank = 0u;
+        for (int o = 0; o < cnt; ++o) {
+          const uint2 x = bcand[o];
+          rank += (x.x > me.x || (x.x == me.x && x.y < me.y)) ? 1u : 0u;
+        }
+        if (rank == want) bk_T = me.x;
+      }
+      __syncthreads();
+      T = bk_T;
+      found = true;
+    }
+  }
+  if (!found) {  // uniform
   for (int i = tid; i < 4 * 256; i += PTK_THREADS) (&dhist[0][0])[i] = 0u;
   __syncthreads();
   {
@@ -529,6 +610,7 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
       remaining -= (uint32_t)__builtin_amdgcn_readlane((int)above, src);
       T |= d << lo;
     }
+  }
   }
   if (staged) {  // uniform
     // The top k are the staged keys above T and the first k - #(> T) keys
