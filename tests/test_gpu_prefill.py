@@ -326,20 +326,37 @@ def test_prefill_selection_sparse_high_scores_over_ties():
     _distinct_over_ties(4 * E, 1_024, high_at=high, seed=5)
 
 
-def _distinct_over_ties(prior_len, top_k, n_high=0, high_at=None, seed=0):
+@pytest.mark.parametrize("n_entries,n_mid", [(30_000, 4_000), (70_000, 8_000)])
+def test_prefill_selection_tied_threshold_bucket(n_entries, n_mid):
+    """40 distinct high scores, n_mid equal middle scores above equal low ones, k = 540: the
+    sample's bracket is the middle value, so the top-k stages the high and middle keys, and
+    the value bucket holding the k-th largest key holds every middle key (more than the 256
+    it ranks directly): radix digits over the staged keys fix T.  30,000 entries take the
+    512-thread variant, 70,000 the 1024-thread one (a CPU replay of the kernel's decisions
+    on these inputs: 4,040 and 8,040 keys staged).  Exact scores: the selection must equal
+    the oracle's (the 40, then the 500 lowest-index middle entries)."""
+    _distinct_over_ties(4 * n_entries, 540, n_high=40, n_mid=n_mid, seed=n_entries + 1)
+
+
+def _distinct_over_ties(prior_len, top_k, n_high=0, high_at=None, seed=0, n_mid=0):
     import torch
     d, C, Hq = 128, 64, 4
     E = prior_len // 4
     announce("pf_tops", "P", prior_len, "E", E, "top_k", top_k, "high", n_high,
-             "high_at", None if high_at is None else len(high_at))
+             "high_at", None if high_at is None else len(high_at), "mid", n_mid)
     rng = np.random.default_rng(seed)
     n_tok = prior_len + C
     # every 4-token group pools to ones (score 256 * 128 with q = ones), except the high
-    # entries, whose dim 0 is 2 + r / 4 (distinct, exact in bf16)
+    # entries, whose dim 0 is 2 + r / 4 (distinct, exact in bf16), and n_mid middle entries
+    # (dim 0 = 1.5: one score between the two)
     k = np.ones((1, 1, n_tok, d), np.float32)
     pos = rng.choice(E, n_high, replace=False) if high_at is None else np.asarray(high_at)
     for r, j in enumerate(pos):
         k[0, 0, 4 * j:4 * j + 4, 0] = 2.0 + 0.25 * (r % 40) + 16.0 * (r // 40)
+    if n_mid:
+        mid = rng.choice(np.setdiff1d(np.arange(E), pos), n_mid, replace=False)
+        for j in mid:
+            k[0, 0, 4 * j:4 * j + 4, 0] = 1.5
     k = synth.bf16_round(k)
     v = synth.bf16_round(rng.standard_normal((1, 1, n_tok, d)).astype(np.float32))
     q = synth.bf16_round(np.ones((1, C, Hq, d), np.float32))
