@@ -497,8 +497,8 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
         }
     }
   }
-  // Staged keys, all in [ts, mx]: T by value buckets first.  PTK_BUCKETS
-  // equal-width buckets over [ts, mx] of the order keys (a key's bucket is a
+  // Staged keys, all in [bracket, row maximum]: T by value buckets first.
+  // PTK_BUCKETS equal-width buckets over that range of the order keys (a key's bucket is a
   // monotone function of it: a subtraction, a conversion, a product and a
   // truncation), one histogram pass over the staged keys, a scan from the top
   // for the bucket holding the k-th largest key; when that bucket holds at
@@ -564,53 +564,53 @@ __global__ __launch_bounds__(PTK_THREADS) void prefill_topk_kernel(const float* 
     }
   }
   if (!found) {  // uniform
-  for (int i = tid; i < 4 * 256; i += PTK_THREADS) (&dhist[0][0])[i] = 0u;
-  __syncthreads();
-  {
-    // The open sh bits of T, in digits of up to 8 bits from the top: a
-    // histogram of the digit over the staged keys that share T's bits above
-    // it, then the digit whose bin reaches the remaining rank counting from
-    // the top.  The histograms were cleared up front and every wave scans the
-    // bins itself, so each digit costs one barrier.  Staged padding keys (0,
-    // past E) lie below the k-th largest key, which is a real one.
-    uint32_t remaining = (uint32_t)(k - n_top);  // rank of T among the staged keys
-    int lo = sh;
-    for (int p = 0; lo > 0; ++p) {  // uniform, at most 4 digits
-      const int w = min(8, lo);
-      lo -= w;
-      const int hi = lo + w;  // bits [lo, hi) are this digit
-      for (int j = tid; j < n_und; j += PTK_THREADS) {
-        const uint32_t kv = und[j];
-        const bool same = hi == 32 || ((kv ^ T) >> hi) == 0u;
-        if (same) atomicAdd(&dhist[p][(kv >> lo) & ((1u << w) - 1u)], 1u);
+    for (int i = tid; i < 4 * 256; i += PTK_THREADS) (&dhist[0][0])[i] = 0u;
+    __syncthreads();
+    {
+      // The open sh bits of T, in digits of up to 8 bits from the top: a
+      // histogram of the digit over the staged keys that share T's bits above
+      // it, then the digit whose bin reaches the remaining rank counting from
+      // the top.  The histograms were cleared up front and every wave scans the
+      // bins itself, so each digit costs one barrier.  Staged padding keys (0,
+      // past E) lie below the k-th largest key, which is a real one.
+      uint32_t remaining = (uint32_t)(k - n_top);  // rank of T among the staged keys
+      int lo = sh;
+      for (int p = 0; lo > 0; ++p) {  // uniform, at most 4 digits
+        const int w = min(8, lo);
+        lo -= w;
+        const int hi = lo + w;  // bits [lo, hi) are this digit
+        for (int j = tid; j < n_und; j += PTK_THREADS) {
+          const uint32_t kv = und[j];
+          const bool same = hi == 32 || ((kv ^ T) >> hi) == 0u;
+          if (same) atomicAdd(&dhist[p][(kv >> lo) & ((1u << w) - 1u)], 1u);
+        }
+        __syncthreads();
+        // lane l owns bins 255-4l .. 252-4l (descending order)
+        uint32_t c4[4];
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) c4[e] = dhist[p][255 - 4 * lane - e];
+        const uint32_t own = c4[0] + c4[1] + c4[2] + c4[3];
+        uint32_t inc = own;
+  #pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t t = __shfl_up(inc, off);
+          if (lane >= off) inc += t;
+        }
+        const uint32_t exc = inc - own;
+        const bool here = exc < remaining && remaining <= inc;  // exactly one lane
+        uint32_t dg = 0u, above = exc;
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool take = dg == 0u && above + c4[e] >= remaining;
+          dg = take ? (uint32_t)(256 - 4 * lane - e) : dg;  // digit + 1
+          above = (dg == 0u) ? above + c4[e] : above;
+        }
+        const int src = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(here));
+        const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)dg, src) - 1u;
+        remaining -= (uint32_t)__builtin_amdgcn_readlane((int)above, src);
+        T |= d << lo;
       }
-      __syncthreads();
-      // lane l owns bins 255-4l .. 252-4l (descending order)
-      uint32_t c4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) c4[e] = dhist[p][255 - 4 * lane - e];
-      const uint32_t own = c4[0] + c4[1] + c4[2] + c4[3];
-      uint32_t inc = own;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t t = __shfl_up(inc, off);
-        if (lane >= off) inc += t;
-      }
-      const uint32_t exc = inc - own;
-      const bool here = exc < remaining && remaining <= inc;  // exactly one lane
-      uint32_t dg = 0u, above = exc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool take = dg == 0u && above + c4[e] >= remaining;
-        dg = take ? (uint32_t)(256 - 4 * lane - e) : dg;  // digit + 1
-        above = (dg == 0u) ? above + c4[e] : above;
-      }
-      const int src = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(here));
-      const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)dg, src) - 1u;
-      remaining -= (uint32_t)__builtin_amdgcn_readlane((int)above, src);
-      T |= d << lo;
     }
-  }
   }
   if (staged) {  // uniform
     // The top k are the staged keys above T and the first k - #(> T) keys
