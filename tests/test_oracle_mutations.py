@@ -106,3 +106,28 @@ def test_pins_catch_mutant(tmp_path, name, old, new):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutant '{name}'\n{r.stdout[-2000:]}"
+
+
+# mutants the randomised properties (test_oracle_properties.py) must catch on their own
+PROPERTY_MUTANTS = ["mean divides by block size", "score sign", "tie-break reversed",
+                    "group drops heads", "no 1/sqrt(d) scale", "K and V swapped",
+                    "wrong GQA head map", "local range off by one", "lse drops the max",
+                    "weights not normalised"]
+
+
+@pytest.mark.parametrize("name", PROPERTY_MUTANTS)
+def test_properties_catch_mutant(tmp_path, name):
+    old, new = next((o, n) for m, o, n in MUTANTS if m == name)
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor missing: {old!r}"
+    cfile = tmp_path / "oracle.c"
+    cfile.write_text(src.replace(old, new, 1))
+    (tmp_path / "oracle.h").write_text(open(os.path.join(ROOT, "oracle", "oracle.h")).read())
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                    str(cfile), "-o", str(lib), "-lm"], check=True)
+    env = dict(os.environ, BSA_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_properties.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"properties did not catch mutant '{name}'\n{r.stdout[-2000:]}"
