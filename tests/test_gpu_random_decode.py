@@ -1,0 +1,72 @@
+"""Randomised GPU parity of the decode path against the oracle.
+
+32 seeded cases draw the batch, kv heads, group size, head dim, length
+(log-uniform from 1 to 24,000 tokens), sink/local counts, top-k or keep ratio,
+split count and the data (planted block strengths or plain Gaussian); each case
+runs the summaries, the selection and the attention on the GPU and checks them
+against the oracle as the fixed-shape tests do (fp32 summaries bit for bit, index
+sets by the near-tie rule, outputs within 2e-3), then requires the fused step to
+give the same list and outputs bit for bit.  Every case prints its parameters
+before any GPU call.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import long_context_block_summary_amd as bsa
+from long_context_block_summary_amd import synth
+from parity_rules import to_dev
+from test_gpu_decode import announce, run_decode_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    bsa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def draw_case(i):
+    rng = np.random.default_rng(7000 + i)
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    hkv = int(rng.choice([1, 2, 4]))
+    n_sink, n_local = int(rng.integers(0, 4)), int(rng.integers(0, 4))
+    ratio = bool(rng.integers(0, 2))
+    top_k = -1 if ratio else int(rng.integers(0, 120))
+    keep = float(rng.choice([0.05, 0.1, 0.15, 0.2, 0.35])) if ratio else 0.0
+    if n_sink + n_local == 0 and (ratio or top_k == 0):
+        n_local = 1  # at least one kept block per list
+    cfg = synth.DecodeConfig(
+        name=f"rand{i}", batch=int(rng.integers(1, 4)), n_q_heads=hkv * g, n_kv_heads=hkv,
+        head_dim=int(rng.choice([64, 128])),
+        seq_len=int(math.exp(rng.uniform(0.0, math.log(24000)))),
+        n_sink=n_sink, n_local=n_local, top_k=top_k, keep_ratio=keep,
+        planted=bool(rng.integers(0, 2)))
+    return cfg, int(rng.choice([0, 1, 3, 8])), int(rng.integers(0, 10**6))
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_random_decode_shapes(i):
+    import torch
+    cfg, n_splits, seed = draw_case(i)
+    run_decode_case(cfg, seed, n_splits=n_splits)
+    # the fused step: the same list and, bit for bit, the same outputs
+    announce("  fused step", cfg.name)
+    t = synth.gen_decode(cfg, seed)
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    N, bs = cfg.seq_len, cfg.block_size
+    summ, _ = bsa.build_block_summaries(k, N, bs)
+    idx, _ = bsa.select_blocks(q, summ, N, bs, cfg.n_sink, cfg.n_local, cfg.top_k,
+                               cfg.keep_ratio)
+    out, lse = bsa.sparse_decode_attn(q, k, v, idx, N, bs)
+    out2, lse2, idx2 = bsa.sparse_decode_step(q, k, v, summ, N, bs, cfg.n_sink, cfg.n_local,
+                                              cfg.top_k, cfg.keep_ratio)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx)
+    assert torch.equal(out2, out) and torch.equal(lse2, lse)
