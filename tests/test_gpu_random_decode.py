@@ -6,8 +6,10 @@ split count and the data (planted block strengths or plain Gaussian); each case
 runs the summaries, the selection and the attention on the GPU and checks them
 against the oracle as the fixed-shape tests do (fp32 summaries bit for bit, index
 sets by the near-tie rule, outputs within 2e-3), then requires the fused step to
-give the same list and outputs bit for bit.  Every case prints its parameters
-before any GPU call.
+give the same list and outputs bit for bit.  16 more draws run the FP8 cache:
+the GPU quantizer against the oracle's codes and scales bit for bit, then the FP8
+attention (a quarter of them over adaptive, -1-padded lists) within 2e-3.  Every
+case prints its parameters before any GPU call.
 """
 import math
 
@@ -70,3 +72,43 @@ def test_random_decode_shapes(i):
     torch.cuda.synchronize()
     assert torch.equal(idx2, idx)
     assert torch.equal(out2, out) and torch.equal(lse2, lse)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_fp8_decode_shapes(i):
+    """The same draws over an FP8 (E4M3) cache: quantize_kv_fp8 writes the oracle's codes
+    and scales bit for bit, and sparse_decode_attn_fp8 on the GPU's selection matches the
+    oracle's attention over the dequantized cache (within 2e-3), with or without an
+    adaptive selection's -1 padding."""
+    import torch
+    import oracle
+    from parity_rules import OUT_ATOL
+    cfg, _, seed = draw_case(100 + i)
+    adaptive = i % 4 == 3
+    announce(cfg.name, "fp8 seed", seed, "B", cfg.batch, "Hq", cfg.n_q_heads, "Hkv",
+             cfg.n_kv_heads, "d", cfg.head_dim, "N", cfg.seq_len, "sink", cfg.n_sink, "local",
+             cfg.n_local, "top_k", cfg.top_k, "ratio", cfg.keep_ratio, "adaptive", adaptive)
+    t = synth.gen_decode(cfg, seed)
+    N, bs = cfg.seq_len, cfg.block_size
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    k8, ks = bsa.quantize_kv_fp8(k, N, bs)
+    v8, vs = bsa.quantize_kv_fp8(v, N, bs)
+    summ, _ = bsa.build_block_summaries(k, N, bs)
+    kw = dict(adaptive=True, keep_ratio_max=0.3) if adaptive else {}
+    idx, _ = bsa.select_blocks(q, summ, N, bs, cfg.n_sink, cfg.n_local, cfg.top_k,
+                               0.1 if adaptive else cfg.keep_ratio, **kw)
+    out, lse = bsa.sparse_decode_attn_fp8(q, k8, v8, ks, vs, idx, N, bs)
+    torch.cuda.synchronize()
+    nb = -(-N // bs)
+    o_k8, o_ks = oracle.quantize_fp8(t["k"], N, bs)
+    o_v8, o_vs = oracle.quantize_fp8(t["v"], N, bs)
+    assert np.array_equal(k8.cpu().numpy()[:, :, :N], o_k8[:, :, :N])
+    assert np.array_equal(v8.cpu().numpy()[:, :, :N], o_v8[:, :, :N])
+    assert np.array_equal(ks.cpu().numpy()[..., :nb].view(np.uint32), o_ks[..., :nb].view(np.uint32))
+    assert np.array_equal(vs.cpu().numpy()[..., :nb].view(np.uint32), o_vs[..., :nb].view(np.uint32))
+    o_out, o_lse = oracle.sparse_decode_attn_fp8(t["q"], o_k8, o_v8, o_ks, o_vs,
+                                                 idx.cpu().numpy(), N, bs)
+    err = float(np.abs(out.cpu().numpy() - o_out).max())
+    lerr = float(np.abs(lse.cpu().numpy() - o_lse).max())
+    announce("  max|out err|", err, "max|lse err|", lerr)
+    assert err <= OUT_ATOL and lerr <= 1e-3
