@@ -477,6 +477,10 @@ def run_prefill(cfg, steps, warmup, flush_bytes=1 << 30):
                      dtype=torch.uint8, device=dev)
     pc_cat = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile,
                              bsa.COMBINE_CONCAT)
+    # the selection against the fp32 means (the other indexer), reported beside the default
+    pc_f32 = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile,
+                             indexer=bsa.INDEXER_F32)
+    k4f, _ = bsa.build_block_summaries(k, cfg.prior_len, cfg.m_sparse, want_f32=True)
     sink = torch.linspace(-2.0, 3.0, cfg.n_q_heads, dtype=torch.float32, device=dev)
     sel = torch.empty((cfg.batch, -(-cfg.chunk_len // cfg.q_tile), cfg.n_kv_heads,
                        min(cfg.top_k_sparse, -(-cfg.prior_len // cfg.m_sparse))),
@@ -485,7 +489,9 @@ def run_prefill(cfg, steps, warmup, flush_bytes=1 << 30):
         "sparse_prefill_attn": lambda: bsa.sparse_prefill_attn(
             q, k, v, *streams, cfg.prior_len, cfg=pc, out=out, workspace=ws),
         "select_prefill_entries": lambda: bsa.select_prefill_entries(
-            q, k, streams[0], cfg.prior_len, cfg=pc, sel=sel, workspace=ws),
+            q, k, None, streams[1], cfg.prior_len, cfg=pc, sel=sel, workspace=ws),
+        "select_prefill_entries_f32": lambda: bsa.select_prefill_entries(
+            q, k, k4f, None, cfg.prior_len, cfg=pc_f32, sel=sel, workspace=ws),
         "sparse_prefill_attn_selected": lambda: bsa.sparse_prefill_attn_selected(
             q, k, v, *streams[1:], sel, cfg.prior_len, cfg=pc, out=out),
         "concat_sink": lambda: bsa.sparse_prefill_attn_selected(
@@ -515,8 +521,11 @@ def run_prefill(cfg, steps, warmup, flush_bytes=1 << 30):
     att = mean(times["sparse_prefill_attn_selected"])
     r2 = mean(times["select_prefill_entries"])
     n_tiles = -(-cfg.chunk_len // cfg.q_tile)
-    r2_bytes = cfg.batch * cfg.n_kv_heads * e4 * cfg.head_dim * 4  # fp32 scoring stream, read once
+    # the bf16 keys read once, the fp32 scores written once and read back by the top-k
+    r2_bytes = (cfg.batch * cfg.n_kv_heads * e4 * cfg.head_dim * 2
+                + 2 * cfg.batch * cfg.n_kv_heads * n_tiles * e4 * 4)
     r2_flops = 2 * cfg.batch * cfg.n_kv_heads * n_tiles * e4 * cfg.head_dim
+    r2_f32 = mean(times["select_prefill_entries_f32"])
     gather_a = cfg.batch * cfg.n_kv_heads * n_tiles * ksel * cfg.head_dim * 2 * 2
     return {"workload": cfg.name, "ms_per_call": ms, "call_pct": pct(times["sparse_prefill_attn"]),
             "algorithmic_gflop": fl / 1e9,
@@ -531,9 +540,10 @@ def run_prefill(cfg, steps, warmup, flush_bytes=1 << 30):
             "attention_concat_sink": {"call": "sparse_prefill_attn_selected, concatenated "
                                               "softmax + per-head sink logits",
                                       "ms": mean(times["concat_sink"])},
-            "selection_R2": {"call": "select_prefill_entries", "ms": r2,
-                             "stream_GBps": r2_bytes / (r2 / 1e3) / 1e9,
-                             "fp32_gflop": r2_flops / 1e9},
+            "selection_R2": {"call": "select_prefill_entries (bf16 compressed keys)", "ms": r2,
+                             "GBps": r2_bytes / (r2 / 1e3) / 1e9,
+                             "bytes": r2_bytes, "gflop": r2_flops / 1e9,
+                             "fp32_means_indexer_ms": r2_f32},
             "streams_ingest_ms": sorted(r1)[1], "inputs": t}
 
 

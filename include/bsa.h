@@ -80,12 +80,22 @@ typedef struct {
   int32_t window;        /* raw tokens attended up to and including the query (128) */
   int32_t q_tile;        /* consecutive queries sharing one selection (64) */
   int32_t combine;       /* BSA_COMBINE_AVERAGE or BSA_COMBINE_CONCAT */
+  int32_t indexer;       /* BSA_INDEXER_BF16 (0) or BSA_INDEXER_F32: the keys the branch-A
+                            selection scores against */
 } bsa_prefill_cfg;
 
 /* how sparse_prefill_attn joins its three branches */
 #define BSA_COMBINE_AVERAGE 0 /* (o_A + o_B + o_C) / 3, each branch its own softmax */
 #define BSA_COMBINE_CONCAT 1  /* one softmax over the concatenated logits of all three
                                  ("CSA + HCA 混合注意力机制" §4.3) */
+
+/* which pooled keys the branch-A selection scores against ("CSA + HCA 混合注意力机制"
+ * §4.2: the indexer scores the compressed entries, its QK product at low precision,
+ * its recall measured against a BF16 indexer) */
+#define BSA_INDEXER_BF16 0 /* the bf16 compressed keys k_cmp_sparse_bf16, the same entries
+                              branch A attends; the pooled query stays fp32 (split exactly
+                              into three bf16 terms on the bf16 matrix cores) */
+#define BSA_INDEXER_F32 1  /* the fp32 means k_cmp_sparse_f32 (fp32 matrix cores) */
 
 /* ceil(n / m): blocks (or compressed entries) covering n tokens; -1 if m <= 0 or n < 0 */
 int32_t bsa_num_blocks(int32_t n, int32_t m);
@@ -307,16 +317,18 @@ int sparse_decode_merge(const bsa_shape* shape, int32_t n_keep, int32_t block_si
  * P + i (P = shape->seq_len prior tokens), three branches averaged:
  *   A ("CSA + HCA 混合注意力机制" §4.1-4.2, §4.4): per (tile of q_tile
  *     consecutive queries, kv head) the pooled query (sum over the tile's
- *     queries and the group's heads) scores every m_sparse entry with the
- *     fp32 stream; the top_k_sparse entries (descending, lower index first)
- *     are attended with the bf16 streams;
+ *     queries and the group's heads, fp32) scores every m_sparse entry against
+ *     the keys cfg->indexer names (by default the bf16 compressed keys); the
+ *     top_k_sparse entries (descending, lower index first) are attended with
+ *     the bf16 streams;
  *   B (§5.1-5.2): all m_dense entries, attended densely;
  *   C (§4.3): raw tokens [P + i - window + 1, P + i] of k, v.
  * The compressed streams cover the P prior tokens only; the chunk's own K/V
  * are already appended at [P, P + C).
  *   q                    bf16 [B][C][Hq][d]
  *   k, v                 bf16 [B][Hkv][seq_stride][d], seq_stride >= P + C
- *   k_cmp_sparse_f32     fp32 [B][Hkv][E_s][d]   (E_s = ceil(P / m_sparse); from build_block_summaries)
+ *   k_cmp_sparse_f32     fp32 [B][Hkv][E_s][d]   (E_s = ceil(P / m_sparse); from build_block_summaries),
+ *                        read only with BSA_INDEXER_F32 (may be NULL otherwise)
  *   k/v_cmp_sparse_bf16  bf16 [B][Hkv][E_s][d]
  *   k/v_cmp_dense_bf16   bf16 [B][Hkv][E_d][d]   (E_d = ceil(P / m_dense))
  *   sink_logits          fp32 [Hq] or NULL: one learnable sink logit per query head
@@ -350,16 +362,18 @@ int sparse_prefill_attn(const void* q, int32_t chunk_len, const void* k, const v
 /* select_prefill_entries -- the selection step of sparse_prefill_attn alone
  * (the indexer role of "CSA + HCA 混合注意力机制" §4.2 with the pooled tile
  * query of §4.4): per (tile, kv head) the pooled query scores every m_sparse
- * entry with the fp32 stream and the top_k_sparse entries are written,
- * ascending (descending score, lower index first on equal scores).
- *   q                 bf16 [B][C][Hq][d]
- *   k_cmp_sparse_f32  fp32 [B][Hkv][E_s][d]
- *   sel_out           int32 [B][ceil(C / q_tile)][Hkv][min(top_k_sparse, E_s)]
- *   workspace         bsa_prefill_workspace_size() bytes, 16-byte aligned
+ * entry against the keys cfg->indexer names and the top_k_sparse entries are
+ * written, ascending (descending score, lower index first on equal scores).
+ *   q                  bf16 [B][C][Hq][d]
+ *   k_cmp_sparse_f32   fp32 [B][Hkv][E_s][d]: read with BSA_INDEXER_F32, else may be NULL
+ *   k_cmp_sparse_bf16  bf16 [B][Hkv][E_s][d]: read with BSA_INDEXER_BF16, else may be NULL
+ *   sel_out            int32 [B][ceil(C / q_tile)][Hkv][min(top_k_sparse, E_s)]
+ *   workspace          bsa_prefill_workspace_size() bytes, 16-byte aligned
  * Same requirements as sparse_prefill_attn. */
 int select_prefill_entries(const void* q, int32_t chunk_len, const float* k_cmp_sparse_f32,
-                           const bsa_shape* shape, const bsa_prefill_cfg* cfg, int32_t* sel_out,
-                           void* workspace, size_t ws_bytes, void* hip_stream);
+                           const void* k_cmp_sparse_bf16, const bsa_shape* shape,
+                           const bsa_prefill_cfg* cfg, int32_t* sel_out, void* workspace,
+                           size_t ws_bytes, void* hip_stream);
 
 /* sparse_prefill_attn_selected -- the three attention branches and their
  * average (§4.3, §5.2 and the average of sparse_prefill_attn) over a given

@@ -41,7 +41,8 @@ class bsa_select_cfg(ctypes.Structure):
 class bsa_prefill_cfg(ctypes.Structure):
     _fields_ = [("m_sparse", ctypes.c_int32), ("top_k_sparse", ctypes.c_int32),
                 ("m_dense", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("q_tile", ctypes.c_int32), ("combine", ctypes.c_int32)]
+                ("q_tile", ctypes.c_int32), ("combine", ctypes.c_int32),
+                ("indexer", ctypes.c_int32)]
 
 
 _lib = None
@@ -84,8 +85,8 @@ def lib():
                                      vp, vp, sz, vp]
     L.sparse_prefill_attn.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, P(bsa_shape),
                                       P(bsa_prefill_cfg), f32, vp, vp, vp, vp, vp, sz, vp]
-    L.select_prefill_entries.argtypes = [vp, i32, vp, P(bsa_shape), P(bsa_prefill_cfg), vp, vp,
-                                         sz, vp]
+    L.select_prefill_entries.argtypes = [vp, i32, vp, vp, P(bsa_shape), P(bsa_prefill_cfg), vp,
+                                         vp, sz, vp]
     L.sparse_prefill_attn_selected.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                                P(bsa_shape), P(bsa_prefill_cfg), f32, vp, vp, vp,
                                                vp]
@@ -139,11 +140,15 @@ def select_cfg(block_size=64, n_sink=1, n_local=2, top_k=-1, keep_ratio=0.0, ada
 
 
 COMBINE_AVERAGE, COMBINE_CONCAT = 0, 1
+INDEXER_BF16, INDEXER_F32 = 0, 1
 
 
 def prefill_cfg(m_sparse=4, top_k_sparse=2048, m_dense=128, window=128, q_tile=64,
-                combine=COMBINE_AVERAGE):
-    return bsa_prefill_cfg(m_sparse, top_k_sparse, m_dense, window, q_tile, combine)
+                combine=COMBINE_AVERAGE, indexer=INDEXER_BF16):
+    """Prefill parameters; indexer picks the keys the branch-A selection scores against:
+    INDEXER_BF16 the bf16 compressed keys (the entries branch A attends), INDEXER_F32 the
+    fp32 means."""
+    return bsa_prefill_cfg(m_sparse, top_k_sparse, m_dense, window, q_tile, combine, indexer)
 
 
 def num_blocks(n, m):
@@ -386,7 +391,8 @@ def sparse_prefill_attn(q, k, v, k_cmp_sparse_f32, k_cmp_sparse_bf16, v_cmp_spar
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
     _need(v, "v", torch.bfloat16, 4)
-    _need(k_cmp_sparse_f32, "k_cmp_sparse_f32", torch.float32, 4)
+    if cfg.indexer == INDEXER_F32:
+        _need(k_cmp_sparse_f32, "k_cmp_sparse_f32", torch.float32, 4)
     for name, t in (("k_cmp_sparse_bf16", k_cmp_sparse_bf16),
                     ("v_cmp_sparse_bf16", v_cmp_sparse_bf16),
                     ("k_cmp_dense_bf16", k_cmp_dense_bf16), ("v_cmp_dense_bf16", v_cmp_dense_bf16)):
@@ -440,12 +446,17 @@ def _prefill_shape(q, k, prior_len, cfg):
     return shape, n_tiles, kk
 
 
-def select_prefill_entries(q, k, k_cmp_sparse_f32, prior_len, cfg=None, sel=None, workspace=None):
+def select_prefill_entries(q, k, k_cmp_sparse_f32, k_cmp_sparse_bf16, prior_len, cfg=None,
+                           sel=None, workspace=None):
     """The prefill's entry selection alone: sel int32 [B][n_tiles][Hkv][min(top_k, E_s)].
-    k (bf16 [B][Hkv][stride][d]) only supplies the cache shape."""
+    k (bf16 [B][Hkv][stride][d]) only supplies the cache shape; of the two key streams only
+    the one cfg.indexer names is read (the other may be None)."""
     import torch
     cfg = cfg or prefill_cfg()
-    _need(k_cmp_sparse_f32, "k_cmp_sparse_f32", torch.float32, 4)
+    if cfg.indexer == INDEXER_F32:
+        _need(k_cmp_sparse_f32, "k_cmp_sparse_f32", torch.float32, 4)
+    else:
+        _need(k_cmp_sparse_bf16, "k_cmp_sparse_bf16", torch.bfloat16, 4)
     shape, n_tiles, kk = _prefill_shape(q, k, prior_len, cfg)
     C = q.shape[1]
     ws_bytes = lib().bsa_prefill_workspace_size(ctypes.byref(shape), C, ctypes.byref(cfg))
@@ -457,7 +468,8 @@ def select_prefill_entries(q, k, k_cmp_sparse_f32, prior_len, cfg=None, sel=None
         sel = torch.empty((q.shape[0], n_tiles, k.shape[1], kk), dtype=torch.int32,
                           device=q.device)
     _check("select_prefill_entries",
-           lib().select_prefill_entries(_ptr(q), C, _ptr(k_cmp_sparse_f32), ctypes.byref(shape),
+           lib().select_prefill_entries(_ptr(q), C, _ptr(k_cmp_sparse_f32),
+                                        _ptr(k_cmp_sparse_bf16), ctypes.byref(shape),
                                         ctypes.byref(cfg), _ptr(sel), _ptr(workspace),
                                         workspace.numel(), _stream(q.device)))
     return sel
@@ -570,11 +582,15 @@ def decode_loop_step(q, k_new, v_new, k_cache, v_cache, summaries, seq_len, bloc
     return out, lse, idx
 
 
-def build_compressed_streams(k, v, prior_len, cfg=None):
-    """The prefill's pooled streams over the prior tokens: fp32 + bf16 keys and bf16 values at
-    m_sparse, bf16 keys and values at m_dense (all via build_block_summaries)."""
+def build_compressed_streams(k, v, prior_len, cfg=None, want_f32=None):
+    """The prefill's pooled streams over the prior tokens: bf16 keys and values at m_sparse
+    (plus the fp32 keys when want_f32, by default when cfg.indexer is INDEXER_F32; else None),
+    bf16 keys and values at m_dense (all via build_block_summaries)."""
     cfg = cfg or prefill_cfg()
-    k4f, k4b = build_block_summaries(k, prior_len, cfg.m_sparse, want_f32=True, want_bf16=True)
+    if want_f32 is None:
+        want_f32 = cfg.indexer == INDEXER_F32
+    k4f, k4b = build_block_summaries(k, prior_len, cfg.m_sparse, want_f32=want_f32,
+                                     want_bf16=True)
     _, v4b = build_block_summaries(v, prior_len, cfg.m_sparse, want_f32=False, want_bf16=True)
     _, k128b = build_block_summaries(k, prior_len, cfg.m_dense, want_f32=False, want_bf16=True)
     _, v128b = build_block_summaries(v, prior_len, cfg.m_dense, want_f32=False, want_bf16=True)

@@ -443,7 +443,8 @@ int prefill_setup(const void* q, int32_t chunk_len, const bsa_shape* shape,
                   const bsa_prefill_cfg* cfg, float scale, bsa::PrefillLaunch* L) {
   if (!q || !shape_ok(shape) || !cfg || chunk_len < 1 || shape->seq_len < 1) return BSA_INVALID_ARG;
   if (cfg->m_sparse < 1 || cfg->m_dense < 1 || cfg->top_k_sparse < 1 || cfg->window < 1 ||
-      cfg->q_tile < 1 || (cfg->combine != BSA_COMBINE_AVERAGE && cfg->combine != BSA_COMBINE_CONCAT))
+      cfg->q_tile < 1 || (cfg->combine != BSA_COMBINE_AVERAGE && cfg->combine != BSA_COMBINE_CONCAT) ||
+      (cfg->indexer != BSA_INDEXER_BF16 && cfg->indexer != BSA_INDEXER_F32))
     return BSA_INVALID_ARG;
   if ((int64_t)shape->seq_len + chunk_len > shape->seq_stride) return BSA_INVALID_ARG;
   if (!aligned16(q)) return BSA_INVALID_ARG;
@@ -477,6 +478,7 @@ int prefill_setup(const void* q, int32_t chunk_len, const bsa_shape* shape,
   L->n_tiles = bsa_num_blocks(chunk_len, cfg->q_tile);
   L->scale = scale == 0.f ? 1.f / sqrtf(128.f) : scale;
   L->combine = cfg->combine;
+  L->indexer_f32 = cfg->indexer == BSA_INDEXER_F32 ? 1 : 0;
   return BSA_OK;
 }
 
@@ -496,22 +498,33 @@ int prefill_set_streams(const void* k, const void* v, const void* k_cmp_sparse_b
   L->out = out;
   return BSA_OK;
 }
+
+// the keys the selection scores against: the one cfg->indexer names must be
+// given (16-byte aligned); the other is not read
+int prefill_set_indexer_keys(const float* k_cmp_sparse_f32, const void* k_cmp_sparse_bf16,
+                             bsa::PrefillLaunch* L) {
+  const void* need = L->indexer_f32 ? static_cast<const void*>(k_cmp_sparse_f32) : k_cmp_sparse_bf16;
+  if (!need || !aligned16(need)) return BSA_INVALID_ARG;
+  L->k4f = k_cmp_sparse_f32;
+  L->k4b = static_cast<const uint16_t*>(k_cmp_sparse_bf16);
+  return BSA_OK;
+}
 }  // namespace
 
 extern "C" {
 
 int select_prefill_entries(const void* q, int32_t chunk_len, const float* k_cmp_sparse_f32,
-                           const bsa_shape* shape, const bsa_prefill_cfg* cfg, int32_t* sel_out,
-                           void* workspace, size_t ws_bytes, void* hip_stream) {
+                           const void* k_cmp_sparse_bf16, const bsa_shape* shape,
+                           const bsa_prefill_cfg* cfg, int32_t* sel_out, void* workspace,
+                           size_t ws_bytes, void* hip_stream) {
   bsa::PrefillLaunch L;
   int st = prefill_setup(q, chunk_len, shape, cfg, 0.f, &L);
   if (st != BSA_OK) return st;
-  if (!k_cmp_sparse_f32 || !aligned16(k_cmp_sparse_f32) || !sel_out || !workspace ||
-      !aligned16(workspace))
-    return BSA_INVALID_ARG;
+  st = prefill_set_indexer_keys(k_cmp_sparse_f32, k_cmp_sparse_bf16, &L);
+  if (st != BSA_OK) return st;
+  if (!sel_out || !workspace || !aligned16(workspace)) return BSA_INVALID_ARG;
   if (ws_bytes < bsa::prefill_workspace_bytes(L.B, L.Hkv, 128, L.n_tiles, L.E4, L.ksel, false))
     return BSA_WORKSPACE_TOO_SMALL;
-  L.k4f = k_cmp_sparse_f32;
   L.workspace = workspace;
   if (!bsa::launch_prefill_select(L, sel_out, static_cast<hipStream_t>(hip_stream)))
     return BSA_UNSUPPORTED;
@@ -552,12 +565,12 @@ int sparse_prefill_attn(const void* q, int32_t chunk_len, const void* k, const v
   st = prefill_set_streams(k, v, k_cmp_sparse_bf16, v_cmp_sparse_bf16, k_cmp_dense_bf16,
                            v_cmp_dense_bf16, out, &L);
   if (st != BSA_OK) return st;
-  if (!k_cmp_sparse_f32 || !aligned16(k_cmp_sparse_f32) || !workspace || !aligned16(workspace))
-    return BSA_INVALID_ARG;
+  st = prefill_set_indexer_keys(k_cmp_sparse_f32, k_cmp_sparse_bf16, &L);
+  if (st != BSA_OK) return st;
+  if (!workspace || !aligned16(workspace)) return BSA_INVALID_ARG;
   if (ws_bytes < bsa::prefill_workspace_bytes(L.B, L.Hkv, 128, L.n_tiles, L.E4, L.ksel,
                                               sel_out == nullptr))
     return BSA_WORKSPACE_TOO_SMALL;
-  L.k4f = k_cmp_sparse_f32;
   L.lse3 = lse3;
   L.sink = sink_logits;
   L.workspace = workspace;

@@ -76,7 +76,7 @@ struct PrefillLaunch {
   const uint16_t* q;      // [B][C][Hq][128]
   const uint16_t* k;      // [B][Hkv][stride][128]
   const uint16_t* v;
-  const float* k4f;       // [B][Hkv][E4][128] fp32 (scoring copy)
+  const float* k4f;       // [B][Hkv][E4][128] fp32 (scoring copy, BSA_INDEXER_F32)
   const uint16_t* k4b;    // [B][Hkv][E4][128] bf16
   const uint16_t* v4b;
   const uint16_t* k128b;  // [B][Hkv][E128][128] bf16
@@ -87,6 +87,7 @@ struct PrefillLaunch {
   void* workspace;        // pooled queries + scores (R2 only)
   int B, C, Hq, Hkv, P, stride, E4, E128, ksel, window, q_tile, n_tiles;
   int combine;            // 0 average, 1 concatenated softmax
+  int indexer_f32;        // 1: R2 scores against k4f, 0: against k4b
   float scale;
 };
 constexpr int PREFILL_MAX_E4 = 131072;  // entries of the selected stream per (b, kv head)

@@ -4,7 +4,8 @@
 // A chunk of C new queries at positions P + i attends, per (tile of q_tile
 // consecutive queries, kv head):
 //   A  the top_k entries of the m_sparse mean-pooled stream, chosen with the
-//      tile's pooled query against the fp32 copy of the pooled keys;
+//      tile's pooled query against the bf16 pooled keys themselves (or, as an
+//      option, against an fp32 copy of them);
 //   B  every entry of the m_dense mean-pooled stream;
 //   C  the raw tokens [p - window + 1, p] of the cache (causal window).
 // The branches are averaged (each with its own softmax) or joined in one
@@ -13,8 +14,10 @@
 //
 // Kernels:
 //   prefill_qbar_kernel    pooled tile queries (fp32)
-//   prefill_scores_kernel  scores = qbar . pooled keys as an fp32 MFMA product
-//                          ([tiles x d] . [d x entries] per kv head)
+//   prefill_scores_bf16_kernel  scores = qbar . bf16 pooled keys ([tiles x d] .
+//                          [d x entries] per kv head) on bf16 MFMA, qbar split
+//                          exactly into three bf16 terms
+//   prefill_scores_kernel  the same against the fp32 keys, fp32 MFMA
 //   prefill_topk_kernel    exact top-k per (tile, kv head): the k-th largest
 //                          key bracketed from a sample (else fixed by MSB-first
 //                          bit passes), its open bits as radix digits over the
@@ -175,6 +178,105 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(const float* __rest
     load(1, gi + 1);
     group(0, gi);
     if (gi + 2 < PSC_GROUPS) load(0, gi + 2);
+    group(1, gi + 1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The same scores against the bf16 pooled keys (the compressed cache branch A
+// attends).  The pooled query of a tile (fp32) is split into three bf16 terms
+// hi + mid + lo, each the next 8 significant bits, which sum to it exactly;
+// v_mfma_f32_16x16x32_bf16 then forms every product key_c * term_c exactly and
+// only the fp32 accumulation rounds, as in the fp32 kernel.  A = key rows
+// (lane l: entry l%16, dims 32f + 8(l/16) .. +8, one 16-byte load per step),
+// B = the terms of 16 tiles (lane l: tile l%16, the same dims), read from LDS
+// rows padded by 16 bytes so the 16 tiles of one read fall on distinct banks.
+// The output layout and the 16-entry groups per wave are the fp32 kernel's.
+constexpr int PSB_GROUPS = 8;  // 16-entry groups per wave
+
+template <int D, int NTB>
+__global__ __launch_bounds__(256) void prefill_scores_bf16_kernel(
+    const uint16_t* __restrict__ kb, const float* __restrict__ qbar, int n_tiles, int Hkv, int E,
+    int Es, float* __restrict__ scores) {
+  constexpr int F = D / 32;      // 32-dim steps of one MFMA
+  constexpr int RU = D / 8 + 1;  // 16-byte units per LDS row (+1 of padding)
+  __shared__ __align__(16) uint4 qt[3][NTB * 16][RU];
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, j4 = lane >> 4;
+  // the three terms of 8 consecutive dims of one tile per thread and step
+  for (int c = tid; c < NTB * 16 * (D / 8); c += 256) {
+    const int tl = c / (D / 8), p = c % (D / 8);
+    float x[8];
+    if (tl < n_tiles) {
+      const float4* src =
+          reinterpret_cast<const float4*>(qbar + (((int64_t)b * n_tiles + tl) * Hkv + kvh) * D + 8 * p);
+      const float4 x0 = src[0], x1 = src[1];
+      x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+      x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    uint32_t t[3][8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // x - hi and r1 - mid are exact in fp32 (at most 16 and 8 significant bits)
+      t[0][e] = bf16_rne(x[e]);
+      const float r1 = x[e] - bf_lo(t[0][e]);
+      t[1][e] = bf16_rne(r1);
+      t[2][e] = bf16_rne(r1 - bf_lo(t[1][e]));
+    }
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+      qt[s][tl][p] = make_uint4(t[s][0] | (t[s][1] << 16), t[s][2] | (t[s][3] << 16),
+                                t[s][4] | (t[s][5] << 16), t[s][6] | (t[s][7] << 16));
+  }
+  __syncthreads();
+  const uint16_t* kbase = kb + ((int64_t)b * Hkv + kvh) * E * D;
+  float* sbase = scores + ((int64_t)b * Hkv + kvh) * n_tiles * Es;
+  const int e_first = (blockIdx.x * 4 + wave) * (16 * PSB_GROUPS);
+  uint4 ka[2][F];
+  auto load = [&](int set, int gi) {
+    const uint4* krow =
+        reinterpret_cast<const uint4*>(kbase + (int64_t)min(e_first + 16 * gi + l16, E - 1) * D);
+#pragma unroll
+    for (int f = 0; f < F; ++f) ka[set][f] = ld_stream(krow + 4 * f + j4);
+  };
+  auto group = [&](int set, int gi) {
+    const int e = e_first + 16 * gi + 4 * j4;  // lane's first entry of the output tile
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int f = 0; f < F; ++f)
+#pragma unroll
+        for (int s = 2; s >= 0; --s)  // smallest term first
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, ka[set][f]),
+              __builtin_bit_cast(bf16x8_t, qt[s][16 * tb + l16][4 * f + j4]), acc, 0, 0, 0);
+      // lane l holds entries e + i of tile 16tb + l%16
+      const int tile = 16 * tb + l16;
+      if (tile < n_tiles) {
+        float* dst = sbase + (int64_t)tile * Es;
+        if (e + 3 < E) {
+          *reinterpret_cast<float4*>(dst + e) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (e + i < E) dst[e + i] = acc[i];
+        }
+      }
+    }
+  };
+  // groups past E are loaded clamped (and their stores skipped)
+  load(0, 0);
+#pragma unroll
+  for (int gi = 0; gi < PSB_GROUPS; gi += 2) {
+    load(1, gi + 1);
+    group(0, gi);
+    if (gi + 2 < PSB_GROUPS) load(0, gi + 2);
     group(1, gi + 1);
   }
 }
@@ -1199,9 +1301,11 @@ int prefill_topk_kpt(int E4, int* threads) {
   return kpt;
 }
 
-// R2: pooled tile queries, scores against the fp32 stream, top-k -> sel
+// R2: pooled tile queries, scores against the bf16 keys (or the fp32 stream),
+// top-k -> sel
 bool launch_prefill_select(const PrefillLaunch& L, int32_t* sel, hipStream_t st) {
   const int D = 128;
+  if (L.n_tiles > PSC_MAX_TILES) return false;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   char* ws = static_cast<char*>(L.workspace);
   float* qbar = reinterpret_cast<float*>(ws);
@@ -1210,14 +1314,25 @@ bool launch_prefill_select(const PrefillLaunch& L, int32_t* sel, hipStream_t st)
   const int Es = (L.E4 + 3) & ~3;
   const unsigned probs = (unsigned)(L.B * L.n_tiles * L.Hkv);
   prefill_qbar_kernel<<<probs, 256, 0, st>>>(L.q, L.C, L.Hq, L.Hkv, L.q_tile, L.n_tiles, qbar);
-  dim3 sg((L.E4 + 64 * PSC_GROUPS - 1) / (64 * PSC_GROUPS), L.Hkv, L.B);
-  if (L.n_tiles > PSC_MAX_TILES) return false;
-  switch ((L.n_tiles + 15) / 16) {
-    case 1: prefill_scores_kernel<128, 1><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
-    case 2: prefill_scores_kernel<128, 2><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
-    case 3: prefill_scores_kernel<128, 3><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
-    case 4: prefill_scores_kernel<128, 4><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
-    default: return false;
+  const int ntb = (L.n_tiles + 15) / 16;
+  if (L.indexer_f32) {
+    dim3 sg((L.E4 + 64 * PSC_GROUPS - 1) / (64 * PSC_GROUPS), L.Hkv, L.B);
+    switch (ntb) {
+      case 1: prefill_scores_kernel<128, 1><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
+      case 2: prefill_scores_kernel<128, 2><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
+      case 3: prefill_scores_kernel<128, 3><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
+      case 4: prefill_scores_kernel<128, 4><<<sg, 256, 0, st>>>(L.k4f, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
+      default: return false;
+    }
+  } else {
+    dim3 sg((L.E4 + 64 * PSB_GROUPS - 1) / (64 * PSB_GROUPS), L.Hkv, L.B);
+    switch (ntb) {
+      case 1: prefill_scores_bf16_kernel<128, 1><<<sg, 256, 0, st>>>(L.k4b, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
+      case 2: prefill_scores_bf16_kernel<128, 2><<<sg, 256, 0, st>>>(L.k4b, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
+      case 3: prefill_scores_bf16_kernel<128, 3><<<sg, 256, 0, st>>>(L.k4b, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
+      case 4: prefill_scores_bf16_kernel<128, 4><<<sg, 256, 0, st>>>(L.k4b, qbar, L.n_tiles, L.Hkv, L.E4, Es, scores); break;
+      default: return false;
+    }
   }
   int nthr;
   const int kpt = prefill_topk_kpt(L.E4, &nthr);

@@ -592,11 +592,13 @@ int oracle_sparse_prefill_attn(const uint16_t* q, int32_t C, const uint16_t* k,
                                int32_t top_k, int32_t m_dense, int32_t window,
                                int32_t q_tile, double scale, const int32_t* sel_in,
                                const int32_t* rows, int32_t n_rows, int32_t combine,
-                               const double* sink_logits, double* out, double* branch_out,
-                               double* lse3, int32_t* sel_out, double* sel_scores) {
+                               int32_t indexer, const double* sink_logits, double* out,
+                               double* branch_out, double* lse3, int32_t* sel_out,
+                               double* sel_scores) {
   if (!q || !k || !v || !out || C <= 0 || B <= 0 || P < 0 || Hq <= 0 || Hkv <= 0 ||
       Hq % Hkv || d <= 0 || stride < P + C || m_sparse <= 0 || top_k < 0 || m_dense <= 0 ||
-      window <= 0 || q_tile <= 0 || d > 512 || (combine != 0 && combine != 1))
+      window <= 0 || q_tile <= 0 || d > 512 || (combine != 0 && combine != 1) ||
+      (indexer != 0 && indexer != 1))
     return -1;
   if (!rows) n_rows = C;
   if (n_rows < 0) return -1;
@@ -613,8 +615,8 @@ int oracle_sparse_prefill_attn(const uint16_t* q, int32_t C, const uint16_t* k,
     for (int64_t i = 0; i < (int64_t)B * n_tiles * Hkv * kk; ++i)
       if (sel_in[i] < 0 || sel_in[i] >= E4) return -1;
 
-  /* compressed streams over the prior tokens: exact means for scoring,
-   * bf16-rounded means for attention (the stored compressed cache is bf16) */
+  /* compressed streams over the prior tokens: bf16-rounded means for
+   * attention (the stored compressed cache is bf16); the scoring keys below */
   double* ks_exact = (double*)malloc(sizeof(double) * (size_t)(npair * E4 * d + 1));
   double* tmp4 = (double*)malloc(sizeof(double) * (size_t)(npair * E4 * d + 1));
   double* tmp128 = (double*)malloc(sizeof(double) * (size_t)(npair * E128 * d + 1));
@@ -632,6 +634,20 @@ int oracle_sparse_prefill_attn(const uint16_t* q, int32_t C, const uint16_t* k,
   for (int64_t i = 0; i < npair * E128 * d; ++i) v128[i] = (float)bf(oracle_round_bf16(tmp128[i]));
   free(tmp4);
   free(tmp128);
+  /* the keys the selection scores against ([CSA] 4.2: the indexer scores the
+   * compressed entries, at low precision, its recall measured against a BF16
+   * indexer).  indexer 0: the bf16 compressed keys as the stream holds them,
+   * the bf16 rounding (ties to even) of the fp32 mean in token order;
+   * indexer 1: the exact means */
+  double* ks_b16 = NULL;
+  if (indexer == 0) {
+    float* f32 = (float*)malloc(sizeof(float) * (size_t)(npair * E4 * d + 1));
+    ks_b16 = (double*)malloc(sizeof(double) * (size_t)(npair * E4 * d + 1));
+    oracle_block_summaries_f32(k, B, Hkv, P, stride, d, m_sparse, f32);
+    for (int64_t i = 0; i < npair * E4 * d; ++i) ks_b16[i] = bf(oracle_round_bf16((double)f32[i]));
+    free(f32);
+  }
+  const double* keys = indexer == 0 ? ks_b16 : ks_exact;
 
   /* which tiles need a selection: all of them when the selection or its
    * scores are requested, else those holding a requested row (unless the
@@ -658,7 +674,7 @@ int oracle_sparse_prefill_attn(const uint16_t* q, int32_t C, const uint16_t* k,
       for (int32_t h = (int32_t)kvh * g; h < (int32_t)kvh * g + g; ++h)
         for (int32_t c = 0; c < d; ++c)
           qbar[c] += bf(q[(((int64_t)b * C + i) * Hq + h) * d + c]);
-    const double* ks = ks_exact + (b * Hkv + kvh) * (int64_t)E4 * d;
+    const double* ks = keys + (b * Hkv + kvh) * (int64_t)E4 * d;
     for (int32_t j = 0; j < E4; ++j) {
       double s = 0.0;
       for (int32_t c = 0; c < d; ++c) s += qbar[c] * ks[(int64_t)j * d + c];
@@ -777,6 +793,7 @@ int oracle_sparse_prefill_attn(const uint16_t* q, int32_t C, const uint16_t* k,
   free(need);
   free(sel);
   free(ks_exact);
+  free(ks_b16);
   free(k4);
   free(v4);
   free(k128);

@@ -98,15 +98,19 @@ int oracle_sparse_decode_attn(const uint16_t* q, const uint16_t* k, const uint16
  * over the concatenated logits of all three branches.  sink_logits [Hq] or
  * NULL: one extra logit per head (natural-log units) with a zero value vector,
  * in each branch's softmax (combine 0) or in the concatenated one (combine 1).
- * branch_out and lse3 always describe the branches without the sink. */
+ * branch_out and lse3 always describe the branches without the sink.
+ * indexer 0: the selection scores the pooled query against the bf16 compressed
+ * keys (bf16 rounding of the fp32 token-order mean, as the stored stream holds
+ * them); 1: against the exact means. */
 int oracle_sparse_prefill_attn(const uint16_t* q, int32_t C, const uint16_t* k,
                                const uint16_t* v, int32_t B, int32_t P, int32_t Hq,
                                int32_t Hkv, int32_t d, int32_t stride, int32_t m_sparse,
                                int32_t top_k, int32_t m_dense, int32_t window,
                                int32_t q_tile, double scale, const int32_t* sel_in,
                                const int32_t* rows, int32_t n_rows, int32_t combine,
-                               const double* sink_logits, double* out, double* branch_out,
-                               double* lse3, int32_t* sel_out, double* sel_scores);
+                               int32_t indexer, const double* sink_logits, double* out,
+                               double* branch_out, double* lse3, int32_t* sel_out,
+                               double* sel_scores);
 
 /* FP8 KV cache: OCP E4M3 codes with one fp32 scale per (pair, block).
  * oracle_e4m3_value: the value of a code (NaN for 0x7F / 0xFF);

@@ -163,15 +163,27 @@ def test_prefill_argument_checks_launch_nothing(L):
     pc = bsa.prefill_cfg()
     sh = bsa.make_shape(1, 32, 8, 128, 4096, 4096 + 128)
     # NULL q; chunk overruns the cache capacity; bad tile shape; workspace too small
-    assert L.select_prefill_entries(None, 128, fake, ctypes.byref(sh), ctypes.byref(pc), fake,
+    assert L.select_prefill_entries(None, 128, fake, fake, ctypes.byref(sh), ctypes.byref(pc), fake,
                                     fake, 1 << 30, None) == -1
-    assert L.select_prefill_entries(fake, 256, fake, ctypes.byref(sh), ctypes.byref(pc), fake,
+    assert L.select_prefill_entries(fake, 256, fake, fake, ctypes.byref(sh), ctypes.byref(pc), fake,
                                     fake, 1 << 30, None) == -1
     odd = bsa.prefill_cfg(q_tile=48)
-    assert L.select_prefill_entries(fake, 128, fake, ctypes.byref(sh), ctypes.byref(odd), fake,
+    assert L.select_prefill_entries(fake, 128, fake, fake, ctypes.byref(sh), ctypes.byref(odd), fake,
                                     fake, 1 << 30, None) == -2
-    assert L.select_prefill_entries(fake, 128, fake, ctypes.byref(sh), ctypes.byref(pc), fake,
-                                    fake, 64, None) == -3
+    assert L.select_prefill_entries(fake, 128, fake, fake, ctypes.byref(sh), ctypes.byref(pc),
+                                    fake, fake, 64, None) == -3
+    # the indexer's keys: the stream cfg.indexer names must be given, the other may be NULL;
+    # an unknown indexer is invalid
+    f32 = bsa.prefill_cfg(indexer=bsa.INDEXER_F32)
+    # (sparse_prefill_attn always reads the bf16 keys: branch A attends them)
+    for cfg, f, b, w_sel, w_all in ((pc, None, fake, -3, -3), (pc, fake, None, -1, -1),
+                                    (f32, fake, None, -3, -1), (f32, None, fake, -1, -1),
+                                    (bsa.prefill_cfg(indexer=2), fake, fake, -1, -1)):
+        assert L.select_prefill_entries(fake, 128, f, b, ctypes.byref(sh), ctypes.byref(cfg),
+                                        fake, fake, 64, None) == w_sel
+        assert L.sparse_prefill_attn(fake, 128, fake, fake, f, b, fake, fake, fake,
+                                     ctypes.byref(sh), ctypes.byref(cfg), 0.0, None, fake, None,
+                                     None, fake, 64, None) == w_all
     # attention over a given selection: NULL selection, misaligned stream
     args = [fake, 128, fake, fake, fake, fake, fake, fake]
     assert L.sparse_prefill_attn_selected(*args, None, ctypes.byref(sh), ctypes.byref(pc), 0.0,
@@ -267,7 +279,7 @@ def test_prefill_rejects_rows_beyond_32bit_offsets(L):
     def call(P, C, **kw):
         sh = bsa.make_shape(1, 32, 8, 128, P, P + C)
         pc = bsa.prefill_cfg(**kw)
-        return S(fake, C, fake, ctypes.byref(sh), ctypes.byref(pc), fake, fake, 64, None)
+        return S(fake, C, fake, fake, ctypes.byref(sh), ctypes.byref(pc), fake, fake, 64, None)
 
     # dense stream: 2^24 entries pass the checks (then the workspace is too small), one more
     # is unsupported

@@ -48,16 +48,16 @@ def check_tile_selection(g_sel, o_sel, o_scores, rel=TIE_REL):
     return exempt
 
 
-def run_prefill_case(cfg, seed, rows=None, combine=0, sink=None):
+def run_prefill_case(cfg, seed, rows=None, combine=0, sink=None, indexer=bsa.INDEXER_BF16):
     import torch
     announce(cfg.name, "seed", seed, "B", cfg.batch, "Hq", cfg.n_q_heads, "Hkv", cfg.n_kv_heads,
              "P", cfg.prior_len, "C", cfg.chunk_len, "m", cfg.m_sparse, cfg.m_dense, "top_k",
              cfg.top_k_sparse, "window", cfg.window, "q_tile", cfg.q_tile, "combine", combine,
-             "sink", None if sink is None else list(np.round(sink, 3)))
+             "sink", None if sink is None else list(np.round(sink, 3)), "indexer", indexer)
     t = synth.gen_prefill(cfg, seed)
     q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
     pc = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile,
-                         combine)
+                         combine, indexer=indexer)
     sink_dev = None if sink is None else torch.from_numpy(
         np.asarray(sink, np.float32)).to(q.device)
     out, lse3, sel = bsa.prefill_step(q, k, v, cfg.prior_len, pc, want_lse3=True, want_sel=True,
@@ -67,7 +67,8 @@ def run_prefill_case(cfg, seed, rows=None, combine=0, sink=None):
     common = dict(m_sparse=cfg.m_sparse, top_k=cfg.top_k_sparse, m_dense=cfg.m_dense,
                   window=cfg.window, q_tile=cfg.q_tile)
     ref_sel = oracle.sparse_prefill_attn(t["q"], t["k"], t["v"], cfg.prior_len, rows=[0],
-                                         want_sel=True, want_sel_scores=True, **common)
+                                         want_sel=True, want_sel_scores=True, indexer=indexer,
+                                         **common)
     exempt = check_tile_selection(g_sel, ref_sel["sel"], ref_sel["sel_scores"])
     ref = oracle.sparse_prefill_attn(t["q"], t["k"], t["v"], cfg.prior_len, sel_in=g_sel,
                                      rows=rows, combine=combine,
@@ -102,7 +103,8 @@ def test_compressed_streams_bit_exact():
     t = synth.gen_prefill(cfg, 71)
     k, v = to_dev(t["k"]), to_dev(t["v"])
     pc = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile)
-    k4f, k4b, v4b, k128b, v128b = bsa.build_compressed_streams(k, v, cfg.prior_len, pc)
+    k4f, k4b, v4b, k128b, v128b = bsa.build_compressed_streams(k, v, cfg.prior_len, pc,
+                                                                want_f32=True)
     torch.cuda.synchronize()
     bits = lambda a: a.view(torch.int16).cpu().numpy().view(np.uint16)
     rne = np.vectorize(oracle.round_bf16, otypes=[np.uint16])
@@ -116,8 +118,21 @@ def test_compressed_streams_bit_exact():
         assert np.array_equal(bits(got), rne(o.astype(np.float64))), m
 
 
-def test_prefill_small_ragged_g4():
-    run_prefill_case(small(), 61)
+@pytest.mark.parametrize("indexer", [bsa.INDEXER_BF16, bsa.INDEXER_F32])
+def test_prefill_small_ragged_g4(indexer):
+    run_prefill_case(small(), 61, indexer=indexer)
+
+
+@pytest.mark.parametrize("chunk_len", [645, 1000])
+@pytest.mark.parametrize("indexer", [bsa.INDEXER_BF16, bsa.INDEXER_F32])
+def test_prefill_many_tiles(chunk_len, indexer):
+    """Tiles of 16 queries (x 4 heads): 41 and 63 tiles, so the scores kernels hold three
+    and four blocks of 16 tiles' pooled queries (the last one partial), over a ragged
+    3,001-entry stream; 40 sampled rows."""
+    cfg = small(name=f"pf_tiles{chunk_len}", prior_len=4 * 3001 - 2, chunk_len=chunk_len,
+                q_tile=16, top_k_sparse=300, window=40)
+    rows = np.sort(np.random.default_rng(chunk_len).choice(chunk_len, 40, replace=False))
+    run_prefill_case(cfg, 63 + indexer, rows=rows, indexer=indexer)
 
 
 @pytest.mark.parametrize("g", [1, 2])
@@ -172,10 +187,11 @@ def test_prefill_full_size_two_whole_tiles():
     run_prefill_case(cfg, synth.DEFAULT_SEED["prefill256k"], rows=rows)
 
 
-def test_prefill_full_size_second_seed():
+@pytest.mark.parametrize("indexer", [bsa.INDEXER_BF16, bsa.INDEXER_F32])
+def test_prefill_full_size_second_seed(indexer):
     cfg = synth.CONFIGS["prefill256k"]
     rows = np.array([0, 5, 63, 64, 130, 999, 1024, 1535, 1536, 2047])
-    run_prefill_case(cfg, 105, rows=rows)
+    run_prefill_case(cfg, 105, rows=rows, indexer=indexer)
 
 
 def test_prefill_values_near_the_fp16_limit():
@@ -208,20 +224,22 @@ def test_prefill_values_near_the_fp16_limit():
     assert np.abs(lse3.cpu().numpy() - ref["lse3"]).max() <= 1e-3
 
 
-def test_prefill_split_entry_points_compose():
+@pytest.mark.parametrize("indexer", [bsa.INDEXER_BF16, bsa.INDEXER_F32])
+def test_prefill_split_entry_points_compose(indexer):
     """select_prefill_entries + sparse_prefill_attn_selected equal sparse_prefill_attn bit for
     bit; the attention step alone matches the oracle on the oracle's own selection; selection
     indices out of range are clamped (memory-safe) like an explicitly clamped list."""
     import torch
     cfg = small(name="pf_split", batch=2, chunk_len=130)
     seed = 81
-    announce(cfg.name, "seed", seed, "split entry points")
+    announce(cfg.name, "seed", seed, "split entry points", "indexer", indexer)
     t = synth.gen_prefill(cfg, seed)
     q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
-    pc = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile)
+    pc = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile,
+                         indexer=indexer)
     st = bsa.build_compressed_streams(k, v, cfg.prior_len, pc)
     out, _, sel = bsa.sparse_prefill_attn(q, k, v, *st, cfg.prior_len, cfg=pc, want_sel=True)
-    sel2 = bsa.select_prefill_entries(q, k, st[0], cfg.prior_len, cfg=pc)
+    sel2 = bsa.select_prefill_entries(q, k, st[0], st[1], cfg.prior_len, cfg=pc)
     out2, _ = bsa.sparse_prefill_attn_selected(q, k, v, *st[1:], sel2, cfg.prior_len, cfg=pc)
     torch.cuda.synchronize()
     assert torch.equal(sel, sel2)
@@ -229,7 +247,7 @@ def test_prefill_split_entry_points_compose():
     common = dict(m_sparse=cfg.m_sparse, top_k=cfg.top_k_sparse, m_dense=cfg.m_dense,
                   window=cfg.window, q_tile=cfg.q_tile)
     o_sel = oracle.sparse_prefill_attn(t["q"], t["k"], t["v"], cfg.prior_len, rows=[0],
-                                       want_sel=True, **common)["sel"]
+                                       want_sel=True, indexer=indexer, **common)["sel"]
     ref = oracle.sparse_prefill_attn(t["q"], t["k"], t["v"], cfg.prior_len, sel_in=o_sel,
                                      **common)
     out3, lse3 = bsa.sparse_prefill_attn_selected(q, k, v, *st[1:],
@@ -251,8 +269,9 @@ def test_prefill_split_entry_points_compose():
     assert torch.equal(o_w, o_t)
 
 
+@pytest.mark.parametrize("indexer", [bsa.INDEXER_BF16, bsa.INDEXER_F32])
 @pytest.mark.parametrize("prior_len", [64 * 40 + 16, 160_000, 270_000])
-def test_prefill_selection_exact_ties(prior_len):
+def test_prefill_selection_exact_ties(prior_len, indexer):
     """Integer keys constant over every 4-token group and integer queries: the pooled m = 4
     keys are exact, the fp32 scores exact integers with many equal values, so the tile
     selection must equal the oracle's exactly (lower entry index first at the k-th score).
@@ -261,20 +280,21 @@ def test_prefill_selection_exact_ties(prior_len):
     take the path without ties."""
     import torch
     B, Hq, Hkv, d, C, top_k = 1, 4, 1, 128, 64, 96
-    announce("pf_ties", "P", prior_len, "top_k", top_k)
+    announce("pf_ties", "P", prior_len, "top_k", top_k, "indexer", indexer)
     rng = np.random.default_rng(prior_len)
     n_tok = prior_len + C
     groups = rng.integers(-2, 3, (B, Hkv, -(-n_tok // 4), d)).astype(np.float32)
     k = synth.bf16_round(np.repeat(groups, 4, axis=2)[:, :, :n_tok])
     v = synth.bf16_round(rng.standard_normal((B, Hkv, n_tok, d)).astype(np.float32))
     q = synth.bf16_round(rng.integers(-1, 2, (B, C, Hq, d)).astype(np.float32))
-    pc = bsa.prefill_cfg(4, top_k, 128, 128, 64)
+    pc = bsa.prefill_cfg(4, top_k, 128, 128, 64, indexer=indexer)
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     st = bsa.build_compressed_streams(kd, vd, prior_len, pc)
-    sel = bsa.select_prefill_entries(qd, kd, st[0], prior_len, cfg=pc)
+    sel = bsa.select_prefill_entries(qd, kd, st[0], st[1], prior_len, cfg=pc)
     torch.cuda.synchronize()
     o_sel = oracle.sparse_prefill_attn(q, k, v, prior_len, m_sparse=4, top_k=top_k, m_dense=128,
-                                       window=128, q_tile=64, rows=[0], want_sel=True)["sel"]
+                                       window=128, q_tile=64, rows=[0], want_sel=True,
+                                       indexer=indexer)["sel"]
     g_sel = sel.cpu().numpy()
     assert g_sel.shape == o_sel.shape
     assert np.array_equal(g_sel, o_sel)
@@ -363,7 +383,7 @@ def _distinct_over_ties(prior_len, top_k, n_high=0, high_at=None, seed=0, n_mid=
     pc = bsa.prefill_cfg(4, top_k, 128, 128, 64)
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     st = bsa.build_compressed_streams(kd, vd, prior_len, pc)
-    sel = bsa.select_prefill_entries(qd, kd, st[0], prior_len, cfg=pc)
+    sel = bsa.select_prefill_entries(qd, kd, st[0], st[1], prior_len, cfg=pc)
     torch.cuda.synchronize()
     o_sel = oracle.sparse_prefill_attn(q, k, v, prior_len, m_sparse=4, top_k=top_k, m_dense=128,
                                        window=128, q_tile=64, rows=[0], want_sel=True)["sel"]
@@ -389,7 +409,7 @@ def _threshold_case(prior_len, top_k, keys, B=1, Hkv=1, Hq=4, C=64):
     pc = bsa.prefill_cfg(4, top_k, 128, 128, 64)
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     st = bsa.build_compressed_streams(kd, vd, prior_len, pc)
-    sel = bsa.select_prefill_entries(qd, kd, st[0], prior_len, cfg=pc)
+    sel = bsa.select_prefill_entries(qd, kd, st[0], st[1], prior_len, cfg=pc)
     torch.cuda.synchronize()
     ref = oracle.sparse_prefill_attn(q, k, v, prior_len, m_sparse=4, top_k=top_k, m_dense=128,
                                      window=128, q_tile=64, rows=[0], want_sel=True,

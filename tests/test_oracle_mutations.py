@@ -87,6 +87,12 @@ MUTANTS = [
      "v128[i] = (float)bf(oracle_round_bf16(tmp128[i]));", "v128[i] = (float)tmp128[i];"),
     ("pooled query skips a dimension", "for (int32_t c = 0; c < d; ++c) qbar[c] += bf(q[(b * Hq + h)",
      "for (int32_t c = 1; c < d; ++c) qbar[c] += bf(q[(b * Hq + h)"),
+    ("indexer scores the exact means", "const double* keys = indexer == 0 ? ks_b16 : ks_exact;",
+     "const double* keys = ks_exact;"),
+    ("indexer rounds the exact mean", "ks_b16[i] = bf(oracle_round_bf16((double)f32[i]));",
+     "ks_b16[i] = bf(oracle_round_bf16(ks_exact[i]));"),
+    ("indexer keys are the unrounded fp32 means", "ks_b16[i] = bf(oracle_round_bf16((double)f32[i]));",
+     "ks_b16[i] = (double)f32[i];"),
 ]
 
 

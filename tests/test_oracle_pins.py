@@ -587,6 +587,51 @@ def test_prefill_tile_selection(orc):
         assert np.all(tied > sel[sc[sel] == sc[sel].min()].max())
 
 
+def _indexer_case(tokens0, tokens1, d=8):
+    """Two m = 4 entries whose first dim holds the given tokens (others zero) and one
+    query along +e0: each entry's score is its key's first component."""
+    P, m = 8, 4
+    k = np.zeros((1, 1, P + 1, d), np.float32)
+    k[0, 0, :m, 0] = tokens0
+    k[0, 0, m:P, 0] = tokens1
+    q = np.zeros((1, 1, 1, d), np.float32)
+    q[0, 0, 0, 0] = 1.0
+    assert np.array_equal(f(bf(k)), k)  # every token is a bf16 value
+    return bf(q), bf(k), P, m
+
+
+def test_prefill_indexer_scores_bf16_keys(orc):
+    # "CSA + HCA 混合注意力机制" §4.2: the indexer scores the compressed entries at low
+    # precision, its recall measured against a BF16 indexer.  Entry 1's mean
+    # 1 + 2^-9 rounds to the bf16 value 1 (the half ulp is 2^-8): with bf16 keys the
+    # two entries tie and the lower index wins; with the exact means entry 1 wins.
+    q, k, P, m = _indexer_case([1.0] * 4, [1.0, 1.0, 1.0, 1.0 + 2.0 ** -7])
+    kw = dict(m_sparse=m, top_k=1, m_dense=m, window=1, want_sel=True, want_sel_scores=True)
+    r = orc.sparse_prefill_attn(q, k, k, P, indexer=0, **kw)
+    assert r["sel"][0, 0, 0].tolist() == [0]
+    assert r["sel_scores"][0, 0, 0].tolist() == [1.0, 1.0]
+    r = orc.sparse_prefill_attn(q, k, k, P, indexer=1, **kw)
+    assert r["sel"][0, 0, 0].tolist() == [1]
+    assert r["sel_scores"][0, 0, 0].tolist() == [1.0, 1.0 + 2.0 ** -9]
+
+
+def test_prefill_indexer_keys_round_the_fp32_token_order_mean(orc):
+    # the bf16 keys are the stream as stored: the fp32 running sum in token order,
+    # divided by the count, then rounded to bf16.  Entry 0's tokens 2^20, 1 + 2^-7,
+    # -2^20, 0 sum in fp32 to 1 (2^20 + 1 + 2^-7 rounds to 2^20 + 1: its ulp is 2^-3),
+    # so its key is 0.25, below entry 1's 0.25 + 2^-9; rounding the exact mean
+    # (0.25 + 2^-9) instead would tie the two and pick entry 0.
+    q, k, P, m = _indexer_case([2.0 ** 20, 1.0 + 2.0 ** -7, -(2.0 ** 20), 0.0],
+                               [0.25 + 2.0 ** -9] * 4)
+    kw = dict(m_sparse=m, top_k=1, m_dense=m, window=1, want_sel=True, want_sel_scores=True)
+    r = orc.sparse_prefill_attn(q, k, k, P, indexer=0, **kw)
+    assert r["sel_scores"][0, 0, 0].tolist() == [0.25, 0.25 + 2.0 ** -9]
+    assert r["sel"][0, 0, 0].tolist() == [1]
+    r = orc.sparse_prefill_attn(q, k, k, P, indexer=1, **kw)
+    assert r["sel_scores"][0, 0, 0].tolist() == [0.25 + 2.0 ** -9] * 2
+    assert r["sel"][0, 0, 0].tolist() == [0]
+
+
 def test_prefill_tile_scores_from_unit_entries(orc):
     # entry j's rows are all e_{c_j}: its score for a tile is the sum of q[., ., c_j]
     # over the tile's queries and the kv head's query heads (ragged last tile too)
