@@ -3,7 +3,8 @@
 20 seeded cases draw the batch, kv heads, group size (64-query tiles of 64, 128
 or 256 (query, head) rows), prior length (log-uniform from 64 to 300,000 tokens),
 chunk length, both pooling ratios, top-k, window, the combine mode and optional
-sink logits; each case checks the tile selections (near-tie rule) and the
+sink logits (every third case selects with the fp32-means indexer, the others
+with the bf16 compressed keys); each case checks the tile selections (near-tie rule) and the
 outputs and per-branch lse against the oracle evaluated on the GPU's selection,
 as the fixed-shape tests do (every row for chunks up to 128 queries, 40 sampled
 rows beyond).  Every case prints its parameters before any GPU call.
@@ -50,4 +51,5 @@ def draw_case(i):
 @pytest.mark.parametrize("i", range(20))
 def test_random_prefill_shapes(i):
     cfg, seed, combine, sink, rows = draw_case(i)
-    run_prefill_case(cfg, seed, rows=rows, combine=combine, sink=sink)
+    indexer = bsa.INDEXER_F32 if i % 3 == 2 else bsa.INDEXER_BF16
+    run_prefill_case(cfg, seed, rows=rows, combine=combine, sink=sink, indexer=indexer)
