@@ -157,6 +157,16 @@ def test_prefill_largest_selection(g):
                            chunk_len=90, top_k_sparse=4096), 74 + g)
 
 
+@pytest.mark.parametrize("indexer", [bsa.INDEXER_BF16, bsa.INDEXER_F32])
+def test_prefill_long_prior_wide_topk(indexer):
+    """A 400,000-token prior context: 100,000 m = 4 entries per kv head, so the selection
+    takes the 1024-thread top-k (up to 131,072 keys per row) and branch A gathers entries
+    past 2^16; 3 tiles, 24 sampled rows."""
+    cfg = small(name="pf_long_prior", prior_len=400_000, chunk_len=130, top_k_sparse=2048)
+    rows = np.sort(np.random.default_rng(400).choice(130, 24, replace=False))
+    run_prefill_case(cfg, 401, rows=rows, indexer=indexer)
+
+
 @pytest.mark.parametrize("combine,with_sink", [(1, False), (0, True), (1, True)])
 def test_prefill_combine_and_sink(combine, with_sink):
     # concatenated softmax over the branches ("CSA + HCA 混合注意力机制" §4.3) and per-head
