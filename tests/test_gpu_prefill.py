@@ -157,12 +157,15 @@ def test_prefill_largest_selection(g):
                            chunk_len=90, top_k_sparse=4096), 74 + g)
 
 
-@pytest.mark.parametrize("indexer", [bsa.INDEXER_BF16, bsa.INDEXER_F32])
-def test_prefill_long_prior_wide_topk(indexer):
-    """A 400,000-token prior context: 100,000 m = 4 entries per kv head, so the selection
-    takes the 1024-thread top-k (up to 131,072 keys per row) and branch A gathers entries
-    past 2^16; 3 tiles, 24 sampled rows."""
-    cfg = small(name="pf_long_prior", prior_len=400_000, chunk_len=130, top_k_sparse=2048)
+@pytest.mark.parametrize("prior_len,indexer", [(400_000, bsa.INDEXER_BF16),
+                                               (400_000, bsa.INDEXER_F32),
+                                               (524_288, bsa.INDEXER_BF16)])
+def test_prefill_long_prior_wide_topk(prior_len, indexer):
+    """Prior contexts of 400,000 and 524,288 tokens: 100,000 and 131,072 (the most the
+    selection supports) m = 4 entries per kv head, so the selection takes the 1024-thread
+    top-k and branch A gathers entries past 2^16; 3 tiles, 24 sampled rows."""
+    cfg = small(name=f"pf_long_prior{prior_len}", prior_len=prior_len, chunk_len=130,
+                top_k_sparse=2048)
     rows = np.sort(np.random.default_rng(400).choice(130, 24, replace=False))
     run_prefill_case(cfg, 401, rows=rows, indexer=indexer)
 
