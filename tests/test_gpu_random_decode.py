@@ -8,7 +8,8 @@ against the oracle as the fixed-shape tests do (fp32 summaries bit for bit, inde
 sets by the near-tie rule, outputs within 2e-3), then requires the fused step to
 give the same list and outputs bit for bit.  16 more draws run the FP8 cache:
 the GPU quantizer against the oracle's codes and scales bit for bit, then the FP8
-attention (a quarter of them over adaptive, -1-padded lists) within 2e-3.  Every
+attention (a quarter of them over adaptive, -1-padded lists) within 2e-3, and 16
+random anchor-adaptive selections are checked against the oracle's rule.  Every
 case prints its parameters before any GPU call.
 """
 import math
@@ -112,3 +113,21 @@ def test_random_fp8_decode_shapes(i):
     lerr = float(np.abs(lse.cpu().numpy() - o_lse).max())
     announce("  max|out err|", err, "max|lse err|", lerr)
     assert err <= OUT_ATOL and lerr <= 1e-3
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_adaptive_shapes(i):
+    """Seeded random anchor-adaptive selections (keep range, anchor margin, batch, heads,
+    head dim, 261 to 40,000 tokens) against the oracle's adaptive rule, and the attention
+    over the -1-padded lists (the checks of test_gpu_adaptive.run_adaptive)."""
+    from test_gpu_adaptive import run_adaptive
+    rng = np.random.default_rng(8000 + i)
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    rmin = float(rng.choice([0.05, 0.1, 0.15]))
+    rmax = rmin + float(rng.choice([0.05, 0.1, 0.2]))
+    margin = float(rng.choice([0.0, rng.uniform(-1.0, 1.0)]))
+    N = int(math.exp(rng.uniform(math.log(64 * 4 + 5), math.log(40000))))
+    run_adaptive(f"rand_adapt{i}", int(rng.integers(0, 10**6)), B=int(rng.integers(1, 4)),
+                 Hq=hkv * g, Hkv=hkv, d=int(rng.choice([64, 128])), N=N, rmin=rmin, rmax=rmax,
+                 margin=margin)
