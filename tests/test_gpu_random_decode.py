@@ -9,8 +9,9 @@ sets by the near-tie rule, outputs within 2e-3), then requires the fused step to
 give the same list and outputs bit for bit.  16 more draws run the FP8 cache:
 the GPU quantizer against the oracle's codes and scales bit for bit, then the FP8
 attention (a quarter of them over adaptive, -1-padded lists) within 2e-3, and 16
-random anchor-adaptive selections are checked against the oracle's rule.  Every
-case prints its parameters before any GPU call.
+random anchor-adaptive selections are checked against the oracle's rule and 8
+random decode loops step by step.  Every case prints its parameters before any
+GPU call.
 """
 import math
 
@@ -131,3 +132,24 @@ def test_random_adaptive_shapes(i):
     run_adaptive(f"rand_adapt{i}", int(rng.integers(0, 10**6)), B=int(rng.integers(1, 4)),
                  Hq=hkv * g, Hkv=hkv, d=int(rng.choice([64, 128])), N=N, rmin=rmin, rmax=rmax,
                  margin=margin)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_decode_loop_shapes(i):
+    """Seeded random decode loops (start length 1 to 6,000 tokens, 40-140 generated tokens,
+    spare capacity, top-k or keep ratio): summaries equal a rebuild bit for bit and
+    selection and outputs match the oracle afresh at every step (the checks of
+    test_gpu_decode_loop.run_loop)."""
+    from test_gpu_decode_loop import run_loop
+    rng = np.random.default_rng(8500 + i)
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    n0 = int(rng.integers(1, 6001))
+    steps = int(rng.integers(40, 141))
+    ratio = bool(rng.integers(0, 2))
+    run_loop(f"rand_loop{i}", int(rng.integers(0, 10**6)), B=int(rng.integers(1, 3)),
+             Hq=hkv * g, Hkv=hkv, d=int(rng.choice([64, 128])), n0=n0, steps=steps,
+             capacity=n0 + steps + int(rng.integers(0, 300)),
+             top_k=-1 if ratio else int(rng.integers(1, 40)),
+             keep_ratio=float(rng.choice([0.1, 0.2, 0.3])) if ratio else 0.0,
+             check_every=max(1, steps // 20))
