@@ -118,7 +118,8 @@ def test_pins_catch_mutant(tmp_path, name, old, new):
 PROPERTY_MUTANTS = ["mean divides by block size", "score sign", "tie-break reversed",
                     "group drops heads", "no 1/sqrt(d) scale", "K and V swapped",
                     "wrong GQA head map", "local range off by one", "lse drops the max",
-                    "weights not normalised"]
+                    "weights not normalised", "indexer scores the exact means",
+                    "indexer rounds the exact mean", "indexer keys are the unrounded fp32 means"]
 
 
 @pytest.mark.parametrize("name", PROPERTY_MUTANTS)

@@ -6,11 +6,13 @@ arithmetic: the scores against a numpy product of the pooled query and the
 summaries, the selection rule applied to those scores by brute force, torch's
 scaled_dot_product_attention in float64 over the gathered tokens, the log-sum-exp
 identity of disjoint token sets, the permutation invariance of a mean and the mean
-of a constant block.  The runs are derandomised, so the examples are the same on
-every run.  Of the oracle mutants that plant a selection or decode-attention mistake
-(wrong mean divisor, score sign, tie order, dropped heads, missing scale, K and V
-swapped, GQA head map, local range, lse without its maximum, unnormalised
-weights), each fails at least one of these properties on its own.
+of a constant block, and the prefill selection against bf16 keys rebuilt in numpy.
+The runs are derandomised, so the examples are the same on every run.  Of the oracle
+mutants that plant a selection or decode-attention mistake (wrong mean divisor, score
+sign, tie order, dropped heads, missing scale, K and V swapped, GQA head map, local
+range, lse without its maximum, unnormalised weights) or a prefill indexer-key
+mistake (exact means, the rounded exact mean, unrounded fp32 means), each fails at
+least one of these properties on its own.
 """
 import math
 
@@ -189,3 +191,67 @@ def test_summaries_of_constant_blocks(orc, N, d, seed):
     x = bf(np.repeat(const, BS, axis=0)[:N][None, None])
     np.testing.assert_array_equal(orc.block_summaries(x, N, BS)[0, 0], const)
     np.testing.assert_array_equal(orc.block_summaries_f32(x, N, BS)[0, 0], const.astype(np.float32))
+
+
+@st.composite
+def prefill_case(draw):
+    Hkv = draw(st.sampled_from([1, 2]))
+    g = draw(st.sampled_from([1, 2, 3]))
+    d = draw(st.sampled_from([8, 16]))
+    m = draw(st.sampled_from([1, 2, 3, 4, 8]))
+    P = draw(st.integers(1, 600))
+    C = draw(st.integers(1, 40))
+    q_tile = draw(st.sampled_from([8, 16, 64]))
+    E = -(-P // m)
+    top_k = draw(st.integers(1, E + 3))
+    seed = draw(st.integers(0, 2**31 - 1))
+    rng = np.random.default_rng(seed)
+    # keys of mixed magnitude (some near 2^12), so the fp32 running sums round; in about
+    # a third of the entries (m >= 3) dim 0 holds 2^20 at the first token and -2^20 at
+    # the third, so the fp32 sum drops the second token's low bits and its bf16 key can
+    # differ from the rounding of the exact mean
+    k = rng.standard_normal((1, Hkv, P + C, d)).astype(np.float32)
+    k *= np.where(rng.random(k.shape) < 0.05, np.float32(4096.0), np.float32(1.0))
+    if m >= 3:
+        for j in range(P // m):
+            if rng.random() < 0.35:
+                k[0, :, j * m, 0] = 2.0 ** 20
+                k[0, :, j * m + 2, 0] = -(2.0 ** 20)
+    q = rng.standard_normal((1, C, Hkv * g, d)).astype(np.float32)
+    return dict(Hkv=Hkv, g=g, d=d, m=m, P=P, C=C, q_tile=q_tile, top_k=top_k,
+                q=bf(q), k=bf(k))
+
+
+@SETTINGS
+@given(prefill_case())
+def test_prefill_selection_is_top_k_against_bf16_keys(orc, c):
+    """The prefill selection (indexer 0) is, per (tile, kv head), the top-k of the pooled
+    query (the exact sum of the tile's query rows of the group) against the bf16 keys:
+    each key the bf16 rounding (ties to even) of the fp32 mean of its m tokens summed in
+    token order, computed here in numpy; lower index first among equal scores.  Entries
+    whose fp32 sum cancels a large pair make the bf16 keys differ from the rounded exact
+    means."""
+    m, P, C, qt, Hkv, g = c["m"], c["P"], c["C"], c["q_tile"], c["Hkv"], c["g"]
+    E = -(-P // m)
+    r = orc.sparse_prefill_attn(c["q"], c["k"], c["k"], P, m_sparse=m, top_k=c["top_k"],
+                                m_dense=m, window=1, q_tile=qt, rows=[0], want_sel=True,
+                                want_sel_scores=True, indexer=0)
+    kx = synth.bf16_to_f32(c["k"])[0]  # [Hkv][P + C][d], float32
+    keys = np.empty((Hkv, E, c["d"]), np.float32)
+    for j in range(E):
+        t0, t1 = j * m, min((j + 1) * m, P)
+        s = np.zeros((Hkv, c["d"]), np.float32)
+        for t in range(t0, t1):
+            s = s + kx[:, t]  # float32 adds in token order
+        keys[:, j] = s / np.float32(t1 - t0)
+    keys = f(bf(keys)).reshape(Hkv, E, c["d"])  # bf16 RNE, as float64
+    q = f(c["q"])[0]  # [C][Hq][d]
+    kk = min(c["top_k"], E)
+    for tile in range(-(-C // qt)):
+        rows = q[tile * qt:min((tile + 1) * qt, C)]
+        for h in range(Hkv):
+            qbar = rows[:, h * g:(h + 1) * g].sum(axis=(0, 1))
+            sc = keys[h] @ qbar
+            np.testing.assert_allclose(r["sel_scores"][0, tile, h], sc, rtol=1e-12, atol=1e-12)
+            order = sorted(range(E), key=lambda j: (-sc[j], j))
+            assert r["sel"][0, tile, h].tolist() == sorted(order[:kk])
