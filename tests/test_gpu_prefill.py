@@ -118,6 +118,46 @@ def test_compressed_streams_bit_exact():
         assert np.array_equal(bits(got), rne(o.astype(np.float64))), m
 
 
+def test_streams_and_selection_with_cancelling_sums():
+    """Keys whose 4-token groups hold 2^20 and -2^20 around a small value in some dims: the
+    fp32 running sums lose that value's low bits, so the pooled keys differ from the
+    rounded exact means.  The GPU's streams equal the oracle's fp32 token-order means and
+    their bf16 roundings bit for bit, and the selection against those bf16 keys matches
+    the oracle's (near-tie rule)."""
+    import torch
+    cfg = small(name="pf_cancel", prior_len=64 * 60 + 9, chunk_len=70, top_k_sparse=200)
+    seed = 79
+    announce(cfg.name, "seed", seed, "P", cfg.prior_len, "cancelling pairs")
+    t = synth.gen_prefill(cfg, seed)
+    k = synth.bf16_to_f32(t["k"]).copy()
+    rng = np.random.default_rng(seed)
+    n_grp = cfg.prior_len // 4
+    grp = rng.choice(n_grp, n_grp // 3, replace=False)
+    dims = rng.choice(128, 16, replace=False)
+    for j in grp:
+        k[:, :, 4 * j, dims] = 2.0 ** 20
+        k[:, :, 4 * j + 2, dims] = -(2.0 ** 20)
+    t["k"] = synth.bf16_round(k)
+    q, kd, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    pc = bsa.prefill_cfg(cfg.m_sparse, cfg.top_k_sparse, cfg.m_dense, cfg.window, cfg.q_tile)
+    st = bsa.build_compressed_streams(kd, v, cfg.prior_len, pc, want_f32=True)
+    sel = bsa.select_prefill_entries(q, kd, None, st[1], cfg.prior_len, cfg=pc)
+    torch.cuda.synchronize()
+    o_k4 = oracle.block_summaries_f32(t["k"], cfg.prior_len, cfg.m_sparse)
+    exact = oracle.block_summaries(t["k"], cfg.prior_len, cfg.m_sparse)
+    assert not np.array_equal(o_k4.astype(np.float64), exact)  # the fp32 sums did round
+    assert np.array_equal(st[0].cpu().numpy(), o_k4)
+    rne = np.vectorize(oracle.round_bf16, otypes=[np.uint16])
+    assert np.array_equal(st[1].view(torch.int16).cpu().numpy().view(np.uint16),
+                          rne(o_k4.astype(np.float64)))
+    ref = oracle.sparse_prefill_attn(t["q"], t["k"], t["v"], cfg.prior_len, rows=[0],
+                                     m_sparse=cfg.m_sparse, top_k=cfg.top_k_sparse,
+                                     m_dense=cfg.m_dense, window=cfg.window,
+                                     q_tile=cfg.q_tile, want_sel=True, want_sel_scores=True)
+    announce("  exempt ties", check_tile_selection(sel.cpu().numpy(), ref["sel"],
+                                                   ref["sel_scores"]))
+
+
 @pytest.mark.parametrize("indexer", [bsa.INDEXER_BF16, bsa.INDEXER_F32])
 def test_prefill_small_ragged_g4(indexer):
     run_prefill_case(small(), 61, indexer=indexer)
