@@ -369,6 +369,56 @@ def run_fused_step(cfg, steps, warmup, t, flush_bytes=1 << 30):
             "timed": "sparse_decode_step (select fused into the attention launch), cold cache"}
 
 
+def run_bf16_summaries(cfg, steps, warmup, t, flush_bytes=1 << 30):
+    """The decode step on bf16 block summaries (half the bytes the scores read): select_blocks
+    alone, select + attend as two calls, and the fused sparse_decode_step, cold cache."""
+    import numpy as np
+    import torch
+
+    import long_context_block_summary_amd as bsa
+
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to(t["q"]), to(t["k"]), to(t["v"])
+    N, bs = cfg.seq_len, cfg.block_size
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    _, s16 = bsa.build_block_summaries(k, N, bs, want_f32=False, want_bf16=True)
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev)
+    sel = dict(n_sink=cfg.n_sink, n_local=cfg.n_local, top_k=cfg.top_k,
+               keep_ratio=cfg.keep_ratio)
+    idx, _ = bsa.select_blocks(q, s16, N, bs, **sel)
+    out, lse = bsa.sparse_decode_attn(q, k, v, idx, N, bs)
+    ws_sel = torch.empty(16 << 20, dtype=torch.uint8, device=dev)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    calls = {
+        "select_blocks": lambda: bsa.select_blocks(q, s16, N, bs, block_idx=idx,
+                                                   workspace=ws_sel, **sel),
+        "step": lambda: (bsa.select_blocks(q, s16, N, bs, block_idx=idx, workspace=ws_sel, **sel),
+                         bsa.sparse_decode_attn(q, k, v, idx, N, bs, out=out, lse=lse,
+                                                workspace=ws)),
+        "fused_step": lambda: bsa.sparse_decode_step(q, k, v, s16, N, bs, block_idx=idx, out=out,
+                                                     lse=lse, workspace=ws, **sel),
+    }
+    res = {"workload": cfg.name,
+           "summary_bytes": cfg.batch * cfg.n_kv_heads * (-(-N // bs)) * cfg.head_dim * 2}
+    for name, fn in calls.items():
+        ts = []
+        for i in range(warmup + steps):
+            flush.add_(1.0)
+            a, c = ev(), ev()
+            a.record(stream)
+            fn()
+            c.record(stream)
+            torch.cuda.synchronize()
+            if i >= warmup:
+                ts.append(a.elapsed_time(c) * 1e3)
+        res[name + "_us"] = sum(ts) / len(ts)
+    res["queries_heads_per_s"] = cfg.batch * cfg.n_q_heads / (res["step_us"] / 1e6)
+    res["timed"] = "bf16 summaries (bsa_select_cfg.summaries_bf16), cold cache"
+    return res
+
+
 def run_decode_loop(cfg, steps, warmup, t, flush_bytes=1 << 30):
     """Per generated token: append K/V, refresh the summary of its block, select, attend.
     The cache holds the workload's tokens; the loop starts `warmup + steps` tokens before
@@ -775,10 +825,14 @@ def main():
                        "s4_us": r2["s4_ms"] * 1e3,
                        "s4_frac": p2 / (r2["s4_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
                        "select_us": r2["sel_ms"] * 1e3, "attn_us": r2["att_ms"] * 1e3}
+        if name == "ctx1m":
+            extra[name]["bf16_summaries"] = run_bf16_summaries(c2, max(10, args.steps // 2), 3,
+                                                               r2["inputs"])
         if name in ("tiny", "gqa32k", "long128k"):
             keep_inputs[name] = (c2, r2["inputs"])
         del r2
     line["fused_step"] = run_fused_step(cfg, max(10, args.steps // 2), 3, r["inputs"])
+    line["bf16_summaries"] = run_bf16_summaries(cfg, max(10, args.steps // 2), 3, r["inputs"])
     line["decode_loop"] = run_decode_loop(cfg, max(10, args.steps // 2), 3, r["inputs"])
     line["adaptive_selection"] = run_adaptive(cfg, max(10, args.steps // 2), 3, r["inputs"])
     line["fp8_kv"] = run_fp8(cfg, max(10, args.steps // 2), 3, r["inputs"])

@@ -71,6 +71,9 @@ typedef struct {
   double keep_ratio_max;   /* adaptive: the largest kept fraction (rounded as keep_ratio) */
   double anchor_margin;    /* adaptive: tau = a_max + anchor_margin * (a_max - a_min); the
                               kernels form tau in fp32 from (float)anchor_margin */
+  int32_t summaries_bf16;  /* 0: the summaries select_blocks / sparse_decode_step read are
+                              fp32; 1: bf16 (build_block_summaries' out_bf16: the rounding,
+                              ties to even, of the fp32 means), half the bytes to score */
 } bsa_select_cfg;
 
 typedef struct {
@@ -169,7 +172,8 @@ int append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache
  * ascending.  hotdry.top post, 稀疏注意力与 KV Cache 压缩的工程实现;
  * "CSA + HCA 混合注意力机制" §4.4 steps 1-3.
  *   q          bf16 [B][Hq][d]
- *   summaries  fp32 [B][Hkv][S][d] from build_block_summaries (S = summary_stride, or
+ *   summaries  fp32 [B][Hkv][S][d] from build_block_summaries, or its bf16 output when
+ *              cfg->summaries_bf16 is 1 (S = summary_stride, or
  *              nb = ceil(seq_len / block_size) when that is 0)
  *   block_idx  int32 [B][Hkv][n_keep] output, n_keep = bsa_num_kept(nb, cfg)
  *   scores_out fp32 [B][Hkv][nb] or NULL: candidate scores (other entries are not written;
@@ -183,7 +187,7 @@ int append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache
  * the list holds sink + top-k + local ascending and is padded with -1 to
  * n_keep.  sparse_decode_attn accepts such padded lists.
  * Requires seq_len >= 1. */
-int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
+int select_blocks(const void* q, const void* summaries, const bsa_shape* shape,
                   const bsa_select_cfg* cfg, int32_t* block_idx, float* scores_out,
                   void* workspace, size_t ws_bytes, void* hip_stream);
 
@@ -195,12 +199,12 @@ int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
  * same steps as separate launches.  block_idx and out/lse are those of the two calls
  * (the same list, the same outputs bit for bit).
  *   q, k, v, out, lse, scale  as for sparse_decode_attn
- *   summaries   fp32 as for select_blocks
+ *   summaries   fp32 or bf16 (cfg->summaries_bf16) as for select_blocks
  *   cfg         as for select_blocks; adaptive selection is BSA_UNSUPPORTED here
  *   block_idx   int32 [B][Hkv][bsa_num_kept(nb, cfg)], written
  *   workspace   bsa_decode_step_workspace_size(shape, cfg) bytes, 16-byte aligned
  *               (block scores, then the split partials); contents on entry irrelevant */
-int sparse_decode_step(const void* q, const void* k, const void* v, const float* summaries,
+int sparse_decode_step(const void* q, const void* k, const void* v, const void* summaries,
                        const bsa_shape* shape, const bsa_select_cfg* cfg, int32_t* block_idx,
                        float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
                        void* hip_stream);
@@ -217,7 +221,7 @@ int sparse_decode_step(const void* q, const void* k, const void* v, const float*
  * race and must be serialised by the caller. */
 #define BSA_NOALLOC_SCRATCH_BYTES (16u << 20)
 int sparse_decode_step_noalloc(const void* q, const void* k, const void* v,
-                               const float* summaries, const bsa_shape* shape,
+                               const void* summaries, const bsa_shape* shape,
                                const bsa_select_cfg* cfg, int32_t* block_idx, float scale,
                                float* out, float* lse, void* hip_stream);
 

@@ -35,7 +35,8 @@ class bsa_select_cfg(ctypes.Structure):
     _fields_ = [("block_size", ctypes.c_int32), ("n_sink_blocks", ctypes.c_int32),
                 ("n_local_blocks", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("keep_ratio", ctypes.c_double), ("adaptive", ctypes.c_int32),
-                ("keep_ratio_max", ctypes.c_double), ("anchor_margin", ctypes.c_double)]
+                ("keep_ratio_max", ctypes.c_double), ("anchor_margin", ctypes.c_double),
+                ("summaries_bf16", ctypes.c_int32)]
 
 
 class bsa_prefill_cfg(ctypes.Structure):
@@ -132,11 +133,22 @@ def make_shape(batch, n_q_heads, n_kv_heads, head_dim, seq_len, seq_stride, summ
 
 
 def select_cfg(block_size=64, n_sink=1, n_local=2, top_k=-1, keep_ratio=0.0, adaptive=False,
-               keep_ratio_max=0.0, anchor_margin=0.0):
+               keep_ratio_max=0.0, anchor_margin=0.0, summaries_bf16=False):
     """Selection parameters; adaptive=True keeps between keep_ratio and keep_ratio_max of the
-    blocks per (b, kv head), set by the anchors' scores (lists padded with -1)."""
+    blocks per (b, kv head), set by the anchors' scores (lists padded with -1);
+    summaries_bf16 when the summaries are bf16 rather than fp32."""
     return bsa_select_cfg(block_size, n_sink, n_local, top_k, keep_ratio, int(adaptive),
-                          keep_ratio_max, anchor_margin)
+                          keep_ratio_max, anchor_margin, int(summaries_bf16))
+
+
+def _summaries_bf16(summaries):
+    """True for bf16 summaries, False for fp32 ones (a contiguous 4-d device tensor)."""
+    import torch
+    if isinstance(summaries, torch.Tensor) and summaries.dtype == torch.bfloat16:
+        _need(summaries, "summaries", torch.bfloat16, 4)
+        return True
+    _need(summaries, "summaries", torch.float32, 4)
+    return False
 
 
 COMBINE_AVERAGE, COMBINE_CONCAT = 0, 1
@@ -198,7 +210,8 @@ def update_block_summaries(x, seq_len, block_size, first_token, out_f32=None, ou
 
 def append_kv(k_new, v_new, k_cache, v_cache, seq_len, block_size=64, summaries=None):
     """Write k_new, v_new bf16 [B][Hkv][n][d] into the caches at [seq_len, seq_len + n); with
-    `summaries` (fp32 [B][Hkv][S][d]) also refresh the summaries of the blocks they land in."""
+    `summaries` (fp32 or bf16 [B][Hkv][S][d]) also refresh the summaries of the blocks they
+    land in."""
     import torch
     for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
                     ("v_cache", v_cache)):
@@ -207,30 +220,34 @@ def append_kv(k_new, v_new, k_cache, v_cache, seq_len, block_size=64, summaries=
     if tuple(v_new.shape) != (B, H, n, d) or k_cache.shape[:2] != (B, H) or \
             tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[3] != d:
         raise ValueError("append_kv: shapes do not match")
-    S = 0
+    S, s32, s16 = 0, None, None
     if summaries is not None:
-        _need(summaries, "summaries", torch.float32, 4)
+        if _summaries_bf16(summaries):
+            s16 = summaries
+        else:
+            s32 = summaries
         S = summaries.shape[2]
     shape = make_shape(B, H, H, d, seq_len, k_cache.shape[2], S)
     _check("append_kv", lib().append_kv(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
-                                        ctypes.byref(shape), n, block_size, _ptr(summaries), None,
+                                        ctypes.byref(shape), n, block_size, _ptr(s32), _ptr(s16),
                                         _stream(k_new.device)))
 
 
 def select_blocks(q, summaries, seq_len, block_size=64, n_sink=1, n_local=2, top_k=-1,
                   keep_ratio=0.0, want_scores=False, block_idx=None, workspace=None,
                   adaptive=False, keep_ratio_max=0.0, anchor_margin=0.0):
-    """q bf16 [B][Hq][d], summaries fp32 [B][Hkv][nb][d] -> (idx int32 [B][Hkv][n_keep], scores)."""
+    """q bf16 [B][Hq][d], summaries fp32 or bf16 [B][Hkv][nb][d] -> (idx int32
+    [B][Hkv][n_keep], scores)."""
     import torch
     _need(q, "q", torch.bfloat16, 3)
-    _need(summaries, "summaries", torch.float32, 4)
+    sb = _summaries_bf16(summaries)
     B, Hq, d = q.shape
     Hkv, S = summaries.shape[1], summaries.shape[2]
     nb = num_blocks(seq_len, block_size)
     if S < nb:
         raise ValueError(f"summaries hold {S} blocks, {nb} are in use")
     cfg = select_cfg(block_size, n_sink, n_local, top_k, keep_ratio, adaptive, keep_ratio_max,
-                     anchor_margin)
+                     anchor_margin, summaries_bf16=sb)
     n_keep = num_kept(nb, cfg)
     if n_keep < 0:
         raise ValueError("invalid selection config")
@@ -262,7 +279,7 @@ def sparse_decode_step(q, k, v, summaries, seq_len, block_size=64, n_sink=1, n_l
     _need(q, "q", torch.bfloat16, 3)
     _need(k, "k", torch.bfloat16, 4)
     _need(v, "v", torch.bfloat16, 4)
-    _need(summaries, "summaries", torch.float32, 4)
+    sb = _summaries_bf16(summaries)
     B, Hq, d = q.shape
     Hkv, stride = k.shape[1], k.shape[2]
     S = summaries.shape[2]
@@ -271,7 +288,7 @@ def sparse_decode_step(q, k, v, summaries, seq_len, block_size=64, n_sink=1, n_l
     nb = num_blocks(seq_len, block_size)
     if S < nb:
         raise ValueError(f"summaries hold {S} blocks, {nb} are in use")
-    cfg = select_cfg(block_size, n_sink, n_local, top_k, keep_ratio)
+    cfg = select_cfg(block_size, n_sink, n_local, top_k, keep_ratio, summaries_bf16=sb)
     n_keep = num_kept(nb, cfg)
     if n_keep < 1:
         raise ValueError("invalid selection config")
@@ -570,7 +587,7 @@ def decode_loop_step(q, k_new, v_new, k_cache, v_cache, summaries, seq_len, bloc
                      n_sink=1, n_local=2, top_k=-1, keep_ratio=0.0, scale=0.0, block_idx=None,
                      out=None, lse=None, sel_workspace=None, dec_workspace=None):
     """One generated token: append its K/V at seq_len, refresh the summary of the block it
-    lands in (or opens), select, attend over seq_len + n tokens.  summaries fp32
+    lands in (or opens), select, attend over seq_len + n tokens.  summaries fp32 or bf16
     [B][Hkv][S][d] with S >= ceil(capacity / block_size).  Returns (out, lse, idx)."""
     n = k_new.shape[2]
     append_kv(k_new, v_new, k_cache, v_cache, seq_len, block_size, summaries)

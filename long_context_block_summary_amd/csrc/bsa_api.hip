@@ -46,6 +46,7 @@ int middle_k(int nb, const bsa_select_cfg* cfg, int n_cand) {
 
 bool select_cfg_ok(const bsa_select_cfg* c) {
   if (!c || c->block_size < 1 || c->n_sink_blocks < 0 || c->n_local_blocks < 0) return false;
+  if (c->summaries_bf16 != 0 && c->summaries_bf16 != 1) return false;
   if (c->adaptive) {
     return c->adaptive == 1 && c->keep_ratio >= 0.0 && c->keep_ratio <= c->keep_ratio_max &&
            c->keep_ratio_max <= 1.0 && std::isfinite((float)c->anchor_margin);
@@ -203,7 +204,7 @@ int append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache
   return launch_status();
 }
 
-int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
+int select_blocks(const void* q, const void* summaries, const bsa_shape* shape,
                   const bsa_select_cfg* cfg, int32_t* block_idx, float* scores_out,
                   void* workspace, size_t ws_bytes, void* hip_stream) {
   if (!q || !summaries || !block_idx || !shape_ok(shape) || !select_cfg_ok(cfg) ||
@@ -230,8 +231,9 @@ int select_blocks(const void* q, const float* summaries, const bsa_shape* shape,
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   // the adaptive threshold needs the anchors' scores too: score every block
   const int s0 = cfg->adaptive ? 0 : c0, s1 = cfg->adaptive ? nb : c1;
-  bsa::launch_scores(static_cast<const uint16_t*>(q), summaries, shape->batch, shape->n_q_heads,
-                     shape->n_kv_heads, shape->head_dim, nb, ss, s0, s1, scores, st);
+  bsa::launch_scores(static_cast<const uint16_t*>(q), summaries, cfg->summaries_bf16 != 0,
+                     shape->batch, shape->n_q_heads, shape->n_kv_heads, shape->head_dim, nb, ss,
+                     s0, s1, scores, st);
   bsa::launch_topk(scores, (int64_t)shape->batch * shape->n_kv_heads, nb, c0, c1, k, n_keep,
                    block_idx, st, cfg->adaptive != 0, k_lo, k_hi, (float)cfg->anchor_margin);
   return launch_status();
@@ -241,7 +243,7 @@ static int decode_checks(const bsa_shape* shape, int32_t n_keep, int32_t block_s
                          int32_t n_splits, const void* workspace, size_t ws_bytes,
                          bsa::DecodePlan* plan, int elem_bytes = 2);
 
-int sparse_decode_step(const void* q, const void* k, const void* v, const float* summaries,
+int sparse_decode_step(const void* q, const void* k, const void* v, const void* summaries,
                        const bsa_shape* shape, const bsa_select_cfg* cfg, int32_t* block_idx,
                        float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
                        void* hip_stream) {
@@ -275,8 +277,8 @@ int sparse_decode_step(const void* q, const void* k, const void* v, const float*
   const auto* kb = static_cast<const uint16_t*>(k);
   const auto* vb = static_cast<const uint16_t*>(v);
   if (c1 > c0)
-    bsa::launch_scores(qb, summaries, shape->batch, shape->n_q_heads, shape->n_kv_heads,
-                       shape->head_dim, nb, ss, c0, c1, scores, st);
+    bsa::launch_scores(qb, summaries, cfg->summaries_bf16 != 0, shape->batch, shape->n_q_heads,
+                       shape->n_kv_heads, shape->head_dim, nb, ss, c0, c1, scores, st);
   if (bsa::decode_select_fusable(shape->head_dim, plan.g, c1 - c0, n_keep)) {
     bsa::launch_decode_select_partials(qb, kb, vb, scores, nb, c0, c1, top_k, block_idx, n_keep,
                                        shape->batch, shape->n_q_heads, shape->n_kv_heads,

@@ -27,9 +27,9 @@ void launch_quantize_fp8(const uint16_t* x, uint8_t* out, float* scales, int64_t
                          int stride, int d, int bs, int sstride, hipStream_t st);
 
 // candidate scores s[pair][j] = qbar . summary_j for j in [c0, c1); summaries
-// rows are sstride blocks apart, scores rows nb apart
-void launch_scores(const uint16_t* q, const float* summ, int B, int Hq, int Hkv, int d, int nb,
-                   int sstride, int c0, int c1, float* scores, hipStream_t st);
+// (fp32, or bf16 when summ_bf16) rows are sstride blocks apart, scores rows nb apart
+void launch_scores(const uint16_t* q, const void* summ, bool summ_bf16, int B, int Hq, int Hkv,
+                   int d, int nb, int sstride, int c0, int c1, float* scores, hipStream_t st);
 
 // per pair: sink [0,c0) + top-k of scores[c0,c1) + local [c1,nb), ascending.
 // adaptive: k per pair from the anchors' scores, clamped to [k_lo, k_hi], the

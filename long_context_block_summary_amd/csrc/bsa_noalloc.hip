@@ -41,7 +41,7 @@ int scratch_address(void** out) {
 }  // namespace
 
 extern "C" int sparse_decode_step_noalloc(const void* q, const void* k, const void* v,
-                                          const float* summaries, const bsa_shape* shape,
+                                          const void* summaries, const bsa_shape* shape,
                                           const bsa_select_cfg* cfg, int32_t* block_idx,
                                           float scale, float* out, float* lse,
                                           void* hip_stream) {

@@ -6,6 +6,8 @@
 // 稀疏注意力与 KV Cache 压缩的工程实现; mean pooling per "CSA + HCA
 // 混合注意力机制" §4.1).  Scoring and top-k follow §4.4 steps 1-3 of that
 // page: every block gets a score, the highest-scoring ones are kept.
+#include <type_traits>
+
 #include "bsa_device.h"
 #include "bsa_launch.h"
 #include "topk_device.h"
@@ -251,28 +253,38 @@ void launch_append(const uint16_t* src, uint16_t* dst, int64_t pairs, int n_new,
 constexpr int SCORE_ROWS_PER_WG = 128;
 constexpr int SCORE_QH = 16;  // query heads staged in LDS at a time
 
-template <int D>
+template <int D, bool BF>
 __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict__ q,
-                                                     const float* __restrict__ summ, int Hq,
+                                                     const void* __restrict__ summ_v, int Hq,
                                                      int Hkv, int nb, int sstride, int c0, int c1,
                                                      float* __restrict__ scores) {
-  constexpr int PER = D / 16;                       // floats of a row per lane
+  constexpr int PER = D / 16;                       // values of a row per lane
   constexpr int PASSES = SCORE_ROWS_PER_WG / 16;    // 16 rows per pass of 256 threads
   const int pair = blockIdx.y;
   const int b = pair / Hkv, kvh = pair % Hkv, g = Hq / Hkv;
   const int tid = threadIdx.x, l16 = tid & 15;
   const int r0 = c0 + blockIdx.x * SCORE_ROWS_PER_WG;
   const int r1 = min(c1, r0 + SCORE_ROWS_PER_WG);
-  const float* base = summ + (int64_t)pair * sstride * D + l16 * PER;
   // every summary load is in flight before the query is read (rows past r1
-  // re-read row r1 - 1 and are not stored)
-  float4 w[PASSES][PER / 4];
+  // re-read row r1 - 1 and are not stored); fp32 rows as float4s, bf16 rows
+  // as PER 2-byte values in one 16- or 8-byte load
+  using BfPiece = typename std::conditional<PER == 8, uint4, uint2>::type;
+  float4 w[PASSES][PER / 4];  // fp32 rows
+  BfPiece wb[PASSES];         // bf16 rows
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int r = min(r0 + (tid >> 4) + 16 * p, r1 - 1);
+    if constexpr (BF) {
+      const uint16_t* base = static_cast<const uint16_t*>(summ_v) + (int64_t)pair * sstride * D +
+                             l16 * PER;
+      wb[p] = ld_stream(reinterpret_cast<const BfPiece*>(base + (int64_t)r * D));
+    } else {
+      const float* base = static_cast<const float*>(summ_v) + (int64_t)pair * sstride * D +
+                          l16 * PER;
 #pragma unroll
-    for (int c = 0; c < PER / 4; ++c)
-      w[p][c] = ld_stream(reinterpret_cast<const float4*>(base + (int64_t)r * D) + c);
+      for (int c = 0; c < PER / 4; ++c)
+        w[p][c] = ld_stream(reinterpret_cast<const float4*>(base + (int64_t)r * D) + c);
+    }
   }
   // pooled query over the g heads of the group, this lane's PER dims: up to
   // SCORE_QH heads at a time are read with one 16-byte load per thread into
@@ -305,29 +317,45 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
   }
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
+    float x[PER];
+    if constexpr (BF) {
+      const uint32_t* u = reinterpret_cast<const uint32_t*>(&wb[p]);
+#pragma unroll
+      for (int c = 0; c < PER / 2; ++c) {
+        x[2 * c] = bf_lo(u[c]);
+        x[2 * c + 1] = bf_hi(u[c]);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < PER / 4; ++c) {
+        x[4 * c] = w[p][c].x;
+        x[4 * c + 1] = w[p][c].y;
+        x[4 * c + 2] = w[p][c].z;
+        x[4 * c + 3] = w[p][c].w;
+      }
+    }
     float sc = 0.f;
 #pragma unroll
-    for (int c = 0; c < PER / 4; ++c) {
-      sc = fmaf(qv[4 * c + 0], w[p][c].x, sc);
-      sc = fmaf(qv[4 * c + 1], w[p][c].y, sc);
-      sc = fmaf(qv[4 * c + 2], w[p][c].z, sc);
-      sc = fmaf(qv[4 * c + 3], w[p][c].w, sc);
-    }
+    for (int c = 0; c < PER; ++c) sc = fmaf(qv[c], x[c], sc);
     sc = row16_sum(sc);
     const int r = r0 + (tid >> 4) + 16 * p;
     if (l16 == 0 && r < r1) scores[(int64_t)pair * nb + r] = sc;
   }
 }
 
-void launch_scores(const uint16_t* q, const float* summ, int B, int Hq, int Hkv, int d, int nb,
-                   int sstride, int c0, int c1, float* scores, hipStream_t st) {
+void launch_scores(const uint16_t* q, const void* summ, bool summ_bf16, int B, int Hq, int Hkv,
+                   int d, int nb, int sstride, int c0, int c1, float* scores, hipStream_t st) {
   const int n = c1 - c0;
   if (n <= 0) return;
   dim3 grid((n + SCORE_ROWS_PER_WG - 1) / SCORE_ROWS_PER_WG, B * Hkv);
-  if (d == 128)
-    scores_kernel<128><<<grid, 256, 0, st>>>(q, summ, Hq, Hkv, nb, sstride, c0, c1, scores);
-  else
-    scores_kernel<64><<<grid, 256, 0, st>>>(q, summ, Hq, Hkv, nb, sstride, c0, c1, scores);
+#define BSA_SCORES(DD, BB)                                                                \
+  scores_kernel<DD, BB><<<grid, 256, 0, st>>>(q, summ, Hq, Hkv, nb, sstride, c0, c1, scores)
+  if (d == 128) {
+    if (summ_bf16) BSA_SCORES(128, true); else BSA_SCORES(128, false);
+  } else {
+    if (summ_bf16) BSA_SCORES(64, true); else BSA_SCORES(64, false);
+  }
+#undef BSA_SCORES
 }
 
 // ---------------------------------------------------------------------------

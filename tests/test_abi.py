@@ -158,6 +158,20 @@ def test_decode_step_checks_arguments(L):
     assert S(*args(cfg=adaptive)) == -2
 
 
+def test_select_cfg_summary_type_checked(L):
+    """bsa_select_cfg.summaries_bf16 takes 0 (fp32 summaries) or 1 (bf16); anything else is
+    an invalid config, refused before any launch."""
+    fake = ctypes.c_void_p(0x1000)
+    sh = bsa.make_shape(1, 8, 2, 128, 4096, 4096)
+    for flag, want in ((0, 67), (1, 67), (2, -1), (-1, -1)):
+        cfg = bsa.select_cfg(top_k=64)
+        cfg.summaries_bf16 = flag
+        assert L.bsa_num_kept(200, ctypes.byref(cfg)) == want
+        if want < 0:
+            assert L.select_blocks(fake, fake, ctypes.byref(sh), ctypes.byref(cfg), fake, None,
+                                   fake, 1 << 20, None) == -1
+
+
 def test_prefill_argument_checks_launch_nothing(L):
     fake = ctypes.c_void_p(0x1000)
     pc = bsa.prefill_cfg()

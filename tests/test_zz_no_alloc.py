@@ -36,10 +36,11 @@ def L():
     return lib
 
 
-def _inputs(cfg, seed):
+def _inputs(cfg, seed, bf16=False):
     t = synth.gen_decode(cfg, seed)
     q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
-    summ, _ = bsa.build_block_summaries(k, cfg.seq_len, 64)
+    s32, s16 = bsa.build_block_summaries(k, cfg.seq_len, 64, want_f32=not bf16, want_bf16=bf16)
+    summ = s16 if bf16 else s32
     return q, k, v, summ
 
 
@@ -48,7 +49,8 @@ def _noalloc(L, q, k, v, summ, cfg):
     B, Hq, d = q.shape
     Hkv, stride = k.shape[1], k.shape[2]
     nb = bsa.num_blocks(cfg.seq_len, 64)
-    sc = bsa.select_cfg(64, cfg.n_sink, cfg.n_local, cfg.top_k, cfg.keep_ratio)
+    sc = bsa.select_cfg(64, cfg.n_sink, cfg.n_local, cfg.top_k, cfg.keep_ratio,
+                        summaries_bf16=summ.dtype == torch.bfloat16)
     n_keep = bsa.num_kept(nb, sc)
     shape = bsa.make_shape(B, Hq, Hkv, d, cfg.seq_len, stride, summ.shape[2])
     idx = torch.full((B, Hkv, n_keep), -5, dtype=torch.int32, device=q.device)
@@ -61,11 +63,12 @@ def _noalloc(L, q, k, v, summ, cfg):
     return out, lse, idx
 
 
-def _compare(L, cfg, seed):
+def _compare(L, cfg, seed, bf16=False):
     import torch
     announce(cfg.name, "seed", seed, "B", cfg.batch, "Hq", cfg.n_q_heads, "Hkv", cfg.n_kv_heads,
-             "N", cfg.seq_len, "top_k", cfg.top_k, "keep_ratio", cfg.keep_ratio)
-    q, k, v, summ = _inputs(cfg, seed)
+             "N", cfg.seq_len, "top_k", cfg.top_k, "keep_ratio", cfg.keep_ratio,
+             "bf16 summaries", bf16)
+    q, k, v, summ = _inputs(cfg, seed, bf16)
     o1, l1, i1 = _noalloc(L, q, k, v, summ, cfg)
     o2, l2, i2 = bsa.sparse_decode_step(q, k, v, summ, cfg.seq_len, 64, cfg.n_sink, cfg.n_local,
                                         cfg.top_k, cfg.keep_ratio)
@@ -87,6 +90,11 @@ def test_noalloc_step_unfused_selection_and_limit(L):
     _compare(L, synth.DecodeConfig("noalloc_unfused", 1, 16, 2, 128, 64 * 5000, top_k=400), 8)
     _compare(L, synth.DecodeConfig("noalloc_keep_ratio", 1, 8, 8, 64, 64 * 40, keep_ratio=0.35),
              9)
+    # on bf16 summaries, fused and unfused
+    _compare(L, synth.DecodeConfig("noalloc_bf16", 2, 16, 4, 128, 64 * 90 + 17, top_k=9), 10,
+             bf16=True)
+    _compare(L, synth.DecodeConfig("noalloc_bf16_unfused", 1, 16, 2, 128, 64 * 5000, top_k=400),
+             11, bf16=True)
     # a step whose workspace would exceed the static scratch is refused before any launch
     fake = ctypes.c_void_p(0x1000)
     big = bsa.make_shape(256, 64, 8, 128, 131072, 131072)
