@@ -5,8 +5,11 @@ temporary directory; the pin suite then runs against it in a subprocess and
 must fail.  Nothing here touches a GPU.
 """
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
@@ -96,24 +99,6 @@ MUTANTS = [
 ]
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_mutant(tmp_path, name, old, new):
-    src = open(SRC).read()
-    assert src.count(old) >= 1, f"mutation anchor missing: {old!r}"
-    mutated = src.replace(old, new, 1)
-    cfile = tmp_path / "oracle.c"
-    cfile.write_text(mutated)
-    (tmp_path / "oracle.h").write_text(open(os.path.join(ROOT, "oracle", "oracle.h")).read())
-    lib = tmp_path / "liboracle_mut.so"
-    subprocess.run(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
-                    str(cfile), "-o", str(lib), "-lm"], check=True)
-    env = dict(os.environ, BSA_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
-                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    assert r.returncode != 0, f"pins did not catch mutant '{name}'\n{r.stdout[-2000:]}"
-
-
 # mutants the randomised properties (test_oracle_properties.py) must catch on their own
 PROPERTY_MUTANTS = ["mean divides by block size", "score sign", "tie-break reversed",
                     "group drops heads", "no 1/sqrt(d) scale", "K and V swapped",
@@ -121,20 +106,62 @@ PROPERTY_MUTANTS = ["mean divides by block size", "score sign", "tie-break rever
                     "weights not normalised", "indexer scores the exact means",
                     "indexer rounds the exact mean", "indexer keys are the unrounded fp32 means"]
 
+SUITES = {"pins": "test_oracle_pins.py", "properties": "test_oracle_properties.py"}
 
-@pytest.mark.parametrize("name", PROPERTY_MUTANTS)
-def test_properties_catch_mutant(tmp_path, name):
+
+def run_mutant(suite, name, workdir):
+    """Build oracle.c with mutant `name` in `workdir` and run the `suite` against it in a
+    subprocess; returns (return code, the end of its output)."""
     old, new = next((o, n) for m, o, n in MUTANTS if m == name)
     src = open(SRC).read()
     assert src.count(old) >= 1, f"mutation anchor missing: {old!r}"
-    cfile = tmp_path / "oracle.c"
-    cfile.write_text(src.replace(old, new, 1))
-    (tmp_path / "oracle.h").write_text(open(os.path.join(ROOT, "oracle", "oracle.h")).read())
-    lib = tmp_path / "liboracle_mut.so"
+    cfile = os.path.join(workdir, "oracle.c")
+    with open(cfile, "w") as f:
+        f.write(src.replace(old, new, 1))
+    with open(os.path.join(workdir, "oracle.h"), "w") as f:
+        f.write(open(os.path.join(ROOT, "oracle", "oracle.h")).read())
+    lib = os.path.join(workdir, "liboracle_mut.so")
     subprocess.run(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
-                    str(cfile), "-o", str(lib), "-lm"], check=True)
-    env = dict(os.environ, BSA_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+                    cfile, "-o", lib, "-lm"], check=True)
+    env = dict(os.environ, BSA_ORACLE_LIB=lib, OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_properties.py")],
+                        os.path.join(ROOT, "tests", SUITES[suite])],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    assert r.returncode != 0, f"properties did not catch mutant '{name}'\n{r.stdout[-2000:]}"
+    return r.returncode, r.stdout[-2000:]
+
+
+_ALL = None
+
+
+def result(suite, name, tmp_path):
+    """The mutant's run.  In a serial session every mutant's run is started on first use,
+    several at a time (each is its own process); under pytest-xdist each test runs its own."""
+    global _ALL
+    if os.environ.get("PYTEST_XDIST_WORKER"):
+        return run_mutant(suite, name, str(tmp_path))
+    if _ALL is None:
+        jobs = [("pins", m[0]) for m in MUTANTS] + [("properties", m) for m in PROPERTY_MUTANTS]
+        base = tempfile.mkdtemp(prefix="oracle_mutants_")
+        dirs = {}
+        for i, job in enumerate(jobs):
+            dirs[job] = os.path.join(base, str(i))
+            os.makedirs(dirs[job])
+        try:
+            with ThreadPoolExecutor(max_workers=max(1, min(6, (os.cpu_count() or 2) - 1))) as ex:
+                futs = {job: ex.submit(run_mutant, job[0], job[1], dirs[job]) for job in jobs}
+                _ALL = {job: f.result() for job, f in futs.items()}
+        finally:
+            shutil.rmtree(base, ignore_errors=True)
+    return _ALL[(suite, name)]
+
+
+@pytest.mark.parametrize("name", [m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name):
+    rc, out = result("pins", name, tmp_path)
+    assert rc != 0, f"pins did not catch mutant '{name}'\n{out}"
+
+
+@pytest.mark.parametrize("name", PROPERTY_MUTANTS)
+def test_properties_catch_mutant(tmp_path, name):
+    rc, out = result("properties", name, tmp_path)
+    assert rc != 0, f"properties did not catch mutant '{name}'\n{out}"
