@@ -9,8 +9,8 @@ sets by the near-tie rule, outputs within 2e-3), then requires the fused step to
 give the same list and outputs bit for bit.  16 more draws run the FP8 cache:
 the GPU quantizer against the oracle's codes and scales bit for bit, then the FP8
 attention (a quarter of them over adaptive, -1-padded lists) within 2e-3, and 16
-random anchor-adaptive selections are checked against the oracle's rule and 8
-random decode loops step by step.  Every case prints its parameters before any
+random anchor-adaptive selections are checked against the oracle's rule, 8
+random decode loops step by step, and 8 long-context cases (20,000-200,000 tokens).  Every case prints its parameters before any
 GPU call.
 """
 import math
@@ -153,3 +153,22 @@ def test_random_decode_loop_shapes(i):
              top_k=-1 if ratio else int(rng.integers(1, 40)),
              keep_ratio=float(rng.choice([0.1, 0.2, 0.3])) if ratio else 0.0,
              check_every=max(1, steps // 20))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_long_decode_shapes(i):
+    """Seeded random decode at long contexts (20,000 to 200,000 tokens log-uniform, 1-4 kv
+    heads, groups 1-16, top-k up to 2,000 or a keep ratio, explicit split counts)."""
+    rng = np.random.default_rng(77000 + i)
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    hkv = int(rng.choice([1, 2, 4]))
+    ratio = bool(rng.integers(0, 2))
+    cfg = synth.DecodeConfig(
+        name=f"long_rand{i}", batch=int(rng.integers(1, 3)), n_q_heads=hkv * g, n_kv_heads=hkv,
+        head_dim=int(rng.choice([64, 128])),
+        seq_len=int(math.exp(rng.uniform(math.log(20000), math.log(200000)))),
+        n_sink=int(rng.integers(0, 3)), n_local=int(rng.integers(1, 4)),
+        top_k=-1 if ratio else int(rng.integers(1, 2000)),
+        keep_ratio=float(rng.choice([0.05, 0.1, 0.15, 0.2])) if ratio else 0.0,
+        planted=bool(rng.integers(0, 2)))
+    run_decode_case(cfg, int(rng.integers(0, 10**6)), n_splits=int(rng.choice([0, 0, 2, 5])))

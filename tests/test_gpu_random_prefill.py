@@ -7,7 +7,8 @@ sink logits (every third case selects with the fp32-means indexer, the others
 with the bf16 compressed keys); each case checks the tile selections (near-tie rule) and the
 outputs and per-branch lse against the oracle evaluated on the GPU's selection,
 as the fixed-shape tests do (every row for chunks up to 128 queries, 40 sampled
-rows beyond).  Every case prints its parameters before any GPU call.
+rows beyond).  8 more cases draw longer chunks in tiles of 16-64 queries (up to 57
+tiles).  Every case prints its parameters before any GPU call.
 """
 import math
 
@@ -53,3 +54,26 @@ def test_random_prefill_shapes(i):
     cfg, seed, combine, sink, rows = draw_case(i)
     indexer = bsa.INDEXER_F32 if i % 3 == 2 else bsa.INDEXER_BF16
     run_prefill_case(cfg, seed, rows=rows, combine=combine, sink=sink, indexer=indexer)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_prefill_many_tiles(i):
+    """Seeded random prefill with longer chunks (100-900 queries) in tiles of 16, 32 or 64
+    queries (up to 57 tiles: three or four blocks of 16 tiles in the scores kernels), priors
+    of 1,000-120,000 tokens, top-k up to 3,000, either indexer and combine mode; 24 sampled
+    rows."""
+    rng = np.random.default_rng(78000 + i)
+    hkv, g = int(rng.choice([1, 2])), int(rng.choice([1, 2, 4]))
+    qt = int(rng.choice([16, 32, 64]))
+    while qt * g not in (64, 128, 256):
+        qt *= 2
+    C = int(rng.integers(100, 900))
+    cfg = synth.PrefillConfig(
+        name=f"pf_tiles_rand{i}", batch=1, n_q_heads=hkv * g, n_kv_heads=hkv, head_dim=128,
+        prior_len=int(rng.integers(1000, 120000)), chunk_len=C, q_tile=qt,
+        m_sparse=int(rng.choice([4, 8])), top_k_sparse=int(rng.integers(1, 3000)),
+        m_dense=int(rng.choice([64, 128])), window=int(rng.integers(1, 300)),
+        planted=bool(rng.integers(0, 2)))
+    rows = np.sort(rng.choice(C, 24, replace=False)).tolist()
+    run_prefill_case(cfg, int(rng.integers(0, 10**6)), rows=rows,
+                     combine=int(rng.integers(0, 2)), indexer=int(rng.integers(0, 2)))
