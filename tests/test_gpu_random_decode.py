@@ -8,10 +8,10 @@ against the oracle as the fixed-shape tests do (fp32 summaries bit for bit, inde
 sets by the near-tie rule, outputs within 2e-3), then requires the fused step to
 give the same list and outputs bit for bit.  16 more draws run the FP8 cache:
 the GPU quantizer against the oracle's codes and scales bit for bit, then the FP8
-attention (a quarter of them over adaptive, -1-padded lists) within 2e-3, and 16
-random anchor-adaptive selections are checked against the oracle's rule, 8
-random decode loops step by step, and 8 long-context cases (20,000-200,000 tokens).  Every case prints its parameters before any
-GPU call.
+attention (a quarter of them over adaptive, -1-padded lists) within 2e-3.  16
+random anchor-adaptive selections are checked against the oracle's rule, 8 random
+decode loops step by step, and 8 long-context cases (20,000 to 200,000 tokens).
+Every case prints its parameters before any GPU call.
 """
 import math
 
