@@ -132,7 +132,27 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30, inputs=None):
                                                            n_keep)),
                          dtype=torch.uint8, device=dev)
 
+    ws_step = torch.empty(bsa.decode_step_workspace_size(cfg.batch, cfg.n_q_heads,
+                                                          cfg.n_kv_heads, cfg.head_dim, N, bs,
+                                                          cfg.n_sink, cfg.n_local, cfg.top_k,
+                                                          cfg.keep_ratio),
+                          dtype=torch.uint8, device=dev)
+
+    def one_call(e0=None, e2=None):
+        """the step as one sparse_decode_step call (S2-S5; S3 and S5 inside the attention
+        launch where the candidate count allows)"""
+        st = torch.cuda.current_stream(dev)
+        if e0 is not None:
+            e0.record(st)
+        bsa.sparse_decode_step(q, k, v, summ, N, bs, cfg.n_sink, cfg.n_local, cfg.top_k,
+                               cfg.keep_ratio, block_idx=idx, out=out, lse=lse,
+                               workspace=ws_step)
+        if e2 is not None:
+            e2.record(st)
+
     def step(e0=None, e1=None, e2=None, e3=None):
+        """the step as its two calls, select_blocks then sparse_decode_attn (or the latter's
+        two steps S4 and S5 as calls of their own)"""
         st = torch.cuda.current_stream(dev)
         if e0 is not None:
             e0.record(st)
@@ -154,17 +174,26 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30, inputs=None):
     for _ in range(warmup):
         flush.add_(1.0)
         step()
-    # headline: events at the step boundaries only (a timing event between the two calls
-    # costs the GPU a few microseconds of idle time)
+        flush.add_(1.0)
+        one_call()
+    # headline: the one-call step, events at the step boundaries only
     events = [(ev(), ev()) for _ in range(steps)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for e0, e2 in events:
         flush.add_(1.0)
-        step(e0=e0, e2=e2)
+        one_call(e0=e0, e2=e2)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     step_ms = [a.elapsed_time(b) for a, b in events]
+    # the same step as the two calls (a timing event between them would cost the GPU a
+    # few microseconds of idle time, so again only at the step boundaries)
+    tevents = [(ev(), ev()) for _ in range(steps)]
+    for e0, e2 in tevents:
+        flush.add_(1.0)
+        step(e0=e0, e2=e2)
+    torch.cuda.synchronize()
+    two_ms = [a.elapsed_time(b) for a, b in tevents]
 
     # per-call breakdown (separate passes with events between the calls): select + the
     # attention call; select + its two steps S4 and S5 as separate calls
@@ -190,10 +219,10 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30, inputs=None):
         side = torch.cuda.Stream(dev)
         side.wait_stream(stream)
         with torch.cuda.stream(side):
-            step()  # warm the side stream once outside capture
+            one_call()  # warm the side stream once outside capture
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=side):
-            step()
+            one_call()
         torch.cuda.synchronize()
         gevents = [(ev(), ev()) for _ in range(steps)]
         for e0, e1 in gevents:
@@ -211,7 +240,7 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30, inputs=None):
     torch.cuda.synchronize()
     we = [(ev(), ev()) for _ in range(steps)]
     for e0, e2 in we:
-        step(e0=e0, e2=e2)
+        one_call(e0=e0, e2=e2)
     torch.cuda.synchronize()
     warm_ms = [a.elapsed_time(b) for a, b in we]
     return {
@@ -223,6 +252,8 @@ def run_gpu(cfg, steps, warmup, flush_bytes=1 << 30, inputs=None):
         "s5_ms": sum(s5_ms) / len(s5_ms),
         "step_ms": sum(step_ms) / len(step_ms),
         "step_pct": pct(step_ms),
+        "two_call_ms": sum(two_ms) / len(two_ms),
+        "two_call_pct": pct(two_ms),
         "graph_ms": graph_ms,
         "warm_step_ms": sum(warm_ms) / len(warm_ms),
         "wall_s": wall,
@@ -332,43 +363,6 @@ def run_fp8(cfg, steps, warmup, t, flush_bytes=1 << 30):
             "timed": "select_blocks + sparse_decode_attn_fp8, cold cache"}
 
 
-def run_fused_step(cfg, steps, warmup, t, flush_bytes=1 << 30):
-    """The same decode step as one sparse_decode_step call (block scores, then the top-k
-    done by every attention workgroup for its own pair inside the attention launch, then
-    the merge); block_idx and outputs equal the two calls' bit for bit."""
-    import numpy as np
-    import torch
-
-    import long_context_block_summary_amd as bsa
-
-    dev = torch.device("cuda:0")
-    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-    q, k, v = to(t["q"]), to(t["k"]), to(t["v"])
-    N, bs = cfg.seq_len, cfg.block_size
-    stream = torch.cuda.current_stream(dev)
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    summ, _ = bsa.build_block_summaries(k, N, bs)
-    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev)
-    out, lse, idx = bsa.sparse_decode_step(q, k, v, summ, N, bs, cfg.n_sink, cfg.n_local,
-                                           cfg.top_k, cfg.keep_ratio)
-    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
-    step_ms = []
-    for i in range(warmup + steps):
-        flush.add_(1.0)
-        a, c = ev(), ev()
-        a.record(stream)
-        bsa.sparse_decode_step(q, k, v, summ, N, bs, cfg.n_sink, cfg.n_local, cfg.top_k,
-                               cfg.keep_ratio, block_idx=idx, out=out, lse=lse, workspace=ws)
-        c.record(stream)
-        torch.cuda.synchronize()
-        if i >= warmup:
-            step_ms.append(a.elapsed_time(c))
-    ms = sum(step_ms) / len(step_ms)
-    return {"workload": cfg.name, "ms_per_step": ms,
-            "queries_heads_per_s": cfg.batch * cfg.n_q_heads / (ms / 1e3), **pct(step_ms),
-            "timed": "sparse_decode_step (select fused into the attention launch), cold cache"}
-
-
 def run_bf16_summaries(cfg, steps, warmup, t, flush_bytes=1 << 30):
     """The decode step on bf16 block summaries (half the bytes the scores read): select_blocks
     alone, select + attend as two calls, and the fused sparse_decode_step, cold cache."""
@@ -414,7 +408,7 @@ def run_bf16_summaries(cfg, steps, warmup, t, flush_bytes=1 << 30):
             if i >= warmup:
                 ts.append(a.elapsed_time(c) * 1e3)
         res[name + "_us"] = sum(ts) / len(ts)
-    res["queries_heads_per_s"] = cfg.batch * cfg.n_q_heads / (res["step_us"] / 1e6)
+    res["queries_heads_per_s"] = cfg.batch * cfg.n_q_heads / (res["fused_step_us"] / 1e6)
     res["timed"] = "bf16 summaries (bsa_select_cfg.summaries_bf16), cold cache"
     return res
 
@@ -455,8 +449,8 @@ def run_decode_loop(cfg, steps, warmup, t, flush_bytes=1 << 30):
     ms = sum(ts) / len(ts)
     return {"workload": cfg.name, "ms_per_token": ms,
             "queries_heads_per_s": cfg.batch * cfg.n_q_heads / (ms / 1e3), **pct(ts),
-            "timed": "decode_loop_step: append_kv (with the summary refresh) + select_blocks + "
-                     "sparse_decode_attn per generated token, cold cache, "
+            "timed": "decode_loop_step: append_kv (with the summary refresh) + "
+                     "sparse_decode_step per generated token, cold cache, "
                      f"context {n0 + warmup}..{N}"}
 
 
@@ -776,6 +770,13 @@ def main():
                    "n_sink_blocks": cfg.n_sink, "n_local_blocks": cfg.n_local,
                    "top_k": cfg.top_k, "n_keep": r["n_keep"],
                    "keep_pct": round(100.0 * r["n_keep"] / -(-cfg.seq_len // cfg.block_size), 2)},
+        "step": "one sparse_decode_step call per step (block scores; the top-k inside the "
+                "split-K attention launch where the candidates fit; the exact merge), 1 GiB "
+                "cache flush before each",
+        "two_call_step": {"calls": "select_blocks + sparse_decode_attn",
+                          "ms_per_step": r["two_call_ms"],
+                          "queries_heads_per_s": qh / (r["two_call_ms"] / 1e3),
+                          **r["two_call_pct"]},
         "step_bytes": step_bytes(cfg, r["n_keep"]),
         "step_GBps": step_bytes(cfg, r["n_keep"]) / step_s / 1e9,
         "step_frac": step_bytes(cfg, r["n_keep"]) / step_s / 1e9 / HBM_PEAK_GBS,
@@ -831,7 +832,6 @@ def main():
         if name in ("tiny", "gqa32k", "long128k"):
             keep_inputs[name] = (c2, r2["inputs"])
         del r2
-    line["fused_step"] = run_fused_step(cfg, max(10, args.steps // 2), 3, r["inputs"])
     line["bf16_summaries"] = run_bf16_summaries(cfg, max(10, args.steps // 2), 3, r["inputs"])
     line["decode_loop"] = run_decode_loop(cfg, max(10, args.steps // 2), 3, r["inputs"])
     line["adaptive_selection"] = run_adaptive(cfg, max(10, args.steps // 2), 3, r["inputs"])

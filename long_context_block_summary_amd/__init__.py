@@ -312,6 +312,17 @@ def sparse_decode_step(q, k, v, summaries, seq_len, block_size=64, n_sink=1, n_l
     return out, lse, block_idx
 
 
+def decode_step_workspace_size(B, Hq, Hkv, d, seq_len, block_size=64, n_sink=1, n_local=2,
+                               top_k=-1, keep_ratio=0.0, summaries_bf16=False):
+    """Bytes of workspace sparse_decode_step needs (block scores, then split partials)."""
+    shape = make_shape(B, Hq, Hkv, d, seq_len, seq_len)
+    cfg = select_cfg(block_size, n_sink, n_local, top_k, keep_ratio, summaries_bf16=summaries_bf16)
+    n = lib().bsa_decode_step_workspace_size(ctypes.byref(shape), ctypes.byref(cfg))
+    if n == SIZE_MAX:
+        raise ValueError("invalid decode step arguments")
+    return max(int(n), 16)
+
+
 def decode_workspace_size(B, Hq, Hkv, d, seq_len, n_keep, block_size=64, n_splits=0):
     shape = make_shape(B, Hq, Hkv, d, seq_len, seq_len)
     return lib().bsa_decode_workspace_size(ctypes.byref(shape), n_keep, block_size, n_splits)
@@ -585,18 +596,16 @@ def decode_step(q, k, v, summaries, seq_len, block_size=64, n_sink=1, n_local=2,
 
 def decode_loop_step(q, k_new, v_new, k_cache, v_cache, summaries, seq_len, block_size=64,
                      n_sink=1, n_local=2, top_k=-1, keep_ratio=0.0, scale=0.0, block_idx=None,
-                     out=None, lse=None, sel_workspace=None, dec_workspace=None):
+                     out=None, lse=None, workspace=None):
     """One generated token: append its K/V at seq_len, refresh the summary of the block it
-    lands in (or opens), select, attend over seq_len + n tokens.  summaries fp32 or bf16
-    [B][Hkv][S][d] with S >= ceil(capacity / block_size).  Returns (out, lse, idx)."""
+    lands in (or opens), then select and attend over seq_len + n tokens in one
+    sparse_decode_step call.  summaries fp32 or bf16 [B][Hkv][S][d] with
+    S >= ceil(capacity / block_size).  Returns (out, lse, idx)."""
     n = k_new.shape[2]
     append_kv(k_new, v_new, k_cache, v_cache, seq_len, block_size, summaries)
-    N = seq_len + n
-    idx, _ = select_blocks(q, summaries, N, block_size, n_sink, n_local, top_k, keep_ratio,
-                           block_idx=block_idx, workspace=sel_workspace)
-    out, lse = sparse_decode_attn(q, k_cache, v_cache, idx, N, block_size, scale, out=out,
-                                  lse=lse, workspace=dec_workspace)
-    return out, lse, idx
+    return sparse_decode_step(q, k_cache, v_cache, summaries, seq_len + n, block_size, n_sink,
+                              n_local, top_k, keep_ratio, scale, block_idx=block_idx, out=out,
+                              lse=lse, workspace=workspace)
 
 
 def build_compressed_streams(k, v, prior_len, cfg=None, want_f32=None):
