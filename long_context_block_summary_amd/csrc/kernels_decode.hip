@@ -488,21 +488,24 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
   const int pair = b * Hkv + h / G, hh = h % G;
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t r0 = (int64_t)pair * S * G + hh;  // row of split s: r0 + s * G
+  const float2* ml2 = reinterpret_cast<const float2*>(part_ml);
   float ov[MERGE_CHUNK];
 #pragma unroll
   for (int i = 0; i < MERGE_CHUNK; ++i)
     ov[i] = (i < S) ? part_o[(r0 + (int64_t)i * G) * D + tid] : 0.f;
-  float M = -INFINITY;
-  for (int s2 = lane; s2 < S; s2 += 64) M = fmaxf(M, part_ml[(r0 + (int64_t)s2 * G) * 2]);
+  // the first 64 splits' (m, l) stay in registers for the weights below
+  const float2 ml0 = (lane < S) ? ml2[r0 + (int64_t)lane * G] : make_float2(-INFINITY, 0.f);
+  float M = ml0.x;
+  for (int s2 = lane + 64; s2 < S; s2 += 64) M = fmaxf(M, ml2[r0 + (int64_t)s2 * G].x);
   M = wave_max(M);
   float L = 0.f, o = 0.f;
   for (int sb = 0; sb < S; sb += 64) {
     const int s2 = sb + lane;
     float w = 0.f;
     if (s2 < S) {
-      const float ms = part_ml[(r0 + (int64_t)s2 * G) * 2];
-      w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      L = fmaf(w, part_ml[(r0 + (int64_t)s2 * G) * 2 + 1], L);
+      const float2 ml = (sb == 0) ? ml0 : ml2[r0 + (int64_t)s2 * G];
+      w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
+      L = fmaf(w, ml.y, L);
     }
     const int ns = min(64, S - sb);
     for (int cb = 0; cb < ns; cb += MERGE_CHUNK) {
