@@ -344,6 +344,18 @@ def test_full_size_1m():
     run_decode_case(synth.CONFIGS["ctx1m"], synth.DEFAULT_SEED["ctx1m"])
 
 
+def test_longest_supported_cache():
+    """The longest cache a decode call takes at d = 128: 2^24 tokens, so one kv head's rows
+    span exactly 2^32 bytes (the kernels address them by 32-bit byte offsets from the head's
+    base; one block more is BSA_UNSUPPORTED).  One kv head with 8 query heads and 262,141
+    candidates (the strided top-k beyond the register kernel's 16,384), 64 of them kept:
+    summaries bit for bit, scores, selection and attention against the oracle.  About a
+    minute, most of it generating the 8 GiB of K and V on the host."""
+    cfg = synth.scaled(synth.CONFIGS["ctx1m"], name="ctx16m", batch=1, n_q_heads=8,
+                       n_kv_heads=1, seq_len=1 << 24, top_k=64)
+    run_decode_case(cfg, 16)
+
+
 @pytest.mark.parametrize("name", ["gqa32k", "long128k", "long128k_15", "ctx1m"])
 def test_full_size_second_seed(name):
     run_decode_case(synth.CONFIGS[name], 101)
