@@ -95,3 +95,54 @@ def test_fp8_decode_adaptive_lists_and_edges():
 def test_fp8_decode_full_size_128k():
     cfg = synth.CONFIGS["long128k_15"]
     run_fp8_decode("fp8_long128k_15", synth.DEFAULT_SEED["long128k_15"], cfg)
+
+
+def test_fp8_longest_supported_cache():
+    """The longest FP8 cache a decode call takes at d = 128: 2^25 tokens, so one kv head's
+    code rows span exactly 2^32 bytes (addressed by 32-bit byte offsets from the head's
+    base).  The GPU quantizes the whole cache; the kept blocks' codes and scales equal the
+    oracle's encoding of those blocks bit for bit, the selection (524,285 candidates, the
+    strided top-k) equals the oracle's, and the attention over the GPU's codes matches the
+    oracle run on the kept blocks gathered into a compact cache (decode attention has no
+    positional mask, so only the set of kept tokens matters).  Host work: generating the
+    16 GiB of bf16 K and V."""
+    import torch
+    from parity_rules import check_index_sets
+    cfg = synth.scaled(synth.CONFIGS["ctx1m"], name="fp8_ctx32m", batch=1, n_q_heads=8,
+                       n_kv_heads=1, seq_len=1 << 25, top_k=64)
+    seed, N, bs, d = 18, cfg.seq_len, cfg.block_size, cfg.head_dim
+    announce(cfg.name, "seed", seed, "Hq", cfg.n_q_heads, "Hkv 1 d", d, "N", N, "top_k", cfg.top_k)
+    t = synth.gen_decode(cfg, seed)
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    summ, _ = bsa.build_block_summaries(k, N, bs)
+    idx, _ = bsa.select_blocks(q, summ, N, bs, cfg.n_sink, cfg.n_local, cfg.top_k)
+    k8, ks = bsa.quantize_kv_fp8(k, N, bs)
+    v8, vs = bsa.quantize_kv_fp8(v, N, bs)
+    del k, v
+    out, lse = bsa.sparse_decode_attn_fp8(q, k8, v8, ks, vs, idx, N, bs)
+    torch.cuda.synchronize()
+    g_idx = idx.cpu().numpy()
+    nb = N // bs
+    o_summ = oracle.block_summaries(t["k"], N, bs)
+    o_idx, o_scores = oracle.select_blocks(t["q"], o_summ, 1, cfg.n_sink, cfg.n_local,
+                                           cfg.top_k, 0.0)
+    assert check_index_sets(g_idx, o_idx, o_scores, nb, cfg.n_sink, cfg.n_local) == 0
+    blocks = g_idx[0, 0]
+    rows = (blocks[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
+    kc = np.ascontiguousarray(t["k"][:, :, rows])  # the kept blocks, in list order
+    vc = np.ascontiguousarray(t["v"][:, :, rows])
+    n_c = len(rows)
+    ok8, oks = oracle.quantize_fp8(kc, n_c, bs)
+    ov8, ovs = oracle.quantize_fp8(vc, n_c, bs)
+    g_k8 = k8[:, :, torch.from_numpy(rows).to(k8.device)].cpu().numpy()
+    g_v8 = v8[:, :, torch.from_numpy(rows).to(v8.device)].cpu().numpy()
+    assert np.array_equal(g_k8, ok8) and np.array_equal(g_v8, ov8), "codes"
+    bt = torch.from_numpy(blocks.astype(np.int64)).to(ks.device)
+    assert np.array_equal(ks[:, :, bt].cpu().numpy(), oks), "key scales"
+    assert np.array_equal(vs[:, :, bt].cpu().numpy(), ovs), "value scales"
+    c_idx = np.arange(len(blocks), dtype=np.int32).reshape(1, 1, -1)
+    o_out, o_lse = oracle.sparse_decode_attn_fp8(t["q"], ok8, ov8, oks, ovs, c_idx, n_c, bs)
+    err = float(np.abs(out.cpu().numpy() - o_out).max())
+    lerr = float(np.abs(lse.cpu().numpy() - o_lse).max())
+    announce("  max|out err|", err, "max|lse err|", lerr)
+    assert err <= OUT_ATOL and lerr <= 1e-3
