@@ -711,7 +711,7 @@ def host_description():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long128k_15")
     ap.add_argument("--also", default="long128k,gqa32k,ctx1m",
